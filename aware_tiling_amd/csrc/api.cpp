@@ -1,0 +1,153 @@
+// C-ABI entry points (include/aware_tiling.h): argument validation, kernel
+// selection and the HIP error translation.  No entry point allocates device
+// memory; every check happens before the first HIP call.
+#include "aware_tiling.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_hip_error[256] = "";
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+attn_status launch_status(hipError_t e) {
+  if (e == hipSuccess) {
+    g_last_hip_error[0] = '\0';
+    return ATTN_OK;
+  }
+  std::strncpy(g_last_hip_error, hipGetErrorString(e), sizeof(g_last_hip_error) - 1);
+  g_last_hip_error[sizeof(g_last_hip_error) - 1] = '\0';
+  return ATTN_ERR_LAUNCH;
+}
+
+// Shapes: bh, n >= 0; per-head element count and the grid must fit the
+// kernels' 32-bit in-head indexing.
+bool shape_ok(int64_t bh, int64_t n, int64_t d) {
+  if (bh < 0 || n < 0 || d <= 0) return false;
+  if (n > (int64_t(1) << 24)) return false;
+  if (n * d >= (int64_t(1) << 31)) return false;
+  if (bh > (int64_t(1) << 20)) return false;
+  return true;
+}
+
+bool scale_ok(float s) { return std::isfinite(s) && s > 0.0f; }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE";
+    case ATTN_ERR_LAUNCH: return "ATTN_ERR_LAUNCH";
+  }
+  return "ATTN_STATUS_UNKNOWN";
+}
+
+const char* attn_last_hip_error(void) { return g_last_hip_error; }
+
+const char* attn_version(void) { return "0.1.0"; }
+
+int64_t attn_fwd_onchip_elems(int64_t d, attn_dtype dtype) {
+  if (dtype == ATTN_BF16) return at::fused_bf16_tile_info(d).onchip;
+  if (dtype == ATTN_F32) return at::fused_f32_tile_info(d).onchip;
+  return 0;
+}
+
+int64_t attn_fwd_query_block(int64_t d, attn_dtype dtype) {
+  if (dtype == ATTN_BF16) return at::fused_bf16_tile_info(d).block_rows;
+  if (dtype == ATTN_F32) return at::fused_f32_tile_info(d).block_rows;
+  return 0;
+}
+
+attn_status attn_fwd(const void* Q, const void* K, const void* V, float* O, float* lse,
+                     int64_t bh, int64_t n, int64_t d, float scale, attn_dtype dtype,
+                     void* stream) {
+  if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  if (!shape_ok(bh, n, d) || !scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
+  if (dtype == ATTN_BF16 ? !at::fused_bf16_supported(d) : !at::fused_f32_supported(d))
+    return ATTN_ERR_UNSUPPORTED;
+  if (bh * n == 0) return ATTN_OK;
+  if (!Q || !K || !V || !O) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return ATTN_ERR_INVALID_ARG;
+  if (lse && !aligned16(lse)) return ATTN_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == ATTN_BF16)
+    return launch_status(at::launch_fwd_fused_bf16(Q, K, V, O, lse, bh, n, d, scale, s));
+  return launch_status(at::launch_fwd_fused_f32(static_cast<const float*>(Q),
+                                                static_cast<const float*>(K),
+                                                static_cast<const float*>(V), O, lse, bh, n, d,
+                                                scale, s));
+}
+
+int64_t attn_smallcache_tile(int64_t d, int64_t m_elems) {
+  if (!at::smallcache_supported(d) || m_elems >= d * d) return 0;
+  return at::smallcache_tile_for_budget(d, m_elems);
+}
+
+int64_t attn_smallcache_onchip_elems(int64_t b) { return at::smallcache_onchip_elems(b); }
+
+size_t attn_fwd_smallcache_workspace_size(int64_t bh, int64_t n, int64_t d, int64_t m_elems) {
+  if (!shape_ok(bh, n, d)) return 0;
+  const int64_t b = attn_smallcache_tile(d, m_elems);
+  if (b == 0) return 0;
+  return at::smallcache_workspace_bytes(bh, n, b);
+}
+
+attn_status attn_fwd_smallcache(const void* Q, const void* K, const void* V, float* O,
+                                float* lse, int64_t bh, int64_t n, int64_t d, float scale,
+                                attn_dtype dtype, int64_t m_elems, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (!shape_ok(bh, n, d) || !scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
+  if (!at::smallcache_supported(d)) return ATTN_ERR_UNSUPPORTED;
+  if (m_elems <= 0 || m_elems >= d * d) return ATTN_ERR_INVALID_ARG;
+  const int64_t b = at::smallcache_tile_for_budget(d, m_elems);
+  if (b == 0) return ATTN_ERR_UNSUPPORTED;
+  if (bh * n == 0) return ATTN_OK;
+  if (!Q || !K || !V || !O) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return ATTN_ERR_INVALID_ARG;
+  if (lse && !aligned16(lse)) return ATTN_ERR_INVALID_ARG;
+  const size_t need = at::smallcache_workspace_bytes(bh, n, b);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned256(workspace)) return ATTN_ERR_WORKSPACE;
+  return launch_status(at::launch_fwd_smallcache_bf16(Q, K, V, O, lse, bh, n, d, scale, b,
+                                                      workspace,
+                                                      static_cast<hipStream_t>(stream)));
+}
+
+size_t attn_bwd_workspace_size(int64_t bh, int64_t n, int64_t d) {
+  if (!shape_ok(bh, n, d) || !at::bwd_supported(d)) return 0;
+  return at::bwd_workspace_bytes(bh, n, d);
+}
+
+attn_status attn_bwd(const void* Q, const void* K, const void* V, const float* O,
+                     const void* dO, const float* lse, float* dQ, float* dK, float* dV,
+                     int64_t bh, int64_t n, int64_t d, float scale, attn_dtype dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (!shape_ok(bh, n, d) || !scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
+  if (!at::bwd_supported(d)) return ATTN_ERR_UNSUPPORTED;
+  if (bh * n == 0) return ATTN_OK;
+  const void* ptrs[] = {Q, K, V, O, dO, lse, dQ, dK, dV};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return ATTN_ERR_INVALID_ARG;
+  const size_t need = at::bwd_workspace_bytes(bh, n, d);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned256(workspace)))
+    return ATTN_ERR_WORKSPACE;
+  return launch_status(at::launch_bwd_bf16(Q, K, V, O, dO, lse, dQ, dK, dV, bh, n, d, scale,
+                                           workspace, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

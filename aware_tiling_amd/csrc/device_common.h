@@ -1,0 +1,102 @@
+// Device-side helpers shared by the gfx950 attention kernels: vector types,
+// MFMA wrappers, bf16 packing, and the LDS swizzles.
+//
+// MFMA operand layouts used throughout (wave64, lane l, h = l / 32, i = l % 32):
+//   v_mfma_f32_32x32x16_bf16  D[32x32] += A[32x16] * B[16x32]
+//     A: lane l holds A[i][8h .. 8h+7]      (8 bf16, k contiguous)
+//     B: lane l holds B[8h .. 8h+7][i]      (8 bf16, k contiguous)
+//     D: lane l, register r holds D[8(r/4) + 4h + r%4][i]
+//   v_mfma_f32_32x32x2_f32    D[32x32] += A[32x2] * B[2x32]
+//     A: lane l holds A[i][h];  B: lane l holds B[h][i];  D as above.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace at {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(const bf16x8& a, const bf16x8& b,
+                                                     const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_f32_32x32x2(float a, float b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Two fp32 values -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  bf16x2 b = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+// fp32 sum of the two bf16 halves of `p` added to `acc` (v_dot2c_f32_bf16
+// against (1, 1)).
+__device__ __forceinline__ float add_bf16x2(uint32_t p, float acc) {
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p), one, acc, false);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __builtin_bit_cast(float, bits16 << 16);
+}
+
+// v_perm_b32 selectors building {lo16(a), lo16(b)} and {hi16(a), hi16(b)}
+// (a in the low half of the result).
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// XOR swizzle of the 16-byte chunk index inside an LDS row, chosen so that
+// when consecutive rows are read at the same logical chunk (one row per
+// lane), the lanes of one ds_read_b128 phase land on distinct banks, whether
+// a phase spans 128 bytes (8 lanes) or 256 bytes (16 lanes).  Rows of 256
+// bytes or more use the low four row bits; 128-byte rows alternate bank
+// halves between even and odd rows, so they fold bit 3 into bit 0; 64-byte
+// rows put four rows in 256 bytes and mix bits 1 and 2.
+template <int ROW_BYTES>
+__device__ __forceinline__ int chunk_swizzle(int row) {
+  static_assert(ROW_BYTES >= 64, "rows shorter than 64 bytes are not swizzled");
+  if constexpr (ROW_BYTES >= 256)
+    return row & 15;
+  else if constexpr (ROW_BYTES == 128)
+    return (row & 7) ^ ((row >> 3) & 1);
+  else
+    return ((row >> 1) ^ (row >> 2)) & 3;
+}
+
+// Position of key k inside a transposed value tile: within each group of 16
+// keys, bits 2 and 3 of the key index are swapped, so that the 8 keys one
+// lane feeds to the P*V product (see the fused kernel) are contiguous.
+__device__ __forceinline__ int vt_key_pos(int k) {
+  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
+// Map the hardware workgroup id to a logical tile id so that consecutive
+// logical tiles run on the same XCD (workgroups are dispatched round robin
+// over the 8 XCDs); tiles that share K/V then share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int w, int total) {
+  const int per = total >> 3;
+  if (w < (per << 3)) return (w & 7) * per + (w >> 3);
+  return w;
+}
+
+}  // namespace at

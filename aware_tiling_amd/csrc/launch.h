@@ -1,0 +1,49 @@
+// Host-side launchers of the HIP kernels.  Arguments are validated by the
+// C-ABI layer (api.cpp) before any of these is called; each launcher only
+// enqueues kernels on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace at {
+
+// Tile configuration of the fused forward for one head dimension.
+struct FusedTileInfo {
+  int block_rows;    // B: query rows per workgroup
+  int key_tile;      // keys per K/V tile
+  int64_t onchip;    // elements held on chip per workgroup (M)
+};
+
+bool fused_bf16_supported(int64_t d);
+bool fused_f32_supported(int64_t d);
+FusedTileInfo fused_bf16_tile_info(int64_t d);
+FusedTileInfo fused_f32_tile_info(int64_t d);
+
+hipError_t launch_fwd_fused_bf16(const void* Q, const void* K, const void* V, float* O,
+                                 float* lse, int64_t bh, int64_t n, int64_t d, float scale,
+                                 hipStream_t stream);
+hipError_t launch_fwd_fused_f32(const float* Q, const float* K, const float* V, float* O,
+                                float* lse, int64_t bh, int64_t n, int64_t d, float scale,
+                                hipStream_t stream);
+
+// Square-tile (small-cache) forward.
+bool smallcache_supported(int64_t d);
+int64_t smallcache_tile_for_budget(int64_t d, int64_t m_elems);
+int64_t smallcache_onchip_elems(int64_t b);
+size_t smallcache_workspace_bytes(int64_t bh, int64_t n, int64_t b);
+hipError_t launch_fwd_smallcache_bf16(const void* Q, const void* K, const void* V, float* O,
+                                      float* lse, int64_t bh, int64_t n, int64_t d,
+                                      float scale, int64_t b, void* workspace,
+                                      hipStream_t stream);
+
+// Backward.
+bool bwd_supported(int64_t d);
+size_t bwd_workspace_bytes(int64_t bh, int64_t n, int64_t d);
+hipError_t launch_bwd_bf16(const void* Q, const void* K, const void* V, const float* O,
+                           const void* dO, const float* lse, float* dQ, float* dK, float* dV,
+                           int64_t bh, int64_t n, int64_t d, float scale, void* workspace,
+                           hipStream_t stream);
+
+}  // namespace at

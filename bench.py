@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+A step is one fused streaming forward (attn_fwd) over the whole workload:
+batch 1 x 32 heads, N = 16384, d = 128, bf16 inputs drawn iid N(0, 1) with Q
+multiplied by 4 (large score ranges), fp32 accumulation, scale 1/sqrt(d).
+Inputs are resident in HBM before timing starts.  W warmup steps run
+untimed; then K steps are timed back to back between two device
+synchronisations, and each launch is also bracketed by HIP events on the
+stream the kernel runs on.
+
+Reported (one JSON line on stdout):
+  value        whole-job TFLOP/s, 4 N^2 d flops per head (both products, mul
+               and add counted apart) / mean step time;
+  roofline     the fused kernel against the dense bf16 MFMA peak (2.5
+               PFLOP/s): achieved = algorithmic flops per launch / mean launch
+               time from the HIP events; traffic = HBM bytes per launch from
+               the committed rocprofv3 counter summary when it was taken on
+               the current kernel source, else null;
+  hbm_gbps     compulsory bytes (Q, K, V read once, O and lse written once) /
+               step time, and as a fraction of 8 TB/s;
+  cpu_baseline the float64 oracle on the host cores, on a bounded sample of
+               rows of the same workload (about 15 s of CPU work);
+  secondary    the small-cache square-tile path (batch 1 x 8 heads, N 4096,
+               d 256) and the backward (batch 2 x 16 heads, N 4096, d 128)
+               timed the same way, when built (not part of `value`).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
+HEADLINE = "fwd_bf16_b1h32_n16384_d128_qx4"
+METRIC = "attention fwd TFLOP/s (4N²d/head) and % of bf16 MFMA peak; HBM GB/s at 1 GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_fwd_n16384_d128.json")
+KERNEL_SOURCES = ["aware_tiling_amd/csrc/fwd_fused.hip", "aware_tiling_amd/csrc/device_common.h"]
+
+
+def kernel_digest(paths=KERNEL_SOURCES) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def time_launches(fn, steps: int, warmup: int):
+    """Mean ms per launch from HIP events on the current stream, and the
+    wall-clock ms per step between synchronisations."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ev = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return sum(ev) / len(ev), wall_ms, ev
+
+
+def traffic_for_launch():
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_digest") != kernel_digest():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, target_s: float = 15.0):
+    """The float64 oracle, as it stands, on a bounded sample of query rows
+    (all keys) of head 0 of the workload."""
+    import numpy as np
+
+    import oracle
+    from aware_tiling_amd.inputs import make_inputs
+
+    q, k, v = make_inputs(1, w.n, w.d, w.dtype, w.seed, w.q_mult)
+    qd, kd, vd = (t.double().numpy() for t in (q, k, v))
+    flops_row = 4.0 * w.n * w.d
+    rows = 32
+    oracle.attn_fwd(qd[:, :8], kd, vd, w.scale)  # load + warm
+    t0 = time.perf_counter()
+    _, _, threads = oracle.attn_fwd(qd[:, :rows], kd, vd, w.scale)
+    dt = time.perf_counter() - t0
+    rows = int(min(w.n, max(rows, rows * target_s / max(dt, 1e-3))))
+    rows = max(threads, (rows // threads) * threads)
+    t0 = time.perf_counter()
+    _, _, threads = oracle.attn_fwd(qd[:, :rows], kd, vd, w.scale)
+    dt = time.perf_counter() - t0
+    tflops = flops_row * rows / dt / 1e12
+    return {"value": tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} query rows x {w.n} keys of head 0 ({w.name}), float64, "
+                      f"{dt:.1f} s; TFLOP/s at 4*N*d flops per row",
+            "seconds": dt, "full_workload_seconds_est": dt * w.n * w.bh / rows}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (heads are "
+              "independent, so a multi-GPU run would shard batch x heads with no communication)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import aware_tiling_amd as at
+    from aware_tiling_amd.inputs import WORKLOADS, workload_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = WORKLOADS[HEADLINE]
+    print(f"[bench] inputs {w.name}", file=sys.stderr, flush=True)
+    q, k, v = (t.to(dev) for t in workload_inputs(w))
+    o = torch.empty((w.bh, w.n, w.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.bh, w.n), dtype=torch.float32, device=dev)
+    fn = lambda: at.attn_fwd(q, k, v, w.scale, out=o, lse=lse)
+    print(f"[bench] timing attn_fwd steps={args.steps} warmup={args.warmup}", file=sys.stderr,
+          flush=True)
+    torch.cuda.synchronize()
+    launch_ms, wall_ms, ev = time_launches(fn, args.steps, args.warmup)
+    flops = w.fwd_flops
+    tflops = flops / (wall_ms * 1e-3) / 1e12
+    achieved = flops / (launch_ms * 1e-3) / 1e12
+    compulsory = w.bh * (3 * w.n * w.d * 2 + w.n * w.d * 4 + w.n * 4)
+    br = at.fwd_query_block(w.d)
+    m_elems = at.fwd_onchip_elems(w.d)
+    # the exposition's fused-schedule models, in bytes (bf16 inputs)
+    sched_bytes = w.bh * (2 * w.n * w.n * w.d / br + 2 * w.n * w.d) * 2
+    model_bytes = w.bh * (w.n * w.n * w.d * w.d / m_elems + w.n * w.d) * 2
+
+    traffic = traffic_for_launch()
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "kernel": "fwd_fused_bf16_kernel",
+                "flops_per_launch": flops, "launch_ms": round(launch_ms, 4)}
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.n,
+                   "head_dim": w.d, "q_scale": w.q_mult, "query_block": br,
+                   "onchip_elems": m_elems, "tile": os.environ.get("ATTN_FWD_TILE", "default")},
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "hbm_gbps": round(compulsory / (wall_ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(compulsory / (wall_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "bytes": {"compulsory": compulsory, "fused_schedule_cu_boundary": sched_bytes,
+                  "page_model_N2d2_over_M_plus_Nd": model_bytes},
+        "roofline": roofline,
+        "launch_ms_min": round(min(ev), 4),
+        "launch_ms_max": round(max(ev), 4),
+    }
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+
+    if not args.no_secondary:
+        out["secondary"] = secondary(args, at, torch, dev)
+
+    if not args.no_cpu:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def secondary(args, at, torch, dev):
+    from aware_tiling_amd.inputs import WORKLOADS, workload_inputs
+
+    res = {}
+    w = WORKLOADS["smallcache_bf16_b1h8_n4096_d256"]
+    m_elems = 40000
+    if at.smallcache_tile(w.d, m_elems) > 0:
+        print(f"[bench] timing {w.name}", file=sys.stderr, flush=True)
+        q, k, v = (t.to(dev) for t in workload_inputs(w))
+        o = torch.empty((w.bh, w.n, w.d), dtype=torch.float32, device=dev)
+        lse = torch.empty((w.bh, w.n), dtype=torch.float32, device=dev)
+        need = int(at.lib().attn_fwd_smallcache_workspace_size(w.bh, w.n, w.d, m_elems))
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        ms_sc, _, _ = time_launches(lambda: at.attn_fwd_smallcache(
+            q, k, v, m_elems, w.scale, out=o, lse=lse, workspace=ws), args.steps, args.warmup)
+        ms_fu, _, _ = time_launches(lambda: at.attn_fwd(q, k, v, w.scale, out=o, lse=lse),
+                                    args.steps, args.warmup)
+        b = at.smallcache_tile(w.d, m_elems)
+        res["smallcache"] = {"workload": w.name, "m_elems": m_elems, "tile_b": b,
+                             "ms": round(ms_sc, 4),
+                             "tflops": round(w.fwd_flops / (ms_sc * 1e-3) / 1e12, 2),
+                             "fused_ms_same_inputs": round(ms_fu, 4),
+                             "fused_tflops": round(w.fwd_flops / (ms_fu * 1e-3) / 1e12, 2),
+                             "exp_matrix_bytes": w.bh * w.n * w.n * 2}
+        del q, k, v, o, lse, ws
+    w = WORKLOADS["bwd_bf16_b2h16_n4096_d128"]
+    q0 = torch.zeros((1, 64, w.d), dtype=torch.bfloat16, device=dev)
+    try:
+        at.attn_bwd(q0, q0, q0, torch.zeros((1, 64, w.d), device=dev), q0,
+                    torch.zeros((1, 64), device=dev))
+        has_bwd = True
+    except at.AttnError:
+        has_bwd = False
+    if has_bwd:
+        print(f"[bench] timing {w.name}", file=sys.stderr, flush=True)
+        q, k, v, do = (t.to(dev) for t in workload_inputs(w))
+        o, lse = at.attn_fwd(q, k, v, w.scale)
+        grads = tuple(torch.empty((w.bh, w.n, w.d), dtype=torch.float32, device=dev)
+                      for _ in range(3))
+        need = int(at.lib().attn_bwd_workspace_size(w.bh, w.n, w.d))
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        ms, _, _ = time_launches(lambda: at.attn_bwd(q, k, v, o, do, lse, w.scale, workspace=ws,
+                                                     grads=grads), args.steps, args.warmup)
+        fl = 10.0 * w.n * w.n * w.d * w.bh  # 2 products recomputed-free count: 5 GEMMs
+        res["backward"] = {"workload": w.name, "ms": round(ms, 4),
+                           "tflops_at_10N2d": round(fl / (ms * 1e-3) / 1e12, 2)}
+    torch.cuda.synchronize()
+    return res
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,166 @@
+/*
+ * aware_tiling.h -- C ABI of the MI355X (gfx950) exact-attention library.
+ *
+ * The library computes exact single-head attention
+ *     O = softmax(scale * Q K^T) V        (row-wise softmax)
+ * for a batch of independent heads, as defined on the page "The I/O
+ * Complexity of Attention, or How Optimal is Flash Attention?" (exposition),
+ * section "Attention as a mathematical problem": the score of query i and key
+ * j is scale * <q_i, k_j>, softmax turns each row of scores into weights, and
+ * the output row is the weighted average of the value rows.  That page omits
+ * the 1/sqrt(d) factor; here it is the explicit `scale` argument.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Layout: Q, K, V, dO, O, dQ, dK, dV are contiguous row-major tensors of
+ *    shape [bh, n, d] (bh = batch x heads, n = sequence length, d = head
+ *    dimension, d fastest).  lse is [bh, n].  Queries and keys have the same
+ *    count n.  Strides are not supported.
+ *  - Pointers are DEVICE pointers (hipMalloc'd or from a framework allocator)
+ *    on the device that is current for the calling thread.  Q, K, V, dO must
+ *    be 16-byte aligned; O, lse, dQ, dK, dV 16-byte aligned as well.
+ *  - Ownership: the caller owns every buffer.  No entry point allocates
+ *    device memory; scratch space is passed in as `workspace`, sized by the
+ *    matching *_workspace_size function.
+ *  - dtype: ATTN_BF16 (bfloat16 inputs, fp32 accumulation, bf16 MFMA) or
+ *    ATTN_F32 (fp32 inputs and arithmetic; forward only).  Outputs are fp32.
+ *  - stream: a hipStream_t passed as void*; NULL means the null stream.
+ *    Calls only enqueue work and return without synchronising the host.
+ *  - scale must be finite and > 0 (callers pass 1/sqrt(d)).
+ *  - Errors: validation happens before any HIP call; on an error nothing is
+ *    enqueued and no output is touched.  ATTN_ERR_LAUNCH reports a HIP error
+ *    seen right after enqueueing (its text is in attn_last_hip_error()).
+ *  - Non-finite inputs propagate to the outputs; they are not detected.
+ */
+#ifndef AWARE_TILING_H_
+#define AWARE_TILING_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size or scale */
+  ATTN_ERR_UNSUPPORTED = 2, /* head dimension or dtype not built */
+  ATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  ATTN_ERR_LAUNCH = 4       /* HIP reported an error when enqueueing */
+} attn_status;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* attn_status_string(attn_status s);
+
+/* Text of the last HIP error seen by this thread's calls ("" if none). */
+const char* attn_last_hip_error(void);
+
+/* Library version as "major.minor.patch" (static storage). */
+const char* attn_version(void);
+
+/*
+ * attn_fwd -- fused streaming forward for the large-cache regime.
+ *
+ * Follows the exposition's sections "Softmax without storing the score
+ * matrix" and "Large caches: where FlashAttention's I/O comes from": each
+ * workgroup keeps a block of queries and, per query, the running maximum m,
+ * the running normaliser l and the unnormalised output u on chip, scans all
+ * key/value tiles once, folds each tile in with the rescaling rule
+ * (m' = max(m, tile max); l and u multiplied by exp(m - m') before the tile's
+ * terms are added), and writes o = u / l.  The N x N score matrix is never
+ * stored.
+ *
+ *   Q, K, V : [bh, n, d] dtype `dtype` (device, read only)
+ *   O       : [bh, n, d] float (device, written)
+ *   lse     : [bh, n] float, natural-log log-sum-exp of each row of scaled
+ *             scores, log(sum_j exp(scale <q_i,k_j>)); may be NULL.
+ *   bh >= 0, n >= 0 (bh*n == 0 is a no-op), d in {64, 128, 256} for bf16,
+ *   d in {64, 128} for f32.
+ */
+attn_status attn_fwd(const void* Q, const void* K, const void* V, float* O,
+                     float* lse, int64_t bh, int64_t n, int64_t d, float scale,
+                     attn_dtype dtype, void* stream);
+
+/*
+ * On-chip elements M held by one workgroup of attn_fwd for head dimension d
+ * (query block, its accumulators and statistics, the key/value tiles and the
+ * score tile, each element counted once whatever its width), the quantity
+ * the exposition calls the fast-memory size M; and the query-block rows B.
+ * Returns 0 for unsupported (d, dtype).
+ */
+int64_t attn_fwd_onchip_elems(int64_t d, attn_dtype dtype);
+int64_t attn_fwd_query_block(int64_t d, attn_dtype dtype);
+
+/*
+ * attn_fwd_smallcache -- square-tile forward for the small-cache regime.
+ *
+ * Follows the exposition's section "Small caches: when storing an
+ * intermediate matrix helps": square tiles of side b (two input tiles and
+ * an output tile fit in an on-chip budget of m_elems elements) compute the
+ * exponentiated score matrix and write it to device memory (the N x N
+ * intermediate, kept in bf16), then a second tiled product multiplies it by
+ * V.  The page does not say how the exponentials are kept in range; this
+ * library shifts each (row, key tile) by that tile's own maximum, keeps the
+ * per-tile sums, merges the per-tile statistics with the same rescaling
+ * rule as the streaming recurrence, and applies the merged factors in the
+ * second product.  The result is the same function as attn_fwd.
+ *
+ *   m_elems : on-chip budget M in elements; must satisfy m_elems < d*d
+ *             (otherwise the large-cache path applies and the call returns
+ *             ATTN_ERR_INVALID_ARG).  The tile side b is the largest
+ *             supported side whose footprint fits in m_elems
+ *             (ATTN_ERR_UNSUPPORTED if none fits); see
+ *             attn_smallcache_tile().
+ *   workspace, workspace_bytes : device scratch of at least
+ *             attn_fwd_smallcache_workspace_size(bh, n, d, m_elems) bytes,
+ *             256-byte aligned.  Its contents on return are unspecified.
+ *   Other arguments as attn_fwd; bf16 only, d in {64, 128, 256}.
+ */
+size_t attn_fwd_smallcache_workspace_size(int64_t bh, int64_t n, int64_t d,
+                                          int64_t m_elems);
+attn_status attn_fwd_smallcache(const void* Q, const void* K, const void* V,
+                                float* O, float* lse, int64_t bh, int64_t n,
+                                int64_t d, float scale, attn_dtype dtype,
+                                int64_t m_elems, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* Tile side b chosen for (d, m_elems), 0 if none fits or m_elems >= d*d;
+ * and the on-chip elements one workgroup of that tile actually holds. */
+int64_t attn_smallcache_tile(int64_t d, int64_t m_elems);
+int64_t attn_smallcache_onchip_elems(int64_t b);
+
+/*
+ * attn_bwd -- gradients of attn_fwd.
+ *
+ * The backward problem is the one the page "On Fine-Grained I/O Complexity
+ * of Attention Backward Passes" (explainer) analyses; it prints no formulas.
+ * This entry point computes the exact derivatives of O with respect to Q, K
+ * and V for an upstream gradient dO, in the blockwise large-cache schedule
+ * that page says is optimal when M >= d^2: the weights P are recomputed
+ * tile by tile from Q, K and the saved log-sum-exp, never stored, and
+ *     dV = P^T dO,  dP = dO V^T,  D_i = <dO_i, o_i>,  dS = P o (dP - D),
+ *     dQ = scale dS K,  dK = scale dS^T Q.
+ *
+ *   Q, K, V, dO : [bh, n, d] bf16 (device, read only)
+ *   O           : [bh, n, d] float, the output of attn_fwd on the same Q,K,V
+ *   lse         : [bh, n] float, the lse of that attn_fwd call (required)
+ *   dQ, dK, dV  : [bh, n, d] float (device, written)
+ *   workspace   : at least attn_bwd_workspace_size(bh, n, d) bytes,
+ *                 256-byte aligned; contents on return unspecified.
+ *   bf16 only, d in {64, 128}.
+ */
+size_t attn_bwd_workspace_size(int64_t bh, int64_t n, int64_t d);
+attn_status attn_bwd(const void* Q, const void* K, const void* V,
+                     const float* O, const void* dO, const float* lse,
+                     float* dQ, float* dK, float* dV, int64_t bh, int64_t n,
+                     int64_t d, float scale, attn_dtype dtype, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AWARE_TILING_H_ */

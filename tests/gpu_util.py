@@ -1,0 +1,61 @@
+"""Helpers for GPU parity tests: seeded inputs, oracle on sampled rows, and
+error reporting.  The oracle always sees exactly the values the GPU sees
+(bf16/fp32 widened to float64)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from aware_tiling_amd.inputs import make_inputs
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def sample_rows(n: int, count: int, seed: int) -> np.ndarray:
+    """First and last rows of the sequence plus seeded random rows."""
+    edge = min(count // 4, n)
+    rows = set(range(edge)) | set(range(max(0, n - edge), n))
+    rng = np.random.default_rng(seed)
+    rows |= set(rng.choice(n, size=min(n, count - len(rows)), replace=False).tolist())
+    return np.array(sorted(rows)[:max(count, 1)])
+
+
+def oracle_fwd_rows(q, k, v, scale, heads, rows):
+    """Oracle O and lse for the given heads and query rows (all keys)."""
+    qs = f64(q[heads][:, rows])
+    o, lse, _ = oracle.attn_fwd(qs, f64(k[heads]), f64(v[heads]), scale)
+    return o, lse
+
+
+def max_abs(a: np.ndarray, b: np.ndarray) -> float:
+    return float(np.max(np.abs(a - b))) if a.size else 0.0
+
+
+def rel_fro(a: np.ndarray, b: np.ndarray) -> float:
+    den = float(np.linalg.norm(b))
+    return float(np.linalg.norm(a - b)) / den if den > 0 else float(np.linalg.norm(a - b))
+
+
+def check(got: np.ndarray, ref: np.ndarray, tol: float, what: str):
+    assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    err = max_abs(got, ref)
+    say(f"  {what}: max|err| {err:.3e} (tol {tol:g}), rel fro {rel_fro(got, ref):.2e}")
+    assert err <= tol, f"{what}: max abs error {err:.3e} > {tol:g}"
+
+
+def inputs(bh, n, d, dtype, seed, q_mult=1.0, with_do=False, device="cuda"):
+    ts = make_inputs(bh, n, d, dtype, seed, q_mult, with_do=with_do)
+    return ts, tuple(t.to(device) for t in ts)

@@ -1,0 +1,152 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/aware_tiling.h declares, and rejects bad arguments before any HIP call
+(CPU only; no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from aware_tiling_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "aware_tiling.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+BF16, F32 = binding.ATTN_BF16, binding.ATTN_F32
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.lib()
+
+
+def test_header_declares_the_three_entry_points():
+    names = header_functions()
+    for f in ("attn_fwd", "attn_fwd_smallcache", "attn_bwd"):
+        assert f in names
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    names = header_functions()
+    assert names, "no declarations parsed"
+    for name in names:
+        assert hasattr(lib, name), f"{name} not exported"
+        assert name in binding.SIGNATURES, f"{name} has no binding signature"
+    # and the binding binds nothing the header does not declare
+    assert set(binding.SIGNATURES) == set(names)
+
+
+def test_status_strings_and_version(lib):
+    for code, name in binding.STATUS.items():
+        assert lib.attn_status_string(code).decode() == name
+    assert lib.attn_status_string(99).decode() == "ATTN_STATUS_UNKNOWN"
+    assert re.fullmatch(r"\d+\.\d+\.\d+", lib.attn_version().decode())
+
+
+FAKE = 0x1000  # aligned, never dereferenced: every call below fails validation first
+
+
+def fwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, bh=1, n=128, d=64, scale=0.125,
+        dtype=BF16):
+    return lib.attn_fwd(q, k, v, o, lse, bh, n, d, scale, dtype, None)
+
+
+def test_fwd_validation(lib):
+    assert fwd(lib, q=None) == INVALID
+    assert fwd(lib, o=None) == INVALID
+    assert fwd(lib, q=FAKE + 2) == INVALID  # misaligned
+    assert fwd(lib, lse=FAKE + 4) == INVALID
+    assert fwd(lib, d=96) == UNSUPPORTED
+    assert fwd(lib, d=256, dtype=F32) == UNSUPPORTED
+    assert fwd(lib, dtype=7) == UNSUPPORTED
+    assert fwd(lib, scale=0.0) == INVALID
+    assert fwd(lib, scale=-1.0) == INVALID
+    assert fwd(lib, scale=float("nan")) == INVALID
+    assert fwd(lib, scale=float("inf")) == INVALID
+    assert fwd(lib, bh=-1) == INVALID
+    assert fwd(lib, n=-5) == INVALID
+    assert fwd(lib, n=1 << 25) == INVALID
+    # empty problems are a no-op even with null pointers
+    assert fwd(lib, q=None, k=None, v=None, o=None, n=0) == OK
+    assert fwd(lib, q=None, k=None, v=None, o=None, bh=0) == OK
+
+
+def test_fwd_tile_queries(lib):
+    for d in (64, 128, 256):
+        m = lib.attn_fwd_onchip_elems(d, BF16)
+        b = lib.attn_fwd_query_block(d, BF16)
+        assert b > 0 and b % 32 == 0
+        # the fused kernel is the large-cache schedule: M >= d^2
+        assert m >= d * d
+    assert lib.attn_fwd_onchip_elems(96, BF16) == 0
+    assert lib.attn_fwd_query_block(64, F32) > 0
+
+
+def test_smallcache_validation(lib):
+    d = 256
+    ws = lib.attn_fwd_smallcache_workspace_size(8, 4096, d, 40000)
+    b = lib.attn_smallcache_tile(d, 40000)
+    if b == 0:
+        pytest.skip("small-cache path not built")
+    assert ws > 0
+    # the page's small-cache regime is M < d^2; the call refuses M >= d^2
+    assert lib.attn_smallcache_tile(d, d * d) == 0
+    call = lambda m=40000, wsb=ws, w=FAKE * 256, q=FAKE: lib.attn_fwd_smallcache(
+        q, FAKE, FAKE, FAKE, None, 8, 4096, d, 0.0625, BF16, m, w, wsb, None)
+    assert call(m=d * d) == INVALID
+    assert call(q=None) == INVALID
+    assert call(w=None) == WORKSPACE
+    assert call(wsb=ws - 1) == WORKSPACE
+    assert call(w=FAKE * 256 + 16) == WORKSPACE  # not 256-byte aligned
+    assert lib.attn_fwd_smallcache(FAKE, FAKE, FAKE, FAKE, None, 8, 4096, d, 0.0625, F32, 40000,
+                                   FAKE, ws, None) == UNSUPPORTED
+
+
+def test_bwd_validation(lib):
+    ws = lib.attn_bwd_workspace_size(2, 512, 128)
+    if lib.attn_bwd_workspace_size(2, 512, 128) == 0 and lib.attn_bwd(
+            FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 512, 128, 0.08, BF16, FAKE,
+            1 << 30, None) == UNSUPPORTED:
+        pytest.skip("backward not built")
+    call = lambda **kw: lib.attn_bwd(*[kw.get(x, FAKE) for x in
+                                       ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv")],
+                                     2, 512, kw.get("d", 128), kw.get("scale", 0.08), BF16,
+                                     kw.get("w", FAKE * 256), kw.get("wsb", ws), None)
+    assert call(lse=None) == INVALID
+    assert call(dv=None) == INVALID
+    assert call(dq=FAKE + 8) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    assert call(scale=-0.5) == INVALID
+    if ws > 0:
+        assert call(wsb=ws - 1) == WORKSPACE
+        assert call(w=None) == WORKSPACE
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    q = torch.zeros(1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        binding.attn_fwd(q, q, q)
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(ImportError):
+        binding.lib()
+
+
+def test_library_links_no_oracle(lib):
+    # the product library must not reference the oracle's symbols
+    so = open(binding.LIB_PATH, "rb").read()
+    assert b"oracle_attn" not in so
+    with pytest.raises(AttributeError):
+        getattr(ctypes.CDLL(binding.LIB_PATH), "oracle_attn_fwd_f64")
