@@ -91,32 +91,37 @@ def traffic_for_launch():
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(w, target_s: float = 15.0):
-    """The float64 oracle, as it stands, on a bounded sample of query rows
-    (all keys) of head 0 of the workload."""
-    import numpy as np
-
+def cpu_baseline(w, cpu_inputs, target_s: float = 15.0):
+    """The float64 oracle, as it stands, on a bounded sample of the same
+    workload: whole heads (all query rows, all keys), as many as fit in about
+    target_s seconds, or the leading rows of head 0 if one head is more."""
     import oracle
-    from aware_tiling_amd.inputs import make_inputs
 
-    q, k, v = make_inputs(1, w.n, w.d, w.dtype, w.seed, w.q_mult)
-    qd, kd, vd = (t.double().numpy() for t in (q, k, v))
+    q, k, v = cpu_inputs
     flops_row = 4.0 * w.n * w.d
-    rows = 32
-    oracle.attn_fwd(qd[:, :8], kd, vd, w.scale)  # load + warm
+    calib = 32
+    qd0 = q[:1, :calib].double().numpy()
+    kd0, vd0 = k[:1].double().numpy(), v[:1].double().numpy()
+    oracle.attn_fwd(qd0[:, :8], kd0, vd0, w.scale)  # load + warm
     t0 = time.perf_counter()
-    _, _, threads = oracle.attn_fwd(qd[:, :rows], kd, vd, w.scale)
+    _, _, threads = oracle.attn_fwd(qd0, kd0, vd0, w.scale)
     dt = time.perf_counter() - t0
-    rows = int(min(w.n, max(rows, rows * target_s / max(dt, 1e-3))))
-    rows = max(threads, (rows // threads) * threads)
+    rows = max(calib, int(calib * target_s / max(dt, 1e-3)))
+    if rows <= w.n:
+        heads, nrows = 1, max(threads, (rows // threads) * threads)
+    else:
+        heads, nrows = min(w.bh, max(1, rows // w.n)), w.n
+    qd = q[:heads, :nrows].double().numpy()
+    kd, vd = k[:heads].double().numpy(), v[:heads].double().numpy()
     t0 = time.perf_counter()
-    _, _, threads = oracle.attn_fwd(qd[:, :rows], kd, vd, w.scale)
+    _, _, threads = oracle.attn_fwd(qd, kd, vd, w.scale)
     dt = time.perf_counter() - t0
-    tflops = flops_row * rows / dt / 1e12
+    tflops = flops_row * heads * nrows / dt / 1e12
     return {"value": tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows} query rows x {w.n} keys of head 0 ({w.name}), float64, "
-                      f"{dt:.1f} s; TFLOP/s at 4*N*d flops per row",
-            "seconds": dt, "full_workload_seconds_est": dt * w.n * w.bh / rows}
+            "sample": f"{heads} head(s) x {nrows} query rows x {w.n} keys of {w.name}, float64, "
+                      f"{dt:.1f} s; TFLOP/s at 4*N*d flops per query row",
+            "seconds": round(dt, 2),
+            "full_workload_seconds_est": round(dt * w.n * w.bh / (heads * nrows), 1)}
 
 
 def main():
@@ -142,7 +147,8 @@ def main():
     torch.cuda.set_device(dev)
     w = WORKLOADS[HEADLINE]
     print(f"[bench] inputs {w.name}", file=sys.stderr, flush=True)
-    q, k, v = (t.to(dev) for t in workload_inputs(w))
+    cpu_inputs = workload_inputs(w)
+    q, k, v = (t.to(dev) for t in cpu_inputs)
     o = torch.empty((w.bh, w.n, w.d), dtype=torch.float32, device=dev)
     lse = torch.empty((w.bh, w.n), dtype=torch.float32, device=dev)
     fn = lambda: at.attn_fwd(q, k, v, w.scale, out=o, lse=lse)
@@ -198,7 +204,7 @@ def main():
 
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w)
+        out["cpu_baseline"] = cpu_baseline(w, cpu_inputs)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
@@ -209,7 +215,7 @@ def secondary(args, at, torch, dev):
 
     res = {}
     w = WORKLOADS["smallcache_bf16_b1h8_n4096_d256"]
-    m_elems = 40000
+    m_elems = 49152  # 3/4 of d^2: the small-cache regime M < d^2
     if at.smallcache_tile(w.d, m_elems) > 0:
         print(f"[bench] timing {w.name}", file=sys.stderr, flush=True)
         q, k, v = (t.to(dev) for t in workload_inputs(w))
