@@ -1,12 +1,459 @@
-// Backward: not built yet; the C ABI reports ATTN_ERR_UNSUPPORTED for it.
+// Backward of exact attention for gfx950: dQ, dK, dV from Q, K, V, the
+// forward's O and log-sum-exp, and the upstream gradient dO.
+//
+// Method: the page "On Fine-Grained I/O Complexity of Attention Backward
+// Passes" (explainer), sections "Methodology" and "Key Contributions and
+// Results" (Theorem 1.1), states the backward problem and that the blockwise
+// large-cache schedule is optimal for M >= d^2; it prints no formulas.  The
+// formulas are the exact derivatives of O = softmax(scale Q K^T) V:
+//     P = exp(scale Q K^T - lse),   dV = P^T dO,   dP = dO V^T,
+//     D_i = <dO_i, O_i> (= sum_j P_ij dP_ij),   dS = P o (dP - D),
+//     dQ = scale dS K,   dK = scale dS^T Q.
+// P is recomputed tile by tile from Q, K and the saved lse; no N x N matrix
+// is stored.
+//
+// Three kernels, stream ordered:
+//  1. bwd_preprocess: D_i = <dO_i, O_i> into the workspace.
+//  2. bwd_dkdv: one workgroup per (head, block of 128 keys), one wave per 32
+//     keys.  Each wave keeps K and V of its keys as MFMA B operands and the
+//     transposed accumulators dK^T, dV^T (d x 32 keys) in registers, and
+//     streams 32-query tiles of Q, dO, lse, D through double-buffered LDS.
+//     Scores are computed as S = Q K^T so that a lane owns one key: the
+//     bf16 P and dS tiles then feed dV^T += dO^T P and dK^T += Q^T dS
+//     straight from registers, with Q and dO also stored transposed in LDS.
+//  3. bwd_dq: one workgroup per (head, block of 128 queries), one wave per
+//     32 queries.  Each wave keeps Q and dO as B operands, lse and D as
+//     per-lane scalars, and dQ^T in registers, and streams 32-key tiles of
+//     K, V (row-major) and K^T through LDS: S^T = K Q^T, dP^T = V dO^T,
+//     dS^T, dQ^T += K^T dS^T.  Recomputing S and dP here costs 4 N^2 d more
+//     flops than accumulating dQ with atomics, and keeps the result
+//     deterministic.
+#include "device_common.h"
 #include "launch.h"
 
 namespace at {
-bool bwd_supported(int64_t) { return false; }
-size_t bwd_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
-hipError_t launch_bwd_bf16(const void*, const void*, const void*, const float*, const void*,
-                           const float*, float*, float*, float*, int64_t, int64_t, int64_t,
-                           float, void*, hipStream_t) {
-  return hipErrorNotSupported;
+
+namespace {
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) {
+  return __builtin_bit_cast(float, w & 0xffff0000u);
 }
+
+// Write one 4-row x 8-column bf16 block (v[e] holds row row0+e, columns
+// col0..col0+7) into a transposed tile dst[col][ROWS]: row col0+2w(+1) of
+// the destination receives the four source rows as four contiguous elements
+// at position vt_key_pos(row0) (row0 a multiple of 4), with the 16-byte
+// chunk swizzle of the destination rows.
+template <int ROWS>
+__device__ __forceinline__ void store_transposed_4x8(bf16* dst, int row0, int col0,
+                                                     const u32x4 (&v)[4]) {
+  const int pos = vt_key_pos(row0);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int r0 = col0 + 2 * w, r1 = r0 + 1;
+    u32x2 lo = {pair_lo(v[0][w], v[1][w]), pair_lo(v[2][w], v[3][w])};
+    u32x2 hi = {pair_hi(v[0][w], v[1][w]), pair_hi(v[2][w], v[3][w])};
+    *reinterpret_cast<u32x2*>(dst + r0 * ROWS + (((pos >> 3) ^ chunk_swizzle<ROWS * 2>(r0)) * 8) +
+                              (pos & 7)) = lo;
+    *reinterpret_cast<u32x2*>(dst + r1 * ROWS + (((pos >> 3) ^ chunk_swizzle<ROWS * 2>(r1)) * 8) +
+                              (pos & 7)) = hi;
+  }
+}
+
+// Write the same block row-major into dst[row][COLS] with swizzled chunks.
+template <int COLS>
+__device__ __forceinline__ void store_rows_4x8(bf16* dst, int row0, int col0,
+                                               const u32x4 (&v)[4]) {
+  const int cc = col0 >> 3;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = row0 + e;
+    *reinterpret_cast<u32x4*>(dst + r * COLS + ((cc ^ chunk_swizzle<COLS * 2>(r)) * 8)) = v[e];
+  }
+}
+
+// A operand (32 rows x 16 k) from a row-major swizzled tile: row `row`,
+// logical 16-byte chunk `chunk`.
+template <int COLS>
+__device__ __forceinline__ bf16x8 lds_operand(const bf16* tile, int row, int chunk) {
+  return *reinterpret_cast<const bf16x8*>(tile + row * COLS +
+                                          ((chunk ^ chunk_swizzle<COLS * 2>(row)) * 8));
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// 1. D_i = <dO_i, O_i>
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_preprocess(const float* __restrict__ O,
+                                                      const bf16* __restrict__ dO,
+                                                      float* __restrict__ Dout, int64_t rows) {
+  constexpr int TPR = D / 8;       // threads per row (8 elements each)
+  constexpr int RPB = 256 / TPR;   // rows per block
+  const int t = threadIdx.x;
+  const int64_t r = (int64_t)blockIdx.x * RPB + t / TPR;
+  const int c = (t % TPR) * 8;
+  float acc = 0.f;
+  if (r < rows) {
+    const u32x4 g = *reinterpret_cast<const u32x4*>(dO + r * D + c);
+    const f32x4 o0 = *reinterpret_cast<const f32x4*>(O + r * D + c);
+    const f32x4 o1 = *reinterpret_cast<const f32x4*>(O + r * D + c + 4);
+    acc = bf_lo(g[0]) * o0[0] + bf_hi(g[0]) * o0[1] + bf_lo(g[1]) * o0[2] + bf_hi(g[1]) * o0[3] +
+          bf_lo(g[2]) * o1[0] + bf_hi(g[2]) * o1[1] + bf_lo(g[3]) * o1[2] + bf_hi(g[3]) * o1[3];
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (r < rows && (t % TPR) == 0) Dout[r] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// 2. dK, dV
+
+template <int D>
+struct DkdvCfg {
+  static constexpr int NW = 4, NT = 256, BKV = NW * 32, BQ = 32;
+  static constexpr int ITEMS = (BQ / 4) * (D / 8);  // 4x8 blocks per tile (per tensor)
+  static constexpr int ITERS = (2 * ITEMS + NT - 1) / NT;
+  static constexpr int TILE = BQ * D;               // bf16 elements per tile
+  // per buffer: Q rows, dO rows, Q^T, dO^T, then lse2 and D (floats)
+  static constexpr int BUF_BF16 = 4 * TILE;
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dg,
+    float* __restrict__ dK, float* __restrict__ dV, int n, int nkb, int total, float c,
+    float scale) {
+  using C = DkdvCfg<D>;
+  constexpr int BQ = C::BQ;
+  __shared__ __attribute__((aligned(16))) bf16 tiles[2][C::BUF_BF16];
+  __shared__ __attribute__((aligned(16))) float stats[2][2 * BQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, li = lane & 31;
+  const int tile = xcd_remap(blockIdx.x, total);
+  const int head = tile / nkb, kblk = tile - head * nkb;
+  const size_t hoff = (size_t)head * n * D;
+  const bf16 *Qh = Q + hoff, *Kh = K + hoff, *Vh = V + hoff, *dOh = dO + hoff;
+  const float* lseh = lse + (size_t)head * n;
+  const float* Dh = Dg + (size_t)head * n;
+  const int key = kblk * C::BKV + wave * 32 + li;
+
+  // K and V rows of this wave's keys as B operands (lane: row `key`).
+  bf16x8 kreg[D / 16], vreg[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    kreg[kk] = key < n ? *reinterpret_cast<const bf16x8*>(Kh + (size_t)key * D + 16 * kk + 8 * h)
+                       : bf16x8{};
+    vreg[kk] = key < n ? *reinterpret_cast<const bf16x8*>(Vh + (size_t)key * D + 16 * kk + 8 * h)
+                       : bf16x8{};
+  }
+  f32x16 dkt[D / 32], dvt[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dkt[db] = dvt[db] = f32x16{};
+
+  // Staging registers: item x < ITEMS is a 4x8 block of Q, else of dO.
+  u32x4 st[C::ITERS][4];
+  float sl = 0.f;
+  auto load = [&](int i) {
+#pragma unroll
+    for (int it = 0; it < C::ITERS; ++it) {
+      const int x = tid + it * C::NT;
+      const int y = x % C::ITEMS;
+      const int g = y % (BQ / 4), cc = y / (BQ / 4);
+      const bf16* src = x < C::ITEMS ? Qh : dOh;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int q = i * BQ + 4 * g + e;
+        st[it][e] = (x < 2 * C::ITEMS && q < n)
+                        ? *reinterpret_cast<const u32x4*>(src + (size_t)q * D + cc * 8)
+                        : u32x4{};
+      }
+    }
+    if (tid < 2 * BQ) {
+      const int q = i * BQ + (tid % BQ);
+      if (tid < BQ)
+        sl = q < n ? lseh[q] * kLog2e : INFINITY;  // +inf: rows past n get P = 0
+      else
+        sl = q < n ? Dh[q] : 0.f;
+    }
+  };
+  auto store = [&](int buf) {
+    bf16* base = tiles[buf];
+#pragma unroll
+    for (int it = 0; it < C::ITERS; ++it) {
+      const int x = tid + it * C::NT;
+      if (x < 2 * C::ITEMS) {
+        const int y = x % C::ITEMS;
+        const int g = y % (BQ / 4), cc = y / (BQ / 4);
+        const int which = x < C::ITEMS ? 0 : 1;  // 0: Q, 1: dO
+        store_rows_4x8<D>(base + which * C::TILE, 4 * g, 8 * cc, st[it]);
+        store_transposed_4x8<BQ>(base + (2 + which) * C::TILE, 4 * g, 8 * cc, st[it]);
+      }
+    }
+    if (tid < 2 * BQ) stats[buf][tid] = sl;
+  };
+
+  const int nqt = (n + BQ - 1) / BQ;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int i = 0; i < nqt; ++i) {
+    const int buf = i & 1;
+    if (i + 1 < nqt) load(i + 1);
+    const bf16* Qs = tiles[buf];
+    const bf16* dOs = tiles[buf] + C::TILE;
+    const bf16* Qt = tiles[buf] + 2 * C::TILE;
+    const bf16* dOt = tiles[buf] + 3 * C::TILE;
+
+    // S = Q K^T and dP = dO V^T (32 queries x 32 keys per wave).
+    f32x16 s = {}, dp = {};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      s = mfma_bf16_32x32x16(lds_operand<D>(Qs, li, 2 * kk + h), kreg[kk], s);
+      dp = mfma_bf16_32x32x16(lds_operand<D>(dOs, li, 2 * kk + h), vreg[kk], dp);
+    }
+    // Lane holds column `key`, rows (queries) 8(r/4) + 4h + r%4.
+    uint32_t pk[8], dsk[8];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 l2 = *reinterpret_cast<const f32x4*>(&stats[buf][8 * g + 4 * h]);
+      const f32x4 dd = *reinterpret_cast<const f32x4*>(&stats[buf][BQ + 8 * g + 4 * h]);
+      float p[4], ds[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p[e] = fast_exp2(__builtin_fmaf(s[4 * g + e], c, -l2[e]));
+        ds[e] = p[e] * (dp[4 * g + e] - dd[e]);
+      }
+      pk[2 * g] = pack_bf16x2(p[0], p[1]);
+      pk[2 * g + 1] = pack_bf16x2(p[2], p[3]);
+      dsk[2 * g] = pack_bf16x2(ds[0], ds[1]);
+      dsk[2 * g + 1] = pack_bf16x2(ds[2], ds[3]);
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS (contraction over the tile's queries).
+#pragma unroll
+    for (int ks = 0; ks < BQ / 16; ++ks) {
+      const bf16x8 bp = __builtin_bit_cast(
+          bf16x8, (u32x4{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]}));
+      const bf16x8 bs = __builtin_bit_cast(
+          bf16x8, (u32x4{dsk[4 * ks], dsk[4 * ks + 1], dsk[4 * ks + 2], dsk[4 * ks + 3]}));
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        dvt[db] = mfma_bf16_32x32x16(lds_operand<BQ>(dOt, db * 32 + li, 2 * ks + h), bp, dvt[db]);
+        dkt[db] = mfma_bf16_32x32x16(lds_operand<BQ>(Qt, db * 32 + li, 2 * ks + h), bs, dkt[db]);
+      }
+    }
+    if (i + 1 < nqt) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (key < n) {
+    float* dKr = dK + hoff + (size_t)key * D;
+    float* dVr = dV + hoff + (size_t)key * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = db * 32 + 8 * g + 4 * h;
+        f32x4 a = {dkt[db][4 * g] * scale, dkt[db][4 * g + 1] * scale, dkt[db][4 * g + 2] * scale,
+                   dkt[db][4 * g + 3] * scale};
+        f32x4 b = {dvt[db][4 * g], dvt[db][4 * g + 1], dvt[db][4 * g + 2], dvt[db][4 * g + 3]};
+        *reinterpret_cast<f32x4*>(dKr + col) = a;
+        *reinterpret_cast<f32x4*>(dVr + col) = b;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. dQ
+
+template <int D>
+struct DqCfg {
+  static constexpr int NW = 4, NT = 256, BQB = NW * 32, BC = 32;
+  static constexpr int ITEMS = (BC / 4) * (D / 8);
+  static constexpr int ITERS = (2 * ITEMS + NT - 1) / NT;
+  static constexpr int TILE = BC * D;
+  static constexpr int BUF_BF16 = 3 * TILE;  // K rows, V rows, K^T
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_dq(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dg,
+    float* __restrict__ dQ, int n, int nqb, int total, float c, float scale) {
+  using C = DqCfg<D>;
+  constexpr int BC = C::BC;
+  __shared__ __attribute__((aligned(16))) bf16 tiles[2][C::BUF_BF16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, li = lane & 31;
+  const int tile = xcd_remap(blockIdx.x, total);
+  const int head = tile / nqb, qblk = tile - head * nqb;
+  const size_t hoff = (size_t)head * n * D;
+  const bf16 *Qh = Q + hoff, *Kh = K + hoff, *Vh = V + hoff, *dOh = dO + hoff;
+  const int q = qblk * C::BQB + wave * 32 + li;
+
+  bf16x8 qreg[D / 16], dogreg[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    qreg[kk] = q < n ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)q * D + 16 * kk + 8 * h)
+                     : bf16x8{};
+    dogreg[kk] = q < n ? *reinterpret_cast<const bf16x8*>(dOh + (size_t)q * D + 16 * kk + 8 * h)
+                       : bf16x8{};
+  }
+  const float l2 = q < n ? lse[(size_t)head * n + q] * kLog2e : 0.f;
+  const float dq_d = q < n ? Dg[(size_t)head * n + q] : 0.f;
+  f32x16 dqt[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dqt[db] = f32x16{};
+
+  u32x4 st[C::ITERS][4];
+  auto load = [&](int j) {
+#pragma unroll
+    for (int it = 0; it < C::ITERS; ++it) {
+      const int x = tid + it * C::NT;
+      const int y = x % C::ITEMS;
+      const int g = y % (BC / 4), cc = y / (BC / 4);
+      const bf16* src = x < C::ITEMS ? Kh : Vh;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = j * BC + 4 * g + e;
+        st[it][e] = (x < 2 * C::ITEMS && key < n)
+                        ? *reinterpret_cast<const u32x4*>(src + (size_t)key * D + cc * 8)
+                        : u32x4{};
+      }
+    }
+  };
+  auto store = [&](int buf) {
+    bf16* base = tiles[buf];
+#pragma unroll
+    for (int it = 0; it < C::ITERS; ++it) {
+      const int x = tid + it * C::NT;
+      if (x < 2 * C::ITEMS) {
+        const int y = x % C::ITEMS;
+        const int g = y % (BC / 4), cc = y / (BC / 4);
+        if (x < C::ITEMS) {
+          store_rows_4x8<D>(base, 4 * g, 8 * cc, st[it]);
+          store_transposed_4x8<BC>(base + 2 * C::TILE, 4 * g, 8 * cc, st[it]);
+        } else {
+          store_rows_4x8<D>(base + C::TILE, 4 * g, 8 * cc, st[it]);
+        }
+      }
+    }
+  };
+
+  const int nkt = (n + BC - 1) / BC;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int j = 0; j < nkt; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < nkt) load(j + 1);
+    const bf16* Ks = tiles[buf];
+    const bf16* Vs = tiles[buf] + C::TILE;
+    const bf16* Kt = tiles[buf] + 2 * C::TILE;
+
+    // S^T = K Q^T and dP^T = V dO^T (32 keys x 32 queries per wave).
+    f32x16 s = {}, dp = {};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      s = mfma_bf16_32x32x16(lds_operand<D>(Ks, li, 2 * kk + h), qreg[kk], s);
+      dp = mfma_bf16_32x32x16(lds_operand<D>(Vs, li, 2 * kk + h), dogreg[kk], dp);
+    }
+    // Lane holds query column q, rows (keys) 8(r/4) + 4h + r%4.
+    const bool tail = j == nkt - 1 && (n % BC) != 0;
+    uint32_t dsk[8];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      float p0 = fast_exp2(__builtin_fmaf(s[r], c, -l2));
+      float p1 = fast_exp2(__builtin_fmaf(s[r + 1], c, -l2));
+      if (tail) {
+        const int k0 = j * BC + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (k0 >= n) p0 = 0.f;
+        if (k0 + 1 >= n) p1 = 0.f;
+      }
+      dsk[r >> 1] = pack_bf16x2(p0 * (dp[r] - dq_d), p1 * (dp[r + 1] - dq_d));
+    }
+    // dQ^T += K^T dS^T (contraction over the tile's keys).
+#pragma unroll
+    for (int ks = 0; ks < BC / 16; ++ks) {
+      const bf16x8 bs = __builtin_bit_cast(
+          bf16x8, (u32x4{dsk[4 * ks], dsk[4 * ks + 1], dsk[4 * ks + 2], dsk[4 * ks + 3]}));
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        dqt[db] = mfma_bf16_32x32x16(lds_operand<BC>(Kt, db * 32 + li, 2 * ks + h), bs, dqt[db]);
+    }
+    if (j + 1 < nkt) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (q < n) {
+    float* dQr = dQ + hoff + (size_t)q * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 a = {dqt[db][4 * g] * scale, dqt[db][4 * g + 1] * scale, dqt[db][4 * g + 2] * scale,
+                   dqt[db][4 * g + 3] * scale};
+        *reinterpret_cast<f32x4*>(dQr + db * 32 + 8 * g + 4 * h) = a;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+
+namespace {
+
+template <int D>
+hipError_t launch(const void* Q, const void* K, const void* V, const float* O, const void* dO,
+                  const float* lse, float* dQ, float* dK, float* dV, int64_t bh, int64_t n,
+                  float scale, void* ws, hipStream_t stream) {
+  const bf16* q = static_cast<const bf16*>(Q);
+  const bf16* k = static_cast<const bf16*>(K);
+  const bf16* v = static_cast<const bf16*>(V);
+  const bf16* g = static_cast<const bf16*>(dO);
+  float* Dbuf = static_cast<float*>(ws);
+  const float c = scale * kLog2e;
+  const int64_t rows = bh * n;
+  constexpr int RPB = 256 / (D / 8);
+  hipLaunchKernelGGL(bwd_preprocess<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
+                     stream, O, g, Dbuf, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nkb = (int)((n + DkdvCfg<D>::BKV - 1) / DkdvCfg<D>::BKV);
+  const int total_kv = (int)(bh * nkb);
+  hipLaunchKernelGGL(bwd_dkdv<D>, dim3(total_kv), dim3(256), 0, stream, q, k, v, g, lse, Dbuf, dK,
+                     dV, (int)n, nkb, total_kv, c, scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nqb = (int)((n + DqCfg<D>::BQB - 1) / DqCfg<D>::BQB);
+  const int total_q = (int)(bh * nqb);
+  hipLaunchKernelGGL(bwd_dq<D>, dim3(total_q), dim3(256), 0, stream, q, k, v, g, lse, Dbuf, dQ,
+                     (int)n, nqb, total_q, c, scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool bwd_supported(int64_t d) { return d == 64 || d == 128; }
+
+size_t bwd_workspace_bytes(int64_t bh, int64_t n, int64_t) {
+  return ((size_t)bh * n * 4 + 255) & ~size_t(255);
+}
+
+hipError_t launch_bwd_bf16(const void* Q, const void* K, const void* V, const float* O,
+                           const void* dO, const float* lse, float* dQ, float* dK, float* dV,
+                           int64_t bh, int64_t n, int64_t d, float scale, void* workspace,
+                           hipStream_t stream) {
+  switch (d) {
+    case 64: return launch<64>(Q, K, V, O, dO, lse, dQ, dK, dV, bh, n, scale, workspace, stream);
+    case 128: return launch<128>(Q, K, V, O, dO, lse, dQ, dK, dV, bh, n, scale, workspace, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace at

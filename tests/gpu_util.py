@@ -48,12 +48,18 @@ def rel_fro(a: np.ndarray, b: np.ndarray) -> float:
     return float(np.linalg.norm(a - b)) / den if den > 0 else float(np.linalg.norm(a - b))
 
 
-def check(got: np.ndarray, ref: np.ndarray, tol: float, what: str):
+def check(got: np.ndarray, ref: np.ndarray, tol: float, what: str, scaled: bool = False):
+    """Max-abs comparison.  With ``scaled`` (stress inputs multiplied beyond
+    the stated workloads, whose outputs grow with them) the bar is tol times
+    max(1, max|ref|), i.e. the same bar relative to the output's size."""
     assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     err = max_abs(got, ref)
-    say(f"  {what}: max|err| {err:.3e} (tol {tol:g}), rel fro {rel_fro(got, ref):.2e}")
-    assert err <= tol, f"{what}: max abs error {err:.3e} > {tol:g}"
+    big = float(np.max(np.abs(ref))) if ref.size else 0.0
+    lim = tol * max(1.0, big) if scaled else tol
+    say(f"  {what}: max|err| {err:.3e} (bar {lim:.3g}), max|ref| {big:.3g}, "
+        f"rel fro {rel_fro(got, ref):.2e}")
+    assert err <= lim, f"{what}: max abs error {err:.3e} > {lim:.3g}"
 
 
 def inputs(bh, n, d, dtype, seed, q_mult=1.0, with_do=False, device="cuda"):
