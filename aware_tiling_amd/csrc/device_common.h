@@ -83,6 +83,38 @@ __device__ __forceinline__ int chunk_swizzle(int row) {
     return ((row >> 1) ^ (row >> 2)) & 3;
 }
 
+// Swizzle of the 16-byte chunk index for a row-major value tile read with
+// ds_read_b64_tr_b16 (rows of ROW_BYTES).  One such read touches 4
+// consecutive rows at the same 4-chunk group per half wave; flipping bits 2-3
+// of the chunk index by the row (d >= 128) or by row bit 1 (d = 64, two rows
+// per 256 bytes) spreads those 4 rows over all 64 banks.
+template <int ROW_BYTES>
+__device__ __forceinline__ int vtr_swizzle(int row) {
+  if constexpr (ROW_BYTES >= 256)
+    return 4 * (row & 3);
+  else
+    return 4 * ((row >> 1) & 1);
+}
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's 16 bytes land at lds_wave_base + 16 l.  lds_wave_base must be
+// uniform across the wave.
+__device__ __forceinline__ void load_lds_16(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_wave_base,
+                                   16, 0, 0);
+}
+
+// Four bf16 of a transposed LDS read (ds_read_b64_tr_b16).  Within each group
+// of 16 lanes, lane i receives element (i mod 4) of the 8 bytes addressed by
+// lanes 4e + i/4, for e = 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const bf16* p) {
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(
+          (__attribute__((address_space(3))) char*)(const_cast<bf16*>(p))));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // Position of key k inside a transposed value tile: within each group of 16
 // keys, bits 2 and 3 of the key index are swapped, so that the 8 keys one
 // lane feeds to the P*V product (see the fused kernel) are contiguous.

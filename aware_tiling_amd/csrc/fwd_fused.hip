@@ -33,8 +33,8 @@
 //
 // The row sum l is accumulated from the bf16-rounded P values (the ones the
 // MFMA multiplies), so the normalisation matches the weights used.
-#include <cstdio>
 #include <cstdlib>
+#include <cstring>
 
 #include "device_common.h"
 #include "launch.h"
@@ -307,6 +307,622 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_fused_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Software-pipelined variant (one 32-row query block per wave).  Within each
+// wave the score tile of step j+1 is issued on the matrix cores before the
+// softmax of step j runs on the vector ALUs, so the two overlap:
+//
+//   step j:  global -> registers: K tile j+2, V tile j+1
+//            S_{j+1} = K_{j+1} Q^T        (MFMA, LDS K buffer (j+1)%2)
+//            softmax(S_j) -> P_j          (VALU)
+//            U^T += V_j^T P_j^T           (MFMA, LDS V buffer j%2)
+//            registers -> LDS: K_{j+2} into K buffer j%2, V_{j+1} into V
+//            buffer (j+1)%2;  barrier
+//
+// K runs two tiles ahead of V, so two buffers of each still need only one
+// barrier per step: the K buffer written in step j held K_j, last read in
+// step j-1, and the V buffer written held V_{j-1}, also last read in step
+// j-1.  Steps are unrolled in pairs so every LDS offset is a compile-time
+// constant; only the last tile takes the guarded loads and the key mask.
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+template <int D, int NW, int BC>
+struct PipeCfg {
+  static constexpr int NT = NW * 64;
+  static constexpr int BR = NW * 32;
+  static constexpr int KEYS = BC;
+  static constexpr int CPR = D / 8;
+  static constexpr int K_CHUNKS = BC * CPR;
+  static constexpr int K_ITERS = (K_CHUNKS + NT - 1) / NT;
+  static constexpr int V_ITEMS = (BC / 4) * CPR;
+  static constexpr int V_ITERS = (V_ITEMS + NT - 1) / NT;
+  static constexpr int KS = BC * D;
+  static constexpr int VT = D * BC;
+  static constexpr int LDS_ELEMS = 2 * (KS + VT);
+  static constexpr int MINB = NW >= 8 ? 1 : 8 / NW;  // two waves per SIMD
+  static constexpr int64_t ONCHIP = (int64_t)BR * D * 2 + 2 * BR + 2 * BC * D + (int64_t)BR * BC;
+};
+
+template <int D, int NW, int BC>
+__global__ __launch_bounds__(NW * 64, (NW >= 8 ? 1 : 8 / NW)) void fwd_fused_bf16_pipe_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    float* __restrict__ O, float* __restrict__ lse, int n, int nqb, int total, float c) {
+  using C = PipeCfg<D, NW, BC>;
+  __shared__ __attribute__((aligned(16))) bf16 smem[C::LDS_ELEMS];
+  bf16* const Ksb = smem;                 // [2][KS]
+  bf16* const Vtb = smem + 2 * C::KS;     // [2][VT]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;
+  const int li = lane & 31;
+
+  const int tile = xcd_remap(blockIdx.x, total);
+  const int head = tile / nqb;
+  const int qblk = tile - head * nqb;
+  const size_t hoff = (size_t)head * (size_t)n * D;
+  const bf16* Qh = Q + hoff;
+  const bf16* Kh = K + hoff;
+  const bf16* Vh = V + hoff;
+  const int q = qblk * C::BR + wave * 32 + li;
+
+  bf16x8 qreg[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    qreg[kk] = q < n ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)q * D + kk * 16 + 8 * h)
+                     : bf16x8{};
+
+  f32x16 uacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) uacc[db] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+  const int nt = (n + BC - 1) / BC;
+
+  u32x4 kreg[C::K_ITERS];
+  u32x4 vreg[C::V_ITERS][4];
+
+  auto load_k = [&](int t) {
+    const int kbase = t * BC;
+    const bool full = kbase + BC <= n;
+#pragma unroll
+    for (int it = 0; it < C::K_ITERS; ++it) {
+      const int x = tid + it * C::NT;
+      const int row = x / C::CPR, cc = x % C::CPR;
+      const bool ok = (C::K_CHUNKS % C::NT == 0 || x < C::K_CHUNKS) && (full || kbase + row < n);
+      kreg[it] = ok ? *reinterpret_cast<const u32x4*>(Kh + (size_t)(kbase + row) * D + cc * 8)
+                    : u32x4{};
+    }
+  };
+  auto load_v = [&](int t) {
+    const int kbase = t * BC;
+    const bool full = kbase + BC <= n;
+#pragma unroll
+    for (int it = 0; it < C::V_ITERS; ++it) {
+      const int x = tid + it * C::NT;
+      const int g = x % (BC / 4), cc = x / (BC / 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool ok =
+            (C::V_ITEMS % C::NT == 0 || x < C::V_ITEMS) && (full || kbase + 4 * g + e < n);
+        vreg[it][e] =
+            ok ? *reinterpret_cast<const u32x4*>(Vh + (size_t)(kbase + 4 * g + e) * D + cc * 8)
+               : u32x4{};
+      }
+    }
+  };
+  auto store_k = [&](bf16* Ks) {
+#pragma unroll
+    for (int it = 0; it < C::K_ITERS; ++it) {
+      const int x = tid + it * C::NT;
+      if (C::K_CHUNKS % C::NT == 0 || x < C::K_CHUNKS) {
+        const int row = x / C::CPR, cc = x % C::CPR;
+        *reinterpret_cast<u32x4*>(Ks + row * D + ((cc ^ chunk_swizzle<D * 2>(row)) * 8)) =
+            kreg[it];
+      }
+    }
+  };
+  auto store_v = [&](bf16* Vt) {
+#pragma unroll
+    for (int it = 0; it < C::V_ITERS; ++it) {
+      const int x = tid + it * C::NT;
+      if (C::V_ITEMS % C::NT == 0 || x < C::V_ITEMS) {
+        const int g = x % (BC / 4), cc = x / (BC / 4);
+        const int pos = vt_key_pos(4 * g);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int r0 = cc * 8 + 2 * w;
+          const int r1 = r0 + 1;
+          u32x2 lo = {pair_lo(vreg[it][0][w], vreg[it][1][w]),
+                      pair_lo(vreg[it][2][w], vreg[it][3][w])};
+          u32x2 hi = {pair_hi(vreg[it][0][w], vreg[it][1][w]),
+                      pair_hi(vreg[it][2][w], vreg[it][3][w])};
+          *reinterpret_cast<u32x2*>(Vt + r0 * BC +
+                                    (((pos >> 3) ^ chunk_swizzle<BC * 2>(r0)) * 8) + (pos & 7)) = lo;
+          *reinterpret_cast<u32x2*>(Vt + r1 * BC +
+                                    (((pos >> 3) ^ chunk_swizzle<BC * 2>(r1)) * 8) + (pos & 7)) = hi;
+        }
+      }
+    }
+  };
+  auto compute_s = [&](const bf16* Ks, f32x16 (&s)[BC / 32]) {
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb) {
+        const int row = kb * 32 + li;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+            Ks + row * D + (((2 * kk + h) ^ chunk_swizzle<D * 2>(row)) * 8));
+        s[kb] = mfma_bf16_32x32x16(a, qreg[kk], s[kb]);
+      }
+  };
+  // Online softmax, part 1: row maximum, the new reference m and the
+  // rescale of l and U (the only branch; taken when some row's maximum rose
+  // by more than kTau).  Returns m.
+  auto softmax_max = [&](f32x16 (&s)[BC / 32], bool mask, int kbase) {
+    if (mask) {
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kbase + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3) >= n) s[kb][r] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mc = mx * c;
+    const bool need = mc > m + kTau;
+    const float mn = need ? mc : m;
+    const float alpha = need ? fast_exp2(m - mn) : 1.0f;
+    m = mn;
+    l *= alpha;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) uacc[db] *= alpha;
+    }
+  };
+  // Online softmax, part 2: exponentials in bf16 and their row sum
+  // (branch-free, so it can interleave with the matrix-core work).
+  auto softmax_exp = [&](const f32x16 (&s)[BC / 32], uint32_t (&pk)[BC / 32][8]) {
+    float lsum = l;
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = fast_exp2(__builtin_fmaf(s[kb][r], c, -m));
+        const float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], c, -m));
+        const uint32_t pp = pack_bf16x2(p0, p1);
+        pk[kb][r >> 1] = pp;
+        lsum = add_bf16x2(pp, lsum);
+      }
+    l = lsum;
+  };
+  auto pv = [&](const bf16* Vt, const uint32_t (&pk)[BC / 32][8]) {
+#pragma unroll
+    for (int ks = 0; ks < BC / 16; ++ks) {
+      const int kb = ks >> 1, half = ks & 1;
+      u32x4 t = {pk[kb][4 * half + 0], pk[kb][4 * half + 1], pk[kb][4 * half + 2],
+                 pk[kb][4 * half + 3]};
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, t);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int row = db * 32 + li;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+            Vt + row * BC + (((4 * kb + 2 * half + h) ^ chunk_swizzle<BC * 2>(row)) * 8));
+        uacc[db] = mfma_bf16_32x32x16(a, pb, uacc[db]);
+      }
+    }
+  };
+
+  // Prologue: K_0, K_1, V_0 into LDS; S_0.
+  load_k(0);
+  load_v(0);
+  store_k(Ksb);
+  store_v(Vtb);
+  if (nt > 1) {
+    load_k(1);
+    store_k(Ksb + C::KS);
+  }
+  __syncthreads();
+  f32x16 s_cur[BC / 32];
+  compute_s(Ksb, s_cur);
+  __syncthreads();  // every wave has read K_0 before step 0 overwrites it
+
+  // Steady state: step j < nt-1, parity P = j % 2.
+  auto step = [&](auto par, int j) {
+    constexpr int P = decltype(par)::value;
+    const bool has2 = j + 2 < nt;
+    if (has2) load_k(j + 2);
+    load_v(j + 1);
+    softmax_max(s_cur, false, 0);
+    // one straight-line block: S_{j+1} on the matrix cores while the
+    // exponentials of S_j run, then U += V_j P_j
+    f32x16 s_next[BC / 32];
+    compute_s(Ksb + (P ^ 1) * C::KS, s_next);
+    uint32_t pk[BC / 32][8];
+    softmax_exp(s_cur, pk);
+    pv(Vtb + P * C::VT, pk);
+    if (has2) store_k(Ksb + P * C::KS);
+    store_v(Vtb + (P ^ 1) * C::VT);
+    __syncthreads();
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb) s_cur[kb] = s_next[kb];
+  };
+  int j = 0;
+  for (; j + 2 < nt; j += 2) {
+    step(IntC<0>{}, j);
+    step(IntC<1>{}, j + 1);
+  }
+  if (j + 1 < nt) {
+    step(IntC<0>{}, j);
+    ++j;
+  }
+  // Last step (j = nt-1): no next tile; mask keys past n.
+  {
+    uint32_t pk[BC / 32][8];
+    softmax_max(s_cur, (n % BC) != 0, j * BC);
+    softmax_exp(s_cur, pk);
+    pv(Vtb + (j & 1) * C::VT, pk);
+  }
+
+  const float lt = l + __shfl_xor(l, 32);
+  const float inv = 1.0f / lt;
+  if (q < n) {
+    float* Oh = O + hoff;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v = {uacc[db][4 * g + 0] * inv, uacc[db][4 * g + 1] * inv,
+                   uacc[db][4 * g + 2] * inv, uacc[db][4 * g + 3] * inv};
+        *reinterpret_cast<f32x4*>(Oh + (size_t)q * D + db * 32 + 8 * g + 4 * h) = v;
+      }
+    if (h == 0 && lse != nullptr) lse[(size_t)head * n + q] = (m + __log2f(lt)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Direct-load variant for gfx950.  K and V tiles travel global -> LDS with
+// global_load_lds_dwordx4 (no staging registers, no vector-ALU work), both
+// kept row-major in LDS.  The V^T operand of U^T += V^T P^T is read with the
+// LDS transpose read ds_read_b64_tr_b16: the four lanes 4e..4e+3 of a
+// 16-lane group point at 4 consecutive d values of key K0+e, so each lane
+// receives one d column across 4 consecutive keys; two reads give the 8
+// k-slots, and K0 of each read follows the key order of the score
+// accumulator, so P^T still feeds the MFMA straight from registers.
+//
+// The schedule is the software-pipelined one above (S_{j+1} on the matrix
+// cores while the softmax of S_j runs; K two tiles ahead, V one tile ahead,
+// two LDS buffers each, one barrier per step).  Rows past n are clamped to
+// row n-1 when loading (finite data; those keys are masked in the last
+// tile), so no load leaves the tensor.
+
+template <int D, int NW, int BC, bool PIPE = true, int WPS = 2, bool SCHED = false,
+          int STAGES = 2>
+struct DirectCfg {
+  static constexpr int NT = NW * 64;
+  static constexpr int BR = NW * 32;
+  static constexpr int KEYS = BC;
+  static constexpr int CPR = D / 8;                // 16-byte chunks per row
+  static constexpr int CHUNKS = BC * CPR;          // per tile, per tensor
+  static constexpr int WAVE_CHUNKS = CHUNKS / NW;  // per wave, per tensor
+  static constexpr int INSTS = WAVE_CHUNKS / 64;   // load instructions per wave per tensor
+  static constexpr int TILE = BC * D;              // bf16 elements per tile
+  static constexpr int LDS_ELEMS = 2 * STAGES * TILE;  // K[STAGES], V[STAGES]
+  static constexpr int64_t ONCHIP = (int64_t)BR * D * 2 + 2 * BR + 2 * BC * D + (int64_t)BR * BC;
+  static_assert(CHUNKS % (NW * 64) == 0, "tile must split into whole wave loads");
+};
+
+// PIPE selects the cross-tile pipelining of S; WPS is the number of waves
+// per SIMD the register budget is sized for (without PIPE each wave holds
+// one score tile, so more waves fit and the hardware interleaves them).
+template <int D, int NW, int BC, bool PIPE, int WPS, bool SCHED, int STAGES>
+__global__ __launch_bounds__(NW * 64, (WPS * 4 / NW > 0 ? WPS * 4 / NW : 1)) void
+fwd_fused_bf16_direct_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                             const bf16* __restrict__ V, float* __restrict__ O,
+                             float* __restrict__ lse, int n, int nqb, int total, float c) {
+  using C = DirectCfg<D, NW, BC, PIPE, WPS, SCHED, STAGES>;
+  __shared__ __attribute__((aligned(1024))) bf16 smem[C::LDS_ELEMS];
+  bf16* const Kb = smem;                     // [STAGES][TILE]
+  bf16* const Vb = smem + STAGES * C::TILE;  // [STAGES][TILE]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+  const int li = lane & 31;
+
+  const int tile = xcd_remap(blockIdx.x, total);
+  const int head = tile / nqb;
+  const int qblk = tile - head * nqb;
+  const size_t hoff = (size_t)head * (size_t)n * D;
+  const bf16* Qh = Q + hoff;
+  const bf16* Kh = K + hoff;
+  const bf16* Vh = V + hoff;
+  const int q = qblk * C::BR + wave * 32 + li;
+
+  bf16x8 qreg[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    qreg[kk] = q < n ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)q * D + kk * 16 + 8 * h)
+                     : bf16x8{};
+
+  f32x16 uacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) uacc[db] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+  const int nt = (n + BC - 1) / BC;
+
+  // Issue the direct loads of tile t of `src` into the LDS tile `dst`.  Lane
+  // chunk p of this wave is LDS chunk (row, phys); it fetches logical chunk
+  // phys ^ swizzle(row) of that row.
+  auto load_tile = [&](const bf16* src, bf16* dst, int t, auto swz) {
+    const int kbase = t * BC;
+#pragma unroll
+    for (int it = 0; it < C::INSTS; ++it) {
+      const int p0 = wave * C::WAVE_CHUNKS + it * 64;  // wave-uniform
+      const int p = p0 + lane;
+      const int row = p / C::CPR, phys = p % C::CPR;
+      const int logical = phys ^ swz(row);
+      const int grow = min(kbase + row, n - 1);
+      load_lds_16(src + (size_t)grow * D + logical * 8, dst + p0 * 8);
+    }
+  };
+  auto kswz = [](int row) { return chunk_swizzle<D * 2>(row); };
+  auto vswz = [](int row) { return vtr_swizzle<D * 2>(row); };
+
+  auto compute_s = [&](const bf16* Ks, f32x16 (&s)[BC / 32]) {
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb) {
+        const int row = kb * 32 + li;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+            Ks + row * D + (((2 * kk + h) ^ chunk_swizzle<D * 2>(row)) * 8));
+        s[kb] = mfma_bf16_32x32x16(a, qreg[kk], s[kb]);
+      }
+  };
+  auto softmax_max = [&](f32x16 (&s)[BC / 32], bool mask, int kbase) {
+    if (mask) {
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kbase + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3) >= n) s[kb][r] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mc = mx * c;
+    const bool need = mc > m + kTau;
+    const float mn = need ? mc : m;
+    const float alpha = need ? fast_exp2(m - mn) : 1.0f;
+    m = mn;
+    l *= alpha;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) uacc[db] *= alpha;
+    }
+  };
+  auto softmax_exp = [&](const f32x16 (&s)[BC / 32], uint32_t (&pk)[BC / 32][8]) {
+    float lsum = l;
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = fast_exp2(__builtin_fmaf(s[kb][r], c, -m));
+        const float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], c, -m));
+        const uint32_t pp = pack_bf16x2(p0, p1);
+        pk[kb][r >> 1] = pp;
+        lsum = add_bf16x2(pp, lsum);
+      }
+    l = lsum;
+  };
+  // U^T += V^T P^T with the V^T operand from transposed LDS reads.  Lane
+  // group G = lane/16 covers d rows 16(G&1)..+15 of the 32-row block and
+  // key half hh = G/2; source lane s points at key K0 + s/4, d D0 + 4(s%4).
+  const int G = lane >> 4, sl = lane & 15;
+  const int hh = G >> 1;
+  auto pv = [&](const bf16* Vs, const uint32_t (&pk)[BC / 32][8]) {
+#pragma unroll
+    for (int ks = 0; ks < BC / 16; ++ks) {
+      const int kb = ks >> 1, half = ks & 1;
+      u32x4 t = {pk[kb][4 * half + 0], pk[kb][4 * half + 1], pk[kb][4 * half + 2],
+                 pk[kb][4 * half + 3]};
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, t);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        u32x2 part[2];
+#pragma unroll
+        for (int piece = 0; piece < 2; ++piece) {
+          const int row = kb * 32 + 16 * half + 8 * piece + 4 * hh + (sl >> 2);
+          const int d0 = db * 32 + 16 * (G & 1) + 4 * (sl & 3);
+          const int phys = (d0 >> 3) ^ vtr_swizzle<D * 2>(row);
+          part[piece] = lds_read_tr16(Vs + row * D + phys * 8 + (d0 & 7));
+        }
+        const bf16x8 a =
+            __builtin_bit_cast(bf16x8, (u32x4{part[0][0], part[0][1], part[1][0], part[1][1]}));
+        uacc[db] = mfma_bf16_32x32x16(a, pb, uacc[db]);
+      }
+    }
+  };
+
+  f32x16 s_cur[BC / 32];
+  int j = 0;
+  if constexpr (PIPE && STAGES == 3) {
+    // Three-slot ring: step j issues K_{j+3} and V_{j+2}, so every load has
+    // two steps to land, and the wait before each barrier leaves the
+    // current step's loads in flight (vmcnt = loads issued this step).
+    load_tile(Kh, Kb, 0, kswz);
+    load_tile(Vh, Vb, 0, vswz);
+    if (nt > 1) {
+      load_tile(Kh, Kb + C::TILE, 1, kswz);
+      load_tile(Vh, Vb + C::TILE, 1, vswz);
+    }
+    if (nt > 2) load_tile(Kh, Kb + 2 * C::TILE, 2, kswz);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    compute_s(Kb, s_cur);
+    __syncthreads();  // every wave has read K_0 before step 0 overwrites it
+
+    auto step = [&](auto par, int j) {
+      constexpr int P = decltype(par)::value;  // j % 3
+      constexpr int P1 = (P + 1) % 3, P2 = (P + 2) % 3;
+      const bool k3 = j + 3 < nt, v2 = j + 2 < nt;
+      if (k3) load_tile(Kh, Kb + P * C::TILE, j + 3, kswz);
+      if (v2) load_tile(Vh, Vb + P2 * C::TILE, j + 2, vswz);
+      softmax_max(s_cur, false, 0);
+      f32x16 s_next[BC / 32];
+      compute_s(Kb + P1 * C::TILE, s_next);
+      uint32_t pk[BC / 32][8];
+      softmax_exp(s_cur, pk);
+      pv(Vb + P * C::TILE, pk);
+      // vmcnt(x): expcnt and lgkmcnt fields left at their maxima
+      static_assert(C::INSTS <= 4, "wait counts below assume at most 4 loads per tensor");
+      if (k3 && v2)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * C::INSTS));
+      else if (k3 || v2)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | C::INSTS);
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb) s_cur[kb] = s_next[kb];
+    };
+    for (; j + 3 < nt; j += 3) {
+      step(IntC<0>{}, j);
+      step(IntC<1>{}, j + 1);
+      step(IntC<2>{}, j + 2);
+    }
+    if (j + 1 < nt) {
+      step(IntC<0>{}, j);
+      ++j;
+    }
+    if (j + 1 < nt) {
+      step(IntC<1>{}, j);
+      ++j;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  } else if constexpr (PIPE) {
+    // Prologue: K_0, V_0, K_1 into LDS; S_0.
+    load_tile(Kh, Kb, 0, kswz);
+    load_tile(Vh, Vb, 0, vswz);
+    if (nt > 1) load_tile(Kh, Kb + C::TILE, 1, kswz);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    compute_s(Kb, s_cur);
+    __syncthreads();  // every wave has read K_0 before step 0 overwrites it
+
+    auto step = [&](auto par, int j) {
+      constexpr int P = decltype(par)::value;
+      if (j + 2 < nt) load_tile(Kh, Kb + P * C::TILE, j + 2, kswz);
+      load_tile(Vh, Vb + (P ^ 1) * C::TILE, j + 1, vswz);
+      softmax_max(s_cur, false, 0);
+      f32x16 s_next[BC / 32];
+      compute_s(Kb + (P ^ 1) * C::TILE, s_next);
+      uint32_t pk[BC / 32][8];
+      softmax_exp(s_cur, pk);
+      pv(Vb + P * C::TILE, pk);
+      if constexpr (SCHED) {
+        // Interleave: each S_{j+1} MFMA with ~7 softmax instructions and
+        // the K operand read of the MFMA two places later; then each PV
+        // MFMA with the two transposed V reads of the MFMA two places later.
+        constexpr int NS = (D / 16) * (BC / 32);  // S MFMAs
+        constexpr int NPV = (BC / 16) * (D / 32);  // PV MFMAs
+        constexpr int AHEAD = 2;
+        __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // DS read
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          if (i + AHEAD < NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          else if (i + AHEAD - NS < AHEAD) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // VALU
+        }
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i + AHEAD < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb) s_cur[kb] = s_next[kb];
+    };
+    for (; j + 2 < nt; j += 2) {
+      step(IntC<0>{}, j);
+      step(IntC<1>{}, j + 1);
+    }
+    if (j + 1 < nt) {
+      step(IntC<0>{}, j);
+      ++j;
+    }
+  } else {
+    // Tile j+1 is fetched into the other buffer while tile j is used.
+    load_tile(Kh, Kb, 0, kswz);
+    load_tile(Vh, Vb, 0, vswz);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    auto step = [&](auto par, int j) {
+      constexpr int P = decltype(par)::value;
+      load_tile(Kh, Kb + (P ^ 1) * C::TILE, j + 1, kswz);
+      load_tile(Vh, Vb + (P ^ 1) * C::TILE, j + 1, vswz);
+      compute_s(Kb + P * C::TILE, s_cur);
+      softmax_max(s_cur, false, 0);
+      uint32_t pk[BC / 32][8];
+      softmax_exp(s_cur, pk);
+      pv(Vb + P * C::TILE, pk);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    };
+    for (; j + 2 < nt; j += 2) {
+      step(IntC<0>{}, j);
+      step(IntC<1>{}, j + 1);
+    }
+    if (j + 1 < nt) {
+      step(IntC<0>{}, j);
+      ++j;
+    }
+    compute_s(Kb + (j & 1) * C::TILE, s_cur);
+  }
+  {
+    uint32_t pk[BC / 32][8];
+    softmax_max(s_cur, (n % BC) != 0, j * BC);
+    softmax_exp(s_cur, pk);
+    pv(Vb + (j % STAGES) * C::TILE, pk);
+  }
+
+  const float lt = l + __shfl_xor(l, 32);
+  const float inv = 1.0f / lt;
+  if (q < n) {
+    float* Oh = O + hoff;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v = {uacc[db][4 * g + 0] * inv, uacc[db][4 * g + 1] * inv,
+                   uacc[db][4 * g + 2] * inv, uacc[db][4 * g + 3] * inv};
+        *reinterpret_cast<f32x4*>(Oh + (size_t)q * D + db * 32 + 8 * g + 4 * h) = v;
+      }
+    if (h == 0 && lse != nullptr) lse[(size_t)head * n + q] = (m + __log2f(lt)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 path: same schedule with v_mfma_f32_32x32x2_f32 and exact per-tile
 // rescaling.  One wave per 32 query rows, 4 waves, 32-key tiles, single
 // LDS buffer.  Each lane holds one element of each MFMA operand, so the
@@ -419,31 +1035,64 @@ __global__ __launch_bounds__(256, 1) void fwd_fused_f32_kernel(
 // ---------------------------------------------------------------------------
 // Host launchers.
 //
-// Several tile shapes are compiled per head dimension; the first entry of
-// each list is the default.  The environment variable ATTN_FWD_TILE
-// ("QBxNWxBC", e.g. "1x8x64") selects another compiled shape, for tile
-// sweeps; an unknown value falls back to the default.
+// Several kernels and tile shapes are compiled per head dimension; the first
+// entry for a head dimension is its default.  The environment variable
+// ATTN_FWD_TILE selects another compiled entry by name, for tile sweeps:
+// "QBxNWxBC" (e.g. "1x8x64") names the basic kernel with QB 32-row query
+// blocks per wave, NW waves and BC-key tiles; "pNWxBC" (e.g. "p8x64") names
+// the software-pipelined kernel.  An unknown name falls back to the default.
 
 namespace {
 
+typedef void (*FusedKernel)(const bf16*, const bf16*, const bf16*, float*, float*, int, int, int,
+                            float);
+
 struct FusedEntry {
-  int d, qb, nw, bc;
+  const char* name;
+  int d, nw;
   FusedTileInfo info;
-  void (*kernel)(const bf16*, const bf16*, const bf16*, float*, float*, int, int, int, float);
+  FusedKernel kernel;
 };
 
 template <int D, int QB, int NW, int BC>
-FusedEntry entry() {
+FusedEntry basic(const char* name) {
   using C = FusedCfg<D, QB, NW, BC>;
-  return FusedEntry{D, QB, NW, BC, FusedTileInfo{C::BR, C::KEYS, C::ONCHIP},
+  return FusedEntry{name, D, NW, FusedTileInfo{C::BR, C::KEYS, C::ONCHIP},
                     &fwd_fused_bf16_kernel<D, QB, NW, BC>};
+}
+
+template <int D, int NW, int BC, bool PIPE = true, int WPS = 2, bool SCHED = false,
+          int STAGES = 2>
+FusedEntry direct(const char* name) {
+  using C = DirectCfg<D, NW, BC, PIPE, WPS, SCHED, STAGES>;
+  return FusedEntry{name, D, NW, FusedTileInfo{C::BR, C::KEYS, C::ONCHIP},
+                    &fwd_fused_bf16_direct_kernel<D, NW, BC, PIPE, WPS, SCHED, STAGES>};
+}
+
+template <int D, int NW, int BC>
+FusedEntry piped(const char* name) {
+  using C = PipeCfg<D, NW, BC>;
+  return FusedEntry{name, D, NW, FusedTileInfo{C::BR, C::KEYS, C::ONCHIP},
+                    &fwd_fused_bf16_pipe_kernel<D, NW, BC>};
 }
 
 const FusedEntry* registry(int& count) {
   static const FusedEntry table[] = {
-      entry<64, 2, 4, 64>(),  entry<64, 2, 8, 32>(),  entry<64, 2, 4, 32>(),
-      entry<128, 1, 8, 64>(), entry<128, 2, 4, 32>(), entry<128, 1, 8, 32>(),
-      entry<128, 1, 4, 64>(), entry<256, 1, 4, 32>(),
+      // head dimension 64
+      direct<64, 8, 64, true, 2, false, 3>("t8x64"),
+      direct<64, 8, 64>("d8x64"),
+      direct<64, 8, 64, true, 2, true>("s8x64"),
+      piped<64, 8, 64>("p8x64"),
+      basic<64, 2, 8, 32>("2x8x32"),
+      // head dimension 128
+      direct<128, 8, 64>("d8x64"),
+      direct<128, 8, 64, true, 2, true>("s8x64"),
+      direct<128, 4, 64>("d4x64"),
+      direct<128, 8, 32, false, 3>("n8x32w3"),
+      piped<128, 8, 64>("p8x64"),
+      basic<128, 1, 8, 64>("1x8x64"),
+      // head dimension 256
+      basic<256, 1, 4, 32>("1x4x32"),
   };
   count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
@@ -460,10 +1109,9 @@ const FusedEntry* pick(int64_t d) {
     }
   if (!def) return nullptr;
   const char* env = getenv("ATTN_FWD_TILE");
-  int qb = 0, nw = 0, bc = 0;
-  if (env && sscanf(env, "%dx%dx%d", &qb, &nw, &bc) == 3)
+  if (env)
     for (int i = 0; i < count; ++i)
-      if (t[i].d == d && t[i].qb == qb && t[i].nw == nw && t[i].bc == bc) return &t[i];
+      if (t[i].d == d && strcmp(t[i].name, env) == 0) return &t[i];
   return def;
 }
 

@@ -25,7 +25,9 @@ Reported (one JSON line on stdout):
                d 256) and the backward (batch 2 x 16 heads, N 4096, d 128)
                timed the same way, when built (not part of `value`).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-secondary]
+       python bench.py --calibrate-copy          (copy kernel for counter scaling)
+       python bench.py --summarize-counters DIR  (write the traffic summary)
 """
 from __future__ import annotations
 
@@ -45,6 +47,7 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
 HEADLINE = "fwd_bf16_b1h32_n16384_d128_qx4"
 METRIC = "attention fwd TFLOP/s (4N²d/head) and % of bf16 MFMA peak; HBM GB/s at 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_fwd_n16384_d128.json")
+COPY_BYTES = 1 << 30  # counter calibration: bytes read and written per copy
 KERNEL_SOURCES = ["aware_tiling_amd/csrc/fwd_fused.hip", "aware_tiling_amd/csrc/device_common.h"]
 
 
@@ -124,13 +127,59 @@ def cpu_baseline(w, cpu_inputs, target_s: float = 15.0):
             "full_workload_seconds_est": round(dt * w.n * w.bh / (heads * nrows), 1)}
 
 
+def summarize_counters(pmc_dir: str, out_path: str = TRAFFIC_FILE):
+    """Turn rocprofv3 --pmc CSVs into the traffic summary bench.py reports.
+
+    Expects <dir>/fetch_counter_collection.csv and write_..., taken on a
+    bench run, and copyfetch_/copywrite_ taken on `--calibrate-copy`.  Each
+    counter (KiB per dispatch) is scaled by what it reads for a plain copy of
+    COPY_BYTES, so bytes = counter * COPY_BYTES / counter_on_copy."""
+    import csv
+    import statistics
+
+    def per_dispatch(fname, counter, kernel_substr):
+        vals = []
+        with open(os.path.join(pmc_dir, fname)) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]:
+                    vals.append(float(r["Counter_Value"]))
+        if not vals:
+            raise SystemExit(f"no {counter} rows for {kernel_substr} in {fname}")
+        return statistics.mean(vals), len(vals)
+
+    fetch, nf = per_dispatch("fetch_counter_collection.csv", "FETCH_SIZE", "fwd_fused_bf16")
+    write, nw = per_dispatch("write_counter_collection.csv", "WRITE_SIZE", "fwd_fused_bf16")
+    cf, _ = per_dispatch("copyfetch_counter_collection.csv", "FETCH_SIZE", "copyBuffer")
+    cw, _ = per_dispatch("copywrite_counter_collection.csv", "WRITE_SIZE", "copyBuffer")
+    rf, rw = COPY_BYTES / cf, COPY_BYTES / cw  # bytes per counter unit
+    summary = {
+        "kernel_digest": kernel_digest(),
+        "bytes_per_launch": round(fetch * rf + write * rw),
+        "read_bytes_per_launch": round(fetch * rf),
+        "write_bytes_per_launch": round(write * rw),
+        "fetch_size_kib_per_dispatch": fetch, "write_size_kib_per_dispatch": write,
+        "dispatches": [nf, nw],
+        "copy_calibration": {"copy_bytes": COPY_BYTES, "fetch_size_kib": cf, "write_size_kib": cw,
+                             "bytes_per_fetch_unit": rf, "bytes_per_write_unit": rw},
+    }
+    with open(out_path, "w") as f:
+        json.dump(summary, f, indent=1)
+    print(json.dumps(summary))
+
+
 def main():
+    if len(sys.argv) >= 3 and sys.argv[1] == "--summarize-counters":
+        summarize_counters(sys.argv[2])
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of 1 GiB three times (to scale the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (heads are "
@@ -145,6 +194,14 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 3}))
+        return
     w = WORKLOADS[HEADLINE]
     print(f"[bench] inputs {w.name}", file=sys.stderr, flush=True)
     cpu_inputs = workload_inputs(w)
@@ -169,7 +226,7 @@ def main():
     traffic = traffic_for_launch()
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic, "kernel": "fwd_fused_bf16_kernel",
+                "traffic": traffic, "kernel": "attn_fwd fused kernel (default tile, d=128)",
                 "flops_per_launch": flops, "launch_ms": round(launch_ms, 4)}
     out = {
         "metric": METRIC,
