@@ -923,6 +923,539 @@ fwd_fused_bf16_direct_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Wide variant: QB 32-row query blocks per wave (64 rows for QB = 2).  Every
+// K operand read from LDS and every transposed V operand read then feeds QB
+// MFMAs instead of one, which halves LDS instructions per MFMA and doubles
+// the independent matrix-core work each wave has in flight.  The price is
+// register space (Q, U, two score tiles and P for 64 rows), so QB = 2 runs
+// one wave per SIMD with the U accumulators in AGPRs, and hides latency with
+// the same schedule as the direct variant: direct global -> LDS tiles, K two
+// tiles ahead of V in two LDS buffers each, S_{j+1} issued before the
+// softmax of S_j, and operand reads two MFMAs ahead.
+
+template <int D, int QB, int NW, int BC>
+struct WideCfg {
+  static constexpr int NT = NW * 64;
+  static constexpr int BR = NW * QB * 32;
+  static constexpr int KEYS = BC;
+  static constexpr int CPR = D / 8;
+  static constexpr int CHUNKS = BC * CPR;
+  static constexpr int WAVE_CHUNKS = CHUNKS / NW;
+  static constexpr int INSTS = WAVE_CHUNKS / 64;
+  static constexpr int TILE = BC * D;
+  static constexpr int LDS_ELEMS = 4 * TILE;
+  static constexpr int WPS = QB >= 2 ? 1 : 2;  // waves per SIMD the registers allow
+  static constexpr int64_t ONCHIP = (int64_t)BR * D * 2 + 2 * BR + 2 * BC * D + (int64_t)BR * BC;
+  static_assert(CHUNKS % (NW * 64) == 0, "tile must split into whole wave loads");
+};
+
+template <int D, int QB, int NW, int BC>
+__global__ __launch_bounds__(NW * 64, ((QB >= 2 ? 1 : 2) * 4 / NW > 0 ? (QB >= 2 ? 1 : 2) * 4 / NW
+                                                                       : 1)) void
+fwd_fused_bf16_wide_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                           const bf16* __restrict__ V, float* __restrict__ O,
+                           float* __restrict__ lse, int n, int nqb, int total, float c) {
+  using C = WideCfg<D, QB, NW, BC>;
+  __shared__ __attribute__((aligned(1024))) bf16 smem[C::LDS_ELEMS];
+  bf16* const Kb = smem;                // [2][TILE]
+  bf16* const Vb = smem + 2 * C::TILE;  // [2][TILE]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+  const int li = lane & 31;
+
+  const int tile = xcd_remap(blockIdx.x, total);
+  const int head = tile / nqb;
+  const int qblk = tile - head * nqb;
+  const size_t hoff = (size_t)head * (size_t)n * D;
+  const bf16* Qh = Q + hoff;
+  const bf16* Kh = K + hoff;
+  const bf16* Vh = V + hoff;
+  const int qw0 = qblk * C::BR + wave * (QB * 32);
+
+  bf16x8 qreg[QB][D / 16];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int q = qw0 + qb * 32 + li;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      qreg[qb][kk] = q < n ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)q * D + kk * 16 + 8 * h)
+                           : bf16x8{};
+  }
+
+  f32x16 uacc[D / 32][QB];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) uacc[db][qb] = f32x16{};
+  float m[QB], l[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = -INFINITY;
+    l[qb] = 0.f;
+  }
+  const int nt = (n + BC - 1) / BC;
+
+  auto load_tile = [&](const bf16* src, bf16* dst, int t, auto swz) {
+    const int kbase = t * BC;
+#pragma unroll
+    for (int it = 0; it < C::INSTS; ++it) {
+      const int p0 = wave * C::WAVE_CHUNKS + it * 64;
+      const int p = p0 + lane;
+      const int row = p / C::CPR, phys = p % C::CPR;
+      const int logical = phys ^ swz(row);
+      const int grow = min(kbase + row, n - 1);
+      load_lds_16(src + (size_t)grow * D + logical * 8, dst + p0 * 8);
+    }
+  };
+  auto kswz = [](int row) { return chunk_swizzle<D * 2>(row); };
+  auto vswz = [](int row) { return vtr_swizzle<D * 2>(row); };
+
+  typedef f32x16 STile[BC / 32][QB];
+  auto compute_s = [&](const bf16* Ks, STile& s) {
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb) {
+        const int row = kb * 32 + li;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+            Ks + row * D + (((2 * kk + h) ^ chunk_swizzle<D * 2>(row)) * 8));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma_bf16_32x32x16(a, qreg[qb][kk], s[kb][qb]);
+      }
+  };
+  auto softmax_max = [&](STile& s, bool mask, int kbase) {
+    if (mask) {
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kbase + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3) >= n) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) s[kb][qb][r] = -INFINITY;
+          }
+    }
+    bool need_any = false;
+    float alpha[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mc = mx * c;
+      const bool need = mc > m[qb] + kTau;
+      const float mn = need ? mc : m[qb];
+      alpha[qb] = need ? fast_exp2(m[qb] - mn) : 1.0f;
+      m[qb] = mn;
+      l[qb] *= alpha[qb];
+      need_any |= need;
+    }
+    if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) uacc[db][qb] *= alpha[qb];
+    }
+  };
+  typedef uint32_t PTile[BC / 32][QB][8];
+  auto softmax_exp = [&](const STile& s, PTile& pk) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float lsum = l[qb];
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = fast_exp2(__builtin_fmaf(s[kb][qb][r], c, -m[qb]));
+          const float p1 = fast_exp2(__builtin_fmaf(s[kb][qb][r + 1], c, -m[qb]));
+          const uint32_t pp = pack_bf16x2(p0, p1);
+          pk[kb][qb][r >> 1] = pp;
+          lsum = add_bf16x2(pp, lsum);
+        }
+      l[qb] = lsum;
+    }
+  };
+  const int G = lane >> 4, sl = lane & 15;
+  const int hh = G >> 1;
+  auto pv = [&](const bf16* Vs, const PTile& pk) {
+#pragma unroll
+    for (int ks = 0; ks < BC / 16; ++ks) {
+      const int kb = ks >> 1, half = ks & 1;
+      bf16x8 pb[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        u32x4 t = {pk[kb][qb][4 * half + 0], pk[kb][qb][4 * half + 1], pk[kb][qb][4 * half + 2],
+                   pk[kb][qb][4 * half + 3]};
+        pb[qb] = __builtin_bit_cast(bf16x8, t);
+      }
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        u32x2 part[2];
+#pragma unroll
+        for (int piece = 0; piece < 2; ++piece) {
+          const int row = kb * 32 + 16 * half + 8 * piece + 4 * hh + (sl >> 2);
+          const int d0 = db * 32 + 16 * (G & 1) + 4 * (sl & 3);
+          const int phys = (d0 >> 3) ^ vtr_swizzle<D * 2>(row);
+          part[piece] = lds_read_tr16(Vs + row * D + phys * 8 + (d0 & 7));
+        }
+        const bf16x8 a =
+            __builtin_bit_cast(bf16x8, (u32x4{part[0][0], part[0][1], part[1][0], part[1][1]}));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) uacc[db][qb] = mfma_bf16_32x32x16(a, pb[qb], uacc[db][qb]);
+      }
+    }
+  };
+
+  load_tile(Kh, Kb, 0, kswz);
+  load_tile(Vh, Vb, 0, vswz);
+  if (nt > 1) load_tile(Kh, Kb + C::TILE, 1, kswz);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  STile s_cur;
+  compute_s(Kb, s_cur);
+  __syncthreads();
+
+  auto step = [&](auto par, int j) {
+    constexpr int P = decltype(par)::value;
+    if (j + 2 < nt) load_tile(Kh, Kb + P * C::TILE, j + 2, kswz);
+    load_tile(Vh, Vb + (P ^ 1) * C::TILE, j + 1, vswz);
+    softmax_max(s_cur, false, 0);
+    STile s_next;
+    compute_s(Kb + (P ^ 1) * C::TILE, s_next);
+    PTile pk;
+    softmax_exp(s_cur, pk);
+    pv(Vb + P * C::TILE, pk);
+    {
+      constexpr int NK = (D / 16) * (BC / 32);   // K operand reads
+      constexpr int NS = NK * QB;                // S MFMAs
+      constexpr int NV = (BC / 16) * (D / 32);   // V operand read pairs
+      constexpr int NPV = NV * QB;               // PV MFMAs
+      constexpr int VALU_PER = 180 * QB / NS + 1;
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i % QB == QB - 1 && i / QB + 2 < NK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i % QB == QB - 1 && i / QB + 2 < NV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s_cur[kb][qb] = s_next[kb][qb];
+  };
+  int j = 0;
+  for (; j + 2 < nt; j += 2) {
+    step(IntC<0>{}, j);
+    step(IntC<1>{}, j + 1);
+  }
+  if (j + 1 < nt) {
+    step(IntC<0>{}, j);
+    ++j;
+  }
+  {
+    PTile pk;
+    softmax_max(s_cur, (n % BC) != 0, j * BC);
+    softmax_exp(s_cur, pk);
+    pv(Vb + (j & 1) * C::TILE, pk);
+  }
+
+  float* Oh = O + hoff;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = l[qb] + __shfl_xor(l[qb], 32);
+    const float inv = 1.0f / lt;
+    const int q = qw0 + qb * 32 + li;
+    if (q < n) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v = {uacc[db][qb][4 * g + 0] * inv, uacc[db][qb][4 * g + 1] * inv,
+                     uacc[db][qb][4 * g + 2] * inv, uacc[db][qb][4 * g + 3] * inv};
+          *reinterpret_cast<f32x4*>(Oh + (size_t)q * D + db * 32 + 8 * g + 4 * h) = v;
+        }
+      if (h == 0 && lse != nullptr) lse[(size_t)head * n + q] = (m[qb] + __log2f(lt)) * kLn2;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Ping-pong variant.  The 8 waves form two groups of four (one wave of each
+// group per SIMD) that run one phase apart.  Each tile j has a matrix phase
+// X_j (S_{j+1} = K_{j+1} Q^T and U^T += V_j^T P_j^T, operands from LDS) and a
+// vector phase Y_j (online softmax of S_{j+1} -> P_{j+1}, including the rare
+// rescale of U).  With workgroup barriers between phases,
+//     slot 2j:   group 0 runs X_j,      group 1 runs Y_{j-1}
+//     slot 2j+1: group 0 runs Y_j,      group 1 runs X_j
+// so at any time each SIMD has one wave issuing MFMAs and one issuing the
+// softmax arithmetic.  Direct loads of K_{j+2} and V_{j+1} are issued at the
+// start of slot 2j into the buffers K_j and V_{j-1} left (both groups
+// finished X_{j-1} before slot 2j) and waited for at the end of slot 2j+1.
+
+template <int D, int QB, int BC>
+struct PingCfg {
+  static constexpr int NW = 8, NT = 512;
+  static constexpr int BR = NW * QB * 32;
+  static constexpr int KEYS = BC;
+  static constexpr int CPR = D / 8;
+  static constexpr int CHUNKS = BC * CPR;
+  static constexpr int WAVE_CHUNKS = CHUNKS / NW;
+  static constexpr int INSTS = WAVE_CHUNKS / 64;
+  static constexpr int TILE = BC * D;
+  static constexpr int LDS_ELEMS = 4 * TILE;
+  static constexpr int64_t ONCHIP = (int64_t)BR * D * 2 + 2 * BR + 2 * BC * D + (int64_t)BR * BC;
+  static_assert(CHUNKS % (NW * 64) == 0, "tile must split into whole wave loads");
+};
+
+template <int D, int QB, int BC, bool PRIO>
+__global__ __launch_bounds__(512, 1) void fwd_fused_bf16_pingpong_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    float* __restrict__ O, float* __restrict__ lse, int n, int nqb, int total, float c) {
+  using C = PingCfg<D, QB, BC>;
+  __shared__ __attribute__((aligned(1024))) bf16 smem[C::LDS_ELEMS];
+  bf16* const Kb = smem;                // [2][TILE]
+  bf16* const Vb = smem + 2 * C::TILE;  // [2][TILE]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int h = lane >> 5;
+  const int li = lane & 31;
+
+  const int tile = xcd_remap(blockIdx.x, total);
+  const int head = tile / nqb;
+  const int qblk = tile - head * nqb;
+  const size_t hoff = (size_t)head * (size_t)n * D;
+  const bf16* Qh = Q + hoff;
+  const bf16* Kh = K + hoff;
+  const bf16* Vh = V + hoff;
+  const int qw0 = qblk * C::BR + wave * (QB * 32);
+
+  bf16x8 qreg[QB][D / 16];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int q = qw0 + qb * 32 + li;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      qreg[qb][kk] = q < n ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)q * D + kk * 16 + 8 * h)
+                           : bf16x8{};
+  }
+
+  f32x16 uacc[D / 32][QB];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) uacc[db][qb] = f32x16{};
+  float m[QB], l[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = -INFINITY;
+    l[qb] = 0.f;
+  }
+  const int nt = (n + BC - 1) / BC;
+
+  auto load_tile = [&](const bf16* src, bf16* dst, int t, auto swz) {
+    const int kbase = t * BC;
+#pragma unroll
+    for (int it = 0; it < C::INSTS; ++it) {
+      const int p0 = wave * C::WAVE_CHUNKS + it * 64;
+      const int p = p0 + lane;
+      const int row = p / C::CPR, phys = p % C::CPR;
+      const int logical = phys ^ swz(row);
+      const int grow = min(kbase + row, n - 1);
+      load_lds_16(src + (size_t)grow * D + logical * 8, dst + p0 * 8);
+    }
+  };
+  auto kswz = [](int row) { return chunk_swizzle<D * 2>(row); };
+  auto vswz = [](int row) { return vtr_swizzle<D * 2>(row); };
+
+  f32x16 s[BC / 32][QB];
+  uint32_t pk[BC / 32][QB][8];
+
+  auto compute_s = [&](const bf16* Ks) {
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb) {
+        const int row = kb * 32 + li;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+            Ks + row * D + (((2 * kk + h) ^ chunk_swizzle<D * 2>(row)) * 8));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma_bf16_32x32x16(a, qreg[qb][kk], s[kb][qb]);
+      }
+  };
+  const int G = lane >> 4, sl = lane & 15;
+  const int hh = G >> 1;
+  auto pv = [&](const bf16* Vs) {
+#pragma unroll
+    for (int ks = 0; ks < BC / 16; ++ks) {
+      const int kb = ks >> 1, half = ks & 1;
+      bf16x8 pb[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        u32x4 t = {pk[kb][qb][4 * half + 0], pk[kb][qb][4 * half + 1], pk[kb][qb][4 * half + 2],
+                   pk[kb][qb][4 * half + 3]};
+        pb[qb] = __builtin_bit_cast(bf16x8, t);
+      }
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        u32x2 part[2];
+#pragma unroll
+        for (int piece = 0; piece < 2; ++piece) {
+          const int row = kb * 32 + 16 * half + 8 * piece + 4 * hh + (sl >> 2);
+          const int d0 = db * 32 + 16 * (G & 1) + 4 * (sl & 3);
+          const int phys = (d0 >> 3) ^ vtr_swizzle<D * 2>(row);
+          part[piece] = lds_read_tr16(Vs + row * D + phys * 8 + (d0 & 7));
+        }
+        const bf16x8 a =
+            __builtin_bit_cast(bf16x8, (u32x4{part[0][0], part[0][1], part[1][0], part[1][1]}));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) uacc[db][qb] = mfma_bf16_32x32x16(a, pb[qb], uacc[db][qb]);
+      }
+    }
+  };
+  // Online softmax of the score tile in `s` (keys from kbase) into pk.
+  auto softmax = [&](bool mask, int kbase) {
+    if (mask) {
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kbase + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3) >= n) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) s[kb][qb][r] = -INFINITY;
+          }
+    }
+    bool need_any = false;
+    float alpha[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mc = mx * c;
+      const bool need = mc > m[qb] + kTau;
+      const float mn = need ? mc : m[qb];
+      alpha[qb] = need ? fast_exp2(m[qb] - mn) : 1.0f;
+      m[qb] = mn;
+      need_any |= need;
+    }
+    if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) uacc[db][qb] *= alpha[qb];
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float lsum = l[qb] * alpha[qb];
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = fast_exp2(__builtin_fmaf(s[kb][qb][r], c, -m[qb]));
+          const float p1 = fast_exp2(__builtin_fmaf(s[kb][qb][r + 1], c, -m[qb]));
+          const uint32_t pp = pack_bf16x2(p0, p1);
+          pk[kb][qb][r >> 1] = pp;
+          lsum = add_bf16x2(pp, lsum);
+        }
+      l[qb] = lsum;
+    }
+  };
+  // Matrix phase X_j and vector phase Y_j.
+  auto phase_x = [&](int j) {
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
+    if (j + 1 < nt) compute_s(Kb + ((j + 1) & 1) * C::TILE);
+    pv(Vb + (j & 1) * C::TILE);
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
+  };
+  auto phase_y = [&](int j) {  // softmax of S_{j+1}
+    softmax((j + 2 == nt) && (n % BC) != 0, (j + 1) * BC);
+  };
+
+  // Prologue: K_0, V_0, K_1; S_0 and P_0 in every wave.
+  load_tile(Kh, Kb, 0, kswz);
+  load_tile(Vh, Vb, 0, vswz);
+  if (nt > 1) load_tile(Kh, Kb + C::TILE, 1, kswz);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  compute_s(Kb);
+  softmax(nt == 1 && (n % BC) != 0, 0);
+  __syncthreads();  // every wave has read K_0 before slot 0 overwrites it
+
+  // Both groups run the same phase sequence X_0, Y_0, X_1, Y_1, ...; group 1
+  // takes one extra barrier first and group 0 one extra barrier last, so
+  // group 1 is always one phase behind.  Loads of step j (K_{j+2}, V_{j+1})
+  // belong to slot 2j and their wait to the end of slot 2j+1; the group
+  // branches below only place those.
+  auto loads = [&](int j) {
+    if (j + 2 < nt) load_tile(Kh, Kb + (j & 1) * C::TILE, j + 2, kswz);
+    if (j + 1 < nt) load_tile(Vh, Vb + ((j + 1) & 1) * C::TILE, j + 1, vswz);
+  };
+  if (grp == 1) {
+    loads(0);
+    __syncthreads();
+  }
+  for (int j = 0; j < nt; ++j) {
+    if (grp == 0) loads(j);
+    phase_x(j);
+    if (grp == 1) __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (grp == 1) loads(j + 1);
+    if (j + 1 < nt) phase_y(j);
+    if (grp == 0) __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  if (grp == 0) __syncthreads();
+
+  float* Oh = O + hoff;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = l[qb] + __shfl_xor(l[qb], 32);
+    const float inv = 1.0f / lt;
+    const int q = qw0 + qb * 32 + li;
+    if (q < n) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v = {uacc[db][qb][4 * g + 0] * inv, uacc[db][qb][4 * g + 1] * inv,
+                     uacc[db][qb][4 * g + 2] * inv, uacc[db][qb][4 * g + 3] * inv};
+          *reinterpret_cast<f32x4*>(Oh + (size_t)q * D + db * 32 + 8 * g + 4 * h) = v;
+        }
+      if (h == 0 && lse != nullptr) lse[(size_t)head * n + q] = (m[qb] + __log2f(lt)) * kLn2;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 path: same schedule with v_mfma_f32_32x32x2_f32 and exact per-tile
 // rescaling.  One wave per 32 query rows, 4 waves, 32-key tiles, single
 // LDS buffer.  Each lane holds one element of each MFMA operand, so the
@@ -1069,6 +1602,20 @@ FusedEntry direct(const char* name) {
                     &fwd_fused_bf16_direct_kernel<D, NW, BC, PIPE, WPS, SCHED, STAGES>};
 }
 
+template <int D, int QB, int NW, int BC>
+FusedEntry wide(const char* name) {
+  using C = WideCfg<D, QB, NW, BC>;
+  return FusedEntry{name, D, NW, FusedTileInfo{C::BR, C::KEYS, C::ONCHIP},
+                    &fwd_fused_bf16_wide_kernel<D, QB, NW, BC>};
+}
+
+template <int D, int QB, int BC, bool PRIO = false>
+FusedEntry pingpong(const char* name) {
+  using C = PingCfg<D, QB, BC>;
+  return FusedEntry{name, D, C::NW, FusedTileInfo{C::BR, C::KEYS, C::ONCHIP},
+                    &fwd_fused_bf16_pingpong_kernel<D, QB, BC, PRIO>};
+}
+
 template <int D, int NW, int BC>
 FusedEntry piped(const char* name) {
   using C = PipeCfg<D, NW, BC>;
@@ -1078,18 +1625,20 @@ FusedEntry piped(const char* name) {
 
 const FusedEntry* registry(int& count) {
   static const FusedEntry table[] = {
-      // head dimension 64
+      // head dimension 64 (first entry is the default)
+      pingpong<64, 2, 64, true>("g2x64p"),
+      pingpong<64, 2, 64>("g2x64"),
+      pingpong<64, 1, 64>("g1x64"),
       direct<64, 8, 64, true, 2, false, 3>("t8x64"),
       direct<64, 8, 64>("d8x64"),
-      direct<64, 8, 64, true, 2, true>("s8x64"),
-      piped<64, 8, 64>("p8x64"),
       basic<64, 2, 8, 32>("2x8x32"),
       // head dimension 128
       direct<128, 8, 64>("d8x64"),
+      pingpong<128, 1, 64, true>("g1x64p"),
+      pingpong<128, 1, 64>("g1x64"),
+      wide<128, 1, 8, 64>("w1x8x64"),
       direct<128, 8, 64, true, 2, true>("s8x64"),
-      direct<128, 4, 64>("d4x64"),
       direct<128, 8, 32, false, 3>("n8x32w3"),
-      piped<128, 8, 64>("p8x64"),
       basic<128, 1, 8, 64>("1x8x64"),
       // head dimension 256
       basic<256, 1, 4, 32>("1x4x32"),
