@@ -28,6 +28,9 @@
 //     dS^T, dQ^T += K^T dS^T.  Recomputing S and dP here costs 4 N^2 d more
 //     flops than accumulating dQ with atomics, and keeps the result
 //     deterministic.
+#include <cstdlib>
+#include <cstring>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -404,10 +407,307 @@ __global__ __launch_bounds__(256, 1) void bwd_dq(
 }
 
 // ---------------------------------------------------------------------------
+// Second-generation kernels (default).  Tiles of Q and dO (dK/dV kernel) and
+// of K and V (dQ kernel) go global -> LDS with global_load_lds_dwordx4 and
+// stay row-major; the transposed operands (Q^T, dO^T, K^T) come from
+// ds_read_b64_tr_b16 on the same tiles, whose swizzle (dual_swizzle) keeps
+// both the row-wise and the transposed reads free of bank conflicts.  No
+// staging registers and no vector-ALU transposition, so two waves fit per
+// SIMD.  Rows past n are clamped to n-1 on load; the kernels give those rows
+// zero weight (lse = +inf for queries, explicit mask for keys).
+
+namespace {
+
+template <int D>
+__device__ __forceinline__ void tile_load_lds(const bf16* src, bf16* dst, int t, int rows_per_tile,
+                                              int n, int wave, int lane, int wave_chunks,
+                                              int insts, bool dual) {
+  constexpr int CPR = D / 8;
+  const int rbase = t * rows_per_tile;
+  for (int it = 0; it < insts; ++it) {
+    const int p0 = wave * wave_chunks + it * 64;
+    const int p = p0 + lane;
+    const int row = p / CPR, phys = p % CPR;
+    const int logical = phys ^ (dual ? dual_swizzle<D * 2>(row) : chunk_swizzle<D * 2>(row));
+    const int grow = min(rbase + row, n - 1);
+    load_lds_16(src + (size_t)grow * D + logical * 8, dst + p0 * 8);
+  }
+}
+
+// Transposed A operand (32 rows of the d dimension x 16 rows of the tile)
+// from a row-major dual-swizzled tile: k-slots follow the score
+// accumulator's row order (tile rows 16 ks + 8 (j/4) + 4 h + j%4).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int ks, int db, int lane) {
+  const int G = lane >> 4, sl = lane & 15, hh = G >> 1;
+  u32x2 part[2];
+#pragma unroll
+  for (int piece = 0; piece < 2; ++piece) {
+    const int row = 16 * ks + 8 * piece + 4 * hh + (sl >> 2);
+    const int d0 = db * 32 + 16 * (G & 1) + 4 * (sl & 3);
+    const int phys = (d0 >> 3) ^ dual_swizzle<D * 2>(row);
+    part[piece] = lds_read_tr16(tile + row * D + phys * 8 + (d0 & 7));
+  }
+  return __builtin_bit_cast(bf16x8, (u32x4{part[0][0], part[0][1], part[1][0], part[1][1]}));
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8 row_operand(const bf16* tile, int row, int chunk, bool dual) {
+  const int sw = dual ? dual_swizzle<D * 2>(row) : chunk_swizzle<D * 2>(row);
+  return *reinterpret_cast<const bf16x8*>(tile + row * D + ((chunk ^ sw) * 8));
+}
+
+}  // namespace
+
+template <int D, int NW>
+struct Dkdv2Cfg {
+  static constexpr int NT = NW * 64, BKV = NW * 32;
+  static constexpr int BQ = (32 * D / 8) % (NW * 64) == 0 ? 32 : 64;  // whole-wave loads
+  static constexpr int CHUNKS = BQ * D / 8;
+  static constexpr int WAVE_CHUNKS = CHUNKS / NW;
+  static constexpr int INSTS = WAVE_CHUNKS / 64;
+  static constexpr int TILE = BQ * D;
+  static_assert(CHUNKS % (NW * 64) == 0, "tile must split into whole wave loads");
+};
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv2(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dg,
+    float* __restrict__ dK, float* __restrict__ dV, int n, int nkb, int total, float c,
+    float scale) {
+  using C = Dkdv2Cfg<D, NW>;
+  constexpr int BQ = C::BQ;
+  __shared__ __attribute__((aligned(1024))) bf16 tiles[2][2 * C::TILE];  // [stage][Q | dO]
+  __shared__ __attribute__((aligned(16))) float stats[2][2 * BQ];          // [stage][lse2 | D]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, li = lane & 31;
+  const int tile = xcd_remap(blockIdx.x, total);
+  const int head = tile / nkb, kblk = tile - head * nkb;
+  const size_t hoff = (size_t)head * n * D;
+  const bf16 *Qh = Q + hoff, *Kh = K + hoff, *Vh = V + hoff, *dOh = dO + hoff;
+  const float* lseh = lse + (size_t)head * n;
+  const float* Dh = Dg + (size_t)head * n;
+  const int key = kblk * C::BKV + wave * 32 + li;
+
+  bf16x8 kreg[D / 16], vreg[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    kreg[kk] = key < n ? *reinterpret_cast<const bf16x8*>(Kh + (size_t)key * D + 16 * kk + 8 * h)
+                       : bf16x8{};
+    vreg[kk] = key < n ? *reinterpret_cast<const bf16x8*>(Vh + (size_t)key * D + 16 * kk + 8 * h)
+                       : bf16x8{};
+  }
+  f32x16 dkt[D / 32], dvt[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dkt[db] = dvt[db] = f32x16{};
+
+  auto load = [&](int i, int buf) {
+    tile_load_lds<D>(Qh, tiles[buf], i, BQ, n, wave, lane, C::WAVE_CHUNKS, C::INSTS, true);
+    tile_load_lds<D>(dOh, tiles[buf] + C::TILE, i, BQ, n, wave, lane, C::WAVE_CHUNKS, C::INSTS,
+                     true);
+    if (tid < 2 * BQ) {
+      const int q = i * BQ + (tid % BQ);
+      float v;
+      if (tid < BQ)
+        v = q < n ? lseh[q] * kLog2e : INFINITY;  // +inf: rows past n get P = 0
+      else
+        v = q < n ? Dh[q] : 0.f;
+      stats[buf][tid] = v;
+    }
+  };
+
+  const int nqt = (n + BQ - 1) / BQ;
+  load(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int i = 0; i < nqt; ++i) {
+    const int buf = i & 1;
+    if (i + 1 < nqt) load(i + 1, buf ^ 1);
+    const bf16* Qs = tiles[buf];
+    const bf16* dOs = tiles[buf] + C::TILE;
+#pragma unroll
+    for (int qb = 0; qb < BQ / 32; ++qb) {
+      // S = Q K^T and dP = dO V^T (32 queries x 32 keys per wave).
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        s = mfma_bf16_32x32x16(row_operand<D>(Qs, qb * 32 + li, 2 * kk + h, true), kreg[kk], s);
+        dp = mfma_bf16_32x32x16(row_operand<D>(dOs, qb * 32 + li, 2 * kk + h, true), vreg[kk], dp);
+      }
+      uint32_t pk[8], dsk[8];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(&stats[buf][qb * 32 + 8 * g + 4 * h]);
+        const f32x4 dd =
+            *reinterpret_cast<const f32x4*>(&stats[buf][BQ + qb * 32 + 8 * g + 4 * h]);
+        float p[4], ds[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[e] = fast_exp2(__builtin_fmaf(s[4 * g + e], c, -l2[e]));
+          ds[e] = p[e] * (dp[4 * g + e] - dd[e]);
+        }
+        pk[2 * g] = pack_bf16x2(p[0], p[1]);
+        pk[2 * g + 1] = pack_bf16x2(p[2], p[3]);
+        dsk[2 * g] = pack_bf16x2(ds[0], ds[1]);
+        dsk[2 * g + 1] = pack_bf16x2(ds[2], ds[3]);
+      }
+      // dV^T += dO^T P, dK^T += Q^T dS over this block's 32 queries.
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 bp = __builtin_bit_cast(
+            bf16x8, (u32x4{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]}));
+        const bf16x8 bs = __builtin_bit_cast(
+            bf16x8, (u32x4{dsk[4 * ks], dsk[4 * ks + 1], dsk[4 * ks + 2], dsk[4 * ks + 3]}));
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          dvt[db] = mfma_bf16_32x32x16(tr_operand<D>(dOs, 2 * qb + ks, db, lane), bp, dvt[db]);
+          dkt[db] = mfma_bf16_32x32x16(tr_operand<D>(Qs, 2 * qb + ks, db, lane), bs, dkt[db]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  if (key < n) {
+    float* dKr = dK + hoff + (size_t)key * D;
+    float* dVr = dV + hoff + (size_t)key * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = db * 32 + 8 * g + 4 * h;
+        f32x4 a = {dkt[db][4 * g] * scale, dkt[db][4 * g + 1] * scale, dkt[db][4 * g + 2] * scale,
+                   dkt[db][4 * g + 3] * scale};
+        f32x4 b = {dvt[db][4 * g], dvt[db][4 * g + 1], dvt[db][4 * g + 2], dvt[db][4 * g + 3]};
+        *reinterpret_cast<f32x4*>(dKr + col) = a;
+        *reinterpret_cast<f32x4*>(dVr + col) = b;
+      }
+  }
+}
+
+template <int D, int NW, int BC>
+struct Dq2Cfg {
+  static constexpr int NT = NW * 64, BQB = NW * 32;
+  static constexpr int CHUNKS = BC * D / 8;
+  static constexpr int WAVE_CHUNKS = CHUNKS / NW;
+  static constexpr int INSTS = WAVE_CHUNKS / 64;
+  static constexpr int TILE = BC * D;
+  static_assert(CHUNKS % (NW * 64) == 0, "tile must split into whole wave loads");
+};
+
+template <int D, int NW, int BC>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq2(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dg,
+    float* __restrict__ dQ, int n, int nqb, int total, float c, float scale) {
+  using C = Dq2Cfg<D, NW, BC>;
+  __shared__ __attribute__((aligned(1024))) bf16 tiles[2][2 * C::TILE];  // [stage][K | V]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, li = lane & 31;
+  const int tile = xcd_remap(blockIdx.x, total);
+  const int head = tile / nqb, qblk = tile - head * nqb;
+  const size_t hoff = (size_t)head * n * D;
+  const bf16 *Qh = Q + hoff, *Kh = K + hoff, *Vh = V + hoff, *dOh = dO + hoff;
+  const int q = qblk * C::BQB + wave * 32 + li;
+
+  bf16x8 qreg[D / 16], dogreg[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    qreg[kk] = q < n ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)q * D + 16 * kk + 8 * h)
+                     : bf16x8{};
+    dogreg[kk] = q < n ? *reinterpret_cast<const bf16x8*>(dOh + (size_t)q * D + 16 * kk + 8 * h)
+                       : bf16x8{};
+  }
+  const float l2 = q < n ? lse[(size_t)head * n + q] * kLog2e : 0.f;
+  const float dq_d = q < n ? Dg[(size_t)head * n + q] : 0.f;
+  f32x16 dqt[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dqt[db] = f32x16{};
+
+  auto load = [&](int j, int buf) {
+    tile_load_lds<D>(Kh, tiles[buf], j, BC, n, wave, lane, C::WAVE_CHUNKS, C::INSTS, true);
+    tile_load_lds<D>(Vh, tiles[buf] + C::TILE, j, BC, n, wave, lane, C::WAVE_CHUNKS, C::INSTS,
+                     false);
+  };
+
+  const int nkt = (n + BC - 1) / BC;
+  load(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int j = 0; j < nkt; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < nkt) load(j + 1, buf ^ 1);
+    const bf16* Ks = tiles[buf];
+    const bf16* Vs = tiles[buf] + C::TILE;
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb) {
+      // S^T = K Q^T and dP^T = V dO^T (32 keys x 32 queries per wave).
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        s = mfma_bf16_32x32x16(row_operand<D>(Ks, kb * 32 + li, 2 * kk + h, true), qreg[kk], s);
+        dp = mfma_bf16_32x32x16(row_operand<D>(Vs, kb * 32 + li, 2 * kk + h, false), dogreg[kk],
+                                dp);
+      }
+      const int kbase = j * BC + kb * 32;
+      const bool tail = kbase + 32 > n;
+      uint32_t dsk[8];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float p0 = fast_exp2(__builtin_fmaf(s[r], c, -l2));
+        float p1 = fast_exp2(__builtin_fmaf(s[r + 1], c, -l2));
+        if (tail) {
+          const int k0 = kbase + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (k0 >= n) p0 = 0.f;
+          if (k0 + 1 >= n) p1 = 0.f;
+        }
+        dsk[r >> 1] = pack_bf16x2(p0 * (dp[r] - dq_d), p1 * (dp[r + 1] - dq_d));
+      }
+      // dQ^T += K^T dS^T over these 32 keys.
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 bs = __builtin_bit_cast(
+            bf16x8, (u32x4{dsk[4 * ks], dsk[4 * ks + 1], dsk[4 * ks + 2], dsk[4 * ks + 3]}));
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          dqt[db] = mfma_bf16_32x32x16(tr_operand<D>(Ks, 2 * kb + ks, db, lane), bs, dqt[db]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  if (q < n) {
+    float* dQr = dQ + hoff + (size_t)q * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 a = {dqt[db][4 * g] * scale, dqt[db][4 * g + 1] * scale, dqt[db][4 * g + 2] * scale,
+                   dqt[db][4 * g + 3] * scale};
+        *reinterpret_cast<f32x4*>(dQr + db * 32 + 8 * g + 4 * h) = a;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 
 namespace {
 
+template <int V>
+struct IntK {
+  static constexpr int value = V;
+};
+
+// Kernel generation: "v2" (default) or "v1" via ATTN_BWD_VARIANT, and the
+// waves per workgroup of the v2 kernels via ATTN_BWD_WAVES ("4" or "8").
 template <int D>
 hipError_t launch(const void* Q, const void* K, const void* V, const float* O, const void* dO,
                   const float* lse, float* dQ, float* dK, float* dV, int64_t bh, int64_t n,
@@ -424,16 +724,50 @@ hipError_t launch(const void* Q, const void* K, const void* V, const float* O, c
                      stream, O, g, Dbuf, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nkb = (int)((n + DkdvCfg<D>::BKV - 1) / DkdvCfg<D>::BKV);
-  const int total_kv = (int)(bh * nkb);
-  hipLaunchKernelGGL(bwd_dkdv<D>, dim3(total_kv), dim3(256), 0, stream, q, k, v, g, lse, Dbuf, dK,
-                     dV, (int)n, nkb, total_kv, c, scale);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int nqb = (int)((n + DqCfg<D>::BQB - 1) / DqCfg<D>::BQB);
-  const int total_q = (int)(bh * nqb);
-  hipLaunchKernelGGL(bwd_dq<D>, dim3(total_q), dim3(256), 0, stream, q, k, v, g, lse, Dbuf, dQ,
-                     (int)n, nqb, total_q, c, scale);
+  const char* var = getenv("ATTN_BWD_VARIANT");
+  const bool v1 = var && strcmp(var, "v1") == 0;
+  const char* wv = getenv("ATTN_BWD_WAVES");
+  const bool w4 = wv && strcmp(wv, "4") == 0;
+  if (v1) {
+    const int nkb = (int)((n + DkdvCfg<D>::BKV - 1) / DkdvCfg<D>::BKV);
+    const int total_kv = (int)(bh * nkb);
+    hipLaunchKernelGGL(bwd_dkdv<D>, dim3(total_kv), dim3(256), 0, stream, q, k, v, g, lse, Dbuf,
+                       dK, dV, (int)n, nkb, total_kv, c, scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nqb = (int)((n + DqCfg<D>::BQB - 1) / DqCfg<D>::BQB);
+    const int total_q = (int)(bh * nqb);
+    hipLaunchKernelGGL(bwd_dq<D>, dim3(total_q), dim3(256), 0, stream, q, k, v, g, lse, Dbuf, dQ,
+                       (int)n, nqb, total_q, c, scale);
+    return hipGetLastError();
+  }
+  auto dkdv = [&](auto nwc) {
+    constexpr int NW = decltype(nwc)::value;
+    using Cf = Dkdv2Cfg<D, NW>;
+    const int nkb = (int)((n + Cf::BKV - 1) / Cf::BKV);
+    const int total_kv = (int)(bh * nkb);
+    hipLaunchKernelGGL((bwd_dkdv2<D, NW>), dim3(total_kv), dim3(NW * 64), 0, stream, q, k, v, g,
+                       lse, Dbuf, dK, dV, (int)n, nkb, total_kv, c, scale);
+  };
+  auto dqk = [&](auto nwc) {
+    constexpr int NW = decltype(nwc)::value;
+    using Cf = Dq2Cfg<D, NW, 64>;
+    const int nqb = (int)((n + Cf::BQB - 1) / Cf::BQB);
+    const int total_q = (int)(bh * nqb);
+    hipLaunchKernelGGL((bwd_dq2<D, NW, 64>), dim3(total_q), dim3(NW * 64), 0, stream, q, k, v, g,
+                       lse, Dbuf, dQ, (int)n, nqb, total_q, c, scale);
+  };
+  if (w4) {
+    dkdv(IntK<4>{});
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dqk(IntK<4>{});
+  } else {
+    dkdv(IntK<8>{});
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dqk(IntK<8>{});
+  }
   return hipGetLastError();
 }
 

@@ -96,6 +96,22 @@ __device__ __forceinline__ int vtr_swizzle(int row) {
     return 4 * ((row >> 1) & 1);
 }
 
+// Swizzle for a row-major tile that is read both ways: row-wise with
+// ds_read_b128 (16 consecutive rows at one logical chunk per phase) and
+// transposed with ds_read_b64_tr_b16 (4 consecutive rows x 4 consecutive
+// chunks per half wave).  The XOR value is a bijection of the low 4 row bits
+// (distinct for any 16 consecutive rows) whose bits 2-3 are the row's low
+// bits (distinct 64-byte chunk groups for any 4 consecutive rows).  For
+// 128-byte rows (two rows per 256-byte bank window) bit 2 follows row bit 1
+// instead.
+template <int ROW_BYTES>
+__device__ __forceinline__ int dual_swizzle(int row) {
+  if constexpr (ROW_BYTES >= 256)
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  else
+    return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
 // lane l's 16 bytes land at lds_wave_base + 16 l.  lds_wave_base must be
 // uniform across the wave.
