@@ -605,6 +605,19 @@ __global__ __launch_bounds__(NW * 64, (NW >= 8 ? 1 : 8 / NW)) void fwd_fused_bf1
 // row n-1 when loading (finite data; those keys are masked in the last
 // tile), so no load leaves the tensor.
 
+// Swizzle functors for the K tile (row-wise reads) and the V tile
+// (transposed reads), tagged so a loader can pick the matching offsets.
+template <int ROW_BYTES>
+struct KTileSwizzle {
+  static constexpr bool is_v = false;
+  __device__ int operator()(int row) const { return chunk_swizzle<ROW_BYTES>(row); }
+};
+template <int ROW_BYTES>
+struct VTileSwizzle {
+  static constexpr bool is_v = true;
+  __device__ int operator()(int row) const { return vtr_swizzle<ROW_BYTES>(row); }
+};
+
 template <int D, int NW, int BC, bool PIPE = true, int WPS = 2, bool SCHED = false,
           int STAGES = 2>
 struct DirectCfg {
@@ -663,21 +676,41 @@ fwd_fused_bf16_direct_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
 
   // Issue the direct loads of tile t of `src` into the LDS tile `dst`.  Lane
   // chunk p of this wave is LDS chunk (row, phys); it fetches logical chunk
-  // phys ^ swizzle(row) of that row.
+  // phys ^ swizzle(row) of that row.  Full tiles use a wave-uniform tile base
+  // plus a per-lane byte offset computed once; only a partial last tile
+  // clamps its rows to n-1.
+  const KTileSwizzle<D * 2> kswz;
+  const VTileSwizzle<D * 2> vswz;
+  uint32_t koff[C::INSTS], voff[C::INSTS];
+#pragma unroll
+  for (int it = 0; it < C::INSTS; ++it) {
+    const int p = wave * C::WAVE_CHUNKS + it * 64 + lane;
+    const int row = p / C::CPR, phys = p % C::CPR;
+    koff[it] = (uint32_t)(row * D + (phys ^ kswz(row)) * 8) * 2u;
+    voff[it] = (uint32_t)(row * D + (phys ^ vswz(row)) * 8) * 2u;
+  }
   auto load_tile = [&](const bf16* src, bf16* dst, int t, auto swz) {
     const int kbase = t * BC;
+    const uint32_t* offs = decltype(swz)::is_v ? voff : koff;
+    if (kbase + BC <= n) {
+      const char* tb = reinterpret_cast<const char*>(src) + (size_t)kbase * (D * 2);
 #pragma unroll
-    for (int it = 0; it < C::INSTS; ++it) {
-      const int p0 = wave * C::WAVE_CHUNKS + it * 64;  // wave-uniform
-      const int p = p0 + lane;
-      const int row = p / C::CPR, phys = p % C::CPR;
-      const int logical = phys ^ swz(row);
-      const int grow = min(kbase + row, n - 1);
-      load_lds_16(src + (size_t)grow * D + logical * 8, dst + p0 * 8);
+      for (int it = 0; it < C::INSTS; ++it) {
+        const int p0 = wave * C::WAVE_CHUNKS + it * 64;  // wave-uniform
+        load_lds_16(tb + offs[it], dst + p0 * 8);
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < C::INSTS; ++it) {
+        const int p0 = wave * C::WAVE_CHUNKS + it * 64;
+        const int p = p0 + lane;
+        const int row = p / C::CPR, phys = p % C::CPR;
+        const int logical = phys ^ swz(row);
+        const int grow = min(kbase + row, n - 1);
+        load_lds_16(src + (size_t)grow * D + logical * 8, dst + p0 * 8);
+      }
     }
   };
-  auto kswz = [](int row) { return chunk_swizzle<D * 2>(row); };
-  auto vswz = [](int row) { return vtr_swizzle<D * 2>(row); };
 
   auto compute_s = [&](const bf16* Ks, f32x16 (&s)[BC / 32]) {
 #pragma unroll
@@ -1274,20 +1307,38 @@ __global__ __launch_bounds__(512, 1) void fwd_fused_bf16_pingpong_kernel(
   }
   const int nt = (n + BC - 1) / BC;
 
+  const KTileSwizzle<D * 2> kswz;
+  const VTileSwizzle<D * 2> vswz;
+  uint32_t koff[C::INSTS], voff[C::INSTS];
+#pragma unroll
+  for (int it = 0; it < C::INSTS; ++it) {
+    const int p = wave * C::WAVE_CHUNKS + it * 64 + lane;
+    const int row = p / C::CPR, phys = p % C::CPR;
+    koff[it] = (uint32_t)(row * D + (phys ^ kswz(row)) * 8) * 2u;
+    voff[it] = (uint32_t)(row * D + (phys ^ vswz(row)) * 8) * 2u;
+  }
+  // Full tiles: wave-uniform tile base + per-lane offsets; a partial last
+  // tile clamps its rows to n-1.
   auto load_tile = [&](const bf16* src, bf16* dst, int t, auto swz) {
     const int kbase = t * BC;
+    const uint32_t* offs = decltype(swz)::is_v ? voff : koff;
+    if (kbase + BC <= n) {
+      const char* tb = reinterpret_cast<const char*>(src) + (size_t)kbase * (D * 2);
 #pragma unroll
-    for (int it = 0; it < C::INSTS; ++it) {
-      const int p0 = wave * C::WAVE_CHUNKS + it * 64;
-      const int p = p0 + lane;
-      const int row = p / C::CPR, phys = p % C::CPR;
-      const int logical = phys ^ swz(row);
-      const int grow = min(kbase + row, n - 1);
-      load_lds_16(src + (size_t)grow * D + logical * 8, dst + p0 * 8);
+      for (int it = 0; it < C::INSTS; ++it)
+        load_lds_16(tb + offs[it], dst + (wave * C::WAVE_CHUNKS + it * 64) * 8);
+    } else {
+#pragma unroll
+      for (int it = 0; it < C::INSTS; ++it) {
+        const int p0 = wave * C::WAVE_CHUNKS + it * 64;
+        const int p = p0 + lane;
+        const int row = p / C::CPR, phys = p % C::CPR;
+        const int logical = phys ^ swz(row);
+        const int grow = min(kbase + row, n - 1);
+        load_lds_16(src + (size_t)grow * D + logical * 8, dst + p0 * 8);
+      }
     }
   };
-  auto kswz = [](int row) { return chunk_swizzle<D * 2>(row); };
-  auto vswz = [](int row) { return vtr_swizzle<D * 2>(row); };
 
   f32x16 s[BC / 32][QB];
   uint32_t pk[BC / 32][QB][8];
