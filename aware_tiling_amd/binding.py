@@ -29,6 +29,10 @@ SIGNATURES = {
     "attn_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _int, _vp]),
     "attn_fwd_onchip_elems": (_i64, [_i64, _int]),
     "attn_fwd_query_block": (_i64, [_i64, _int]),
+    "attn_fwd_splitk_splits": (_i64, [_i64, _i64, _i64, _i64, _i64]),
+    "attn_fwd_splitk_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64]),
+    "attn_fwd_splitk": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _int, _i64,
+                               _vp, _sz, _vp]),
     "attn_fwd_smallcache_workspace_size": (_sz, [_i64, _i64, _i64, _i64]),
     "attn_fwd_smallcache": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _int, _i64,
                                    _vp, _sz, _vp]),
@@ -126,6 +130,41 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | N
                         lse.data_ptr() if lse is not None else None, bh, n, d, scale,
                         _dtype_code(q), _stream(q, stream))
     _check("attn_fwd", rc)
+    return out, lse
+
+
+def splitk_splits(bh: int, nq: int, nk: int, d: int, splits: int = 0) -> int:
+    """Key chunks attn_fwd_splitk uses for this shape and request (0 = auto)."""
+    return int(lib().attn_fwd_splitk_splits(bh, nq, nk, d, splits))
+
+
+def attn_fwd_splitk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, splits: int = 0,
+                    scale: float | None = None, out: torch.Tensor | None = None,
+                    lse: torch.Tensor | bool = True, workspace: torch.Tensor | None = None,
+                    stream=None):
+    """Rectangular forward (nq queries, nk keys per head) with the keys split
+    into chunks whose partial results are merged.  Returns (O, lse)."""
+    _check_inputs(q, k, v)
+    if k.shape != v.shape or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2] \
+            or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("Q [bh,nq,d], K and V [bh,nk,d] must agree in bh, d and dtype")
+    bh, nq, d = q.shape
+    nk = k.shape[1]
+    scale = default_scale(d) if scale is None else float(scale)
+    need = int(lib().attn_fwd_splitk_workspace_size(bh, nq, nk, d, int(splits)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((bh, nq, d), dtype=torch.float32, device=q.device)
+    if lse is True:
+        lse = torch.empty((bh, nq), dtype=torch.float32, device=q.device)
+    elif lse is False:
+        lse = None
+    rc = lib().attn_fwd_splitk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               lse.data_ptr() if lse is not None else None, bh, nq, nk, d, scale,
+                               _dtype_code(q), int(splits), workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), _stream(q, stream))
+    _check("attn_fwd_splitk", rc)
     return out, lse
 
 

@@ -91,6 +91,54 @@ attn_status attn_fwd(const void* Q, const void* K, const void* V, float* O, floa
                                                 scale, s));
 }
 
+namespace {
+
+// Effective split count of attn_fwd_splitk, or 0 if the request is invalid.
+int64_t splitk_count(int64_t bh, int64_t nq, int64_t nk, int64_t splits) {
+  if (splits < 0 || splits > 256 || nk <= 0) return 0;
+  const int64_t req = splits == 0 ? at::splitk_auto_splits(bh, nq, nk) : splits;
+  return req;
+}
+
+}  // namespace
+
+int64_t attn_fwd_splitk_splits(int64_t bh, int64_t nq, int64_t nk, int64_t d, int64_t splits) {
+  if (!shape_ok(bh, nq, d) || !shape_ok(bh, nk, d) || !at::splitk_supported(d)) return 0;
+  const int64_t req = splitk_count(bh, nq, nk, splits);
+  return req ? at::splitk_effective_splits(nk, req) : 0;
+}
+
+size_t attn_fwd_splitk_workspace_size(int64_t bh, int64_t nq, int64_t nk, int64_t d,
+                                      int64_t splits) {
+  if (!shape_ok(bh, nq, d) || !shape_ok(bh, nk, d) || !at::splitk_supported(d)) return 0;
+  const int64_t req = splitk_count(bh, nq, nk, splits);
+  return req ? at::splitk_workspace_bytes(bh, nq, nk, d, req) : 0;
+}
+
+attn_status attn_fwd_splitk(const void* Q, const void* K, const void* V, float* O, float* lse,
+                            int64_t bh, int64_t nq, int64_t nk, int64_t d, float scale,
+                            attn_dtype dtype, int64_t splits, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (!shape_ok(bh, nq, d) || !shape_ok(bh, nk, d) || !scale_ok(scale))
+    return ATTN_ERR_INVALID_ARG;
+  if (!at::splitk_supported(d)) return ATTN_ERR_UNSUPPORTED;
+  if (splits < 0 || splits > 256) return ATTN_ERR_INVALID_ARG;
+  if (bh * nq == 0) return ATTN_OK;
+  if (nk == 0) return ATTN_ERR_INVALID_ARG;  // softmax over no keys is undefined
+  const int64_t req = splitk_count(bh, nq, nk, splits);
+  const int64_t eff = at::splitk_effective_splits(nk, req);
+  if (eff * bh * ((nq + 127) / 128) >= (int64_t(1) << 31)) return ATTN_ERR_INVALID_ARG;
+  if (!Q || !K || !V || !O) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return ATTN_ERR_INVALID_ARG;
+  if (lse && !aligned16(lse)) return ATTN_ERR_INVALID_ARG;
+  const size_t need = at::splitk_workspace_bytes(bh, nq, nk, d, req);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned256(workspace)))
+    return ATTN_ERR_WORKSPACE;
+  return launch_status(at::launch_fwd_splitk_bf16(Q, K, V, O, lse, bh, nq, nk, d, scale, req,
+                                                  workspace, static_cast<hipStream_t>(stream)));
+}
+
 int64_t attn_smallcache_tile(int64_t d, int64_t m_elems) {
   if (!at::smallcache_supported(d) || m_elems >= d * d) return 0;
   return at::smallcache_tile_for_budget(d, m_elems);

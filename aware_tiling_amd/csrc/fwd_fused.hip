@@ -33,6 +33,7 @@
 //
 // The row sum l is accumulated from the bf16-rounded P values (the ones the
 // MFMA multiplies), so the normalisation matches the weights used.
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 
@@ -605,6 +606,18 @@ __global__ __launch_bounds__(NW * 64, (NW >= 8 ? 1 : 8 / NW)) void fwd_fused_bf1
 // row n-1 when loading (finite data; those keys are masked in the last
 // tile), so no load leaves the tensor.
 
+// Arguments of the direct-load forward body.  Queries [bh, nq, d], keys and
+// values [bh, nk, d]; outputs [splits, bh, nq, d] and [splits, bh, nq].
+struct DirectArgs {
+  const bf16* Q;
+  const bf16* K;
+  const bf16* V;
+  float* O;
+  float* lse;
+  int nq, nk, nqb, total, bh, kchunk;
+  float c;
+};
+
 // Swizzle functors for the K tile (row-wise reads) and the V tile
 // (transposed reads), tagged so a loader can pick the matching offsets.
 template <int ROW_BYTES>
@@ -637,12 +650,14 @@ struct DirectCfg {
 // PIPE selects the cross-tile pipelining of S; WPS is the number of waves
 // per SIMD the register budget is sized for (without PIPE each wave holds
 // one score tile, so more waves fit and the hardware interleaves them).
-template <int D, int NW, int BC, bool PIPE, int WPS, bool SCHED, int STAGES>
-__global__ __launch_bounds__(NW * 64, (WPS * 4 / NW > 0 ? WPS * 4 / NW : 1)) void
-fwd_fused_bf16_direct_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
-                             const bf16* __restrict__ V, float* __restrict__ O,
-                             float* __restrict__ lse, int n, int nqb, int total, float c) {
+// With SKIP (two-stage PIPE only) a wave whose 32 query rows all lie past
+// nq still loads its share of every tile but does no arithmetic; short query
+// blocks (decoding) then cost little beyond the key/value stream.
+template <int D, int NW, int BC, bool PIPE, int WPS, bool SCHED, int STAGES, bool SKIP = false>
+__device__ __forceinline__ void direct_body(const DirectArgs& A) {
+  static_assert(!SKIP || (PIPE && STAGES == 2), "SKIP is built for the two-stage pipeline");
   using C = DirectCfg<D, NW, BC, PIPE, WPS, SCHED, STAGES>;
+  const float c = A.c;
   __shared__ __attribute__((aligned(1024))) bf16 smem[C::LDS_ELEMS];
   bf16* const Kb = smem;                     // [STAGES][TILE]
   bf16* const Vb = smem + STAGES * C::TILE;  // [STAGES][TILE]
@@ -653,20 +668,30 @@ fwd_fused_bf16_direct_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
   const int h = lane >> 5;
   const int li = lane & 31;
 
-  const int tile = xcd_remap(blockIdx.x, total);
-  const int head = tile / nqb;
-  const int qblk = tile - head * nqb;
-  const size_t hoff = (size_t)head * (size_t)n * D;
-  const bf16* Qh = Q + hoff;
-  const bf16* Kh = K + hoff;
-  const bf16* Vh = V + hoff;
+  // Workgroup -> (key split, head, query block); keys of this workgroup are
+  // [kbeg, kend), addressed relative to kbeg below (n counts them).
+  const int tile = xcd_remap(blockIdx.x, A.total);
+  const int per_split = A.bh * A.nqb;
+  const int split = tile / per_split;
+  const int rem = tile - split * per_split;
+  const int head = rem / A.nqb;
+  const int qblk = rem - head * A.nqb;
+  const int nq = A.nq;
+  const int kbeg = split * A.kchunk;
+  const int n = min(A.nk, kbeg + A.kchunk) - kbeg;
+  const bf16* Qh = A.Q + (size_t)head * nq * D;
+  const bf16* Kh = A.K + ((size_t)head * A.nk + kbeg) * D;
+  const bf16* Vh = A.V + ((size_t)head * A.nk + kbeg) * D;
+  float* const Oh = A.O + ((size_t)split * A.bh + head) * nq * D;
+  float* const lseh = A.lse ? A.lse + ((size_t)split * A.bh + head) * nq : nullptr;
   const int q = qblk * C::BR + wave * 32 + li;
+  const bool active = !SKIP || qblk * C::BR + wave * 32 < nq;  // wave-uniform
 
   bf16x8 qreg[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk)
-    qreg[kk] = q < n ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)q * D + kk * 16 + 8 * h)
-                     : bf16x8{};
+    qreg[kk] = q < nq ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)q * D + kk * 16 + 8 * h)
+                      : bf16x8{};
 
   f32x16 uacc[D / 32];
 #pragma unroll
@@ -856,19 +881,21 @@ fwd_fused_bf16_direct_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
     if (nt > 1) load_tile(Kh, Kb + C::TILE, 1, kswz);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    compute_s(Kb, s_cur);
+    if (active) compute_s(Kb, s_cur);
     __syncthreads();  // every wave has read K_0 before step 0 overwrites it
 
     auto step = [&](auto par, int j) {
       constexpr int P = decltype(par)::value;
       if (j + 2 < nt) load_tile(Kh, Kb + P * C::TILE, j + 2, kswz);
       load_tile(Vh, Vb + (P ^ 1) * C::TILE, j + 1, vswz);
-      softmax_max(s_cur, false, 0);
       f32x16 s_next[BC / 32];
-      compute_s(Kb + (P ^ 1) * C::TILE, s_next);
-      uint32_t pk[BC / 32][8];
-      softmax_exp(s_cur, pk);
-      pv(Vb + P * C::TILE, pk);
+      if (active) {
+        softmax_max(s_cur, false, 0);
+        compute_s(Kb + (P ^ 1) * C::TILE, s_next);
+        uint32_t pk[BC / 32][8];
+        softmax_exp(s_cur, pk);
+        pv(Vb + P * C::TILE, pk);
+      }
       if constexpr (SCHED) {
         // Interleave: each S_{j+1} MFMA with ~7 softmax instructions and
         // the K operand read of the MFMA two places later; then each PV
@@ -932,7 +959,7 @@ fwd_fused_bf16_direct_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
     }
     compute_s(Kb + (j & 1) * C::TILE, s_cur);
   }
-  {
+  if (active) {
     uint32_t pk[BC / 32][8];
     softmax_max(s_cur, (n % BC) != 0, j * BC);
     softmax_exp(s_cur, pk);
@@ -941,8 +968,7 @@ fwd_fused_bf16_direct_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
 
   const float lt = l + __shfl_xor(l, 32);
   const float inv = 1.0f / lt;
-  if (q < n) {
-    float* Oh = O + hoff;
+  if (q < nq) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -951,8 +977,55 @@ fwd_fused_bf16_direct_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
                    uacc[db][4 * g + 2] * inv, uacc[db][4 * g + 3] * inv};
         *reinterpret_cast<f32x4*>(Oh + (size_t)q * D + db * 32 + 8 * g + 4 * h) = v;
       }
-    if (h == 0 && lse != nullptr) lse[(size_t)head * n + q] = (m + __log2f(lt)) * kLn2;
+    if (h == 0 && lseh != nullptr) lseh[q] = (m + __log2f(lt)) * kLn2;
   }
+}
+
+template <int D, int NW, int BC, bool PIPE, int WPS, bool SCHED, int STAGES>
+__global__ __launch_bounds__(NW * 64, (WPS * 4 / NW > 0 ? WPS * 4 / NW : 1)) void
+fwd_fused_bf16_direct_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                             const bf16* __restrict__ V, float* __restrict__ O,
+                             float* __restrict__ lse, int n, int nqb, int total, float c) {
+  direct_body<D, NW, BC, PIPE, WPS, SCHED, STAGES>(
+      DirectArgs{Q, K, V, O, lse, n, n, nqb, total, total / nqb, n, c});
+}
+
+// Key-split entry: grid = splits x bh x query blocks; split s covers keys
+// [s kchunk, (s+1) kchunk) and writes its own normalised output and lse
+// (the partials that the merge kernel combines).
+template <int D, int NW, int BC>
+__global__ __launch_bounds__(NW * 64, (8 / NW > 0 ? 8 / NW : 1)) void fwd_split_bf16_kernel(
+    const DirectArgs A) {
+  direct_body<D, NW, BC, true, 2, false, 2, true>(A);
+}
+
+// Combines the key-split partials of each query row with the rescaling
+// rule: lse = log sum_s exp(lse_s), o = sum_s exp(lse_s - lse) o_s.  One
+// thread per four output columns; partials are [splits][rows][D] and
+// [splits][rows].
+template <int D>
+__global__ __launch_bounds__(256) void fwd_split_merge_kernel(const float* __restrict__ Op,
+                                                              const float* __restrict__ lsep,
+                                                              float* __restrict__ O,
+                                                              float* __restrict__ lse,
+                                                              int64_t rows, int splits) {
+  constexpr int TPR = D / 4;  // threads per row
+  const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const int col = (threadIdx.x % TPR) * 4;
+  if (row >= rows) return;
+  float mx = -INFINITY;
+  for (int sp = 0; sp < splits; ++sp) mx = fmaxf(mx, lsep[(int64_t)sp * rows + row]);
+  float wsum = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < splits; ++sp) {
+    const float w = expf(lsep[(int64_t)sp * rows + row] - mx);
+    const f32x4 o = *reinterpret_cast<const f32x4*>(Op + ((int64_t)sp * rows + row) * D + col);
+    acc += w * o;
+    wsum += w;
+  }
+  const float inv = 1.0f / wsum;
+  *reinterpret_cast<f32x4*>(O + row * D + col) = acc * inv;
+  if (col == 0 && lse != nullptr) lse[row] = mx + logf(wsum);
 }
 
 // ---------------------------------------------------------------------------
@@ -1726,7 +1799,86 @@ hipError_t launch_f32(const float* Q, const float* K, const float* V, float* O, 
   return hipGetLastError();
 }
 
+// Key-split (rectangular / decoding) forward: the direct kernel in its
+// SKIP form with four waves (128-row query blocks) when a head has at most
+// 128 queries, else eight.
+typedef void (*SplitKernel)(DirectArgs);
+
+template <int D>
+hipError_t launch_split(const void* Q, const void* K, const void* V, float* O, float* lse,
+                        int64_t bh, int64_t nq, int64_t nk, float c, int64_t splits,
+                        void* workspace, hipStream_t stream) {
+  const bool narrow = nq <= 128;
+  const int nw = narrow ? 4 : 8;
+  const SplitKernel kern = narrow ? &fwd_split_bf16_kernel<D, 4, 64> : &fwd_split_bf16_kernel<D, 8, 64>;
+  const int br = nw * 32;
+  const int64_t kchunk = splitk_key_chunk(nk, splits);
+  const int64_t eff = (nk + kchunk - 1) / kchunk;
+  const int nqb = (int)((nq + br - 1) / br);
+  const int total = (int)(eff * bh * nqb);
+  float* Op = O;
+  float* lsep = lse;
+  if (eff > 1) {
+    Op = static_cast<float*>(workspace);
+    lsep = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                    align256_bytes((size_t)(splits * bh * nq * D) * 4));
+  }
+  const DirectArgs args{static_cast<const bf16*>(Q), static_cast<const bf16*>(K),
+                        static_cast<const bf16*>(V), Op, lsep, (int)nq, (int)nk, nqb, total,
+                        (int)bh, (int)kchunk, c};
+  hipLaunchKernelGGL(kern, dim3(total), dim3(nw * 64), 0, stream, args);
+  if (eff > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t rows = bh * nq;
+    constexpr int RPB = 256 / (D / 4);
+    hipLaunchKernelGGL((fwd_split_merge_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)),
+                       dim3(256), 0, stream, Op, lsep, O, lse, rows, (int)eff);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+size_t align256_bytes(size_t b) { return (b + 255) / 256 * 256; }
+
+bool splitk_supported(int64_t d) { return d == 64 || d == 128; }
+
+int64_t splitk_auto_splits(int64_t bh, int64_t nq, int64_t nk) {
+  const int64_t br = nq <= 128 ? 128 : 256;
+  const int64_t wgs = bh * ((nq + br - 1) / br);
+  int64_t s = (1024 + wgs - 1) / wgs;                    // aim for >= 1024 workgroups
+  s = std::min<int64_t>(s, (nk + 255) / 256);            // at least 256 keys per split
+  return std::max<int64_t>(1, std::min<int64_t>(s, 256));
+}
+
+int64_t splitk_key_chunk(int64_t nk, int64_t splits) {
+  const int64_t per = (nk + splits - 1) / splits;
+  return (per + 63) / 64 * 64;
+}
+
+int64_t splitk_effective_splits(int64_t nk, int64_t splits) {
+  const int64_t kc = splitk_key_chunk(nk, splits);
+  return (nk + kc - 1) / kc;
+}
+
+size_t splitk_workspace_bytes(int64_t bh, int64_t nq, int64_t nk, int64_t d, int64_t splits) {
+  if (splitk_effective_splits(nk, splits) <= 1) return 0;
+  return align256_bytes((size_t)(splits * bh * nq * d) * 4) +
+         align256_bytes((size_t)(splits * bh * nq) * 4);
+}
+
+hipError_t launch_fwd_splitk_bf16(const void* Q, const void* K, const void* V, float* O,
+                                  float* lse, int64_t bh, int64_t nq, int64_t nk, int64_t d,
+                                  float scale, int64_t splits, void* workspace,
+                                  hipStream_t stream) {
+  const float c = scale * kLog2e;
+  switch (d) {
+    case 64: return launch_split<64>(Q, K, V, O, lse, bh, nq, nk, c, splits, workspace, stream);
+    case 128: return launch_split<128>(Q, K, V, O, lse, bh, nq, nk, c, splits, workspace, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 bool fused_bf16_supported(int64_t d) { return pick(d) != nullptr; }
 bool fused_f32_supported(int64_t d) { return d == 64 || d == 128; }

@@ -28,6 +28,22 @@ hipError_t launch_fwd_fused_f32(const float* Q, const float* K, const float* V, 
                                 float* lse, int64_t bh, int64_t n, int64_t d, float scale,
                                 hipStream_t stream);
 
+// Key-split forward for rectangular shapes (nq queries, nk keys per head).
+// `splits` is the requested count (>= 1); the keys are cut into chunks of
+// splitk_key_chunk() keys (a multiple of the 64-key tile), so the effective
+// count can be smaller.  With one effective split the kernel writes O and lse
+// directly and needs no workspace.
+size_t align256_bytes(size_t b);
+bool splitk_supported(int64_t d);
+int64_t splitk_auto_splits(int64_t bh, int64_t nq, int64_t nk);
+int64_t splitk_key_chunk(int64_t nk, int64_t splits);
+int64_t splitk_effective_splits(int64_t nk, int64_t splits);
+size_t splitk_workspace_bytes(int64_t bh, int64_t nq, int64_t nk, int64_t d, int64_t splits);
+hipError_t launch_fwd_splitk_bf16(const void* Q, const void* K, const void* V, float* O,
+                                  float* lse, int64_t bh, int64_t nq, int64_t nk, int64_t d,
+                                  float scale, int64_t splits, void* workspace,
+                                  hipStream_t stream);
+
 // Square-tile (small-cache) forward.
 bool smallcache_supported(int64_t d);
 int64_t smallcache_tile_for_budget(int64_t d, int64_t m_elems);

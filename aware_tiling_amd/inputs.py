@@ -29,7 +29,7 @@ import torch
 class Workload:
     name: str
     bh: int  # batch x heads
-    n: int  # sequence length (queries = keys)
+    n: int  # sequence length: keys (and queries unless nq is set)
     d: int  # head dimension
     dtype: str  # "f32" or "bf16" input storage
     seed: int
@@ -37,6 +37,11 @@ class Workload:
     kind: str = "fwd"  # "fwd", "smallcache" or "bwd"
     batch: int = 1
     heads: int = 1
+    nq: int = 0  # query rows per head for rectangular workloads (0: n)
+
+    @property
+    def queries(self) -> int:
+        return self.nq or self.n
 
     @property
     def scale(self) -> float:
@@ -44,13 +49,15 @@ class Workload:
 
     @property
     def fwd_flops(self) -> float:
-        """4 N^2 d per head: the two products, mul and add counted apart."""
-        return 4.0 * self.n * self.n * self.d * self.bh
+        """4 nq nk d per head: the two products, mul and add counted apart."""
+        return 4.0 * self.queries * self.n * self.d * self.bh
 
 
-# The five workloads: a tiny fp32 case, the N=4096/d=64 teaching shape, the
-# long-sequence d=128 case with large score ranges, the small-cache d=256
-# case, and the backward case.
+# The five square workloads: a tiny fp32 case, the N=4096/d=64 teaching
+# shape, the long-sequence d=128 case with large score ranges, the small-cache
+# d=256 case, and the backward case; then two rectangular ones for the
+# key-split forward: single-query decoding of 8 sequences x 32 heads against a
+# 16384-key cache, and a 1024-query chunk against the same cache length.
 WORKLOADS = {
     w.name: w
     for w in (
@@ -62,6 +69,10 @@ WORKLOADS = {
                  kind="smallcache", batch=1, heads=8),
         Workload("bwd_bf16_b2h16_n4096_d128", 32, 4096, 128, "bf16", 5, kind="bwd",
                  batch=2, heads=16),
+        Workload("decode_bf16_b8h32_q1_k16384_d128", 256, 16384, 128, "bf16", 6, kind="splitk",
+                 batch=8, heads=32, nq=1),
+        Workload("chunk_bf16_b1h32_q1024_k16384_d128", 32, 16384, 128, "bf16", 7,
+                 kind="splitk", batch=1, heads=32, nq=1024),
     )
 }
 
@@ -91,4 +102,5 @@ def make_inputs(bh: int, n: int, d: int, dtype: str = "bf16", seed: int = 0,
 
 
 def workload_inputs(w: Workload):
-    return make_inputs(w.bh, w.n, w.d, w.dtype, w.seed, w.q_mult, with_do=(w.kind == "bwd"))
+    return make_inputs(w.bh, w.queries, w.d, w.dtype, w.seed, w.q_mult,
+                       with_do=(w.kind == "bwd"), nk=w.n)

@@ -313,6 +313,28 @@ def secondary(args, at, torch, dev):
         fl = 10.0 * w.n * w.n * w.d * w.bh  # 2 products recomputed-free count: 5 GEMMs
         res["backward"] = {"workload": w.name, "ms": round(ms, 4),
                            "tflops_at_10N2d": round(fl / (ms * 1e-3) / 1e12, 2)}
+    for name in ("decode_bf16_b8h32_q1_k16384_d128", "chunk_bf16_b1h32_q1024_k16384_d128"):
+        w = WORKLOADS[name]
+        print(f"[bench] timing {w.name}", file=sys.stderr, flush=True)
+        q, k, v = (t.to(dev) for t in workload_inputs(w))
+        nq = w.queries
+        o = torch.empty((w.bh, nq, w.d), dtype=torch.float32, device=dev)
+        lse = torch.empty((w.bh, nq), dtype=torch.float32, device=dev)
+        splits = at.splitk_splits(w.bh, nq, w.n, w.d, 0)
+        need = int(at.lib().attn_fwd_splitk_workspace_size(w.bh, nq, w.n, w.d, 0))
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        ms, _, _ = time_launches(lambda: at.attn_fwd_splitk(q, k, v, 0, w.scale, out=o, lse=lse,
+                                                            workspace=ws),
+                                 args.steps, args.warmup)
+        # compulsory bytes: Q, K, V in bf16; O and lse in fp32
+        byts = w.bh * (nq * w.d * 2 + 2 * w.n * w.d * 2 + nq * w.d * 4 + nq * 4)
+        res[w.kind + "_" + name.split("_")[0]] = {
+            "workload": w.name, "splits": splits, "ms": round(ms, 4),
+            "tflops": round(w.fwd_flops / (ms * 1e-3) / 1e12, 2),
+            "compulsory_bytes": byts,
+            "hbm_gbps": round(byts / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+        del q, k, v, o, lse, ws
     torch.cuda.synchronize()
     return res
 

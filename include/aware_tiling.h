@@ -95,6 +95,45 @@ int64_t attn_fwd_onchip_elems(int64_t d, attn_dtype dtype);
 int64_t attn_fwd_query_block(int64_t d, attn_dtype dtype);
 
 /*
+ * attn_fwd_splitk -- fused forward for rectangular shapes, nq queries against
+ * nk keys per head (nq much smaller than nk: decoding, chunked prefill).
+ *
+ * The exposition's closing section notes that single-token decoding (query
+ * length one) is outside the square N x N analysis and needs a rectangular
+ * account.  This entry point cuts the keys of every head into `splits`
+ * contiguous chunks, runs the streaming computation of attn_fwd on each
+ * (query block, chunk) pair in its own workgroup, and merges the per-chunk
+ * results with the same rescaling rule the streaming recurrence uses within
+ * a chunk ("Softmax without storing the score matrix"): with lse_s and o_s
+ * the log-sum-exp and normalised output of chunk s,
+ *     lse = log sum_s exp(lse_s),   o = sum_s exp(lse_s - lse) o_s.
+ * The result is the same function as attn_fwd (identical when nq == nk).
+ *
+ *   Q       : [bh, nq, d] bf16;  K, V : [bh, nk, d] bf16 (device, read only)
+ *   O       : [bh, nq, d] float; lse : [bh, nq] float or NULL (as attn_fwd)
+ *   splits  : requested chunk count, 1..256, or 0 for an automatic choice
+ *             (enough workgroups to fill the device, >= 256 keys a chunk).
+ *             Chunks are whole 64-key tiles, so fewer may be used; see
+ *             attn_fwd_splitk_splits().
+ *   workspace, workspace_bytes : device scratch of at least
+ *             attn_fwd_splitk_workspace_size(bh, nq, nk, d, splits) bytes,
+ *             256-byte aligned (0 bytes, and NULL allowed, when one chunk
+ *             is used).  It holds the per-chunk o_s and lse_s; contents on
+ *             return are unspecified.
+ *   bh*nq == 0 is a no-op; nk must be >= 1 otherwise (ATTN_ERR_INVALID_ARG).
+ *   bf16 only, d in {64, 128}.
+ */
+int64_t attn_fwd_splitk_splits(int64_t bh, int64_t nq, int64_t nk, int64_t d,
+                               int64_t splits);
+size_t attn_fwd_splitk_workspace_size(int64_t bh, int64_t nq, int64_t nk,
+                                      int64_t d, int64_t splits);
+attn_status attn_fwd_splitk(const void* Q, const void* K, const void* V,
+                            float* O, float* lse, int64_t bh, int64_t nq,
+                            int64_t nk, int64_t d, float scale,
+                            attn_dtype dtype, int64_t splits, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * attn_fwd_smallcache -- square-tile forward for the small-cache regime.
  *
  * Follows the exposition's section "Small caches: when storing an

@@ -77,7 +77,8 @@ def pin_golden_forward(lib):
 
 
 def pin_torch_library(lib):
-    shapes = [(1, 1, 1, 1), (2, 17, 17, 5), (3, 64, 33, 16), (1, 40, 512, 64), (2, 9, 3, 7)]
+    shapes = [(1, 1, 1, 1), (2, 17, 17, 5), (3, 64, 33, 16), (1, 40, 512, 64), (2, 9, 3, 7),
+              (3, 1, 700, 8)]
     for i, (bh, nq, nk, d) in enumerate(shapes):
         q, k, v = _rand(100 + i, bh, nq, nk, d)
         scale = 1.0 / math.sqrt(d)

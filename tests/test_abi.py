@@ -163,3 +163,36 @@ def test_smallcache_tile_selection(lib):
     assert lib.attn_smallcache_tile(128, 16000) == 64  # b=128 would not be below d^2
     assert lib.attn_smallcache_tile(256, 65536) == 0  # not the small-cache regime
     assert lib.attn_smallcache_tile(64, 4000) == 0  # no tile fits below d^2 = 4096
+
+
+def test_splitk_validation_and_sizes(lib):
+    bh, nq, nk, d = 32, 1, 16384, 128
+    call = lambda q=FAKE, o=FAKE, nq_=nq, nk_=nk, d_=d, s=8, w=FAKE * 256, wsb=1 << 30, \
+        dt=BF16, scale=0.088: lib.attn_fwd_splitk(q, FAKE, FAKE, o, None, bh, nq_, nk_, d_,
+                                                  scale, dt, s, w, wsb, None)
+    assert call(q=None) == INVALID
+    assert call(o=FAKE + 4) == INVALID
+    assert call(nk_=0) == INVALID  # softmax over no keys
+    assert call(s=-1) == INVALID
+    assert call(s=257) == INVALID
+    assert call(d_=256) == UNSUPPORTED
+    assert call(dt=F32) == UNSUPPORTED
+    assert call(scale=0.0) == INVALID
+    assert call(q=None, o=None, nq_=0) == OK  # empty query set is a no-op
+    # chunks are whole 64-key tiles: 16384 keys in 8 requested chunks -> 8 of 2048
+    assert lib.attn_fwd_splitk_splits(bh, nq, nk, d, 8) == 8
+    # 100 keys in 4 requested chunks -> chunks of 64 keys -> 2 chunks
+    assert lib.attn_fwd_splitk_splits(bh, nq, 100, d, 4) == 2
+    assert lib.attn_fwd_splitk_splits(bh, nq, 64, d, 4) == 1
+    # workspace: splits x bh x nq x (d + 1) floats, each part 256-byte aligned
+    ws = lib.attn_fwd_splitk_workspace_size(bh, nq, nk, d, 8)
+    assert ws == ((8 * bh * nq * d * 4 + 255) // 256 + (8 * bh * nq * 4 + 255) // 256) * 256
+    assert lib.attn_fwd_splitk_workspace_size(bh, nq, 64, d, 4) == 0  # one chunk: none needed
+    assert call(w=None, wsb=ws) == WORKSPACE
+    assert call(wsb=ws - 1) == WORKSPACE
+    assert call(w=FAKE * 256 + 16, wsb=ws) == WORKSPACE
+    # automatic choice: >= 1 chunk, never more than 256, >= 256 keys per chunk
+    for (b_, q_, k_) in ((1, 1, 100), (32, 1, 131072), (8, 512, 8192), (64, 4096, 4096)):
+        s = lib.attn_fwd_splitk_splits(b_, q_, k_, d, 0)
+        assert 1 <= s <= 256
+        assert s == 1 or (k_ + s - 1) // s >= 192
