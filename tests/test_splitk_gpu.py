@@ -56,14 +56,20 @@ def test_splitk_matches_oracle(bh, nq, nk, d, splits, seed, q_mult):
 
 
 def test_splitk_square_agrees_with_fused():
-    """nq == nk: the key-split call computes the same function as attn_fwd."""
+    """nq == nk: with one chunk the key-split call runs the fused schedule
+    and matches attn_fwd bit for bit; with three chunks each chunk rounds its
+    weights to bf16 against its own running maximum, so it agrees with the
+    oracle to the same bar as attn_fwd does (not bit for bit)."""
     (qc, kc, vc), (q, k, v) = _inputs(2, 500, 500, 128, 211, 1.0)
     o1, l1 = at.attn_fwd(q, k, v)
-    for s in (1, 3):
-        o2, l2 = at.attn_fwd_splitk(q, k, v, s)
-        torch.cuda.synchronize()
-        check(f64(o2), f64(o1), 1e-5, f"split {s} vs fused O")
-        check(f64(l2), f64(l1), 1e-5, f"split {s} vs fused lse")
+    o2, l2 = at.attn_fwd_splitk(q, k, v, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    o3, l3 = at.attn_fwd_splitk(q, k, v, 3)
+    torch.cuda.synchronize()
+    ro, rl, _ = oracle.attn_fwd(f64(qc), f64(kc), f64(vc), at.default_scale(128))
+    check(f64(o3), ro, TOL["bf16"], "split 3 O")
+    check(f64(l3), rl, TOL["bf16"], "split 3 lse")
 
 
 def test_splitk_decode_workload_every_output():
