@@ -41,6 +41,11 @@ SIGNATURES = {
     "attn_bwd_workspace_size": (_sz, [_i64, _i64, _i64]),
     "attn_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _int,
                         _vp, _sz, _vp]),
+    "attn_bwd_smallcache_tile": (_i64, [_i64, _i64]),
+    "attn_bwd_smallcache_onchip_elems": (_i64, [_i64, _i64]),
+    "attn_bwd_smallcache_workspace_size": (_sz, [_i64, _i64, _i64, _i64]),
+    "attn_bwd_smallcache": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                   _f32, _int, _i64, _vp, _sz, _vp]),
 }
 
 _lib = None
@@ -219,6 +224,34 @@ def attn_bwd(q, k, v, o, do, lse, scale: float | None = None, workspace=None, gr
                         workspace.numel() * workspace.element_size(), _stream(q, stream))
     _check("attn_bwd", rc)
     return dq, dk, dv
+
+
+def attn_bwd_smallcache(q, k, v, o, do, lse, m_elems: int, scale: float | None = None,
+                        workspace=None, grads=None, stream=None):
+    """Square-tile (small-cache) gradients (dQ, dK, dV) in fp32; the n x n
+    P^T and dS^T live in the workspace."""
+    _check_inputs(q, k, v, o, do)
+    bh, n, d = q.shape
+    scale = default_scale(d) if scale is None else float(scale)
+    need = int(lib().attn_bwd_smallcache_workspace_size(bh, n, d, int(m_elems)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if grads is None:
+        grads = tuple(torch.empty((bh, n, d), dtype=torch.float32, device=q.device)
+                      for _ in range(3))
+    dq, dk, dv = grads
+    rc = lib().attn_bwd_smallcache(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                   dv.data_ptr(), bh, n, d, scale, _dtype_code(q), int(m_elems),
+                                   workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(),
+                                   _stream(q, stream))
+    _check("attn_bwd_smallcache", rc)
+    return dq, dk, dv
+
+
+def bwd_smallcache_tile(d: int, m_elems: int) -> int:
+    return int(lib().attn_bwd_smallcache_tile(d, m_elems))
 
 
 def fwd_onchip_elems(d: int, dtype: torch.dtype = torch.bfloat16) -> int:

@@ -198,4 +198,46 @@ attn_status attn_bwd(const void* Q, const void* K, const void* V, const float* O
                                            workspace, static_cast<hipStream_t>(stream)));
 }
 
+int64_t attn_bwd_smallcache_tile(int64_t d, int64_t m_elems) {
+  return at::bwd_smallcache_tile(d, m_elems).b;
+}
+
+int64_t attn_bwd_smallcache_onchip_elems(int64_t d, int64_t m_elems) {
+  const at::SmallBwdTile t = at::bwd_smallcache_tile(d, m_elems);
+  return t.b ? at::bwd_smallcache_onchip_elems(t.b, t.stages) : 0;
+}
+
+size_t attn_bwd_smallcache_workspace_size(int64_t bh, int64_t n, int64_t d, int64_t m_elems) {
+  if (!shape_ok(bh, n, d)) return 0;
+  const at::SmallBwdTile t = at::bwd_smallcache_tile(d, m_elems);
+  if (t.b == 0) return 0;
+  return at::bwd_smallcache_workspace_bytes(bh, n, t.b);
+}
+
+attn_status attn_bwd_smallcache(const void* Q, const void* K, const void* V, const float* O,
+                                const void* dO, const float* lse, float* dQ, float* dK,
+                                float* dV, int64_t bh, int64_t n, int64_t d, float scale,
+                                attn_dtype dtype, int64_t m_elems, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (!shape_ok(bh, n, d) || !scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
+  if (!at::bwd_smallcache_supported(d)) return ATTN_ERR_UNSUPPORTED;
+  if (m_elems <= 0 || m_elems >= d * d) return ATTN_ERR_INVALID_ARG;
+  const at::SmallBwdTile t = at::bwd_smallcache_tile(d, m_elems);
+  if (t.b == 0) return ATTN_ERR_UNSUPPORTED;
+  if (bh * n == 0) return ATTN_OK;
+  // the n x n intermediates are indexed per head with 32-bit tile counts
+  const int64_t nt = (n + t.b - 1) / t.b;
+  if (nt * t.b > (int64_t(1) << 20) || bh * nt * nt >= (int64_t(1) << 31))
+    return ATTN_ERR_INVALID_ARG;
+  const void* ptrs[] = {Q, K, V, O, dO, lse, dQ, dK, dV};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return ATTN_ERR_INVALID_ARG;
+  const size_t need = at::bwd_smallcache_workspace_bytes(bh, n, t.b);
+  if (!workspace || workspace_bytes < need || !aligned256(workspace)) return ATTN_ERR_WORKSPACE;
+  return launch_status(at::launch_bwd_smallcache_bf16(Q, K, V, O, dO, lse, dQ, dK, dV, bh, n, d,
+                                                      scale, t, workspace,
+                                                      static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -773,6 +773,27 @@ hipError_t launch(const void* Q, const void* K, const void* V, const float* O, c
 
 }  // namespace
 
+hipError_t launch_bwd_preprocess(const float* O, const void* dO, float* Dout, int64_t rows,
+                                 int64_t d, hipStream_t stream) {
+  const bf16* g = static_cast<const bf16*>(dO);
+  switch (d) {
+    case 64:
+      hipLaunchKernelGGL(bwd_preprocess<64>, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0,
+                         stream, O, g, Dout, rows);
+      break;
+    case 128:
+      hipLaunchKernelGGL(bwd_preprocess<128>, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0,
+                         stream, O, g, Dout, rows);
+      break;
+    case 256:
+      hipLaunchKernelGGL(bwd_preprocess<256>, dim3((unsigned)((rows + 7) / 8)), dim3(256), 0,
+                         stream, O, g, Dout, rows);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 bool bwd_supported(int64_t d) { return d == 64 || d == 128; }
 
 size_t bwd_workspace_bytes(int64_t bh, int64_t n, int64_t) {

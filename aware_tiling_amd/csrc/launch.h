@@ -62,4 +62,24 @@ hipError_t launch_bwd_bf16(const void* Q, const void* K, const void* V, const fl
                            int64_t bh, int64_t n, int64_t d, float scale, void* workspace,
                            hipStream_t stream);
 
+// D_i = <dO_i, O_i> for rows = bh * n rows of width d in {64, 128, 256}.
+hipError_t launch_bwd_preprocess(const float* O, const void* dO, float* Dout, int64_t rows,
+                                 int64_t d, hipStream_t stream);
+
+// Square-tile (small-cache) backward.  The tile side b and the number of
+// staged panels are chosen from the on-chip budget M (elements, M < d^2).
+struct SmallBwdTile {
+  int b;       // square tile side, 0 if none fits
+  int stages;  // LDS panel stages (1 or 2)
+};
+bool bwd_smallcache_supported(int64_t d);
+int64_t bwd_smallcache_onchip_elems(int64_t b, int64_t stages);
+SmallBwdTile bwd_smallcache_tile(int64_t d, int64_t m_elems);
+size_t bwd_smallcache_workspace_bytes(int64_t bh, int64_t n, int64_t b);
+hipError_t launch_bwd_smallcache_bf16(const void* Q, const void* K, const void* V,
+                                      const float* O, const void* dO, const float* lse,
+                                      float* dQ, float* dK, float* dV, int64_t bh, int64_t n,
+                                      int64_t d, float scale, SmallBwdTile t, void* workspace,
+                                      hipStream_t stream);
+
 }  // namespace at

@@ -55,9 +55,11 @@ class Workload:
 
 # The five square workloads: a tiny fp32 case, the N=4096/d=64 teaching
 # shape, the long-sequence d=128 case with large score ranges, the small-cache
-# d=256 case, and the backward case; then two rectangular ones for the
-# key-split forward: single-query decoding of 8 sequences x 32 heads against a
-# 16384-key cache, and a 1024-query chunk against the same cache length.
+# d=256 case, and the backward case; the backward of the d=256 shape (run by
+# the small-cache backward, the one backward built for d=256); then two
+# rectangular ones for the key-split forward: single-query decoding of 8
+# sequences x 32 heads against a 16384-key cache, and a 1024-query chunk
+# against the same cache length.
 WORKLOADS = {
     w.name: w
     for w in (
@@ -69,6 +71,8 @@ WORKLOADS = {
                  kind="smallcache", batch=1, heads=8),
         Workload("bwd_bf16_b2h16_n4096_d128", 32, 4096, 128, "bf16", 5, kind="bwd",
                  batch=2, heads=16),
+        Workload("bwd_smallcache_bf16_b1h8_n4096_d256", 8, 4096, 256, "bf16", 8, kind="bwd",
+                 batch=1, heads=8),
         Workload("decode_bf16_b8h32_q1_k16384_d128", 256, 16384, 128, "bf16", 6, kind="splitk",
                  batch=8, heads=32, nq=1),
         Workload("chunk_bf16_b1h32_q1024_k16384_d128", 32, 16384, 128, "bf16", 7,

@@ -313,6 +313,34 @@ def secondary(args, at, torch, dev):
         fl = 10.0 * w.n * w.n * w.d * w.bh  # 2 products recomputed-free count: 5 GEMMs
         res["backward"] = {"workload": w.name, "ms": round(ms, 4),
                            "tflops_at_10N2d": round(fl / (ms * 1e-3) / 1e12, 2)}
+    for name, m_sc in (("bwd_smallcache_bf16_b1h8_n4096_d256", 49152),
+                       ("bwd_bf16_b2h16_n4096_d128", 12288)):
+        w = WORKLOADS[name]
+        b = at.bwd_smallcache_tile(w.d, m_sc)
+        print(f"[bench] timing small-cache backward {w.name} M={m_sc}", file=sys.stderr,
+              flush=True)
+        q, k, v, do = (t.to(dev) for t in workload_inputs(w))
+        o, lse = at.attn_fwd(q, k, v, w.scale)
+        grads = tuple(torch.empty((w.bh, w.n, w.d), dtype=torch.float32, device=dev)
+                      for _ in range(3))
+        need = int(at.lib().attn_bwd_smallcache_workspace_size(w.bh, w.n, w.d, m_sc))
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        ms, _, _ = time_launches(lambda: at.attn_bwd_smallcache(
+            q, k, v, o, do, lse, m_sc, w.scale, workspace=ws, grads=grads),
+            args.steps, args.warmup)
+        npad = -(-w.n // b) * b
+        fl = 10.0 * w.n * w.n * w.d * w.bh
+        # n x n traffic of the schedule: P^T and dS^T written once, P^T read
+        # once (dV), dS^T read twice (dK, dQ); bf16
+        nn_bytes = 5 * w.bh * npad * npad * 2
+        res["smallcache_backward_d%d" % w.d] = {
+            "workload": w.name, "m_elems": m_sc, "tile_b": b,
+            "onchip_elems": int(at.lib().attn_bwd_smallcache_onchip_elems(w.d, m_sc)),
+            "ms": round(ms, 4), "tflops_at_10N2d": round(fl / (ms * 1e-3) / 1e12, 2),
+            "nxn_bytes": nn_bytes,
+            "nxn_gbps": round(nn_bytes / (ms * 1e-3) / 1e9, 1)}
+        del q, k, v, do, o, lse, grads, ws
+        torch.cuda.empty_cache()
     for name in ("decode_bf16_b8h32_q1_k16384_d128", "chunk_bf16_b1h32_q1024_k16384_d128"):
         w = WORKLOADS[name]
         print(f"[bench] timing {w.name}", file=sys.stderr, flush=True)

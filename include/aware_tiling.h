@@ -198,6 +198,45 @@ attn_status attn_bwd(const void* Q, const void* K, const void* V,
                      int64_t d, float scale, attn_dtype dtype, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/*
+ * attn_bwd_smallcache -- gradients of attn_fwd for the small-cache regime.
+ *
+ * The page "On Fine-Grained I/O Complexity of Attention Backward Passes"
+ * (explainer), sections "Methodology" and "Key Contributions and Results"
+ * (Theorem 1.1): when the on-chip budget M is below d^2 the blockwise
+ * schedule of attn_bwd is not optimal, and the page's Algorithm 6 writes the
+ * n x n attention matrices and the n x d intermediates to device memory and
+ * works on square tiles sized to M, for Theta((n^2 d + n d^2)/sqrt(M))
+ * transfers.  The page gives no further steps; this entry point computes the
+ * same gradients as attn_bwd (same formulas) in that form: square tiles of
+ * side b write P^T and dS^T (bf16, key-major) to the workspace, then three
+ * square-tile products give dV = P^T dO, dK = scale dS^T Q, dQ = scale dS K.
+ *
+ *   m_elems : on-chip budget M in elements, m_elems < d*d (otherwise
+ *             ATTN_ERR_INVALID_ARG).  The tile side b in {128, 64} and the
+ *             number of staged panels are the largest whose footprint
+ *             (accumulators plus staged panels, see
+ *             attn_bwd_smallcache_onchip_elems) fits m_elems
+ *             (ATTN_ERR_UNSUPPORTED if none fits).
+ *   workspace, workspace_bytes : at least
+ *             attn_bwd_smallcache_workspace_size(bh, n, d, m_elems) bytes,
+ *             256-byte aligned: D, P^T and dS^T, about 4 bh ceil(n/b)^2 b^2
+ *             bytes.  Contents on return unspecified.
+ *   Other arguments as attn_bwd.  bf16 only, d in {128, 256};
+ *   ceil(n/b) b <= 2^20.
+ */
+int64_t attn_bwd_smallcache_tile(int64_t d, int64_t m_elems);
+int64_t attn_bwd_smallcache_onchip_elems(int64_t d, int64_t m_elems);
+size_t attn_bwd_smallcache_workspace_size(int64_t bh, int64_t n, int64_t d,
+                                          int64_t m_elems);
+attn_status attn_bwd_smallcache(const void* Q, const void* K, const void* V,
+                                const float* O, const void* dO,
+                                const float* lse, float* dQ, float* dK,
+                                float* dV, int64_t bh, int64_t n, int64_t d,
+                                float scale, attn_dtype dtype, int64_t m_elems,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -196,3 +196,35 @@ def test_splitk_validation_and_sizes(lib):
         s = lib.attn_fwd_splitk_splits(b_, q_, k_, d, 0)
         assert 1 <= s <= 256
         assert s == 1 or (k_ + s - 1) // s >= 192
+
+
+def test_bwd_smallcache_tile_selection_and_validation(lib):
+    # footprint(b, stages) = max(2 b^2 + 4 b 16 stages, b^2 + 2 b 16 stages)
+    tile, onchip = lib.attn_bwd_smallcache_tile, lib.attn_bwd_smallcache_onchip_elems
+    assert (tile(256, 49152), onchip(256, 49152)) == (128, 49152)
+    assert (tile(256, 40960), onchip(256, 40960)) == (128, 40960)
+    assert (tile(256, 40959), onchip(256, 40959)) == (64, 16384)
+    assert (tile(256, 16383), onchip(256, 16383)) == (64, 12288)
+    assert tile(256, 12287) == 0
+    assert (tile(128, 12288), onchip(128, 12288)) == (64, 12288)
+    assert tile(128, 16384) == 0  # M >= d^2 is the large-cache regime
+    assert tile(64, 4000) == 0  # nothing fits below d^2 = 4096
+    b = 64
+    npad = (300 + b - 1) // b * b
+    ws = lib.attn_bwd_smallcache_workspace_size(2, 300, 128, 12288)
+    assert ws == ((2 * 300 * 4 + 255) // 256 * 256
+                  + 2 * ((2 * npad * npad * 2 + 255) // 256 * 256))
+    call = lambda **kw: lib.attn_bwd_smallcache(
+        *[kw.get(x, FAKE) for x in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv")],
+        2, 300, kw.get("d", 128), kw.get("scale", 0.08), kw.get("dt", BF16),
+        kw.get("m", 12288), kw.get("w", FAKE * 256), kw.get("wsb", ws), None)
+    assert call(lse=None) == INVALID
+    assert call(dk=FAKE + 4) == INVALID
+    assert call(d=64, m=4000) == UNSUPPORTED
+    assert call(m=16384) == INVALID
+    assert call(m=0) == INVALID
+    assert call(d=256, m=12000) == UNSUPPORTED  # below d^2 but no tile fits
+    assert call(dt=F32) == UNSUPPORTED
+    assert call(wsb=ws - 1) == WORKSPACE
+    assert call(w=None) == WORKSPACE
+    assert call(w=FAKE * 256 + 32) == WORKSPACE
