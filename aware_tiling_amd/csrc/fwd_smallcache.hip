@@ -309,15 +309,16 @@ __global__ __launch_bounds__(B * 2, 1) void sc_value_product(
 
 namespace {
 
-// On-chip elements per workgroup, each counted once whatever its width: the
-// larger of the two products' footprints.  Scores: the b x b score tile and
-// one Q and one K panel (b x KP each).  Value product: the b x bd output
-// tile, the b x bd partial for the current key tile, one E panel (b x KP)
-// and one V panel (KP x bd).
+// On-chip elements per workgroup, each counted once whatever its width, and
+// every pipeline stage counted: the larger of the two products' footprints.
+// Scores: the b x b score tile and two stages of the Q and K panels (b x KP
+// each).  Value product: the b x bd output tile, the b x bd partial for the
+// current key tile, the E panel in registers (b x KP) and two stages of the
+// V panel (KP x bd).
 int64_t footprint(int64_t b, int64_t d) {
   const int64_t bd = b < d ? b : d;
-  const int64_t s = b * b + 2 * b * KP;
-  const int64_t v = 2 * b * bd + b * KP + KP * bd;
+  const int64_t s = b * b + 2 * 2 * b * KP;
+  const int64_t v = 2 * b * bd + b * KP + 2 * KP * bd;
   return s > v ? s : v;
 }
 
