@@ -23,6 +23,9 @@ Entry points (all shapes ``[bh, rows, d]``, d fastest):
 * :func:`attn_fwd_square` -- the square-tile schedule of page 1, "Small caches:
   when storing an intermediate matrix helps" (per-tile exponentials, merged
   statistics, second product).
+* :func:`attn_fwd_masked` -- the direct definition restricted to the
+  query-key pairs a block mask keeps (page 3's sparse attention), rows with
+  no kept key giving O = 0 and lse = -inf.
 * :func:`attn_bwd` -- exact gradients dQ, dK, dV of the same function for an
   upstream gradient dO (page 3 states the backward problem; the formulas are
   ordinary calculus, written out in ``attn_oracle.c``).
@@ -70,8 +73,11 @@ def _bind(lib):
     lib.oracle_attn_fwd_stream_f64.argtypes = [_F64P] * 5 + [i64] * 4 + [dbl, i64, cint]
     lib.oracle_attn_fwd_square_f64.argtypes = [_F64P] * 5 + [i64] * 4 + [dbl, i64, cint]
     lib.oracle_attn_bwd_f64.argtypes = [_F64P] * 8 + [i64] * 4 + [dbl, cint]
+    lib.oracle_attn_fwd_masked_f64.argtypes = ([_F64P] * 5 + [i64] * 4 +
+                                               [dbl, ctypes.c_void_p, i64, i64, i64, cint])
     for f in (lib.oracle_attn_fwd_f64, lib.oracle_attn_fwd_stream_f64,
-              lib.oracle_attn_fwd_square_f64, lib.oracle_attn_bwd_f64):
+              lib.oracle_attn_fwd_square_f64, lib.oracle_attn_bwd_f64,
+              lib.oracle_attn_fwd_masked_f64):
         f.restype = cint
     return lib
 
@@ -113,6 +119,30 @@ def attn_fwd(q, k, v, scale: float, threads: int = 0, lib=None):
     lib = lib or load()
     t = _check(lib.oracle_attn_fwd_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                        bh, nq, nk, d, float(scale), int(threads)), "fwd")
+    return o, lse, t
+
+
+def attn_fwd_masked(q, k, v, scale: float, mask, bq: int, bk: int, threads: int = 0,
+                    lib=None):
+    """Definition over the pairs a block mask keeps.  ``mask`` is
+    [mask_heads, ceil(nq/bq), ceil(nk/bk)] (nonzero = kept), mask_heads 1 or
+    bh.  Returns (O, lse, threads_used); rows with no kept key give O = 0,
+    lse = -inf."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    bh, nq, nk, d = _shapes(q, k, v)
+    if hasattr(mask, "detach"):
+        mask = mask.detach().to("cpu").numpy()
+    m = np.ascontiguousarray(np.asarray(mask) != 0, dtype=np.uint8)
+    nbq, nbk = -(-nq // bq), -(-nk // bk)
+    if m.ndim != 3 or m.shape[1:] != (nbq, nbk) or m.shape[0] not in (1, bh):
+        raise ValueError(f"mask shape {m.shape} does not match ({bh} or 1, {nbq}, {nbk})")
+    o = np.empty((bh, nq, d))
+    lse = np.empty((bh, nq))
+    lib = lib or load()
+    t = _check(lib.oracle_attn_fwd_masked_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                              bh, nq, nk, d, float(scale),
+                                              m.ctypes.data_as(ctypes.c_void_p), m.shape[0],
+                                              int(bq), int(bk), int(threads)), "fwd_masked")
     return o, lse, t
 
 

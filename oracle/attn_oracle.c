@@ -179,6 +179,97 @@ int oracle_attn_fwd_f64(const double* Q, const double* K, const double* V,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Masked (block-sparse) definition.  Sparse attention (page 3, "Sparse
+ * Attention Extension" and result 2) keeps only some query-key pairs; the
+ * page gives lower bounds in terms of the kept entries and no algorithm.
+ * Here the kept pairs are given by a block mask: query i and key j interact
+ * iff mask[hm][i / bq][j / bk] != 0, with hm = h when mask_heads == bh and
+ * hm = 0 when mask_heads == 1 (one mask for every head); the mask is
+ * [mask_heads][ceil(nq/bq)][ceil(nk/bk)] bytes.  Each output row is the
+ * softmax-weighted average over its kept keys only:
+ *     o_i = sum_{j kept} exp(s_ij) v_j / sum_{j kept} exp(s_ij),
+ *     lse_i = log sum_{j kept} exp(s_ij).
+ * A row with no kept key has no softmax; by convention o_i = 0 and
+ * lse_i = -inf.  The same three loops as the direct definition, visiting
+ * only kept keys. */
+
+typedef struct {
+  const double *Q, *K, *V;
+  double *O, *lse;
+  int64_t nq, nk, d;
+  double scale;
+  const uint8_t* mask;
+  int64_t mask_heads, bq, bk, nbq, nbk;
+  double** scratch; /* per thread, nk doubles */
+} masked_args;
+
+static void masked_rows(void* p, int64_t lo, int64_t hi, int tid) {
+  masked_args* a = (masked_args*)p;
+  double* e = a->scratch[tid];
+  const int64_t nq = a->nq, nk = a->nk, d = a->d;
+  for (int64_t r = lo; r < hi; ++r) {
+    const int64_t h = r / nq, i = r % nq;
+    const int64_t hm = a->mask_heads == 1 ? 0 : h;
+    const uint8_t* mrow = a->mask + (hm * a->nbq + i / a->bq) * a->nbk;
+    const double* q = a->Q + (h * nq + i) * d;
+    const double* K = a->K + h * nk * d;
+    const double* V = a->V + h * nk * d;
+    double* o = a->O + (h * nq + i) * d;
+    /* loop 1: scores of the kept keys and their maximum */
+    double m = -INFINITY;
+    int64_t kept = 0;
+    for (int64_t j = 0; j < nk; ++j) {
+      if (!mrow[j / a->bk]) continue;
+      double dot = 0.0;
+      for (int64_t k = 0; k < d; ++k) dot += q[k] * K[j * d + k];
+      e[j] = a->scale * dot;
+      if (e[j] > m) m = e[j];
+      ++kept;
+    }
+    if (kept == 0) {
+      for (int64_t k = 0; k < d; ++k) o[k] = 0.0;
+      if (a->lse) a->lse[h * nq + i] = -INFINITY;
+      continue;
+    }
+    /* loop 2: shifted exponentials of the kept keys and their sum */
+    double ell = 0.0;
+    for (int64_t j = 0; j < nk; ++j) {
+      if (!mrow[j / a->bk]) continue;
+      e[j] = exp(e[j] - m);
+      ell += e[j];
+    }
+    /* loop 3: o_i = (sum over kept j of e_j v_j) / ell */
+    for (int64_t k = 0; k < d; ++k) {
+      double acc = 0.0;
+      for (int64_t j = 0; j < nk; ++j)
+        if (mrow[j / a->bk]) acc += e[j] * V[j * d + k];
+      o[k] = acc / ell;
+    }
+    if (a->lse) a->lse[h * nq + i] = m + log(ell);
+  }
+}
+
+int oracle_attn_fwd_masked_f64(const double* Q, const double* K, const double* V,
+                               double* O, double* lse, int64_t bh, int64_t nq,
+                               int64_t nk, int64_t d, double scale,
+                               const uint8_t* mask, int64_t mask_heads,
+                               int64_t bq, int64_t bk, int threads) {
+  if (!Q || !K || !V || !O || !mask || bh < 0 || nq < 0 || nk < 1 || d < 1 ||
+      bq < 1 || bk < 1 || !(mask_heads == 1 || mask_heads == bh))
+    return -1;
+  int64_t rows = bh * nq;
+  if (rows == 0) return 1;
+  threads = resolve_threads(threads, rows);
+  masked_args a = {Q, K, V, O, lse, nq, nk, d, scale, mask, mask_heads, bq, bk,
+                   (nq + bq - 1) / bq, (nk + bk - 1) / bk,
+                   alloc_scratch(threads, nk)};
+  if (!a.scratch) return -2;
+  int rc = run_parallel(masked_rows, &a, rows, threads);
+  free_scratch(a.scratch, threads);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Streaming recurrence (page 1, "Softmax without storing the score
  * matrix"): keys are consumed in blocks J of `block` consecutive indices.
  * For each block the running maximum m, normaliser ell and unnormalised

@@ -9,8 +9,10 @@ shows that a plausible slip in the oracle is caught by at least one pin).
 Definition pinned (page 1, "Attention as a mathematical problem"):
 s_ij = scale <q_i, k_j>, p_ij = softmax_j(s_ij), o_i = sum_j p_ij v_j.
 Streaming recurrence pinned (page 1, "Softmax without storing the score
-matrix").  Square-tile schedule pinned (page 1, "Small caches").  Gradients
-pinned by finite differences of the forward and by closed forms.
+matrix").  Square-tile schedule pinned (page 1, "Small caches").  The
+block-masked definition (page 3's sparse attention) pinned against plain
+attention over each row's kept keys.  Gradients pinned by finite
+differences of the forward and by closed forms.
 """
 from __future__ import annotations
 
@@ -309,6 +311,72 @@ def pin_gradient_invariants(lib):
     _close(D, np.sum(do * o, axis=-1), 1e-12, 1e-12, "D = <dO, O>")
 
 
+# --------------------------------------------------------------------------
+# masked (block-sparse) pins
+
+
+def _random_mask(seed, heads, nbq, nbk, density):
+    return (_rng(seed).random((heads, nbq, nbk)) < density).astype(np.uint8)
+
+
+def pin_masked_all_kept_is_dense(lib):
+    q, k, v = _rand(40, 2, 37, 53, 8)
+    for bq, bk in ((1, 1), (16, 8), (128, 128)):
+        m = np.ones((1, -(-37 // bq), -(-53 // bk)), np.uint8)
+        o, lse, _ = oracle.attn_fwd_masked(q, k, v, 0.3, m, bq, bk, lib=lib)
+        ro, rl, _ = oracle.attn_fwd(q, k, v, 0.3, lib=lib)
+        _close(o, ro, 1e-15, 1e-14, f"all-kept O bq={bq} bk={bk}")
+        _close(lse, rl, 1e-15, 1e-14, f"all-kept lse bq={bq} bk={bk}")
+
+
+def pin_masked_equals_definition_on_kept_keys(lib):
+    """Each row equals plain attention (torch float64 softmax / matmul) over
+    just the keys its mask blocks keep."""
+    cases = [(41, 2, 30, 45, 6, 8, 16, 2), (42, 3, 17, 64, 4, 4, 8, 1), (43, 1, 50, 33, 5, 7, 5, 1)]
+    for seed, bh, nq, nk, d, bq, bk, mh in cases:
+        q, k, v = _rand(seed, bh, nq, nk, d, qs=1.5)
+        m = _random_mask(seed + 100, mh if mh == 1 else bh, -(-nq // bq), -(-nk // bk), 0.55)
+        m[:, :, 0] = 1  # every row keeps something
+        o, lse, _ = oracle.attn_fwd_masked(q, k, v, 0.4, m, bq, bk, lib=lib)
+        for h in range(bh):
+            for i in range(nq):
+                keep = np.flatnonzero(m[0 if mh == 1 else h, i // bq][np.arange(nk) // bk])
+                ro, rl = _torch_fwd(q[h:h + 1, i:i + 1], k[h:h + 1, keep], v[h:h + 1, keep], 0.4)
+                _close(o[h, i], ro[0, 0], 1e-13, 1e-12, f"masked O h{h} i{i}")
+                _close(lse[h, i], rl[0, 0], 1e-13, 1e-12, f"masked lse h{h} i{i}")
+
+
+def pin_masked_empty_row_and_single_key(lib):
+    q, k, v = _rand(44, 1, 6, 5, 3)
+    # bk = 1: mask row block 0 keeps key 3 only, block 1 keeps nothing
+    m = np.zeros((1, 2, 5), np.uint8)
+    m[0, 0, 3] = 1
+    o, lse, _ = oracle.attn_fwd_masked(q, k, v, 0.7, m, 3, 1, lib=lib)
+    for i in range(3):
+        _close(o[0, i], v[0, 3], 1e-15, 1e-15, "single kept key gives its value")
+        _close(lse[0, i], 0.7 * float(q[0, i] @ k[0, 3]), 1e-14, 1e-14, "lse = its score")
+    assert np.all(o[0, 3:] == 0.0), "rows with no kept key give O = 0"
+    assert np.all(np.isneginf(lse[0, 3:])), "rows with no kept key give lse = -inf"
+
+
+def pin_masked_block_permutation(lib):
+    """Permuting key blocks together with the mask's columns changes nothing."""
+    q, k, v = _rand(45, 2, 24, 40, 4)
+    m = _random_mask(145, 2, 3, 5, 0.6)
+    m[:, :, 1] = 1
+    perm = np.array([3, 0, 4, 1, 2])
+    kidx = np.concatenate([np.arange(b * 8, b * 8 + 8) for b in perm])
+    o1, l1, _ = oracle.attn_fwd_masked(q, k, v, 0.5, m, 8, 8, lib=lib)
+    o2, l2, _ = oracle.attn_fwd_masked(q, k[:, kidx], v[:, kidx], 0.5, m[:, :, perm], 8, 8,
+                                       lib=lib)
+    _close(o2, o1, 1e-14, 1e-13, "key block permutation O")
+    _close(l2, l1, 1e-14, 1e-13, "key block permutation lse")
+
+
+MASKED_PINS = [pin_masked_all_kept_is_dense, pin_masked_equals_definition_on_kept_keys,
+               pin_masked_empty_row_and_single_key, pin_masked_block_permutation]
+
+
 FORWARD_PINS = [pin_golden_forward, pin_torch_library, pin_identity_values_give_weights,
                 pin_constant_values, pin_zero_queries_mean_pool, pin_single_key,
                 pin_two_keys_logistic, pin_permutations, pin_shift_and_linearity,
@@ -317,4 +385,4 @@ FORWARD_PINS = [pin_golden_forward, pin_torch_library, pin_identity_values_give_
                 pin_stream_and_square_vs_torch, pin_thread_count]
 BACKWARD_PINS = [pin_golden_backward, pin_finite_differences, pin_autograd,
                  pin_gradient_invariants]
-ALL_PINS = FORWARD_PINS + BACKWARD_PINS
+ALL_PINS = FORWARD_PINS + MASKED_PINS + BACKWARD_PINS

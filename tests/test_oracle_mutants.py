@@ -31,6 +31,16 @@ MUTANTS = [
      "for (int64_t j = 1; j < nk; ++j) acc += e[j] * V[j * d + k];", 0),
     ("direct_lse_without_max", "a->lse[h * nq + i] = m + log(ell);",
      "a->lse[h * nq + i] = log(ell);", 0),
+    ("masked_row_block_uses_key_block_size",
+     "a->mask + (hm * a->nbq + i / a->bq) * a->nbk", "a->mask + (hm * a->nbq + i / a->bk) * a->nbk",
+     0),
+    ("masked_mask_shared_by_all_heads", "const int64_t hm = a->mask_heads == 1 ? 0 : h;",
+     "const int64_t hm = 0;", 0),
+    ("masked_sum_over_dropped_keys",
+     "      if (!mrow[j / a->bk]) continue;\n      e[j] = exp(e[j] - m);",
+     "      e[j] = mrow[j / a->bk] ? exp(e[j] - m) : exp(-1.0);", 0),
+    ("masked_empty_row_lse_zero", "if (a->lse) a->lse[h * nq + i] = -INFINITY;",
+     "if (a->lse) a->lse[h * nq + i] = 0.0;", 0),
     ("stream_sum_not_rescaled", "ell *= alpha;", "", 0),
     ("stream_output_not_rescaled", "for (int64_t k = 0; k < d; ++k) u[k] *= alpha;", "", 0),
     ("stream_max_not_carried", "const double mnew = m > mb ? m : mb;",
