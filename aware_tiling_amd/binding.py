@@ -33,6 +33,9 @@ SIGNATURES = {
     "attn_fwd_splitk_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "attn_fwd_splitk": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _int, _i64,
                                _vp, _sz, _vp]),
+    "attn_fwd_blocksparse_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "attn_fwd_blocksparse": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _int, _vp,
+                                    _i64, _vp, _sz, _vp]),
     "attn_fwd_smallcache_workspace_size": (_sz, [_i64, _i64, _i64, _i64]),
     "attn_fwd_smallcache": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _int, _i64,
                                    _vp, _sz, _vp]),
@@ -170,6 +173,48 @@ def attn_fwd_splitk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, splits: i
                                _dtype_code(q), int(splits), workspace.data_ptr(),
                                workspace.numel() * workspace.element_size(), _stream(q, stream))
     _check("attn_fwd_splitk", rc)
+    return out, lse
+
+
+SPARSE_BLOCK = 128  # ATTN_SPARSE_BLOCK: queries and keys per mask block
+
+
+def attn_fwd_blocksparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         block_mask: torch.Tensor, scale: float | None = None,
+                         out: torch.Tensor | None = None, lse: torch.Tensor | bool = True,
+                         workspace: torch.Tensor | None = None, stream=None):
+    """Forward over the 128 x 128 blocks that ``block_mask`` ([1 or bh, nb, nb],
+    uint8 or bool on the GPU, nonzero = kept) keeps.  Returns (O, lse); rows
+    with no kept key give O = 0, lse = -inf."""
+    _check_inputs(q, k, v)
+    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("Q, K, V must share shape and dtype")
+    bh, n, d = q.shape
+    nb = -(-n // SPARSE_BLOCK)
+    if block_mask.dtype == torch.bool:
+        block_mask = block_mask.to(torch.uint8)
+    if (block_mask.dtype != torch.uint8 or not block_mask.is_cuda or block_mask.dim() != 3
+            or tuple(block_mask.shape[1:]) != (nb, nb) or block_mask.shape[0] not in (1, bh)):
+        raise ValueError(f"block_mask must be uint8 [1 or {bh}, {nb}, {nb}] on the GPU")
+    block_mask = block_mask.contiguous()
+    mh = block_mask.shape[0]
+    scale = default_scale(d) if scale is None else float(scale)
+    need = int(lib().attn_fwd_blocksparse_workspace_size(bh, n, mh))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((bh, n, d), dtype=torch.float32, device=q.device)
+    if lse is True:
+        lse = torch.empty((bh, n), dtype=torch.float32, device=q.device)
+    elif lse is False:
+        lse = None
+    rc = lib().attn_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                    lse.data_ptr() if lse is not None else None, bh, n, d, scale,
+                                    _dtype_code(q), block_mask.data_ptr(), mh,
+                                    workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(),
+                                    _stream(q, stream))
+    _check("attn_fwd_blocksparse", rc)
     return out, lse
 
 

@@ -139,6 +139,31 @@ attn_status attn_fwd_splitk(const void* Q, const void* K, const void* V, float* 
                                                   workspace, static_cast<hipStream_t>(stream)));
 }
 
+size_t attn_fwd_blocksparse_workspace_size(int64_t bh, int64_t n, int64_t mask_heads) {
+  if (!shape_ok(bh, n, 64) || !(mask_heads == 1 || mask_heads == bh)) return 0;
+  return at::sparse_workspace_bytes(n, mask_heads);
+}
+
+attn_status attn_fwd_blocksparse(const void* Q, const void* K, const void* V, float* O,
+                                 float* lse, int64_t bh, int64_t n, int64_t d, float scale,
+                                 attn_dtype dtype, const uint8_t* block_mask,
+                                 int64_t mask_heads, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (!shape_ok(bh, n, d) || !scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (bh * n == 0) return ATTN_OK;
+  if (!(mask_heads == 1 || mask_heads == bh) || !block_mask) return ATTN_ERR_INVALID_ARG;
+  if (!Q || !K || !V || !O) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return ATTN_ERR_INVALID_ARG;
+  if (lse && !aligned16(lse)) return ATTN_ERR_INVALID_ARG;
+  const size_t need = at::sparse_workspace_bytes(n, mask_heads);
+  if (!workspace || workspace_bytes < need || !aligned256(workspace)) return ATTN_ERR_WORKSPACE;
+  return launch_status(at::launch_fwd_sparse_bf16(Q, K, V, O, lse, bh, n, d, scale, block_mask,
+                                                  mask_heads, workspace,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 int64_t attn_smallcache_tile(int64_t d, int64_t m_elems) {
   if (!at::smallcache_supported(d) || m_elems >= d * d) return 0;
   return at::smallcache_tile_for_budget(d, m_elems);

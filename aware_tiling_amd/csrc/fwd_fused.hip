@@ -616,6 +616,11 @@ struct DirectArgs {
   float* lse;
   int nq, nk, nqb, total, bh, kchunk;
   float c;
+  // Tile lists (block-sparse form only): row (mask head, query block) holds
+  // counts[row] ascending key-tile indices at tiles + row * tile_cap.
+  const int* tiles = nullptr;
+  const int* counts = nullptr;
+  int tile_cap = 0, mask_heads = 1;
 };
 
 // Swizzle functors for the K tile (row-wise reads) and the V tile
@@ -653,9 +658,14 @@ struct DirectCfg {
 // With SKIP (two-stage PIPE only) a wave whose 32 query rows all lie past
 // nq still loads its share of every tile but does no arithmetic; short query
 // blocks (decoding) then cost little beyond the key/value stream.
-template <int D, int NW, int BC, bool PIPE, int WPS, bool SCHED, int STAGES, bool SKIP = false>
+// With LIST (two-stage PIPE only) the workgroup visits only the key tiles of
+// its tile list, in ascending order; a workgroup with an empty list writes
+// O = 0 and lse = -inf (no kept key, no softmax).
+template <int D, int NW, int BC, bool PIPE, int WPS, bool SCHED, int STAGES, bool SKIP = false,
+          bool LIST = false>
 __device__ __forceinline__ void direct_body(const DirectArgs& A) {
   static_assert(!SKIP || (PIPE && STAGES == 2), "SKIP is built for the two-stage pipeline");
+  static_assert(!LIST || (PIPE && STAGES == 2), "LIST is built for the two-stage pipeline");
   using C = DirectCfg<D, NW, BC, PIPE, WPS, SCHED, STAGES>;
   const float c = A.c;
   __shared__ __attribute__((aligned(1024))) bf16 smem[C::LDS_ELEMS];
@@ -697,7 +707,32 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) uacc[db] = f32x16{};
   float m = -INFINITY, l = 0.f;
-  const int nt = (n + BC - 1) / BC;
+  const int* tlist = nullptr;
+  int nt = (n + BC - 1) / BC;
+  if constexpr (LIST) {
+    const int row = (A.mask_heads == 1 ? 0 : head) * A.nqb + qblk;
+    tlist = A.tiles + (size_t)row * A.tile_cap;
+    nt = A.counts[row];
+    if (nt == 0) {
+      if (q < nq) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<f32x4*>(Oh + (size_t)q * D + db * 32 + 8 * g + 4 * h) =
+                f32x4{0.f, 0.f, 0.f, 0.f};
+        if (h == 0 && lseh != nullptr) lseh[q] = -INFINITY;
+      }
+      return;
+    }
+  }
+  // first key of the t-th tile visited
+  auto kbase_of = [&](int t) -> int {
+    if constexpr (LIST)
+      return tlist[t] * BC;
+    else
+      return t * BC;
+  };
 
   // Issue the direct loads of tile t of `src` into the LDS tile `dst`.  Lane
   // chunk p of this wave is LDS chunk (row, phys); it fetches logical chunk
@@ -715,7 +750,7 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
     voff[it] = (uint32_t)(row * D + (phys ^ vswz(row)) * 8) * 2u;
   }
   auto load_tile = [&](const bf16* src, bf16* dst, int t, auto swz) {
-    const int kbase = t * BC;
+    const int kbase = kbase_of(t);
     const uint32_t* offs = decltype(swz)::is_v ? voff : koff;
     if (kbase + BC <= n) {
       const char* tb = reinterpret_cast<const char*>(src) + (size_t)kbase * (D * 2);
@@ -961,7 +996,10 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
   }
   if (active) {
     uint32_t pk[BC / 32][8];
-    softmax_max(s_cur, (n % BC) != 0, j * BC);
+    if constexpr (LIST)
+      softmax_max(s_cur, kbase_of(j) + BC > n, kbase_of(j));
+    else
+      softmax_max(s_cur, (n % BC) != 0, j * BC);
     softmax_exp(s_cur, pk);
     pv(Vb + (j % STAGES) * C::TILE, pk);
   }
@@ -997,6 +1035,41 @@ template <int D, int NW, int BC>
 __global__ __launch_bounds__(NW * 64, (8 / NW > 0 ? 8 / NW : 1)) void fwd_split_bf16_kernel(
     const DirectArgs A) {
   direct_body<D, NW, BC, true, 2, false, 2, true>(A);
+}
+
+// Block-sparse entry: one workgroup per (head, 128-query block), visiting
+// the key tiles its tile list names.
+template <int D, int NW, int BC>
+__global__ __launch_bounds__(NW * 64, (8 / NW > 0 ? 8 / NW : 1)) void fwd_sparse_bf16_kernel(
+    const DirectArgs A) {
+  direct_body<D, NW, BC, true, 2, false, 2, false, true>(A);
+}
+
+// Compacts one row of the block mask (mask head, query block) into the
+// ascending list of 64-key tiles it keeps: a kept 128-key block contributes
+// its two tiles, less a second tile that starts at or past n.  One wave per
+// row; ballots give each lane's position in the list.
+__global__ __launch_bounds__(64) void sparse_tile_lists(const uint8_t* __restrict__ mask,
+                                                        int* __restrict__ tiles,
+                                                        int* __restrict__ counts, int nkb, int n,
+                                                        int tile_cap) {
+  const int row = blockIdx.x, lane = threadIdx.x;
+  const uint8_t* mrow = mask + (size_t)row * nkb;
+  int* out = tiles + (size_t)row * tile_cap;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  int base = 0;
+  for (int kb0 = 0; kb0 < nkb; kb0 += 64) {
+    const int kb = kb0 + lane;
+    const bool first = kb < nkb && mrow[kb] != 0;
+    const bool second = first && (2 * kb + 1) * 64 < n;
+    const uint64_t bf = __builtin_amdgcn_ballot_w64(first);
+    const uint64_t bs = __builtin_amdgcn_ballot_w64(second);
+    const int pos = base + __popcll(bf & below) + __popcll(bs & below);
+    if (first) out[pos] = 2 * kb;
+    if (second) out[pos + 1] = 2 * kb + 1;
+    base += __popcll(bf) + __popcll(bs);
+  }
+  if (lane == 0) counts[row] = base;
 }
 
 // Combines the key-split partials of each query row with the rescaling
@@ -1878,6 +1951,48 @@ hipError_t launch_fwd_splitk_bf16(const void* Q, const void* K, const void* V, f
     case 128: return launch_split<128>(Q, K, V, O, lse, bh, nq, nk, c, splits, workspace, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+size_t sparse_workspace_bytes(int64_t n, int64_t mask_heads) {
+  const int64_t nqb = (n + kSparseBlock - 1) / kSparseBlock;
+  const int64_t cap = (n + 63) / 64;
+  return align256_bytes((size_t)(mask_heads * nqb) * 4) +
+         align256_bytes((size_t)(mask_heads * nqb * cap) * 4);
+}
+
+hipError_t launch_fwd_sparse_bf16(const void* Q, const void* K, const void* V, float* O,
+                                  float* lse, int64_t bh, int64_t n, int64_t d, float scale,
+                                  const uint8_t* mask, int64_t mask_heads, void* workspace,
+                                  hipStream_t stream) {
+  const int nqb = (int)((n + kSparseBlock - 1) / kSparseBlock);
+  const int cap = (int)((n + 63) / 64);
+  int* counts = static_cast<int*>(workspace);
+  int* tiles = reinterpret_cast<int*>(static_cast<char*>(workspace) +
+                                      align256_bytes((size_t)(mask_heads * nqb) * 4));
+  hipLaunchKernelGGL(sparse_tile_lists, dim3((unsigned)(mask_heads * nqb)), dim3(64), 0, stream,
+                     mask, tiles, counts, nqb, (int)n, cap);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int total = (int)(bh * nqb);
+  DirectArgs args{static_cast<const bf16*>(Q), static_cast<const bf16*>(K),
+                  static_cast<const bf16*>(V), O, lse, (int)n, (int)n, nqb, total, (int)bh,
+                  (int)n, scale * kLog2e};
+  args.tiles = tiles;
+  args.counts = counts;
+  args.tile_cap = cap;
+  args.mask_heads = (int)mask_heads;
+  switch (d) {
+    case 64:
+      hipLaunchKernelGGL((fwd_sparse_bf16_kernel<64, 4, 64>), dim3(total), dim3(256), 0, stream,
+                         args);
+      break;
+    case 128:
+      hipLaunchKernelGGL((fwd_sparse_bf16_kernel<128, 4, 64>), dim3(total), dim3(256), 0, stream,
+                         args);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 bool fused_bf16_supported(int64_t d) { return pick(d) != nullptr; }

@@ -44,6 +44,17 @@ hipError_t launch_fwd_splitk_bf16(const void* Q, const void* K, const void* V, f
                                   float scale, int64_t splits, void* workspace,
                                   hipStream_t stream);
 
+// Block-sparse forward: a byte mask [mask_heads][nb][nb] over square blocks
+// of kSparseBlock queries x kSparseBlock keys (nb = ceil(n / kSparseBlock));
+// mask_heads is 1 (shared) or bh.  The workspace holds per-row tile counts
+// and tile lists.
+constexpr int kSparseBlock = 128;
+size_t sparse_workspace_bytes(int64_t n, int64_t mask_heads);
+hipError_t launch_fwd_sparse_bf16(const void* Q, const void* K, const void* V, float* O,
+                                  float* lse, int64_t bh, int64_t n, int64_t d, float scale,
+                                  const uint8_t* mask, int64_t mask_heads, void* workspace,
+                                  hipStream_t stream);
+
 // Square-tile (small-cache) forward.
 bool smallcache_supported(int64_t d);
 int64_t smallcache_tile_for_budget(int64_t d, int64_t m_elems);

@@ -38,6 +38,7 @@ class Workload:
     batch: int = 1
     heads: int = 1
     nq: int = 0  # query rows per head for rectangular workloads (0: n)
+    density: float = 1.0  # fraction of 128 x 128 blocks kept (block-sparse workloads)
 
     @property
     def queries(self) -> int:
@@ -59,7 +60,9 @@ class Workload:
 # the small-cache backward, the one backward built for d=256); then two
 # rectangular ones for the key-split forward: single-query decoding of 8
 # sequences x 32 heads against a 16384-key cache, and a 1024-query chunk
-# against the same cache length.
+# against the same cache length; and a block-sparse one at the headline
+# shape with a quarter of the 128 x 128 blocks kept (per head, seed + 1000,
+# diagonal always kept).
 WORKLOADS = {
     w.name: w
     for w in (
@@ -73,6 +76,8 @@ WORKLOADS = {
                  batch=2, heads=16),
         Workload("bwd_smallcache_bf16_b1h8_n4096_d256", 8, 4096, 256, "bf16", 8, kind="bwd",
                  batch=1, heads=8),
+        Workload("sparse_bf16_b1h32_n16384_d128_keep25", 32, 16384, 128, "bf16", 9,
+                 kind="sparse", batch=1, heads=32, density=0.25),
         Workload("decode_bf16_b8h32_q1_k16384_d128", 256, 16384, 128, "bf16", 6, kind="splitk",
                  batch=8, heads=32, nq=1),
         Workload("chunk_bf16_b1h32_q1024_k16384_d128", 32, 16384, 128, "bf16", 7,
@@ -103,6 +108,21 @@ def make_inputs(bh: int, n: int, d: int, dtype: str = "bf16", seed: int = 0,
     if q_mult != 1.0:
         out[0] = (out[0] * q_mult).to(tdt)
     return tuple(out)
+
+
+def make_block_mask(heads: int, nb: int, density: float, seed: int,
+                    keep_diagonal: bool = True) -> torch.Tensor:
+    """A seeded random block mask [heads, nb, nb] (uint8, 1 = kept): each
+    block kept independently with probability ``density`` (one
+    ``torch.rand`` draw per block from a CPU generator seeded with ``seed``),
+    plus the diagonal blocks when ``keep_diagonal`` (so no query row is left
+    without keys)."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    m = (torch.rand((heads, nb, nb), generator=g) < density).to(torch.uint8)
+    if keep_diagonal:
+        idx = torch.arange(nb)
+        m[:, idx, idx] = 1
+    return m
 
 
 def workload_inputs(w: Workload):

@@ -341,6 +341,34 @@ def secondary(args, at, torch, dev):
             "nxn_gbps": round(nn_bytes / (ms * 1e-3) / 1e9, 1)}
         del q, k, v, do, o, lse, grads, ws
         torch.cuda.empty_cache()
+    from aware_tiling_amd.inputs import make_block_mask
+
+    w = WORKLOADS["sparse_bf16_b1h32_n16384_d128_keep25"]
+    print(f"[bench] timing {w.name}", file=sys.stderr, flush=True)
+    q, k, v = (t.to(dev) for t in workload_inputs(w))
+    nb = -(-w.n // at.SPARSE_BLOCK)
+    mask = make_block_mask(w.bh, nb, w.density, w.seed + 1000).to(dev)
+    o = torch.empty((w.bh, w.n, w.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.bh, w.n), dtype=torch.float32, device=dev)
+    need = int(at.lib().attn_fwd_blocksparse_workspace_size(w.bh, w.n, w.bh))
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    ms, _, _ = time_launches(lambda: at.attn_fwd_blocksparse(q, k, v, mask, w.scale, out=o,
+                                                             lse=lse, workspace=ws),
+                             args.steps, args.warmup)
+    ms_dense, _, _ = time_launches(lambda: at.attn_fwd(q, k, v, w.scale, out=o, lse=lse),
+                                   args.steps, args.warmup)
+    # kept query-key pairs: per kept block, its valid queries x valid keys
+    sizes = torch.full((nb,), at.SPARSE_BLOCK, dtype=torch.float64)
+    sizes[-1] = w.n - (nb - 1) * at.SPARSE_BLOCK
+    pairs = float(torch.einsum("hij,i,j->", mask.cpu().double(), sizes, sizes))
+    fl = 4.0 * w.d * pairs
+    kept = float(mask.float().mean())
+    res["blocksparse"] = {
+        "workload": w.name, "kept_block_fraction": round(kept, 4), "ms": round(ms, 4),
+        "tflops_on_kept_pairs": round(fl / (ms * 1e-3) / 1e12, 2),
+        "dense_ms_same_inputs": round(ms_dense, 4),
+        "time_fraction_of_dense": round(ms / ms_dense, 4)}
+    del q, k, v, o, lse, ws, mask
     for name in ("decode_bf16_b8h32_q1_k16384_d128", "chunk_bf16_b1h32_q1024_k16384_d128"):
         w = WORKLOADS[name]
         print(f"[bench] timing {w.name}", file=sys.stderr, flush=True)

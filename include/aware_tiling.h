@@ -134,6 +134,40 @@ attn_status attn_fwd_splitk(const void* Q, const void* K, const void* V,
                             size_t workspace_bytes, void* stream);
 
 /*
+ * attn_fwd_blocksparse -- fused forward restricted to the query/key blocks a
+ * block mask keeps (block-sparse attention).
+ *
+ * The explainer's "Sparse Attention Extension" and its result 2 bound the
+ * I/O of sparse attention by the number of kept entries; it gives no
+ * algorithm.  Here the kept pairs are square blocks of ATTN_SPARSE_BLOCK
+ * queries x ATTN_SPARSE_BLOCK keys: query i and key j interact iff
+ * block_mask[hm][i / B][j / B] != 0 (B = ATTN_SPARSE_BLOCK).  Each workgroup
+ * runs the streaming computation of attn_fwd over only the key tiles of its
+ * kept blocks (the others are neither read nor computed), so
+ *     o_i = sum_{j kept} exp(s_ij) v_j / sum_{j kept} exp(s_ij),
+ *     lse_i = log sum_{j kept} exp(s_ij);
+ * a row with no kept key gets o_i = 0 and lse_i = -inf.
+ *
+ *   block_mask : device bytes [mask_heads][nb][nb], nb = ceil(n / B),
+ *                nonzero = kept; mask_heads is 1 (one mask for all heads,
+ *                hm = 0) or bh (hm = head).
+ *   workspace, workspace_bytes : at least
+ *                attn_fwd_blocksparse_workspace_size(bh, n, mask_heads)
+ *                bytes, 256-byte aligned (per-row tile lists built from the
+ *                mask on the device).  Contents on return unspecified.
+ *   Other arguments as attn_fwd; bf16 only, d in {64, 128}.
+ */
+#define ATTN_SPARSE_BLOCK 128
+size_t attn_fwd_blocksparse_workspace_size(int64_t bh, int64_t n,
+                                           int64_t mask_heads);
+attn_status attn_fwd_blocksparse(const void* Q, const void* K, const void* V,
+                                 float* O, float* lse, int64_t bh, int64_t n,
+                                 int64_t d, float scale, attn_dtype dtype,
+                                 const uint8_t* block_mask, int64_t mask_heads,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
  * attn_fwd_smallcache -- square-tile forward for the small-cache regime.
  *
  * Follows the exposition's section "Small caches: when storing an

@@ -230,3 +230,26 @@ def test_bwd_smallcache_tile_selection_and_validation(lib):
     assert call(wsb=ws - 1) == WORKSPACE
     assert call(w=None) == WORKSPACE
     assert call(w=FAKE * 256 + 32) == WORKSPACE
+
+
+def test_blocksparse_validation_and_sizes(lib):
+    bh, n, d = 4, 1000, 128
+    nb = (n + 127) // 128
+    cap = (n + 63) // 64
+    ws = lib.attn_fwd_blocksparse_workspace_size(bh, n, bh)
+    assert ws == ((bh * nb * 4 + 255) // 256 + (bh * nb * cap * 4 + 255) // 256) * 256
+    assert lib.attn_fwd_blocksparse_workspace_size(bh, n, 1) < ws
+    assert lib.attn_fwd_blocksparse_workspace_size(bh, n, 3) == 0  # 1 or bh only
+    call = lambda q=FAKE, mask=FAKE, mh=bh, d_=d, dt=BF16, w=FAKE * 256, wsb=ws: \
+        lib.attn_fwd_blocksparse(q, FAKE, FAKE, FAKE, None, bh, n, d_, 0.088, dt, mask, mh, w,
+                                 wsb, None)
+    assert call(q=None) == INVALID
+    assert call(mask=None) == INVALID
+    assert call(mh=2) == INVALID
+    assert call(d_=256) == UNSUPPORTED
+    assert call(dt=F32) == UNSUPPORTED
+    assert call(w=None) == WORKSPACE
+    assert call(wsb=ws - 1) == WORKSPACE
+    assert call(w=FAKE * 256 + 64) == WORKSPACE
+    assert lib.attn_fwd_blocksparse(None, None, None, None, None, 0, n, d, 0.088, BF16, None, 1,
+                                    None, 0, None) == OK  # empty batch
