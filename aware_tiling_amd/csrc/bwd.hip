@@ -89,10 +89,14 @@ __device__ __forceinline__ bf16x8 lds_operand(const bf16* tile, int row, int chu
 // ---------------------------------------------------------------------------
 // 1. D_i = <dO_i, O_i>
 
+// Also writes lse2 = lse log2(e) (the exponent base of the kernels) when
+// lse2 is non-null.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_preprocess(const float* __restrict__ O,
                                                       const bf16* __restrict__ dO,
-                                                      float* __restrict__ Dout, int64_t rows) {
+                                                      float* __restrict__ Dout, int64_t rows,
+                                                      const float* __restrict__ lse,
+                                                      float* __restrict__ lse2) {
   constexpr int TPR = D / 8;       // threads per row (8 elements each)
   constexpr int RPB = 256 / TPR;   // rows per block
   const int t = threadIdx.x;
@@ -108,7 +112,10 @@ __global__ __launch_bounds__(256) void bwd_preprocess(const float* __restrict__ 
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (r < rows && (t % TPR) == 0) Dout[r] = acc;
+  if (r < rows && (t % TPR) == 0) {
+    Dout[r] = acc;
+    if (lse2 != nullptr) lse2[r] = lse[r] * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -473,7 +480,7 @@ struct Dkdv2Cfg {
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv2(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dg,
+    const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ Dg,
     float* __restrict__ dK, float* __restrict__ dV, int n, int nkb, int total, float c,
     float scale) {
   using C = Dkdv2Cfg<D, NW>;
@@ -488,7 +495,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv2(
   const int head = tile / nkb, kblk = tile - head * nkb;
   const size_t hoff = (size_t)head * n * D;
   const bf16 *Qh = Q + hoff, *Kh = K + hoff, *Vh = V + hoff, *dOh = dO + hoff;
-  const float* lseh = lse + (size_t)head * n;
+  const float* lseh = lse2 + (size_t)head * n;
   const float* Dh = Dg + (size_t)head * n;
   const int key = kblk * C::BKV + wave * 32 + li;
 
@@ -504,18 +511,36 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv2(
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dkt[db] = dvt[db] = f32x16{};
 
+  // Tiles of Q and dO and the rows' lse2 and D go global -> LDS with direct
+  // loads (no registers, one wait): full tiles from a wave-uniform base plus
+  // per-lane offsets computed once; a partial last tile clamps its rows to
+  // n-1, and those rows are masked after the exponentials.
+  uint32_t toff[C::INSTS];
+#pragma unroll
+  for (int it = 0; it < C::INSTS; ++it) {
+    const int p = wave * C::WAVE_CHUNKS + it * 64 + lane;
+    const int row = p / (D / 8), phys = p % (D / 8);
+    toff[it] = (uint32_t)(row * D + (phys ^ dual_swizzle<D * 2>(row)) * 8) * 2u;
+  }
   auto load = [&](int i, int buf) {
-    tile_load_lds<D>(Qh, tiles[buf], i, BQ, n, wave, lane, C::WAVE_CHUNKS, C::INSTS, true);
-    tile_load_lds<D>(dOh, tiles[buf] + C::TILE, i, BQ, n, wave, lane, C::WAVE_CHUNKS, C::INSTS,
-                     true);
-    if (tid < 2 * BQ) {
-      const int q = i * BQ + (tid % BQ);
-      float v;
-      if (tid < BQ)
-        v = q < n ? lseh[q] * kLog2e : INFINITY;  // +inf: rows past n get P = 0
-      else
-        v = q < n ? Dh[q] : 0.f;
-      stats[buf][tid] = v;
+    if ((i + 1) * BQ <= n) {
+      const char* qb = reinterpret_cast<const char*>(Qh) + (size_t)i * BQ * D * 2;
+      const char* gb = reinterpret_cast<const char*>(dOh) + (size_t)i * BQ * D * 2;
+#pragma unroll
+      for (int it = 0; it < C::INSTS; ++it) {
+        const int p0 = wave * C::WAVE_CHUNKS + it * 64;
+        load_lds_16(qb + toff[it], tiles[buf] + p0 * 8);
+        load_lds_16(gb + toff[it], tiles[buf] + C::TILE + p0 * 8);
+      }
+    } else {
+      tile_load_lds<D>(Qh, tiles[buf], i, BQ, n, wave, lane, C::WAVE_CHUNKS, C::INSTS, true);
+      tile_load_lds<D>(dOh, tiles[buf] + C::TILE, i, BQ, n, wave, lane, C::WAVE_CHUNKS, C::INSTS,
+                       true);
+    }
+    if (wave * 64 < 2 * BQ) {  // whole waves: 2 BQ is a multiple of 64
+      const int which = tid / BQ, r = tid - which * BQ;
+      const int qrow = min(i * BQ + r, n - 1);
+      load_lds_4((which == 0 ? lseh : Dh) + qrow, &stats[buf][wave * 64]);
     }
   };
 
@@ -528,44 +553,64 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv2(
     if (i + 1 < nqt) load(i + 1, buf ^ 1);
     const bf16* Qs = tiles[buf];
     const bf16* dOs = tiles[buf] + C::TILE;
+    const bool tailq = (i + 1) * BQ > n;  // rows past n (clamped copies) get P = 0
+    // Opaque copies of the lane index: the LDS addresses derived from them
+    // are recomputed each iteration (a few integer ops) rather than held in
+    // registers across the loop, which would not fit.
+    int lio = li, laneo = lane;
+    asm volatile("" : "+v"(lio), "+v"(laneo));
 #pragma unroll
     for (int qb = 0; qb < BQ / 32; ++qb) {
-      // S = Q K^T and dP = dO V^T (32 queries x 32 keys per wave).
-      f32x16 s = {}, dp = {};
+      // S = Q K^T (32 queries x 32 keys per wave), P in bf16, dV^T += dO^T P;
+      // then dP = dO V^T, dS = P o (dP - D) from the same bf16 P, and
+      // dK^T += Q^T dS.  Only one score-sized accumulator is live at a time.
+      f32x16 s = {};
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        s = mfma_bf16_32x32x16(row_operand<D>(Qs, qb * 32 + li, 2 * kk + h, true), kreg[kk], s);
-        dp = mfma_bf16_32x32x16(row_operand<D>(dOs, qb * 32 + li, 2 * kk + h, true), vreg[kk], dp);
-      }
-      uint32_t pk[8], dsk[8];
+      for (int kk = 0; kk < D / 16; ++kk)
+        s = mfma_bf16_32x32x16(row_operand<D>(Qs, qb * 32 + lio, 2 * kk + h, true), kreg[kk], s);
+      uint32_t pk[8];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x4 l2 = *reinterpret_cast<const f32x4*>(&stats[buf][qb * 32 + 8 * g + 4 * h]);
-        const f32x4 dd =
-            *reinterpret_cast<const f32x4*>(&stats[buf][BQ + qb * 32 + 8 * g + 4 * h]);
-        float p[4], ds[4];
+        float p[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           p[e] = fast_exp2(__builtin_fmaf(s[4 * g + e], c, -l2[e]));
-          ds[e] = p[e] * (dp[4 * g + e] - dd[e]);
+          if (tailq && i * BQ + qb * 32 + 8 * g + 4 * h + e >= n) p[e] = 0.f;
         }
         pk[2 * g] = pack_bf16x2(p[0], p[1]);
         pk[2 * g + 1] = pack_bf16x2(p[2], p[3]);
-        dsk[2 * g] = pack_bf16x2(ds[0], ds[1]);
-        dsk[2 * g + 1] = pack_bf16x2(ds[2], ds[3]);
       }
-      // dV^T += dO^T P, dK^T += Q^T dS over this block's 32 queries.
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const bf16x8 bp = __builtin_bit_cast(
             bf16x8, (u32x4{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]}));
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          dvt[db] = mfma_bf16_32x32x16(tr_operand<D>(dOs, 2 * qb + ks, db, laneo), bp, dvt[db]);
+      }
+      f32x16 dp = {};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk)
+        dp = mfma_bf16_32x32x16(row_operand<D>(dOs, qb * 32 + lio, 2 * kk + h, true), vreg[kk],
+                                dp);
+      uint32_t dsk[8];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 dd =
+            *reinterpret_cast<const f32x4*>(&stats[buf][BQ + qb * 32 + 8 * g + 4 * h]);
+        const float p0 = bf_lo(pk[2 * g]), p1 = bf_hi(pk[2 * g]);
+        const float p2 = bf_lo(pk[2 * g + 1]), p3 = bf_hi(pk[2 * g + 1]);
+        dsk[2 * g] = pack_bf16x2(p0 * (dp[4 * g] - dd[0]), p1 * (dp[4 * g + 1] - dd[1]));
+        dsk[2 * g + 1] = pack_bf16x2(p2 * (dp[4 * g + 2] - dd[2]), p3 * (dp[4 * g + 3] - dd[3]));
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
         const bf16x8 bs = __builtin_bit_cast(
             bf16x8, (u32x4{dsk[4 * ks], dsk[4 * ks + 1], dsk[4 * ks + 2], dsk[4 * ks + 3]}));
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          dvt[db] = mfma_bf16_32x32x16(tr_operand<D>(dOs, 2 * qb + ks, db, lane), bp, dvt[db]);
-          dkt[db] = mfma_bf16_32x32x16(tr_operand<D>(Qs, 2 * qb + ks, db, lane), bs, dkt[db]);
-        }
+        for (int db = 0; db < D / 32; ++db)
+          dkt[db] = mfma_bf16_32x32x16(tr_operand<D>(Qs, 2 * qb + ks, db, laneo), bs, dkt[db]);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -717,11 +762,13 @@ hipError_t launch(const void* Q, const void* K, const void* V, const float* O, c
   const bf16* v = static_cast<const bf16*>(V);
   const bf16* g = static_cast<const bf16*>(dO);
   float* Dbuf = static_cast<float*>(ws);
+  float* lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                         ((size_t)bh * n * 4 + 255) / 256 * 256);
   const float c = scale * kLog2e;
   const int64_t rows = bh * n;
   constexpr int RPB = 256 / (D / 8);
   hipLaunchKernelGGL(bwd_preprocess<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
-                     stream, O, g, Dbuf, rows);
+                     stream, O, g, Dbuf, rows, lse, lse2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const char* var = getenv("ATTN_BWD_VARIANT");
@@ -747,7 +794,7 @@ hipError_t launch(const void* Q, const void* K, const void* V, const float* O, c
     const int nkb = (int)((n + Cf::BKV - 1) / Cf::BKV);
     const int total_kv = (int)(bh * nkb);
     hipLaunchKernelGGL((bwd_dkdv2<D, NW>), dim3(total_kv), dim3(NW * 64), 0, stream, q, k, v, g,
-                       lse, Dbuf, dK, dV, (int)n, nkb, total_kv, c, scale);
+                       lse2, Dbuf, dK, dV, (int)n, nkb, total_kv, c, scale);
   };
   auto dqk = [&](auto nwc) {
     constexpr int NW = decltype(nwc)::value;
@@ -779,15 +826,15 @@ hipError_t launch_bwd_preprocess(const float* O, const void* dO, float* Dout, in
   switch (d) {
     case 64:
       hipLaunchKernelGGL(bwd_preprocess<64>, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0,
-                         stream, O, g, Dout, rows);
+                         stream, O, g, Dout, rows, nullptr, nullptr);
       break;
     case 128:
       hipLaunchKernelGGL(bwd_preprocess<128>, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0,
-                         stream, O, g, Dout, rows);
+                         stream, O, g, Dout, rows, nullptr, nullptr);
       break;
     case 256:
       hipLaunchKernelGGL(bwd_preprocess<256>, dim3((unsigned)((rows + 7) / 8)), dim3(256), 0,
-                         stream, O, g, Dout, rows);
+                         stream, O, g, Dout, rows, nullptr, nullptr);
       break;
     default: return hipErrorInvalidValue;
   }
@@ -797,7 +844,7 @@ hipError_t launch_bwd_preprocess(const float* O, const void* dO, float* Dout, in
 bool bwd_supported(int64_t d) { return d == 64 || d == 128; }
 
 size_t bwd_workspace_bytes(int64_t bh, int64_t n, int64_t) {
-  return ((size_t)bh * n * 4 + 255) & ~size_t(255);
+  return 2 * (((size_t)bh * n * 4 + 255) & ~size_t(255));  // D, then lse log2(e)
 }
 
 hipError_t launch_bwd_bf16(const void* Q, const void* K, const void* V, const float* O,

@@ -120,6 +120,13 @@ __device__ __forceinline__ void load_lds_16(const void* gsrc, void* lds_wave_bas
                                    16, 0, 0);
 }
 
+// The same with 4 bytes per lane (global_load_lds_dword): lane l's 4 bytes
+// land at lds_wave_base + 4 l.
+__device__ __forceinline__ void load_lds_4(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_wave_base,
+                                   4, 0, 0);
+}
+
 // Four bf16 of a transposed LDS read (ds_read_b64_tr_b16).  Within each group
 // of 16 lanes, lane i receives element (i mod 4) of the 8 bytes addressed by
 // lanes 4e + i/4, for e = 0..3.

@@ -661,8 +661,13 @@ struct DirectCfg {
 // With LIST (two-stage PIPE only) the workgroup visits only the key tiles of
 // its tile list, in ascending order; a workgroup with an empty list writes
 // O = 0 and lse = -inf (no kept key, no softmax).
+// PRIO (two-stage PIPE only) sets wave issue priorities: 1 = the first half
+// of the waves (one per SIMD pair) at priority 1 throughout, so the two
+// waves that share a SIMD drift into opposite phases instead of competing
+// for the same unit; 2 = every wave at priority 1 while it issues its score
+// MFMAs and back to 0 for the rest of the step.
 template <int D, int NW, int BC, bool PIPE, int WPS, bool SCHED, int STAGES, bool SKIP = false,
-          bool LIST = false>
+          bool LIST = false, int PRIO = 0>
 __device__ __forceinline__ void direct_body(const DirectArgs& A) {
   static_assert(!SKIP || (PIPE && STAGES == 2), "SKIP is built for the two-stage pipeline");
   static_assert(!LIST || (PIPE && STAGES == 2), "LIST is built for the two-stage pipeline");
@@ -696,6 +701,9 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
   float* const lseh = A.lse ? A.lse + ((size_t)split * A.bh + head) * nq : nullptr;
   const int q = qblk * C::BR + wave * 32 + li;
   const bool active = !SKIP || qblk * C::BR + wave * 32 < nq;  // wave-uniform
+  if constexpr (PRIO == 1) {
+    if (wave < NW / 2) __builtin_amdgcn_s_setprio(1);
+  }
 
   bf16x8 qreg[D / 16];
 #pragma unroll
@@ -926,7 +934,9 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
       f32x16 s_next[BC / 32];
       if (active) {
         softmax_max(s_cur, false, 0);
+        if constexpr (PRIO == 2) __builtin_amdgcn_s_setprio(1);
         compute_s(Kb + (P ^ 1) * C::TILE, s_next);
+        if constexpr (PRIO == 2) __builtin_amdgcn_s_setprio(0);
         uint32_t pk[BC / 32][8];
         softmax_exp(s_cur, pk);
         pv(Vb + P * C::TILE, pk);
@@ -1019,12 +1029,12 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
   }
 }
 
-template <int D, int NW, int BC, bool PIPE, int WPS, bool SCHED, int STAGES>
+template <int D, int NW, int BC, bool PIPE, int WPS, bool SCHED, int STAGES, int PRIO = 0>
 __global__ __launch_bounds__(NW * 64, (WPS * 4 / NW > 0 ? WPS * 4 / NW : 1)) void
 fwd_fused_bf16_direct_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                              const bf16* __restrict__ V, float* __restrict__ O,
                              float* __restrict__ lse, int n, int nqb, int total, float c) {
-  direct_body<D, NW, BC, PIPE, WPS, SCHED, STAGES>(
+  direct_body<D, NW, BC, PIPE, WPS, SCHED, STAGES, false, false, PRIO>(
       DirectArgs{Q, K, V, O, lse, n, n, nqb, total, total / nqb, n, c});
 }
 
@@ -1792,11 +1802,11 @@ FusedEntry basic(const char* name) {
 }
 
 template <int D, int NW, int BC, bool PIPE = true, int WPS = 2, bool SCHED = false,
-          int STAGES = 2>
+          int STAGES = 2, int PRIO = 0>
 FusedEntry direct(const char* name) {
   using C = DirectCfg<D, NW, BC, PIPE, WPS, SCHED, STAGES>;
   return FusedEntry{name, D, NW, FusedTileInfo{C::BR, C::KEYS, C::ONCHIP},
-                    &fwd_fused_bf16_direct_kernel<D, NW, BC, PIPE, WPS, SCHED, STAGES>};
+                    &fwd_fused_bf16_direct_kernel<D, NW, BC, PIPE, WPS, SCHED, STAGES, PRIO>};
 }
 
 template <int D, int QB, int NW, int BC>
@@ -1831,6 +1841,8 @@ const FusedEntry* registry(int& count) {
       basic<64, 2, 8, 32>("2x8x32"),
       // head dimension 128
       direct<128, 8, 64>("d8x64"),
+      direct<128, 8, 64, true, 2, false, 2, 1>("d8x64q1"),
+      direct<128, 8, 64, true, 2, false, 2, 2>("d8x64q2"),
       pingpong<128, 1, 64, true>("g1x64p"),
       pingpong<128, 1, 64>("g1x64"),
       wide<128, 1, 8, 64>("w1x8x64"),
