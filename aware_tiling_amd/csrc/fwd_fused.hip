@@ -1929,11 +1929,20 @@ size_t align256_bytes(size_t b) { return (b + 255) / 256 * 256; }
 
 bool splitk_supported(int64_t d) { return d == 64 || d == 128; }
 
+// Automatic chunk count.  The eight-wave form (more than 128 queries per
+// head) is bound by the matrix core and one workgroup fills a CU, so one
+// round of 256 workgroups is the target (more chunks only add merge
+// traffic); the four-wave form serves short query blocks (decoding), which
+// are bound by the K/V stream, and two rounds of its two-per-CU workgroups
+// (1024) keep the most loads in flight.  Measured on the decode and chunk
+// workloads: 4 and 2 chunks, the fastest of 1..64.
 int64_t splitk_auto_splits(int64_t bh, int64_t nq, int64_t nk) {
-  const int64_t br = nq <= 128 ? 128 : 256;
+  const bool narrow = nq <= 128;
+  const int64_t br = narrow ? 128 : 256;
+  const int64_t target = narrow ? 1024 : 256;
   const int64_t wgs = bh * ((nq + br - 1) / br);
-  int64_t s = (1024 + wgs - 1) / wgs;                    // aim for >= 1024 workgroups
-  s = std::min<int64_t>(s, (nk + 255) / 256);            // at least 256 keys per split
+  int64_t s = (target + wgs - 1) / wgs;
+  s = std::min<int64_t>(s, (nk + 255) / 256);  // at least 256 keys per chunk
   return std::max<int64_t>(1, std::min<int64_t>(s, 256));
 }
 

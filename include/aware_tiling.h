@@ -112,7 +112,8 @@ int64_t attn_fwd_query_block(int64_t d, attn_dtype dtype);
  *   Q       : [bh, nq, d] bf16;  K, V : [bh, nk, d] bf16 (device, read only)
  *   O       : [bh, nq, d] float; lse : [bh, nq] float or NULL (as attn_fwd)
  *   splits  : requested chunk count, 1..256, or 0 for an automatic choice
- *             (enough workgroups to fill the device, >= 256 keys a chunk).
+ *             (one round of workgroups over the device for more than 128
+ *             queries a head, two rounds for fewer; >= 256 keys a chunk).
  *             Chunks are whole 64-key tiles, so fewer may be used; see
  *             attn_fwd_splitk_splits().
  *   workspace, workspace_bytes : device scratch of at least
