@@ -675,10 +675,32 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq2(
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dqt[db] = f32x16{};
 
+  // Full tiles from a wave-uniform base plus per-lane offsets computed once
+  // (K with the dual swizzle, V with the row swizzle); a partial last tile
+  // clamps its rows to n-1 (those keys are masked below).
+  uint32_t koff[C::INSTS], voff[C::INSTS];
+#pragma unroll
+  for (int it = 0; it < C::INSTS; ++it) {
+    const int p = wave * C::WAVE_CHUNKS + it * 64 + lane;
+    const int row = p / (D / 8), phys = p % (D / 8);
+    koff[it] = (uint32_t)(row * D + (phys ^ dual_swizzle<D * 2>(row)) * 8) * 2u;
+    voff[it] = (uint32_t)(row * D + (phys ^ chunk_swizzle<D * 2>(row)) * 8) * 2u;
+  }
   auto load = [&](int j, int buf) {
-    tile_load_lds<D>(Kh, tiles[buf], j, BC, n, wave, lane, C::WAVE_CHUNKS, C::INSTS, true);
-    tile_load_lds<D>(Vh, tiles[buf] + C::TILE, j, BC, n, wave, lane, C::WAVE_CHUNKS, C::INSTS,
-                     false);
+    if ((j + 1) * BC <= n) {
+      const char* kb = reinterpret_cast<const char*>(Kh) + (size_t)j * BC * D * 2;
+      const char* vb = reinterpret_cast<const char*>(Vh) + (size_t)j * BC * D * 2;
+#pragma unroll
+      for (int it = 0; it < C::INSTS; ++it) {
+        const int p0 = wave * C::WAVE_CHUNKS + it * 64;
+        load_lds_16(kb + koff[it], tiles[buf] + p0 * 8);
+        load_lds_16(vb + voff[it], tiles[buf] + C::TILE + p0 * 8);
+      }
+    } else {
+      tile_load_lds<D>(Kh, tiles[buf], j, BC, n, wave, lane, C::WAVE_CHUNKS, C::INSTS, true);
+      tile_load_lds<D>(Vh, tiles[buf] + C::TILE, j, BC, n, wave, lane, C::WAVE_CHUNKS, C::INSTS,
+                       false);
+    }
   };
 
   const int nkt = (n + BC - 1) / BC;
@@ -690,14 +712,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq2(
     if (j + 1 < nkt) load(j + 1, buf ^ 1);
     const bf16* Ks = tiles[buf];
     const bf16* Vs = tiles[buf] + C::TILE;
+    // Opaque copies of the lane index: LDS addresses derived from them are
+    // recomputed each iteration instead of being held across the loop.
+    int lio = li, laneo = lane;
+    asm volatile("" : "+v"(lio), "+v"(laneo));
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb) {
       // S^T = K Q^T and dP^T = V dO^T (32 keys x 32 queries per wave).
       f32x16 s = {}, dp = {};
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        s = mfma_bf16_32x32x16(row_operand<D>(Ks, kb * 32 + li, 2 * kk + h, true), qreg[kk], s);
-        dp = mfma_bf16_32x32x16(row_operand<D>(Vs, kb * 32 + li, 2 * kk + h, false), dogreg[kk],
+        s = mfma_bf16_32x32x16(row_operand<D>(Ks, kb * 32 + lio, 2 * kk + h, true), qreg[kk], s);
+        dp = mfma_bf16_32x32x16(row_operand<D>(Vs, kb * 32 + lio, 2 * kk + h, false), dogreg[kk],
                                 dp);
       }
       const int kbase = j * BC + kb * 32;
@@ -721,7 +747,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq2(
             bf16x8, (u32x4{dsk[4 * ks], dsk[4 * ks + 1], dsk[4 * ks + 2], dsk[4 * ks + 3]}));
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
-          dqt[db] = mfma_bf16_32x32x16(tr_operand<D>(Ks, 2 * kb + ks, db, lane), bs, dqt[db]);
+          dqt[db] = mfma_bf16_32x32x16(tr_operand<D>(Ks, 2 * kb + ks, db, laneo), bs, dqt[db]);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
