@@ -1843,6 +1843,14 @@ const FusedEntry* registry(int& count) {
       direct<128, 8, 64>("d8x64"),
       direct<128, 8, 64, true, 2, false, 2, 1>("d8x64q1"),
       direct<128, 8, 64, true, 2, false, 2, 2>("d8x64q2"),
+      // query-block x key-tile sweep (B_r = 32 x waves, B_c = keys per tile;
+      // 128-key tiles spill registers at d = 128 and are left out)
+      direct<128, 2, 32>("r64c32"),
+      direct<128, 2, 64>("r64c64"),
+      direct<128, 4, 32>("r128c32"),
+      direct<128, 4, 64, true, 1>("r128c64"),
+      direct<128, 8, 32>("r256c32"),
+      direct<128, 8, 64>("r256c64"),
       pingpong<128, 1, 64, true>("g1x64p"),
       pingpong<128, 1, 64>("g1x64"),
       wide<128, 1, 8, 64>("w1x8x64"),

@@ -28,6 +28,8 @@ Reported (one JSON line on stdout):
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-secondary]
        python bench.py --calibrate-copy          (copy kernel for counter scaling)
        python bench.py --summarize-counters DIR  (write the traffic summary)
+       python bench.py --tile-sweep [--steps K]   (fused forward at B_r x B_c shapes)
+       python bench.py --summarize-sweep DIR TIMING.jsonl OUT.md  (sweep table)
 """
 from __future__ import annotations
 
@@ -167,9 +169,67 @@ def summarize_counters(pmc_dir: str, out_path: str = TRAFFIC_FILE):
     print(json.dumps(summary))
 
 
+def summarize_sweep(pmc_dir: str, timing_path: str, out_path: str):
+    """Combine the tile sweep's timing lines with its counter runs into a
+    markdown table: CU<->L2 read bytes (TCC_READ_SECTORS) and L2-miss read
+    bytes (FETCH_SIZE), each scaled by what the counter reads for a plain
+    copy of COPY_BYTES, against the schedule-exact and the page's models.
+    Expects <dir>/sweepread_, sweepfetch_, copyread_ and copyfetch_
+    counter_collection.csv."""
+    import csv
+    import re
+    import statistics
+
+    def per_tile(fname, counter):
+        vals = {}
+        with open(os.path.join(pmc_dir, fname)) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                m = re.search(r"fwd_fused_bf16_direct_kernel<128, (\d+), (\d+),", r["Kernel_Name"])
+                if m:
+                    key = (32 * int(m.group(1)), int(m.group(2)))
+                    vals.setdefault(key, []).append(float(r["Counter_Value"]))
+        return {k: statistics.mean(v) for k, v in vals.items()}
+
+    def copy_value(fname, counter):
+        with open(os.path.join(pmc_dir, fname)) as f:
+            v = [float(r["Counter_Value"]) for r in csv.DictReader(f)
+                 if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"]]
+        return statistics.mean(v)
+
+    rd = per_tile("sweepread_counter_collection.csv", "TCC_READ_SECTORS_sum")
+    fe = per_tile("sweepfetch_counter_collection.csv", "FETCH_SIZE")
+    rd_unit = COPY_BYTES / copy_value("copyread_counter_collection.csv", "TCC_READ_SECTORS_sum")
+    fe_unit = COPY_BYTES / copy_value("copyfetch_counter_collection.csv", "FETCH_SIZE")
+    rows = [json.loads(line) for line in open(timing_path) if line.startswith("{")]
+    compulsory = 402653184  # Q, K, V once (bf16)
+    lines = ["| tile | B_r | B_c | M (elements) | ms | TFLOP/s | CU->L2 read bytes | "
+             "schedule 2N^2d/B_r+Nd | ratio | page N^2d^2/M+Nd | ratio | L2-miss read bytes "
+             "| / compulsory |", "|" + "---|" * 13]
+    for r in rows:
+        key = (r["block_rows"], r["key_tile"])
+        cu = rd.get(key, float("nan")) * rd_unit
+        miss = fe.get(key, float("nan")) * fe_unit
+        lines.append(
+            f"| {r['tile']} | {r['block_rows']} | {r['key_tile']} | {r['onchip_elems']:,} | "
+            f"{r['ms']} | {r['tflops']} | {cu / 1e9:.2f} GB | {r['sched_read_bytes'] / 1e9:.2f} GB | "
+            f"{cu / r['sched_read_bytes']:.3f} | {r['page_model_bytes'] / 1e9:.2f} GB | "
+            f"{cu / r['page_model_bytes']:.3f} | {miss / 1e9:.3f} GB | {miss / compulsory:.2f} |")
+    text = "\n".join(lines) + "\n"
+    text += (f"\nCounter scaling: one TCC_READ_SECTORS unit = {rd_unit:.2f} bytes and one "
+             f"FETCH_SIZE unit = {fe_unit:.1f} bytes (a plain copy of {COPY_BYTES} bytes).\n")
+    with open(out_path, "w") as f:
+        f.write(text)
+    print(text)
+
+
 def main():
     if len(sys.argv) >= 3 and sys.argv[1] == "--summarize-counters":
         summarize_counters(sys.argv[2])
+        return
+    if len(sys.argv) >= 5 and sys.argv[1] == "--summarize-sweep":
+        summarize_sweep(sys.argv[2], sys.argv[3], sys.argv[4])
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +237,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--tile-sweep", action="store_true",
+                    help="time every query-block x key-tile shape of the fused forward on the "
+                         "headline workload (one JSON line per shape) and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB three times (to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -201,6 +264,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 3}))
+        return
+    if args.tile_sweep:
+        tile_sweep(args, at, torch, dev)
         return
     w = WORKLOADS[HEADLINE]
     print(f"[bench] inputs {w.name}", file=sys.stderr, flush=True)
@@ -265,6 +331,36 @@ def main():
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
+
+
+SWEEP_TILES = ["r64c32", "r64c64", "r128c32", "r128c64", "r256c32", "r256c64"]
+
+
+def tile_sweep(args, at, torch, dev):
+    """The fused forward at B_r in {64, 128, 256} query rows and B_c in
+    {32, 64} keys per tile, on the headline workload: time and the byte
+    models of each shape (the counters come from rocprofv3 runs of this
+    same mode; see --summarize-sweep)."""
+    from aware_tiling_amd.inputs import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[HEADLINE]
+    q, k, v = (t.to(dev) for t in workload_inputs(w))
+    o = torch.empty((w.bh, w.n, w.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.bh, w.n), dtype=torch.float32, device=dev)
+    for name in SWEEP_TILES:
+        os.environ["ATTN_FWD_TILE"] = name
+        br, m_elems = at.fwd_query_block(w.d), at.fwd_onchip_elems(w.d)
+        print(f"[bench] tile {name}", file=sys.stderr, flush=True)
+        ms, _, _ = time_launches(lambda: at.attn_fwd(q, k, v, w.scale, out=o, lse=lse),
+                                 args.steps, args.warmup)
+        # per launch, in bytes (bf16 K/V stream + Q once); elements x 2
+        sched = w.bh * (2 * w.n * w.n * w.d / br + w.n * w.d) * 2
+        model = w.bh * (w.n * w.n * w.d * w.d / m_elems + w.n * w.d) * 2
+        print(json.dumps({"tile": name, "block_rows": br, "key_tile": int(name.split("c")[1]),
+                          "onchip_elems": m_elems, "ms": round(ms, 4),
+                          "tflops": round(w.fwd_flops / (ms * 1e-3) / 1e12, 1),
+                          "sched_read_bytes": sched, "page_model_bytes": model}), flush=True)
+    os.environ.pop("ATTN_FWD_TILE", None)
 
 
 def secondary(args, at, torch, dev):
