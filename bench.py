@@ -18,7 +18,12 @@ Reported (one JSON line on stdout):
                the committed rocprofv3 counter summary when it was taken on
                the current kernel source, else null;
   hbm_gbps     compulsory bytes (Q, K, V read once, O and lse written once) /
-               step time, and as a fraction of 8 TB/s;
+               step time, and as a fraction of 8 TB/s; l2miss_gbps the
+               measured L2-miss bytes (traffic) / launch time;
+  launch_ms_*  min, median, p90, max over the timed launches, and
+               cold_launch_ms with L2 and MALL flushed by a 512 MB write;
+  measured_peaks  a library bf16 GEMM and a device copy on the same GPU,
+               the reachable rates beside the published peaks;
   cpu_baseline the float64 oracle on the host cores, on a bounded sample of
                rows of the same workload (about 15 s of CPU work);
   secondary    the small-cache square-tile path (batch 1 x 8 heads, N 4096,
@@ -81,6 +86,47 @@ def time_launches(fn, steps: int, warmup: int):
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     ev = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     return sum(ev) / len(ev), wall_ms, ev
+
+
+def percentile(xs, p):
+    ys = sorted(xs)
+    i = min(len(ys) - 1, max(0, int(round(p / 100.0 * (len(ys) - 1)))))
+    return ys[i]
+
+
+def cold_launch_ms(fn, torch, dev, reps: int = 5) -> float:
+    """Median launch time with the caches flushed first: a 512 MB buffer is
+    written before each launch (more than L2 and the 256 MB MALL), and the
+    HIP events bracket the launch alone."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(reps):
+        flush.fill_(1)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        fn()
+        e.record(stream)
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e))
+    del flush
+    return percentile(times, 50)
+
+
+def measured_peaks(torch, dev) -> dict:
+    """Reference rates measured on this device: a library bf16 GEMM
+    (8192^3, torch.matmul) and a 1 GiB device-to-device copy."""
+    a = torch.randn((8192, 8192), device=dev).to(torch.bfloat16)
+    b = torch.randn((8192, 8192), device=dev).to(torch.bfloat16)
+    gemm_ms, _, _ = time_launches(lambda: torch.matmul(a, b), 10, 3)
+    del a, b
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    copy_ms, _, _ = time_launches(lambda: dst.copy_(src), 10, 3)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"gemm_bf16_tflops": round(2 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
+            "copy_gbps": round(2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9, 1)}
 
 
 def traffic_for_launch():
@@ -318,9 +364,16 @@ def main():
         "roofline": roofline,
         "launch_ms_min": round(min(ev), 4),
         "launch_ms_max": round(max(ev), 4),
+        "launch_ms_median": round(percentile(ev, 50), 4),
+        "launch_ms_p90": round(percentile(ev, 90), 4),
     }
+    if traffic:
+        out["l2miss_gbps"] = round(traffic / (launch_ms * 1e-3) / 1e9, 1)
+    out["cold_launch_ms"] = round(cold_launch_ms(fn, torch, dev), 4)
     del q, k, v, o, lse
     torch.cuda.empty_cache()
+    out["measured_peaks"] = measured_peaks(torch, dev)
+    out["frac_of_measured_gemm"] = round(achieved / out["measured_peaks"]["gemm_bf16_tflops"], 4)
 
     if not args.no_secondary:
         out["secondary"] = secondary(args, at, torch, dev)
