@@ -666,8 +666,11 @@ struct DirectCfg {
 // waves that share a SIMD drift into opposite phases instead of competing
 // for the same unit; 2 = every wave at priority 1 while it issues its score
 // MFMAs and back to 0 for the rest of the step.
+// BUF loads full K/V tiles with buffer instructions (buffer_load ... lds):
+// the tile base goes into a per-tile buffer resource (scalar arithmetic), so
+// no per-lane 64-bit address arithmetic is needed.
 template <int D, int NW, int BC, bool PIPE, int WPS, bool SCHED, int STAGES, bool SKIP = false,
-          bool LIST = false, int PRIO = 0>
+          bool LIST = false, int PRIO = 0, bool BUF = false>
 __device__ __forceinline__ void direct_body(const DirectArgs& A) {
   static_assert(!SKIP || (PIPE && STAGES == 2), "SKIP is built for the two-stage pipeline");
   static_assert(!LIST || (PIPE && STAGES == 2), "LIST is built for the two-stage pipeline");
@@ -737,7 +740,7 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
   // first key of the t-th tile visited
   auto kbase_of = [&](int t) -> int {
     if constexpr (LIST)
-      return tlist[t] * BC;
+      return __builtin_amdgcn_readfirstlane(tlist[t]) * BC;  // uniform: keeps the base scalar
     else
       return t * BC;
   };
@@ -760,7 +763,18 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
   auto load_tile = [&](const bf16* src, bf16* dst, int t, auto swz) {
     const int kbase = kbase_of(t);
     const uint32_t* offs = decltype(swz)::is_v ? voff : koff;
-    if (kbase + BC <= n) {
+    if (BUF && kbase + BC <= n) {
+      // one buffer resource per tile: scalar base arithmetic only
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<bf16*>(src + (size_t)kbase * D), (short)0, BC * D * 2, 0x00020000);
+#pragma unroll
+      for (int it = 0; it < C::INSTS; ++it) {
+        const int p0 = wave * C::WAVE_CHUNKS + it * 64;  // wave-uniform
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(dst + p0 * 8), 16, (int)offs[it], 0, 0,
+            0);
+      }
+    } else if (kbase + BC <= n) {
       const char* tb = reinterpret_cast<const char*>(src) + (size_t)kbase * (D * 2);
 #pragma unroll
       for (int it = 0; it < C::INSTS; ++it) {
@@ -1029,12 +1043,13 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
   }
 }
 
-template <int D, int NW, int BC, bool PIPE, int WPS, bool SCHED, int STAGES, int PRIO = 0>
+template <int D, int NW, int BC, bool PIPE, int WPS, bool SCHED, int STAGES, int PRIO = 0,
+          bool BUF = false>
 __global__ __launch_bounds__(NW * 64, (WPS * 4 / NW > 0 ? WPS * 4 / NW : 1)) void
 fwd_fused_bf16_direct_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                              const bf16* __restrict__ V, float* __restrict__ O,
                              float* __restrict__ lse, int n, int nqb, int total, float c) {
-  direct_body<D, NW, BC, PIPE, WPS, SCHED, STAGES, false, false, PRIO>(
+  direct_body<D, NW, BC, PIPE, WPS, SCHED, STAGES, false, false, PRIO, BUF>(
       DirectArgs{Q, K, V, O, lse, n, n, nqb, total, total / nqb, n, c});
 }
 
@@ -1044,7 +1059,7 @@ fwd_fused_bf16_direct_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
 template <int D, int NW, int BC>
 __global__ __launch_bounds__(NW * 64, (8 / NW > 0 ? 8 / NW : 1)) void fwd_split_bf16_kernel(
     const DirectArgs A) {
-  direct_body<D, NW, BC, true, 2, false, 2, true>(A);
+  direct_body<D, NW, BC, true, 2, false, 2, true, false, 0, true>(A);
 }
 
 // Block-sparse entry: one workgroup per (head, 128-query block), visiting
@@ -1052,7 +1067,7 @@ __global__ __launch_bounds__(NW * 64, (8 / NW > 0 ? 8 / NW : 1)) void fwd_split_
 template <int D, int NW, int BC>
 __global__ __launch_bounds__(NW * 64, (8 / NW > 0 ? 8 / NW : 1)) void fwd_sparse_bf16_kernel(
     const DirectArgs A) {
-  direct_body<D, NW, BC, true, 2, false, 2, false, true>(A);
+  direct_body<D, NW, BC, true, 2, false, 2, false, true, 0, true>(A);
 }
 
 // Compacts one row of the block mask (mask head, query block) into the
@@ -1802,11 +1817,12 @@ FusedEntry basic(const char* name) {
 }
 
 template <int D, int NW, int BC, bool PIPE = true, int WPS = 2, bool SCHED = false,
-          int STAGES = 2, int PRIO = 0>
+          int STAGES = 2, int PRIO = 0, bool BUF = false>
 FusedEntry direct(const char* name) {
   using C = DirectCfg<D, NW, BC, PIPE, WPS, SCHED, STAGES>;
-  return FusedEntry{name, D, NW, FusedTileInfo{C::BR, C::KEYS, C::ONCHIP},
-                    &fwd_fused_bf16_direct_kernel<D, NW, BC, PIPE, WPS, SCHED, STAGES, PRIO>};
+  return FusedEntry{
+      name, D, NW, FusedTileInfo{C::BR, C::KEYS, C::ONCHIP},
+      &fwd_fused_bf16_direct_kernel<D, NW, BC, PIPE, WPS, SCHED, STAGES, PRIO, BUF>};
 }
 
 template <int D, int QB, int NW, int BC>
@@ -1837,10 +1853,11 @@ const FusedEntry* registry(int& count) {
       pingpong<64, 2, 64>("g2x64"),
       pingpong<64, 1, 64>("g1x64"),
       direct<64, 8, 64, true, 2, false, 3>("t8x64"),
-      direct<64, 8, 64>("d8x64"),
+      direct<64, 8, 64, true, 2, false, 2, 0, true>("d8x64"),
       basic<64, 2, 8, 32>("2x8x32"),
       // head dimension 128
-      direct<128, 8, 64>("d8x64"),
+      direct<128, 8, 64, true, 2, false, 2, 0, true>("d8x64"),
+      direct<128, 8, 64>("d8x64g"),  // 64-bit per-lane addresses instead of buffer loads
       direct<128, 8, 64, true, 2, false, 2, 1>("d8x64q1"),
       direct<128, 8, 64, true, 2, false, 2, 2>("d8x64q2"),
       // query-block x key-tile sweep (B_r = 32 x waves, B_c = keys per tile;

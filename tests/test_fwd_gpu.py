@@ -59,7 +59,7 @@ def test_fwd_matches_oracle_small(bh, n, d, dtype, seed, q_mult):
 
 # Every compiled tile shape of the bf16 kernel, on ragged shapes.
 TILES = {64: ["g2x64p", "g2x64", "g1x64", "t8x64", "d8x64", "2x8x32"],
-         128: ["d8x64", "d8x64q1", "d8x64q2", "r64c32", "r64c64", "r128c32", "r128c64",
+         128: ["d8x64", "d8x64g", "d8x64q1", "d8x64q2", "r64c32", "r64c64", "r128c32", "r128c64",
                "r256c32", "r256c64", "g1x64p", "g1x64", "w1x8x64", "s8x64", "n8x32w3", "1x8x64"],
          256: ["1x4x32"]}
 
