@@ -8,25 +8,40 @@
 // memory, and a second tiled product multiplies it by V; the table under
 // "Putting the regimes together" gives the N^2 d / sqrt(M) movement term.
 //
-// Three kernels, stream ordered:
-//  1. sc_scores_exp: one workgroup per (head, query tile I, key tile J), b x b.
-//     S^T = K_J Q_I^T is accumulated over d in panels of KP = 32 columns
-//     staged in LDS.  The epilogue takes each query row's maximum over the
-//     tile, m_IJ (base-2 units, c = scale log2 e), writes
-//     E = exp2(c S - m_IJ) in bf16 to the workspace, and the tile sum l_IJ of
-//     the stored bf16 values.  The page does not say how the exponentials are
-//     kept in range; the per-tile shift is the reading used here.
-//  2. sc_merge_stats: per query row, m = max_J m_IJ, l = sum_J 2^(m_IJ - m)
-//     l_IJ (the streaming rescale rule applied across tiles), then the factor
-//     f_IJ = 2^(m_IJ - m) / l overwrites m_IJ, and lse = (m + log2 l) ln 2.
-//  3. sc_value_product: one workgroup per (head, query tile I, d tile), b x
-//     b.  For each key tile J, A_J = V_J^T E_IJ^T is accumulated over keys in
-//     panels of KP (V panel transposed into LDS, E read as MFMA B operand),
-//     then O^T += f_IJ * A_J with f a per-lane scalar (one query per lane).
+// Two kernels, stream ordered:
+//  1. sc_scores_exp: one workgroup per (head, query tile I, run of jc key
+//     tiles J), b x b tiles.  S^T = K_J Q_I^T is accumulated over d in
+//     panels of KP = 32 columns: the K panel goes global -> LDS with direct
+//     loads (two stages), the Q panel goes straight into registers as the
+//     MFMA B operand (two stages), and the panel pipeline runs on across tile
+//     boundaries.  The epilogue takes each query row's maximum over the tile,
+//     m_IJ (base-2 units, c = scale log2 e), writes E = exp2(c S - m_IJ) in
+//     bf16, and the tile sum l_IJ of the stored bf16 values.  The page does
+//     not say how the exponentials are kept in range; the per-tile shift is
+//     the reading used here.
+//  2. sc_value_product: one workgroup per (head, query tile I, d tile), b x
+//     b.  It first merges its rows' statistics: m = max_J m_IJ,
+//     l = sum_J 2^(m_IJ - m) l_IJ (the streaming rescale rule applied across
+//     tiles), lse = (m + log2 l) ln 2.  Then for each key tile J it
+//     accumulates A_J = V_J^T E_IJ^T over 32-key panels (V panel global ->
+//     LDS with direct loads and read transposed, E straight from global
+//     memory into registers as the MFMA B operand) and adds
+//     f_IJ A_J with f_IJ = 2^(m_IJ - m) / l, a per-lane scalar (one query per
+//     lane).
 //
-// Workspace layout (256-byte aligned pieces): E [bh][n][npad] bf16 with
-// npad = ceil(n/b) b (padded keys hold 0), then stats m|f [bh][n][nt] and
-// l [bh][n][nt] fp32 with nt = ceil(n/b).
+// E is stored in the score kernel's accumulator order, so both kernels move
+// it with 16-byte lane accesses that are contiguous per wave: unit
+// (head, I, J, wave w, 32-key block kb, half) holds, for each lane, the 8
+// bf16 values of accumulator registers 8 half .. 8 half + 7 of that block,
+// i.e. keys kb 32 + 16 half + {0..3, 8..11} + 4 (lane / 32) of query
+// I b + 32 w + lane % 32.  That key order inside a 16-key step is the one
+// the transposed V reads produce, so the contraction pairs every E value
+// with its own V row.
+//
+// Workspace layout (256-byte aligned pieces): E, bh nt^2 b^2 bf16 in the
+// unit order above (tiles past n hold finite values that only reach
+// discarded rows or are multiplied by 0), then m_IJ [bh][n][nt] and
+// l_IJ [bh][n][nt] fp32 with nt = ceil(n/b).
 #include "device_common.h"
 #include "launch.h"
 
@@ -40,72 +55,149 @@ __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~si
 
 struct ScLayout {
   size_t e_off, m_off, l_off, total;
-  int64_t npad, nt;
+  int64_t nt;
 };
 
 ScLayout sc_layout(int64_t bh, int64_t n, int64_t b) {
   ScLayout L;
   L.nt = (n + b - 1) / b;
-  L.npad = L.nt * b;
   L.e_off = 0;
-  L.m_off = align256((size_t)bh * n * L.npad * 2);
+  L.m_off = align256((size_t)bh * L.nt * L.nt * b * b * 2);
   L.l_off = L.m_off + align256((size_t)bh * n * L.nt * 4);
   L.total = L.l_off + align256((size_t)bh * n * L.nt * 4);
   return L;
 }
 
+// Index of the first 16-byte E unit of (tile (head, I, J), wave, block kb).
+template <int B>
+__device__ __forceinline__ size_t e_unit(int head, int I, int J, int nt, int wave, int kb) {
+  constexpr int NW = B / 32;
+  return ((((size_t)head * nt + I) * nt + J) * NW + wave) * (B / 32) * 2 + (size_t)kb * 2;
+}
+
 }  // namespace
 
+// Prefetch distance: every operand panel is copied global -> LDS DIST
+// panels ahead of the one being multiplied, into a ring of R = DIST + 1
+// slots.  The on-chip footprint is then b^2 + 2 R b KP for the scores (K and
+// Q panels, b x KP each) and b bd + R (KP bd + b KP) for the value product
+// (V panels KP x bd, E panels b x KP).
+template <int B>
+struct ScDist {
+  static constexpr int DIST = B >= 128 ? 2 : 1;
+  static constexpr int R = DIST + 1;
+};
+
+// s_waitcnt with vmcnt = N and the other counters left at their maxima.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4),
+// issued from inline assembly: lane l's 16 bytes land at lds_wave_base +
+// 16 l (lds_wave_base uniform across the wave).  The compiler does not see
+// this as an LDS write, so it does not make every later LDS read wait for
+// all such copies in flight (it cannot tell the ring slots apart); the
+// kernels wait for exactly the copies they need with wait_vm before the
+// slot barrier.  Its own waits for ordinary loads stay correct: copies it
+// does not count only lengthen them.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0: only LDS copies use it here
+__device__ __forceinline__ void dma16(const void* gsrc, bf16* lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
+      __attribute__((address_space(3))) char*)(reinterpret_cast<char*>(lds_wave_base)));
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(gsrc), "s"(lds)
+      : "memory", "m0");
+}
+// The same with 4 bytes per lane (global_load_lds_dword): lane l's 4 bytes
+// land at lds_wave_base + 4 l.
+__device__ __forceinline__ void dma4(const void* gsrc, float* lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
+      __attribute__((address_space(3))) char*)(reinterpret_cast<char*>(lds_wave_base)));
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, off"
+      :
+      : "v"(gsrc), "s"(lds)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Workgroup barrier without a memory fence: the LDS slots are filled by
+// direct loads whose completion each lane has already waited for with an
+// exact vmcnt, and later panels' loads must stay in flight across it (a
+// fence would wait for them).  The empty asm statements keep the compiler
+// from moving memory accesses across the barrier.
+__device__ __forceinline__ void slot_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
-// 1. Scores and exponentials of one b x b tile.
+// 1. Scores and exponentials of b x b tiles.
 
 template <int D, int B>
-__global__ __launch_bounds__(B * 2, 1) void sc_scores_exp(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, bf16* __restrict__ E,
-    float* __restrict__ mst, float* __restrict__ lst, int n, int nt, int npad, int total,
-    float c) {
+__global__ __launch_bounds__(B * 2) void sc_scores_exp(const bf16* __restrict__ Q,
+                                                       const bf16* __restrict__ K,
+                                                       u32x4* __restrict__ E,
+                                                       float* __restrict__ mst,
+                                                       float* __restrict__ lst, int n, int nt,
+                                                       int jc, int njc, int total, float c) {
   constexpr int NW = B / 32, NT = NW * 64;
-  constexpr int CH = KP / 8;                // 16-byte chunks per panel row
-  constexpr int PCH = B * CH;               // chunks per panel
-  constexpr int ITERS = (PCH + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) bf16 Qp[2][B * KP];
-  __shared__ __attribute__((aligned(16))) bf16 Kp[2][B * KP];
+  constexpr int CPR = KP / 8;       // 16-byte chunks per panel row
+  constexpr int PCH = B * CPR;      // chunks per panel
+  constexpr int LI = PCH / NT;      // copies per lane per panel and operand
+  constexpr int NP = D / KP;        // panels per tile
+  constexpr int DIST = ScDist<B>::DIST, R = ScDist<B>::R;
+  static_assert(PCH % NT == 0, "panel chunks must split evenly over the lanes");
+  __shared__ __attribute__((aligned(16))) bf16 Kp[R][B * KP];
+  __shared__ __attribute__((aligned(16))) bf16 Qp[R][B * KP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, li = lane & 31;
   const int tile = xcd_remap(blockIdx.x, total);
-  const int head = tile / (nt * nt);
-  const int rem = tile - head * nt * nt;
-  const int I = rem / nt, J = rem - (rem / nt) * nt;
-  const size_t hoff = (size_t)head * n * D;
-  const bf16* Qh = Q + hoff;
-  const bf16* Kh = K + hoff;
+  const int head = tile / (nt * njc);
+  const int rem = tile - head * nt * njc;
+  const int I = rem / njc, jr = rem - (rem / njc) * njc;
+  const int J0 = jr * jc, J1 = min(nt, J0 + jc);
+  const int T = (J1 - J0) * NP;
+  const bf16* Qh = Q + (size_t)head * n * D;
+  const bf16* Kh = K + (size_t)head * n * D;
+  const int q = I * B + wave * 32 + li;
+  const bool qok = q < n;
 
-  u32x4 qr[ITERS], kr[ITERS];
-  auto load = [&](int p) {
+  // lane chunk p = (wave LI + it) 64 + lane of a panel: row p / CPR,
+  // physical chunk p % CPR, which holds logical chunk phys ^ swizzle(row);
+  // rows past n are clamped (their scores are masked, or belong to rows
+  // that are not stored)
+  int prow[LI], pcol[LI];
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int x = tid + it * NT;
-      const int row = x / CH, cc = x % CH;
-      const int q = I * B + row, key = J * B + row;
-      const bool ok = x < PCH;
-      qr[it] = (ok && q < n) ? *reinterpret_cast<const u32x4*>(Qh + (size_t)q * D + p * KP + cc * 8)
-                             : u32x4{};
-      kr[it] = (ok && key < n)
-                   ? *reinterpret_cast<const u32x4*>(Kh + (size_t)key * D + p * KP + cc * 8)
-                   : u32x4{};
-    }
-  };
-  auto store = [&](int buf) {
+  for (int it = 0; it < LI; ++it) {
+    const int p = (wave * LI + it) * 64 + lane;
+    const int row = p / CPR, phys = p % CPR;
+    prow[it] = row;
+    pcol[it] = (phys ^ chunk_swizzle<KP * 2>(row)) * 8;
+  }
+  // Copy panel t's K and Q into slot t % R.  Panels past the end copy the
+  // last one again, so every step issues the same number of copies.
+  auto issue = [&](int t) {
+    t = min(t, T - 1);
+    const int J = J0 + t / NP, pan = t - (t / NP) * NP, slot = t % R;
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int x = tid + it * NT;
-      if (x < PCH) {
-        const int row = x / CH, cc = x % CH;
-        const int off = row * KP + ((cc ^ chunk_swizzle<KP * 2>(row)) * 8);
-        *reinterpret_cast<u32x4*>(&Qp[buf][off]) = qr[it];
-        *reinterpret_cast<u32x4*>(&Kp[buf][off]) = kr[it];
-      }
+    for (int it = 0; it < LI; ++it) {
+      const int key = min(J * B + prow[it], n - 1);
+      const int qrow = min(I * B + prow[it], n - 1);
+      dma16(Kh + (size_t)key * D + pan * KP + pcol[it], &Kp[slot][(wave * LI + it) * 64 * 8]);
+      dma16(Qh + (size_t)qrow * D + pan * KP + pcol[it], &Qp[slot][(wave * LI + it) * 64 * 8]);
     }
   };
 
@@ -113,100 +205,114 @@ __global__ __launch_bounds__(B * 2, 1) void sc_scores_exp(
 #pragma unroll
   for (int kb = 0; kb < B / 32; ++kb) acc[kb] = f32x16{};
 
-  constexpr int NP = D / KP;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int p = 0; p < NP; ++p) {
-    const int buf = p & 1;
-    if (p + 1 < NP) load(p + 1);
+#pragma unroll
+  for (int s = 0; s < DIST; ++s) issue(s);
+  for (int t = 0; t < T; ++t) {
+    // panel t is complete once at most the later DIST - 1 panels' copies
+    // are outstanding (vector-memory operations complete in issue order; an
+    // E store in between only makes this wait longer)
+    wait_vm<(DIST - 1) * 2 * LI>();
+    slot_barrier();  // every lane's part of panel t; slot (t - 1) % R is free
+    issue(t + DIST);
+    const int slot = t % R;
+    const bf16* Ks = Kp[slot];
+    const bf16* Qs = Qp[slot];
+    const int qrow = wave * 32 + li;
 #pragma unroll
     for (int kk = 0; kk < KP / 16; ++kk) {
-      const int qrow = wave * 32 + li;
       const bf16x8 bq = *reinterpret_cast<const bf16x8*>(
-          &Qp[buf][qrow * KP + (((2 * kk + h) ^ chunk_swizzle<KP * 2>(qrow)) * 8)]);
+          Qs + qrow * KP + (((2 * kk + h) ^ chunk_swizzle<KP * 2>(qrow)) * 8));
 #pragma unroll
       for (int kb = 0; kb < B / 32; ++kb) {
-        const int krow = kb * 32 + li;
+        const int row = kb * 32 + li;
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            &Kp[buf][krow * KP + (((2 * kk + h) ^ chunk_swizzle<KP * 2>(krow)) * 8)]);
+            Ks + row * KP + (((2 * kk + h) ^ chunk_swizzle<KP * 2>(row)) * 8));
         acc[kb] = mfma_bf16_32x32x16(a, bq, acc[kb]);
       }
     }
-    if (p + 1 < NP) store(buf ^ 1);
-    __syncthreads();
-  }
-
-  // Epilogue: tile maximum, exponentials, tile sum.
-  if (J == nt - 1 && (n % B) != 0) {
+    if (t % NP == NP - 1) {
+      // Epilogue of tile J: tile maximum, exponentials, tile sum.
+      const int J = J0 + t / NP;
+      if (J == nt - 1 && (n % B) != 0) {
 #pragma unroll
-    for (int kb = 0; kb < B / 32; ++kb)
+        for (int kb = 0; kb < B / 32; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (J * B + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3) >= n) acc[kb][r] = -INFINITY;
-  }
-  float mx = -INFINITY;
+          for (int r = 0; r < 16; ++r)
+            if (J * B + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3) >= n) acc[kb][r] = -INFINITY;
+      }
+      float mx = -INFINITY;
 #pragma unroll
-  for (int kb = 0; kb < B / 32; ++kb)
+      for (int kb = 0; kb < B / 32; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[kb][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m = mx * c;
-  const int q = I * B + wave * 32 + li;
-  float lsum = 0.f;
-  bf16* Er = E + ((size_t)head * n + (q < n ? q : 0)) * npad + (size_t)J * B;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m = mx * c;
+      float lsum = 0.f;
+      u32x4* Eu = E + e_unit<B>(head, I, J, nt, wave, 0) * 64 + lane;
 #pragma unroll
-  for (int kb = 0; kb < B / 32; ++kb)
+      for (int kb = 0; kb < B / 32; ++kb) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const uint32_t p01 = pack_bf16x2(fast_exp2(__builtin_fmaf(acc[kb][4 * g + 0], c, -m)),
-                                       fast_exp2(__builtin_fmaf(acc[kb][4 * g + 1], c, -m)));
-      const uint32_t p23 = pack_bf16x2(fast_exp2(__builtin_fmaf(acc[kb][4 * g + 2], c, -m)),
-                                       fast_exp2(__builtin_fmaf(acc[kb][4 * g + 3], c, -m)));
-      lsum = add_bf16x2(p23, add_bf16x2(p01, lsum));
-      if (q < n) *reinterpret_cast<u32x2*>(Er + kb * 32 + 8 * g + 4 * h) = u32x2{p01, p23};
+        for (int half = 0; half < 2; ++half) {
+          uint32_t pk[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 8 * half + 2 * i;
+            pk[i] = pack_bf16x2(fast_exp2(__builtin_fmaf(acc[kb][r], c, -m)),
+                                fast_exp2(__builtin_fmaf(acc[kb][r + 1], c, -m)));
+            lsum = add_bf16x2(pk[i], lsum);
+          }
+          Eu[(kb * 2 + half) * 64] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+        }
+        acc[kb] = f32x16{};
+      }
+      lsum += __shfl_xor(lsum, 32);
+      if (qok && h == 0) {
+        const size_t sidx = ((size_t)head * n + q) * nt + J;
+        mst[sidx] = m;
+        lst[sidx] = lsum;
+      }
     }
-  lsum += __shfl_xor(lsum, 32);
-  if (q < n && h == 0) {
-    const size_t s = ((size_t)head * n + q) * nt + J;
-    mst[s] = m;
-    lst[s] = lsum;
   }
+  wait_vm<0>();  // no copy into LDS may outlive the workgroup
 }
 
 // ---------------------------------------------------------------------------
-// 2. Merge the per-tile statistics of each query row.
+// 2. Statistics merge and second product with per-tile row factors.
 
-__global__ __launch_bounds__(256) void sc_merge_stats(float* __restrict__ mst,
-                                                      const float* __restrict__ lst,
-                                                      float* __restrict__ lse, int64_t rows,
-                                                      int nt) {
-  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (r >= rows) return;
-  float* mr = mst + r * nt;
-  const float* lr = lst + r * nt;
-  float m = -INFINITY;
-  for (int t = 0; t < nt; ++t) m = fmaxf(m, mr[t]);
-  float l = 0.f;
-  for (int t = 0; t < nt; ++t) l += fast_exp2(mr[t] - m) * lr[t];
-  const float inv = 1.0f / l;
-  for (int t = 0; t < nt; ++t) mr[t] = fast_exp2(mr[t] - m) * inv;
-  if (lse) lse[r] = (m + __log2f(l)) * kLn2;
+// (E * f) in bf16 for 8 packed bf16 values and one fp32 factor.
+__device__ __forceinline__ bf16x8 scale_bf16x8(const u32x4& e, float f) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __builtin_bit_cast(float, e[i] << 16);
+    const float hi = __builtin_bit_cast(float, e[i] & 0xFFFF0000u);
+    r[i] = pack_bf16x2(lo * f, hi * f);
+  }
+  return __builtin_bit_cast(bf16x8, r);
 }
-
-// ---------------------------------------------------------------------------
-// 3. Second product with per-tile row factors.
 
 template <int D, int B>
-__global__ __launch_bounds__(B * 2, 1) void sc_value_product(
-    const bf16* __restrict__ V, const bf16* __restrict__ E, const float* __restrict__ fst,
-    float* __restrict__ O, int n, int nt, int npad, int total) {
-  constexpr int BD = B < D ? B : D;          // d columns per output tile
+__global__ __launch_bounds__(B * 2) void sc_value_product(const bf16* __restrict__ V,
+                                                          const u32x4* __restrict__ E,
+                                                          const float* __restrict__ mst,
+                                                          const float* __restrict__ lst,
+                                                          float* __restrict__ O,
+                                                          float* __restrict__ lse, int n, int nt,
+                                                          int total) {
+  constexpr int BD = B < D ? B : D;  // d columns per output tile
   constexpr int NCT = D / BD;
   constexpr int NW = B / 32, NT = NW * 64;
-  constexpr int ITEMS = (KP / 4) * (BD / 8);  // (4 keys x 8 d) blocks per V panel
-  constexpr int ITERS = (ITEMS + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) bf16 Vt[2][BD * KP];
+  constexpr int CPR = BD / 8;        // 16-byte chunks per V panel row
+  constexpr int PCH = KP * CPR;      // chunks per V panel (KP keys)
+  constexpr int LI = PCH / NT;
+  constexpr int PPT = B / KP;        // panels per key tile
+  constexpr int DIST = ScDist<B>::DIST, R = ScDist<B>::R;
+  constexpr int OPS = LI + 2 + 1;    // copies per lane per panel: V, E (2 units), m_IJ
+  static_assert(PCH % NT == 0, "panel chunks must split evenly over the lanes");
+  static_assert(KP == 32 && B / 32 == PPT, "one panel is one 32-key block of the score tile");
+  __shared__ __attribute__((aligned(16))) bf16 Vp[R][KP * BD];
+  __shared__ __attribute__((aligned(16))) bf16 Ep[R][NW * 2 * 64 * 8];  // [wave][half][lane]
+  __shared__ __attribute__((aligned(16))) float Ms[R][NW * 64];        // m_IJ per lane
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, li = lane & 31;
@@ -216,83 +322,91 @@ __global__ __launch_bounds__(B * 2, 1) void sc_value_product(
   const int I = rem / NCT, ct = rem - (rem / NCT) * NCT;
   const bf16* Vh = V + (size_t)head * n * D + ct * BD;
   const int q = I * B + wave * 32 + li;
-  const bf16* Er = E + ((size_t)head * n + (q < n ? q : 0)) * npad;
-  const float* fr = fst + ((size_t)head * n + (q < n ? q : 0)) * nt;
+  const bool qok = q < n;
 
-  u32x4 vr[ITERS][4];
-  auto load = [&](int kbase) {
-#pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int x = tid + it * NT;
-      const int g = x % (KP / 4), cc = x / (KP / 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = kbase + 4 * g + e;
-        vr[it][e] = (x < ITEMS && key < n)
-                        ? *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + cc * 8)
-                        : u32x4{};
-      }
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int x = tid + it * NT;
-      if (x < ITEMS) {
-        const int g = x % (KP / 4), cc = x / (KP / 4);
-        const int pos = 4 * g;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int r0 = cc * 8 + 2 * w, r1 = r0 + 1;
-          u32x2 lo = {pair_lo(vr[it][0][w], vr[it][1][w]), pair_lo(vr[it][2][w], vr[it][3][w])};
-          u32x2 hi = {pair_hi(vr[it][0][w], vr[it][1][w]), pair_hi(vr[it][2][w], vr[it][3][w])};
-          *reinterpret_cast<u32x2*>(
-              &Vt[buf][r0 * KP + (((pos >> 3) ^ chunk_swizzle<KP * 2>(r0)) * 8) + (pos & 7)]) = lo;
-          *reinterpret_cast<u32x2*>(
-              &Vt[buf][r1 * KP + (((pos >> 3) ^ chunk_swizzle<KP * 2>(r1)) * 8) + (pos & 7)]) = hi;
-        }
-      }
-    }
-  };
+  // merged statistics of this lane's query row
+  const float* mr = mst + ((size_t)head * n + (qok ? q : 0)) * nt;
+  const float* lr = lst + ((size_t)head * n + (qok ? q : 0)) * nt;
+  float m = -INFINITY;
+  for (int t = 0; t < nt; ++t) m = fmaxf(m, mr[t]);
+  float l = 0.f;
+  for (int t = 0; t < nt; ++t) l += fast_exp2(mr[t] - m) * lr[t];
+  const float inv = 1.0f / l;
+  if (ct == 0 && lse != nullptr && qok && h == 0)
+    lse[(size_t)head * n + q] = (m + __log2f(l)) * kLn2;
 
-  f32x16 out[BD / 32], acc[BD / 32];
+  int vrow[LI], vcol[LI];
 #pragma unroll
-  for (int db = 0; db < BD / 32; ++db) out[db] = acc[db] = f32x16{};
-
-  constexpr int PPT = B / KP;  // panels per key tile
-  const int np = nt * PPT;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int p = 0; p < np; ++p) {
-    const int buf = p & 1;
-    if (p + 1 < np) load((p + 1) * KP);
-#pragma unroll
-    for (int ks = 0; ks < KP / 16; ++ks) {
-      const bf16x8 be = q < n ? *reinterpret_cast<const bf16x8*>(Er + p * KP + ks * 16 + 8 * h)
-                              : bf16x8{};
-#pragma unroll
-      for (int db = 0; db < BD / 32; ++db) {
-        const int row = db * 32 + li;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            &Vt[buf][row * KP + (((2 * ks + h) ^ chunk_swizzle<KP * 2>(row)) * 8)]);
-        acc[db] = mfma_bf16_32x32x16(a, be, acc[db]);
-      }
-    }
-    if ((p + 1) % PPT == 0) {
-      const float f = q < n ? fr[p / PPT] : 0.f;
-#pragma unroll
-      for (int db = 0; db < BD / 32; ++db) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) out[db][r] = __builtin_fmaf(f, acc[db][r], out[db][r]);
-        acc[db] = f32x16{};
-      }
-    }
-    if (p + 1 < np) store(buf ^ 1);
-    __syncthreads();
+  for (int it = 0; it < LI; ++it) {
+    const int p = (wave * LI + it) * 64 + lane;
+    const int row = p / CPR, phys = p % CPR;
+    vrow[it] = row;
+    vcol[it] = (phys ^ vtr_swizzle<BD * 2>(row)) * 8;
   }
+  // E units of this wave: (J, wave, kb, half) order
+  const u32x4* Ew = E + e_unit<B>(head, I, 0, nt, wave, 0) * 64 + lane;
+  const int T = nt * PPT;
+  // Copy panel t's V, this wave's two E units and each lane's m_IJ into
+  // slot t % R.  Panels past the end copy the last one again (same number
+  // of copies every step).
+  auto issue = [&](int t) {
+    t = min(t, T - 1);
+    const int J = t / PPT, kb = t - (t / PPT) * PPT, slot = t % R;
+#pragma unroll
+    for (int it = 0; it < LI; ++it) {
+      const int key = min(J * B + kb * KP + vrow[it], n - 1);  // E is 0 for keys past n
+      dma16(Vh + (size_t)key * D + vcol[it], &Vp[slot][(wave * LI + it) * 64 * 8]);
+    }
+    const u32x4* p = Ew + ((size_t)J * NW * PPT * 2 + kb * 2) * 64;
+    dma16(p, &Ep[slot][(wave * 2 + 0) * 64 * 8]);
+    dma16(p + 64, &Ep[slot][(wave * 2 + 1) * 64 * 8]);
+    dma4(mr + J, &Ms[slot][wave * 64]);
+  };
 
-  if (q < n) {
+  f32x16 out[BD / 32];
+#pragma unroll
+  for (int db = 0; db < BD / 32; ++db) out[db] = f32x16{};
+
+  // transposed V reads: lane group G = lane / 16 covers d rows 16 (G & 1)
+  // .. +15 of a 32-row block and key half hh = G / 2; source lane sl points
+  // at key K0 + sl / 4, d D0 + 4 (sl % 4)
+  const int G = lane >> 4, sl = lane & 15, hh = G >> 1;
+  float f = 0.f;
+#pragma unroll
+  for (int s = 0; s < DIST; ++s) issue(s);
+  for (int t = 0; t < T; ++t) {
+    // panel t's copies are complete once at most the later DIST - 1 panels'
+    // copies are outstanding (vector-memory operations complete in issue
+    // order)
+    wait_vm<(DIST - 1) * OPS>();
+    slot_barrier();  // every lane's part of panel t; slot (t - 1) % R is free
+    issue(t + DIST);
+    const int slot = t % R;
+    if (t % PPT == 0) f = qok ? fast_exp2(Ms[slot][wave * 64 + lane] - m) * inv : 0.f;  // f_IJ
+    const bf16* Vs = Vp[slot];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const u32x4 e = *reinterpret_cast<const u32x4*>(&Ep[slot][((wave * 2 + half) * 64 + lane) * 8]);
+      const bf16x8 pb = scale_bf16x8(e, f);
+#pragma unroll
+      for (int db = 0; db < BD / 32; ++db) {
+        u32x2 part[2];
+#pragma unroll
+        for (int piece = 0; piece < 2; ++piece) {
+          const int row = 16 * half + 8 * piece + 4 * hh + (sl >> 2);
+          const int d0 = db * 32 + 16 * (G & 1) + 4 * (sl & 3);
+          const int phys = (d0 >> 3) ^ vtr_swizzle<BD * 2>(row);
+          part[piece] = lds_read_tr16(Vs + row * BD + phys * 8 + (d0 & 7));
+        }
+        const bf16x8 a =
+            __builtin_bit_cast(bf16x8, (u32x4{part[0][0], part[0][1], part[1][0], part[1][1]}));
+        out[db] = mfma_bf16_32x32x16(a, pb, out[db]);
+      }
+    }
+  }
+  wait_vm<0>();  // no copy into LDS may outlive the workgroup
+
+  if (qok) {
     float* Or = O + ((size_t)head * n + q) * D + ct * BD;
 #pragma unroll
     for (int db = 0; db < BD / 32; ++db)
@@ -310,16 +424,28 @@ __global__ __launch_bounds__(B * 2, 1) void sc_value_product(
 namespace {
 
 // On-chip elements per workgroup, each counted once whatever its width, and
-// every pipeline stage counted: the larger of the two products' footprints.
-// Scores: the b x b score tile and two stages of the Q and K panels (b x KP
-// each).  Value product: the b x bd output tile, the b x bd partial for the
-// current key tile, the E panel in registers (b x KP) and two stages of the
-// V panel (KP x bd).
+// every pipeline slot counted: the larger of the two products' footprints.
+// Scores: the b x b score tile and R slots each of the K and Q panels (LDS,
+// b x KP each).  Value product: the b x bd output tile and R slots each of
+// the V panel (KP x bd) and the E panel (b x KP), both in LDS; the per-row
+// statistics (b values per slot) are not counted.  R = 3 for b = 128, 2 for
+// b = 64.
 int64_t footprint(int64_t b, int64_t d) {
   const int64_t bd = b < d ? b : d;
-  const int64_t s = b * b + 2 * 2 * b * KP;
-  const int64_t v = 2 * b * bd + b * KP + 2 * KP * bd;
+  const int64_t r = b >= 128 ? 3 : 2;  // ScDist<b>::R
+  const int64_t s = b * b + 2 * r * b * KP;
+  const int64_t v = b * bd + r * (KP * bd + b * KP);
   return s > v ? s : v;
+}
+
+// Key tiles per score workgroup: enough workgroups to fill the chip twice
+// over, and otherwise long runs so the panel pipeline is rarely restarted.
+int score_run(int64_t bh, int64_t nt) {
+  const int64_t tiles = bh * nt * nt;
+  int64_t jc = (tiles + 2047) / 2048;
+  if (jc < 1) jc = 1;
+  if (jc > nt) jc = nt;
+  return (int)jc;
 }
 
 template <int D, int B>
@@ -327,27 +453,24 @@ hipError_t launch(const void* Q, const void* K, const void* V, float* O, float* 
                   int64_t n, float scale, void* ws, hipStream_t stream) {
   const ScLayout L = sc_layout(bh, n, B);
   char* base = static_cast<char*>(ws);
-  bf16* E = reinterpret_cast<bf16*>(base + L.e_off);
+  u32x4* E = reinterpret_cast<u32x4*>(base + L.e_off);
   float* mst = reinterpret_cast<float*>(base + L.m_off);
   float* lst = reinterpret_cast<float*>(base + L.l_off);
-  const int nt = (int)L.nt, npad = (int)L.npad;
+  const int nt = (int)L.nt;
   const float c = scale * kLog2e;
 
-  const int total1 = (int)(bh * L.nt * L.nt);
+  const int jc = score_run(bh, L.nt);
+  const int njc = (nt + jc - 1) / jc;
+  const int total1 = (int)(bh * L.nt * njc);
   hipLaunchKernelGGL((sc_scores_exp<D, B>), dim3(total1), dim3(B * 2), 0, stream,
                      static_cast<const bf16*>(Q), static_cast<const bf16*>(K), E, mst, lst,
-                     (int)n, nt, npad, total1, c);
+                     (int)n, nt, jc, njc, total1, c);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t rows = bh * n;
-  hipLaunchKernelGGL(sc_merge_stats, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream,
-                     mst, lst, lse, rows, nt);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   constexpr int BD = B < D ? B : D;
-  const int total3 = (int)(bh * L.nt * (D / BD));
-  hipLaunchKernelGGL((sc_value_product<D, B>), dim3(total3), dim3(B * 2), 0, stream,
-                     static_cast<const bf16*>(V), E, mst, O, (int)n, nt, npad, total3);
+  const int total2 = (int)(bh * L.nt * (D / BD));
+  hipLaunchKernelGGL((sc_value_product<D, B>), dim3(total2), dim3(B * 2), 0, stream,
+                     static_cast<const bf16*>(V), E, mst, lst, O, lse, (int)n, nt, total2);
   return hipGetLastError();
 }
 

@@ -153,15 +153,16 @@ def test_library_links_no_oracle(lib):
 
 
 def test_smallcache_tile_selection(lib):
-    # footprint(b) = max(b^2 + 2*2*b*32, 2*b*bd + b*32 + 2*32*bd), bd = min(b, d):
-    # score tile plus two stages of the Q and K panels, or the two output
-    # accumulators, the E panel and two stages of the V panel
-    assert lib.attn_smallcache_onchip_elems(128) == 45056
-    assert lib.attn_smallcache_onchip_elems(64) == 14336
+    # footprint(b) = max(b^2 + 2*R*b*32, b*bd + R*(32*bd + b*32)), bd = min(b, d),
+    # R = 3 slots for b = 128 and 2 for b = 64: the score tile plus R slots of
+    # the Q and K panels, or the output tile plus R slots of the V and E panels
+    assert lib.attn_smallcache_onchip_elems(128) == 40960
+    assert lib.attn_smallcache_onchip_elems(64) == 12288
     assert lib.attn_smallcache_tile(256, 49152) == 128
-    assert lib.attn_smallcache_tile(256, 45056) == 128
-    assert lib.attn_smallcache_tile(256, 45055) == 64
-    assert lib.attn_smallcache_tile(256, 14335) == 0
+    assert lib.attn_smallcache_tile(256, 40960) == 128
+    assert lib.attn_smallcache_tile(256, 40959) == 64
+    assert lib.attn_smallcache_tile(256, 12288) == 64
+    assert lib.attn_smallcache_tile(256, 12287) == 0
     assert lib.attn_smallcache_tile(128, 16000) == 64  # b=128 would not be below d^2
     assert lib.attn_smallcache_tile(256, 65536) == 0  # not the small-cache regime
     assert lib.attn_smallcache_tile(64, 4000) == 0  # no tile fits below d^2 = 4096

@@ -24,7 +24,7 @@ CASES = [
     (2, 17, 256, 49152, 64, 1.0),
     (1, 513, 256, 49152, 65, 4.0),
     (3, 200, 128, 16000, 66, 1.0),  # d = 128 -> b = 64
-    (1, 257, 128, 14336, 67, 1.0),  # budget = the b = 64 footprint
+    (1, 257, 128, 12288, 67, 1.0),  # budget = the b = 64 footprint
     (1, 640, 256, 49152, 68, 40.0),  # scores in the hundreds
 ]
 
