@@ -79,6 +79,43 @@ __device__ __forceinline__ bf16x8 tr_panel(const bf16* panel, int col0, int lane
   return __builtin_bit_cast(bf16x8, (u32x4{part[0][0], part[0][1], part[1][0], part[1][1]}));
 }
 
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4)
+// from inline assembly: lane l's 16 bytes land at lds_wave_base + 16 l
+// (lds_wave_base uniform across the wave).  The compiler does not see these
+// as LDS writes, so it does not make every LDS read wait for all copies in
+// flight (it cannot tell the ring slots apart); the kernels wait for the
+// copies they need with an exact vmcnt before a barrier without a fence.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0: only LDS copies use it here
+__device__ __forceinline__ void sb_copy16(const void* gsrc, bf16* lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
+      __attribute__((address_space(3))) char*)(reinterpret_cast<char*>(lds_wave_base)));
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(gsrc), "s"(lds)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt with vmcnt = N and the other counters left at their maxima.
+template <int N>
+__device__ __forceinline__ void sb_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier without a memory fence (a fence would wait for the
+// later panels' copies); the empty asm statements keep the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void sb_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Direct load of one 16-row x W-column panel (row stride `stride` elements,
 // rows clamped to rmax) into LDS with vtr_swizzle, by one wave-load of 64
 // lanes per 64 chunks: part `part` covers chunks 64 part .. +63.
@@ -91,12 +128,16 @@ __device__ __forceinline__ void load_tr_panel(const bf16* src, int64_t stride, i
   const int row = p / CPR, phys = p % CPR;
   const int logical = phys ^ vtr_swizzle<W * 2>(row);
   const int grow = min(r0 + row, rmax);
-  load_lds_16(src + (size_t)grow * stride + c0 + logical * 8, dst + p0 * 8);
+  sb_copy16(src + (size_t)grow * stride + c0 + logical * 8, dst + p0 * 8);
 }
 
 // ---------------------------------------------------------------------------
 // 1. P and dS of one b x b tile.
 
+// S = Q_I K_J^T is accumulated first, over d in panels of 16 columns, then
+// dP = dO_I V_J^T: each step copies two panels (Q and K, or dO and V), so the
+// ST stages of four panels the footprint counts make R = 2 ST ring slots of
+// two, filled R - 1 steps ahead.
 template <int D, int B, int ST>
 __global__ __launch_bounds__(B * 4) void sb_scores_grads(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
@@ -106,8 +147,9 @@ __global__ __launch_bounds__(B * 4) void sb_scores_grads(
   constexpr int RB = B / 32;  // 32-row query blocks (and wave-loads per tensor panel)
   constexpr int CB = B / 64;  // 32-key blocks per wave
   constexpr int PANEL = B * SKP;
-  static_assert(2 * NW == 4 * RB, "two wave-loads per wave cover the four panels");
-  __shared__ __attribute__((aligned(16))) bf16 sm[ST][4][PANEL];  // Q, dO, K, V
+  constexpr int R = 2 * ST, DIST = R - 1;
+  static_assert(NW == 2 * RB, "one wave-load per wave covers the step's two panels");
+  __shared__ __attribute__((aligned(16))) bf16 sm[R][2][PANEL];  // (Q or dO), (K or V)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -118,57 +160,54 @@ __global__ __launch_bounds__(B * 4) void sb_scores_grads(
   const int J = rem / nt, I = rem - J * nt;  // neighbours share the key tile
   const size_t hoff = (size_t)head * n * D;
   const int ib = wave % RB, jh = wave / RB;
+  constexpr int NP = D / SKP;
+  constexpr int T = 2 * NP;  // steps: NP for S, then NP for dP
 
-  auto load_panel = [&](int kp, int st) {
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int g = wave * 2 + it;
-      const int tensor = g / RB, part = g - tensor * RB;
-      const int p0 = part * 64, p = p0 + lane;
-      const int row = p >> 1, half = p & 1;
-      const int r0 = tensor < 2 ? I * B : J * B;
-      const int grow = min(r0 + row, n - 1);
-      const bf16* src = tensor == 0 ? Q : tensor == 1 ? dO : tensor == 2 ? K : V;
-      load_lds_16(src + hoff + (size_t)grow * D + kp * SKP + half * 8, &sm[st][tensor][p0 * 8]);
-    }
+  // step t's two panels into slot t % R (steps past the end copy the last
+  // one again, so every step issues one copy per lane)
+  const int side = wave / RB, part = wave - side * RB;  // side 0: query rows, 1: key rows
+  auto issue = [&](int t) {
+    t = min(t, T - 1);
+    const bool second = t >= NP;
+    const int kp = second ? t - NP : t;
+    const int p0 = part * 64, p = p0 + lane;
+    const int row = p >> 1, hf = p & 1;
+    const int grow = min((side == 0 ? I * B : J * B) + row, n - 1);
+    const bf16* src = side == 0 ? (second ? dO : Q) : (second ? V : K);
+    sb_copy16(src + hoff + (size_t)grow * D + kp * SKP + hf * 8, &sm[t % R][side][p0 * 8]);
   };
 
   f32x16 s[CB], dp[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) s[cb] = dp[cb] = f32x16{};
 
-  auto compute = [&](int st) {
-    const int qrow = ib * 32 + li;
-    const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sm[st][0][qrow * SKP + h * 8]);
-    const bf16x8 ado = *reinterpret_cast<const bf16x8*>(&sm[st][1][qrow * SKP + h * 8]);
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const int krow = jh * (B / 2) + cb * 32 + li;
-      const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&sm[st][2][krow * SKP + h * 8]);
-      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&sm[st][3][krow * SKP + h * 8]);
-      s[cb] = mfma_bf16_32x32x16(aq, bk, s[cb]);
-      dp[cb] = mfma_bf16_32x32x16(ado, bv, dp[cb]);
-    }
-  };
-
-  constexpr int NP = D / SKP;
-  if constexpr (ST == 2) {
-    load_panel(0, 0);
-    for (int kp = 0; kp < NP; ++kp) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();  // panel kp landed; every wave is done with panel kp-1
-      if (kp + 1 < NP) load_panel(kp + 1, (kp + 1) & 1);
-      compute(kp & 1);
-    }
-  } else {
-    for (int kp = 0; kp < NP; ++kp) {
-      load_panel(kp, 0);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      compute(0);
-      __syncthreads();
+  for (int i = 0; i < DIST; ++i) issue(i);
+  for (int t = 0; t < T; ++t) {
+    sb_wait_vm<DIST - 1>();  // step t's copy is done; the later DIST - 1 may be in flight
+    sb_barrier();            // every lane's copy of step t; slot (t - 1) % R is free
+    issue(t + DIST);
+    const bf16* qs = sm[t % R][0];
+    const bf16* ks = sm[t % R][1];
+    const int qrow = ib * 32 + li;
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(&qs[qrow * SKP + h * 8]);
+    if (t < NP) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int krow = jh * (B / 2) + cb * 32 + li;
+        const bf16x8 bk = *reinterpret_cast<const bf16x8*>(&ks[krow * SKP + h * 8]);
+        s[cb] = mfma_bf16_32x32x16(a, bk, s[cb]);
+      }
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int krow = jh * (B / 2) + cb * 32 + li;
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&ks[krow * SKP + h * 8]);
+        dp[cb] = mfma_bf16_32x32x16(a, bv, dp[cb]);
+      }
     }
   }
+  sb_wait_vm<0>();  // no copy into LDS may outlive the workgroup
 
   // Epilogue.  Accumulator register r of a lane holds query row
   // i0 + 8 (r/4) + 4 h + r%4 and key column j of the lane.
@@ -220,6 +259,14 @@ struct SbJobs {
   SbJob job[2];
 };
 
+// The product kernels' footprint (b^2 + R 2 b 16) may be as large as the
+// scores kernel's (2 b^2 + ST 4 b 16), which decides the tile choice: R =
+// b / 32 + 2 ST ring slots of the two panels, filled R - 1 steps ahead.
+template <int B, int ST>
+struct SbProductRing {
+  static constexpr int R = B / 32 + 2 * ST;
+};
+
 template <int D, int B, int ST, bool A_TR>
 __global__ __launch_bounds__(B * 4) void sb_product(const SbJobs jobs, int n, int nt, int npad,
                                                    int per_job, int total) {
@@ -228,8 +275,9 @@ __global__ __launch_bounds__(B * 4) void sb_product(const SbJobs jobs, int n, in
   constexpr int CB = B / 64;   // 32-column blocks per wave
   constexpr int NDT = D / B;   // column tiles
   constexpr int PANEL = SKP * B;
+  constexpr int R = SbProductRing<B, ST>::R, DIST = R - 1;
   static_assert(NW == 2 * RB, "one wave-load per wave covers both panels");
-  __shared__ __attribute__((aligned(16))) bf16 sm[ST][2][PANEL];  // A panel, Bm panel
+  __shared__ __attribute__((aligned(16))) bf16 sm[R][2][PANEL];  // A panel, Bm panel
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -246,15 +294,19 @@ __global__ __launch_bounds__(B * 4) void sb_product(const SbJobs jobs, int n, in
   const int R0 = T * B, C0 = dt * B;
   const int rb = wave % RB, ch = wave / RB;
 
-  auto load_panel = [&](int kp, int st) {
-    const int k0 = kp * SKP;
+  const int NP = npad / SKP;
+  // panel kp into slot kp % R (panels past the end copy the last one again,
+  // so every step issues one copy per lane)
+  auto issue = [&](int kp) {
+    kp = min(kp, NP - 1);
+    const int k0 = kp * SKP, st = kp % R;
     if (wave < RB) {  // A panel: 2B chunks, RB wave-loads
       if constexpr (A_TR) {
         load_tr_panel<B>(Ah, npad, k0, npad - 1, R0, sm[st][0], wave, lane);
       } else {
         const int p0 = wave * 64, p = p0 + lane;
         const int row = p >> 1, half = p & 1;
-        load_lds_16(Ah + (size_t)(R0 + row) * npad + k0 + half * 8, &sm[st][0][p0 * 8]);
+        sb_copy16(Ah + (size_t)(R0 + row) * npad + k0 + half * 8, &sm[st][0][p0 * 8]);
       }
     } else {
       load_tr_panel<B>(Bh, D, k0, n - 1, C0, sm[st][1], wave - RB, lane);
@@ -279,24 +331,15 @@ __global__ __launch_bounds__(B * 4) void sb_product(const SbJobs jobs, int n, in
     }
   };
 
-  const int NP = npad / SKP;
-  if constexpr (ST == 2) {
-    load_panel(0, 0);
-    for (int kp = 0; kp < NP; ++kp) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (kp + 1 < NP) load_panel(kp + 1, (kp + 1) & 1);
-      compute(kp & 1);
-    }
-  } else {
-    for (int kp = 0; kp < NP; ++kp) {
-      load_panel(kp, 0);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      compute(0);
-      __syncthreads();
-    }
+#pragma unroll
+  for (int i = 0; i < DIST; ++i) issue(i);
+  for (int kp = 0; kp < NP; ++kp) {
+    sb_wait_vm<DIST - 1>();  // panel kp is done; the later DIST - 1 may be in flight
+    sb_barrier();            // every lane's copy of panel kp; slot (kp - 1) % R is free
+    issue(kp + DIST);
+    compute(kp % R);
   }
+  sb_wait_vm<0>();  // no copy into LDS may outlive the workgroup
 
   // acc[cb] register r: column C0 + ch B/2 + 32 cb + 8 (r/4) + 4 h + r%4,
   // output row R0 + rb*32 + l%32.
