@@ -98,6 +98,18 @@ __device__ __forceinline__ void sb_copy16(const void* gsrc, bf16* lds_wave_base)
       : "v"(gsrc), "s"(lds)
       : "memory", "m0");
 }
+// The same with 4 bytes per lane (global_load_lds_dword).
+__device__ __forceinline__ void sb_copy4(const void* gsrc, float* lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
+      __attribute__((address_space(3))) char*)(reinterpret_cast<char*>(lds_wave_base)));
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, off"
+      :
+      : "v"(gsrc), "s"(lds)
+      : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // s_waitcnt with vmcnt = N and the other counters left at their maxima.
@@ -150,6 +162,7 @@ __global__ __launch_bounds__(B * 4) void sb_scores_grads(
   constexpr int R = 2 * ST, DIST = R - 1;
   static_assert(NW == 2 * RB, "one wave-load per wave covers the step's two panels");
   __shared__ __attribute__((aligned(16))) bf16 sm[R][2][PANEL];  // (Q or dO), (K or V)
+  __shared__ __attribute__((aligned(16))) float rowstat[2][B];     // lse, D of the query rows
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -181,6 +194,13 @@ __global__ __launch_bounds__(B * 4) void sb_scores_grads(
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) s[cb] = dp[cb] = f32x16{};
 
+  // the query rows' lse and D go to LDS ahead of the panels (the first
+  // step's wait covers them): waves 0 .. 2 B / 64 - 1 copy 64 values each
+  if (wave < 2 * B / 64) {
+    const int which = wave / (B / 64), r0 = (wave % (B / 64)) * 64;
+    const int i = min(I * B + r0 + lane, n - 1);
+    sb_copy4((which == 0 ? lse : Dv) + (size_t)head * n + i, &rowstat[which][r0]);
+  }
 #pragma unroll
   for (int i = 0; i < DIST; ++i) issue(i);
   for (int t = 0; t < T; ++t) {
@@ -212,28 +232,25 @@ __global__ __launch_bounds__(B * 4) void sb_scores_grads(
   // Epilogue.  Accumulator register r of a lane holds query row
   // i0 + 8 (r/4) + 4 h + r%4 and key column j of the lane.
   const int i0 = I * B + ib * 32;
-  float l2[16], dd[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int i = min(i0 + 8 * (r >> 2) + 4 * h + (r & 3), n - 1);
-    l2[r] = lse[(size_t)head * n + i] * kLog2e;
-    dd[r] = Dv[(size_t)head * n + i];
-  }
+  for (int g = 0; g < 4; ++g) {
+    // rows i0 + 8 g + 4 h + e of this lane's accumulator registers 4 g + e
+    const int ir = ib * 32 + 8 * g + 4 * h;  // row within the tile
+    const f32x4 l2 = *reinterpret_cast<const f32x4*>(&rowstat[0][ir]) * kLog2e;
+    const f32x4 dd = *reinterpret_cast<const f32x4*>(&rowstat[1][ir]);
+    const int i = i0 + 8 * g + 4 * h;
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    const int j = J * B + jh * (B / 2) + cb * 32 + li;
-    const size_t rowoff = ((size_t)head * npad + j) * npad;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int cb = 0; cb < CB; ++cb) {
+      const int j = J * B + jh * (B / 2) + cb * 32 + li;
+      const size_t rowoff = ((size_t)head * npad + j) * npad;
       float p[4], ds[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * g + e;
-        const bool ok = j < n && i0 + 8 * g + 4 * h + e < n;
-        p[e] = ok ? fast_exp2(__builtin_fmaf(s[cb][r], c, -l2[r])) : 0.f;
-        ds[e] = p[e] * (dp[cb][r] - dd[r]);
+        const bool ok = j < n && i + e < n;
+        p[e] = ok ? fast_exp2(__builtin_fmaf(s[cb][r], c, -l2[e])) : 0.f;
+        ds[e] = p[e] * (dp[cb][r] - dd[e]);
       }
-      const int i = i0 + 8 * g + 4 * h;
       *reinterpret_cast<u32x2*>(Pt + rowoff + i) = u32x2{pack_bf16x2(p[0], p[1]),
                                                         pack_bf16x2(p[2], p[3])};
       *reinterpret_cast<u32x2*>(dSt + rowoff + i) = u32x2{pack_bf16x2(ds[0], ds[1]),
