@@ -29,6 +29,8 @@ SIGNATURES = {
     "attn_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _int, _vp]),
     "attn_fwd_onchip_elems": (_i64, [_i64, _int]),
     "attn_fwd_query_block": (_i64, [_i64, _int]),
+    "attn_fwd_budget": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _int, _i64, _vp]),
+    "attn_fwd_budget_onchip_elems": (_i64, [_i64]),
     "attn_fwd_splitk_splits": (_i64, [_i64, _i64, _i64, _i64, _i64]),
     "attn_fwd_splitk_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "attn_fwd_splitk": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _int, _i64,
@@ -138,6 +140,34 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | N
                         lse.data_ptr() if lse is not None else None, bh, n, d, scale,
                         _dtype_code(q), _stream(q, stream))
     _check("attn_fwd", rc)
+    return out, lse
+
+
+def fwd_budget_onchip_elems(d: int) -> int:
+    """On-chip elements of one attn_fwd_budget workgroup (0 = unsupported d)."""
+    return int(lib().attn_fwd_budget_onchip_elems(d))
+
+
+def attn_fwd_budget(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, m_elems: int,
+                    scale: float | None = None, out: torch.Tensor | None = None,
+                    lse: torch.Tensor | bool = True, stream=None):
+    """Fused streaming forward with 32-row query blocks, for an on-chip budget
+    of m_elems elements below d^2. Returns (O, lse)."""
+    _check_inputs(q, k, v)
+    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("Q, K, V must share shape and dtype")
+    bh, n, d = q.shape
+    scale = default_scale(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((bh, n, d), dtype=torch.float32, device=q.device)
+    if lse is True:
+        lse = torch.empty((bh, n), dtype=torch.float32, device=q.device)
+    elif lse is False:
+        lse = None
+    rc = lib().attn_fwd_budget(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               lse.data_ptr() if lse is not None else None, bh, n, d, scale,
+                               _dtype_code(q), int(m_elems), _stream(q, stream))
+    _check("attn_fwd_budget", rc)
     return out, lse
 
 

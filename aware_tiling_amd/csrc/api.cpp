@@ -91,6 +91,24 @@ attn_status attn_fwd(const void* Q, const void* K, const void* V, float* O, floa
                                                 scale, s));
 }
 
+int64_t attn_fwd_budget_onchip_elems(int64_t d) { return at::fused_budget_onchip(d); }
+
+attn_status attn_fwd_budget(const void* Q, const void* K, const void* V, float* O, float* lse,
+                            int64_t bh, int64_t n, int64_t d, float scale, attn_dtype dtype,
+                            int64_t m_elems, void* stream) {
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (!shape_ok(bh, n, d) || !scale_ok(scale) || m_elems <= 0) return ATTN_ERR_INVALID_ARG;
+  if (!at::fused_budget_supported(d)) return ATTN_ERR_UNSUPPORTED;
+  if (at::fused_budget_onchip(d) > m_elems) return ATTN_ERR_UNSUPPORTED;
+  if (bh * ((n + 31) / 32) > INT32_MAX) return ATTN_ERR_INVALID_ARG;  // one workgroup per 32 rows
+  if (bh * n == 0) return ATTN_OK;
+  if (!Q || !K || !V || !O) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return ATTN_ERR_INVALID_ARG;
+  if (lse && !aligned16(lse)) return ATTN_ERR_INVALID_ARG;
+  return launch_status(at::launch_fwd_budget_bf16(Q, K, V, O, lse, bh, n, d, scale,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 namespace {
 
 // Effective split count of attn_fwd_splitk, or 0 if the request is invalid.

@@ -24,6 +24,14 @@ FusedTileInfo fused_f32_tile_info(int64_t d);
 hipError_t launch_fwd_fused_bf16(const void* Q, const void* K, const void* V, float* O,
                                  float* lse, int64_t bh, int64_t n, int64_t d, float scale,
                                  hipStream_t stream);
+// Fused forward with 32-row query blocks and 32-key tiles, four waves each
+// owning a quarter of d (fwd_budget.hip): the fused schedule held to a
+// budget below d^2.
+bool fused_budget_supported(int64_t d);
+int64_t fused_budget_onchip(int64_t d);
+hipError_t launch_fwd_budget_bf16(const void* Q, const void* K, const void* V, float* O,
+                                  float* lse, int64_t bh, int64_t n, int64_t d, float scale,
+                                  hipStream_t stream);
 hipError_t launch_fwd_fused_f32(const float* Q, const float* K, const float* V, float* O,
                                 float* lse, int64_t bh, int64_t n, int64_t d, float scale,
                                 hipStream_t stream);

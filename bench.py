@@ -440,6 +440,25 @@ def secondary(args, at, torch, dev):
                              "fused_ms_same_inputs": round(ms_fu, 4),
                              "fused_tflops": round(w.fwd_flops / (ms_fu * 1e-3) / 1e12, 2),
                              "exp_matrix_bytes": w.bh * w.n * w.n * 2}
+        # both schedules held to the same budget below d^2: the fused one with
+        # 32-row query blocks (K, V read once per block) and the square tiles
+        m_same = at.fwd_budget_onchip_elems(w.d)
+        if m_same > 0 and at.smallcache_tile(w.d, m_same) > 0:
+            need = int(at.lib().attn_fwd_smallcache_workspace_size(w.bh, w.n, w.d, m_same))
+            ws2 = torch.empty(need, dtype=torch.uint8, device=dev)
+            ms_fb, _, _ = time_launches(lambda: at.attn_fwd_budget(
+                q, k, v, m_same, w.scale, out=o, lse=lse), args.steps, args.warmup)
+            ms_sb, _, _ = time_launches(lambda: at.attn_fwd_smallcache(
+                q, k, v, m_same, w.scale, out=o, lse=lse, workspace=ws2), args.steps, args.warmup)
+            res["smallcache"]["same_budget"] = {
+                "m_elems": m_same,
+                "fused_query_rows": 32, "fused_ms": round(ms_fb, 4),
+                "fused_tflops": round(w.fwd_flops / (ms_fb * 1e-3) / 1e12, 2),
+                "fused_kv_bytes": w.bh * (w.n // 32) * 2 * w.n * w.d * 2,
+                "smallcache_tile_b": at.smallcache_tile(w.d, m_same),
+                "smallcache_ms": round(ms_sb, 4),
+                "smallcache_tflops": round(w.fwd_flops / (ms_sb * 1e-3) / 1e12, 2)}
+            del ws2
         del q, k, v, o, lse, ws
     w = WORKLOADS["bwd_bf16_b2h16_n4096_d128"]
     q0 = torch.zeros((1, 64, w.d), dtype=torch.bfloat16, device=dev)

@@ -95,6 +95,34 @@ int64_t attn_fwd_onchip_elems(int64_t d, attn_dtype dtype);
 int64_t attn_fwd_query_block(int64_t d, attn_dtype dtype);
 
 /*
+ * attn_fwd_budget -- the fused streaming forward held to an on-chip budget
+ * below d^2, for comparing the two forward schedules at the same M.
+ *
+ * Follows the exposition's sections "Softmax without storing the score
+ * matrix" and "Large caches: where FlashAttention's I/O comes from": the
+ * same streaming recurrence as attn_fwd, but each workgroup keeps only a
+ * 32-row query block (the smallest the matrix cores take) with 32-key
+ * tiles, so its on-chip footprint fits a budget below d^2 at d = 256 and
+ * K and V are read once per 32 query rows.  The result is the same
+ * function as attn_fwd.
+ *
+ *   m_elems : on-chip budget M in elements (> 0); the call returns
+ *             ATTN_ERR_UNSUPPORTED when attn_fwd_budget_onchip_elems(d)
+ *             exceeds it.
+ *   Other arguments as attn_fwd; bf16 only, d in {128, 256};
+ *   bh * ceil(n / 32) must not exceed 2^31 - 1.
+ */
+attn_status attn_fwd_budget(const void* Q, const void* K, const void* V,
+                            float* O, float* lse, int64_t bh, int64_t n,
+                            int64_t d, float scale, attn_dtype dtype,
+                            int64_t m_elems, void* stream);
+/* On-chip elements of one attn_fwd_budget workgroup at head dimension d
+ * (every buffer counted once whatever its width: the Q and U blocks, (m, l),
+ * two slots each of the K and V tiles, the four partial score tiles and
+ * the summed one); 54,336 at d = 256.  0 for unsupported d. */
+int64_t attn_fwd_budget_onchip_elems(int64_t d);
+
+/*
  * attn_fwd_splitk -- fused forward for rectangular shapes, nq queries against
  * nk keys per head (nq much smaller than nk: decoding, chunked prefill).
  *

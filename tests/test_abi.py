@@ -109,6 +109,25 @@ def test_smallcache_validation(lib):
                                    FAKE, ws, None) == UNSUPPORTED
 
 
+def test_budget_forward_validation(lib):
+    # Q and U blocks 2*32*d, (m, l) 64, two slots of K and V 4*32*d, four partial
+    # score tiles and the summed one 5*32*32
+    assert lib.attn_fwd_budget_onchip_elems(256) == 2 * 32 * 256 + 64 + 4 * 32 * 256 + 5 * 1024
+    assert lib.attn_fwd_budget_onchip_elems(256) == 54336 < 256 * 256
+    assert lib.attn_fwd_budget_onchip_elems(128) == 29760
+    assert lib.attn_fwd_budget_onchip_elems(64) == 0
+    call = lambda m=54336, d=256, dtype=BF16, q=FAKE, bh=8, n=4096, scale=0.0625: \
+        lib.attn_fwd_budget(q, FAKE, FAKE, FAKE, None, bh, n, d, scale, dtype, m, None)
+    assert call(m=54335) == UNSUPPORTED  # the tile does not fit the budget
+    assert call(dtype=F32) == UNSUPPORTED
+    assert call(d=64) == UNSUPPORTED
+    assert call(m=0) == INVALID
+    assert call(scale=-1.0) == INVALID
+    assert call(q=None) == INVALID
+    assert call(bh=1 << 20, n=1 << 20) == INVALID  # more workgroups than a grid holds
+    assert call(q=None, n=0) == OK  # empty: no launch, no pointer needed
+
+
 def test_bwd_validation(lib):
     ws = lib.attn_bwd_workspace_size(2, 512, 128)
     if lib.attn_bwd_workspace_size(2, 512, 128) == 0 and lib.attn_bwd(
