@@ -31,6 +31,7 @@ Reported (one JSON line on stdout):
                timed the same way, when built (not part of `value`).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-secondary]
+                       [--legs a,b] [--secondary-only]
        python bench.py --calibrate-copy          (copy kernel for counter scaling)
        python bench.py --summarize-counters DIR  (write the traffic summary)
        python bench.py --tile-sweep [--steps K]   (fused forward at B_r x B_c shapes)
@@ -283,6 +284,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--legs", default=None,
+                    help="comma-separated secondary legs to run (smallcache, backward, "
+                         "smallcache_backward, blocksparse, splitk); default all")
+    ap.add_argument("--secondary-only", action="store_true",
+                    help="skip the headline and print only the secondary legs' JSON")
     ap.add_argument("--tile-sweep", action="store_true",
                     help="time every query-block x key-tile shape of the fused forward on the "
                          "headline workload (one JSON line per shape) and exit")
@@ -313,6 +319,9 @@ def main():
         return
     if args.tile_sweep:
         tile_sweep(args, at, torch, dev)
+        return
+    if args.secondary_only:
+        print(json.dumps({"secondary": secondary(args, at, torch, dev)}), flush=True)
         return
     w = WORKLOADS[HEADLINE]
     print(f"[bench] inputs {w.name}", file=sys.stderr, flush=True)
@@ -420,9 +429,14 @@ def secondary(args, at, torch, dev):
     from aware_tiling_amd.inputs import WORKLOADS, workload_inputs
 
     res = {}
+    legs = set(args.legs.split(",")) if args.legs else None
+
+    def want(name):
+        return legs is None or name in legs
+
     w = WORKLOADS["smallcache_bf16_b1h8_n4096_d256"]
     m_elems = 49152  # 3/4 of d^2: the small-cache regime M < d^2
-    if at.smallcache_tile(w.d, m_elems) > 0:
+    if want("smallcache") and at.smallcache_tile(w.d, m_elems) > 0:
         print(f"[bench] timing {w.name}", file=sys.stderr, flush=True)
         q, k, v = (t.to(dev) for t in workload_inputs(w))
         o = torch.empty((w.bh, w.n, w.d), dtype=torch.float32, device=dev)
@@ -468,7 +482,7 @@ def secondary(args, at, torch, dev):
         has_bwd = True
     except at.AttnError:
         has_bwd = False
-    if has_bwd:
+    if want("backward") and has_bwd:
         print(f"[bench] timing {w.name}", file=sys.stderr, flush=True)
         q, k, v, do = (t.to(dev) for t in workload_inputs(w))
         o, lse = at.attn_fwd(q, k, v, w.scale)
@@ -481,8 +495,9 @@ def secondary(args, at, torch, dev):
         fl = 10.0 * w.n * w.n * w.d * w.bh  # 2 products recomputed-free count: 5 GEMMs
         res["backward"] = {"workload": w.name, "ms": round(ms, 4),
                            "tflops_at_10N2d": round(fl / (ms * 1e-3) / 1e12, 2)}
-    for name, m_sc in (("bwd_smallcache_bf16_b1h8_n4096_d256", 49152),
-                       ("bwd_bf16_b2h16_n4096_d128", 12288)):
+    for name, m_sc in ((("bwd_smallcache_bf16_b1h8_n4096_d256", 49152),
+                        ("bwd_bf16_b2h16_n4096_d128", 12288))
+                       if want("smallcache_backward") else ()):
         w = WORKLOADS[name]
         b = at.bwd_smallcache_tile(w.d, m_sc)
         print(f"[bench] timing small-cache backward {w.name} M={m_sc}", file=sys.stderr,
@@ -511,33 +526,35 @@ def secondary(args, at, torch, dev):
         torch.cuda.empty_cache()
     from aware_tiling_amd.inputs import make_block_mask
 
-    w = WORKLOADS["sparse_bf16_b1h32_n16384_d128_keep25"]
-    print(f"[bench] timing {w.name}", file=sys.stderr, flush=True)
-    q, k, v = (t.to(dev) for t in workload_inputs(w))
-    nb = -(-w.n // at.SPARSE_BLOCK)
-    mask = make_block_mask(w.bh, nb, w.density, w.seed + 1000).to(dev)
-    o = torch.empty((w.bh, w.n, w.d), dtype=torch.float32, device=dev)
-    lse = torch.empty((w.bh, w.n), dtype=torch.float32, device=dev)
-    need = int(at.lib().attn_fwd_blocksparse_workspace_size(w.bh, w.n, w.bh))
-    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    ms, _, _ = time_launches(lambda: at.attn_fwd_blocksparse(q, k, v, mask, w.scale, out=o,
-                                                             lse=lse, workspace=ws),
-                             args.steps, args.warmup)
-    ms_dense, _, _ = time_launches(lambda: at.attn_fwd(q, k, v, w.scale, out=o, lse=lse),
-                                   args.steps, args.warmup)
-    # kept query-key pairs: per kept block, its valid queries x valid keys
-    sizes = torch.full((nb,), at.SPARSE_BLOCK, dtype=torch.float64)
-    sizes[-1] = w.n - (nb - 1) * at.SPARSE_BLOCK
-    pairs = float(torch.einsum("hij,i,j->", mask.cpu().double(), sizes, sizes))
-    fl = 4.0 * w.d * pairs
-    kept = float(mask.float().mean())
-    res["blocksparse"] = {
-        "workload": w.name, "kept_block_fraction": round(kept, 4), "ms": round(ms, 4),
-        "tflops_on_kept_pairs": round(fl / (ms * 1e-3) / 1e12, 2),
-        "dense_ms_same_inputs": round(ms_dense, 4),
-        "time_fraction_of_dense": round(ms / ms_dense, 4)}
-    del q, k, v, o, lse, ws, mask
-    for name in ("decode_bf16_b8h32_q1_k16384_d128", "chunk_bf16_b1h32_q1024_k16384_d128"):
+    if want("blocksparse"):
+        w = WORKLOADS["sparse_bf16_b1h32_n16384_d128_keep25"]
+        print(f"[bench] timing {w.name}", file=sys.stderr, flush=True)
+        q, k, v = (t.to(dev) for t in workload_inputs(w))
+        nb = -(-w.n // at.SPARSE_BLOCK)
+        mask = make_block_mask(w.bh, nb, w.density, w.seed + 1000).to(dev)
+        o = torch.empty((w.bh, w.n, w.d), dtype=torch.float32, device=dev)
+        lse = torch.empty((w.bh, w.n), dtype=torch.float32, device=dev)
+        need = int(at.lib().attn_fwd_blocksparse_workspace_size(w.bh, w.n, w.bh))
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        ms, _, _ = time_launches(lambda: at.attn_fwd_blocksparse(q, k, v, mask, w.scale, out=o,
+                                                                 lse=lse, workspace=ws),
+                                 args.steps, args.warmup)
+        ms_dense, _, _ = time_launches(lambda: at.attn_fwd(q, k, v, w.scale, out=o, lse=lse),
+                                       args.steps, args.warmup)
+        # kept query-key pairs: per kept block, its valid queries x valid keys
+        sizes = torch.full((nb,), at.SPARSE_BLOCK, dtype=torch.float64)
+        sizes[-1] = w.n - (nb - 1) * at.SPARSE_BLOCK
+        pairs = float(torch.einsum("hij,i,j->", mask.cpu().double(), sizes, sizes))
+        fl = 4.0 * w.d * pairs
+        kept = float(mask.float().mean())
+        res["blocksparse"] = {
+            "workload": w.name, "kept_block_fraction": round(kept, 4), "ms": round(ms, 4),
+            "tflops_on_kept_pairs": round(fl / (ms * 1e-3) / 1e12, 2),
+            "dense_ms_same_inputs": round(ms_dense, 4),
+            "time_fraction_of_dense": round(ms / ms_dense, 4)}
+        del q, k, v, o, lse, ws, mask
+    for name in (("decode_bf16_b8h32_q1_k16384_d128", "chunk_bf16_b1h32_q1024_k16384_d128")
+                 if want("splitk") else ()):
         w = WORKLOADS[name]
         print(f"[bench] timing {w.name}", file=sys.stderr, flush=True)
         q, k, v = (t.to(dev) for t in workload_inputs(w))
