@@ -1875,6 +1875,9 @@ const FusedEntry* registry(int& count) {
       direct<128, 8, 32, false, 3>("n8x32w3"),
       basic<128, 1, 8, 64>("1x8x64"),
       // head dimension 256
+      direct<256, 4, 32, true, 1, false, 2, 0, true>("d4x32b"),
+      direct<256, 4, 32, true, 1>("d4x32"),
+      direct<256, 2, 32, true, 1, false, 2, 0, true>("d2x32b"),
       basic<256, 1, 4, 32>("1x4x32"),
   };
   count = (int)(sizeof(table) / sizeof(table[0]));

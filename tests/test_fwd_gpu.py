@@ -61,7 +61,7 @@ def test_fwd_matches_oracle_small(bh, n, d, dtype, seed, q_mult):
 TILES = {64: ["g2x64p", "g2x64", "g1x64", "t8x64", "d8x64", "2x8x32"],
          128: ["d8x64", "d8x64g", "d8x64q1", "d8x64q2", "r64c32", "r64c64", "r128c32", "r128c64",
                "r256c32", "r256c64", "g1x64p", "g1x64", "w1x8x64", "s8x64", "n8x32w3", "1x8x64"],
-         256: ["1x4x32"]}
+         256: ["d4x32b", "d4x32", "d2x32b", "1x4x32"]}
 
 
 @pytest.mark.parametrize("d,tile", [(d, t) for d, ts in TILES.items() for t in ts])
