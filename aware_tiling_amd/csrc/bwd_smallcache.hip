@@ -149,7 +149,7 @@ __device__ __forceinline__ void load_tr_panel(const bf16* src, int64_t stride, i
 // S = Q_I K_J^T is accumulated first, over d in panels of 16 columns, then
 // dP = dO_I V_J^T: each step copies two panels (Q and K, or dO and V), so the
 // ST stages of four panels the footprint counts make R = 2 ST ring slots of
-// two, filled R - 1 steps ahead.
+// two.
 template <int D, int B, int ST>
 __global__ __launch_bounds__(B * 4) void sb_scores_grads(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(B * 4) void sb_scores_grads(
   constexpr int RB = B / 32;  // 32-row query blocks (and wave-loads per tensor panel)
   constexpr int CB = B / 64;  // 32-key blocks per wave
   constexpr int PANEL = B * SKP;
-  constexpr int R = 2 * ST, DIST = R - 1;
+  constexpr int R = 2 * ST;
   static_assert(NW == 2 * RB, "one wave-load per wave covers the step's two panels");
   __shared__ __attribute__((aligned(16))) bf16 sm[R][2][PANEL];  // (Q or dO), (K or V)
   __shared__ __attribute__((aligned(16))) float rowstat[2][B];     // lse, D of the query rows
@@ -170,7 +170,25 @@ __global__ __launch_bounds__(B * 4) void sb_scores_grads(
   const int tile = xcd_remap(blockIdx.x, total);
   const int head = tile / (nt * nt);
   const int rem = tile - head * nt * nt;
-  const int J = rem / nt, I = rem - J * nt;  // neighbours share the key tile
+  // b = 128: grouped order, consecutive tiles run over a group of 8 key
+  // tiles for each query tile in turn, so the workgroups resident on one
+  // XCD at a time read about 8 + 8 row panels of each tensor, which stay in
+  // its L2 (in key-major order they read every query tile's panels at once
+  // and the streaming P^T / dS^T writes evict them: 6x the HBM reads at
+  // d = 256).  b = 64: key-major order, neighbours share the key tile (the
+  // grouped order reads more there, with four times the resident tiles).
+  int J, I;
+  if constexpr (B >= 128) {
+    constexpr int GROUP = 8;
+    const int g0 = (rem / (GROUP * nt)) * GROUP;
+    const int gsize = min(nt - g0, GROUP);
+    const int local = rem - g0 * nt;
+    J = g0 + local % gsize;
+    I = local / gsize;
+  } else {
+    J = rem / nt;
+    I = rem - J * nt;
+  }
   const size_t hoff = (size_t)head * n * D;
   const int ib = wave % RB, jh = wave / RB;
   constexpr int NP = D / SKP;
@@ -201,12 +219,7 @@ __global__ __launch_bounds__(B * 4) void sb_scores_grads(
     const int i = min(I * B + r0 + lane, n - 1);
     sb_copy4((which == 0 ? lse : Dv) + (size_t)head * n + i, &rowstat[which][r0]);
   }
-#pragma unroll
-  for (int i = 0; i < DIST; ++i) issue(i);
-  for (int t = 0; t < T; ++t) {
-    sb_wait_vm<DIST - 1>();  // step t's copy is done; the later DIST - 1 may be in flight
-    sb_barrier();            // every lane's copy of step t; slot (t - 1) % R is free
-    issue(t + DIST);
+  auto compute = [&](int t) {
     const bf16* qs = sm[t % R][0];
     const bf16* ks = sm[t % R][1];
     const int qrow = ib * 32 + li;
@@ -226,12 +239,33 @@ __global__ __launch_bounds__(B * 4) void sb_scores_grads(
         dp[cb] = mfma_bf16_32x32x16(a, bv, dp[cb]);
       }
     }
+  };
+  // PPS steps per barrier (two when the ring has four slots: half the
+  // barriers, two steps in flight while two are used)
+  constexpr int PPS = R >= 4 ? 2 : 1;
+  constexpr int AHEAD = R - PPS;  // steps issued ahead of the ones being used
+  static_assert(T % PPS == 0, "whole barrier groups");
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) issue(i);
+  for (int t = 0; t < T; t += PPS) {
+    sb_wait_vm<AHEAD - PPS>();  // steps t .. t+PPS-1 are done; later ones may be in flight
+    sb_barrier();               // every lane's copies; the slots of steps t-PPS.. are free
+#pragma unroll
+    for (int p = 0; p < PPS; ++p) issue(t + AHEAD + p);
+#pragma unroll
+    for (int p = 0; p < PPS; ++p) compute(t + p);
   }
   sb_wait_vm<0>();  // no copy into LDS may outlive the workgroup
 
   // Epilogue.  Accumulator register r of a lane holds query row
-  // i0 + 8 (r/4) + 4 h + r%4 and key column j of the lane.
+  // i0 + 8 (r/4) + 4 h + r%4 and key column j of the lane.  P and dS are
+  // packed to bf16 in registers; when the panel slots (free now) hold a
+  // b x b tile, each tile goes through them so that the P^T / dS^T rows
+  // leave as whole 16-byte lane stores, four 2b-byte rows per wave store,
+  // instead of 8-byte pieces of 32 rows (the footprint does not grow); else
+  // (b = 128 with one stage) the pieces are stored directly.
   const int i0 = I * B + ib * 32;
+  uint32_t pp[CB][4][2], pd[CB][4][2];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     // rows i0 + 8 g + 4 h + e of this lane's accumulator registers 4 g + e
@@ -242,7 +276,6 @@ __global__ __launch_bounds__(B * 4) void sb_scores_grads(
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const int j = J * B + jh * (B / 2) + cb * 32 + li;
-      const size_t rowoff = ((size_t)head * npad + j) * npad;
       float p[4], ds[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -251,12 +284,53 @@ __global__ __launch_bounds__(B * 4) void sb_scores_grads(
         p[e] = ok ? fast_exp2(__builtin_fmaf(s[cb][r], c, -l2[e])) : 0.f;
         ds[e] = p[e] * (dp[cb][r] - dd[e]);
       }
-      *reinterpret_cast<u32x2*>(Pt + rowoff + i) = u32x2{pack_bf16x2(p[0], p[1]),
-                                                        pack_bf16x2(p[2], p[3])};
-      *reinterpret_cast<u32x2*>(dSt + rowoff + i) = u32x2{pack_bf16x2(ds[0], ds[1]),
-                                                         pack_bf16x2(ds[2], ds[3])};
+      pp[cb][g][0] = pack_bf16x2(p[0], p[1]);
+      pp[cb][g][1] = pack_bf16x2(p[2], p[3]);
+      pd[cb][g][0] = pack_bf16x2(ds[0], ds[1]);
+      pd[cb][g][1] = pack_bf16x2(ds[2], ds[3]);
     }
   }
+  if constexpr (sizeof(sm) < (size_t)B * B * 2) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int j = J * B + jh * (B / 2) + cb * 32 + li;
+        const size_t off = ((size_t)head * npad + j) * npad + i0 + 8 * g + 4 * h;
+        *reinterpret_cast<u32x2*>(Pt + off) = u32x2{pp[cb][g][0], pp[cb][g][1]};
+        *reinterpret_cast<u32x2*>(dSt + off) = u32x2{pd[cb][g][0], pd[cb][g][1]};
+      }
+    return;
+  }
+  // the b x b tile as [key row][query], 16-byte chunks swizzled by row
+  bf16* tileb = &sm[0][0][0];
+  constexpr int CPT = B / 8;  // 16-byte chunks per tile row
+  auto to_global = [&](const uint32_t (&v)[CB][4][2], bf16* dst) {
+    sb_barrier();  // the slots (or the previous tile) are no longer read
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int row = jh * (B / 2) + cb * 32 + li;  // key within the tile
+        const int col = ib * 32 + 8 * g + 4 * h;      // query within the tile
+        const int phys = (col >> 3) ^ chunk_swizzle<B * 2>(row);
+        *reinterpret_cast<u32x2*>(tileb + row * B + phys * 8 + (col & 7)) =
+            u32x2{v[cb][g][0], v[cb][g][1]};
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this lane's tile writes are done
+    sb_barrier();
+#pragma unroll
+    for (int it = 0; it < B * CPT / (B * 4); ++it) {
+      const int x = tid + it * B * 4;
+      const int row = x / CPT, chunk = x % CPT;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(
+          tileb + row * B + ((chunk ^ chunk_swizzle<B * 2>(row)) * 8));
+      *reinterpret_cast<u32x4*>(dst + ((size_t)head * npad + J * B + row) * npad + I * B +
+                                chunk * 8) = val;
+    }
+  };
+  to_global(pp, Pt);
+  to_global(pd, dSt);
 }
 
 // ---------------------------------------------------------------------------
