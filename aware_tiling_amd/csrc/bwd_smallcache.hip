@@ -33,7 +33,11 @@
 // owns one output row and stores four consecutive columns at once.
 //
 // Workspace (256-byte aligned pieces): D [bh][n] fp32, then P^T and dS^T,
-// each [bh][npad][npad] bf16 with npad = ceil(n/b) b.
+// each bh npad^2 bf16 with npad = ceil(n/b) b, stored panel-major:
+// [head][key tile][16-query panel][b keys][16 queries].  A b x 16 panel of
+// the dV / dK products is then 4 KB of contiguous memory, a 16 x b panel of
+// the dQ product b/16 contiguous pieces of 512 bytes, and a b x b tile of
+// the scores kernel 2 b^2 contiguous bytes.
 #include "device_common.h"
 #include "launch.h"
 
@@ -60,6 +64,13 @@ SbLayout sb_layout(int64_t bh, int64_t n, int64_t b) {
   L.s_off = L.p_off + mat;
   L.total = L.s_off + mat;
   return L;
+}
+
+// Element offset of (key j, query i) in a panel-major P^T / dS^T matrix.
+template <int B>
+__device__ __forceinline__ size_t pt_offset(int head, int j, int i, int nt, int npad) {
+  return (((size_t)head * nt + j / B) * (size_t)(npad / 16) + (size_t)(i / 16)) * (B * 16) +
+         (size_t)(j % B) * 16 + (i % 16);
 }
 
 // Transposed operand (32 columns x 16 panel rows, natural k order) from an
@@ -296,7 +307,7 @@ __global__ __launch_bounds__(B * 4) void sb_scores_grads(
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int j = J * B + jh * (B / 2) + cb * 32 + li;
-        const size_t off = ((size_t)head * npad + j) * npad + i0 + 8 * g + 4 * h;
+        const size_t off = pt_offset<B>(head, j, i0 + 8 * g + 4 * h, nt, npad);
         *reinterpret_cast<u32x2*>(Pt + off) = u32x2{pp[cb][g][0], pp[cb][g][1]};
         *reinterpret_cast<u32x2*>(dSt + off) = u32x2{pd[cb][g][0], pd[cb][g][1]};
       }
@@ -319,14 +330,16 @@ __global__ __launch_bounds__(B * 4) void sb_scores_grads(
       }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this lane's tile writes are done
     sb_barrier();
+    // the tile is one contiguous region [16-query panel q][key r][16
+    // queries]: 16-byte chunk x holds panel q = x / 2b, key r, half c
+    bf16* region = dst + pt_offset<B>(head, J * B, I * B, nt, npad);
 #pragma unroll
     for (int it = 0; it < B * CPT / (B * 4); ++it) {
       const int x = tid + it * B * 4;
-      const int row = x / CPT, chunk = x % CPT;
+      const int q = x / (2 * B), r = (x % (2 * B)) >> 1, c = x & 1;
       const u32x4 val = *reinterpret_cast<const u32x4*>(
-          tileb + row * B + ((chunk ^ chunk_swizzle<B * 2>(row)) * 8));
-      *reinterpret_cast<u32x4*>(dst + ((size_t)head * npad + J * B + row) * npad + I * B +
-                                chunk * 8) = val;
+          tileb + r * B + (((2 * q + c) ^ chunk_swizzle<B * 2>(r)) * 8));
+      *reinterpret_cast<u32x4*>(region + (size_t)x * 8) = val;
     }
   };
   to_global(pp, Pt);
@@ -335,9 +348,9 @@ __global__ __launch_bounds__(B * 4) void sb_scores_grads(
 
 // ---------------------------------------------------------------------------
 // 2/3. Out[r][d] = scale sum_k A(r, k) Bm[k][d] over k < npad, for b x b
-// output tiles.  A is stored row-major [r][k] (A_TR false: P^T or dS^T with
-// r = key) or key-major [k][r] (A_TR true: dS^T read as dS, r = query); Bm
-// is [n][D] (dO, Q or K).  Up to two jobs share one launch.
+// output tiles.  A is P^T or dS^T in the panel-major layout, read with
+// r = key (A_TR false: dV, dK) or with r = query (A_TR true: dS^T read as
+// dS for dQ); Bm is [n][D] (dO, Q or K).  Up to two jobs share one launch.
 
 struct SbJob {
   const bf16* A;
@@ -380,7 +393,7 @@ __global__ __launch_bounds__(B * 4) void sb_product(const SbJobs jobs, int n, in
   const int rem2 = rem - head * nt * NDT;
   const int T = rem2 / NDT, dt = rem2 - T * NDT;
   const SbJob job = jb == 0 ? jobs.job[0] : jobs.job[1];
-  const bf16* Ah = job.A + (size_t)head * npad * npad;
+  const bf16* A = job.A;
   const bf16* Bh = job.Bm + (size_t)head * n * D;
   const int R0 = T * B, C0 = dt * B;
   const int rb = wave % RB, ch = wave / RB;
@@ -393,11 +406,18 @@ __global__ __launch_bounds__(B * 4) void sb_product(const SbJobs jobs, int n, in
     const int k0 = kp * SKP, st = kp % R;
     if (wave < RB) {  // A panel: 2B chunks, RB wave-loads
       if constexpr (A_TR) {
-        load_tr_panel<B>(Ah, npad, k0, npad - 1, R0, sm[st][0], wave, lane);
-      } else {
+        // keys k0 .. k0+15 x queries R0 .. R0+b-1, stored [16][b] with the
+        // transposed-read swizzle; chunk p: key row p / (b/8), 8 queries
+        constexpr int CPR = B / 8;
         const int p0 = wave * 64, p = p0 + lane;
-        const int row = p >> 1, half = p & 1;
-        sb_copy16(Ah + (size_t)(R0 + row) * npad + k0 + half * 8, &sm[st][0][p0 * 8]);
+        const int row = p / CPR, phys = p % CPR;
+        const int logical = phys ^ vtr_swizzle<B * 2>(row);
+        sb_copy16(A + pt_offset<B>(head, k0 + row, R0 + logical * 8, nt, npad),
+                  &sm[st][0][p0 * 8]);
+      } else {
+        // keys R0 .. R0+b-1 x queries k0 .. k0+15: one contiguous 4 KB panel
+        const int p0 = wave * 64, p = p0 + lane;
+        sb_copy16(A + pt_offset<B>(head, R0, k0, nt, npad) + (size_t)p * 8, &sm[st][0][p0 * 8]);
       }
     } else {
       load_tr_panel<B>(Bh, D, k0, n - 1, C0, sm[st][1], wave - RB, lane);
