@@ -476,7 +476,8 @@ hipError_t launch(const void* Q, const void* K, const void* V, float* O, float* 
 
 }  // namespace
 
-bool smallcache_supported(int64_t d) { return d == 64 || d == 128 || d == 256; }
+// d = 64 is not offered: no supported tile has a footprint below d^2 = 4096.
+bool smallcache_supported(int64_t d) { return d == 128 || d == 256; }
 
 int64_t smallcache_onchip_elems(int64_t b) { return (b == 64 || b == 128) ? footprint(b, 256) : 0; }
 
@@ -494,8 +495,6 @@ hipError_t launch_fwd_smallcache_bf16(const void* Q, const void* K, const void* 
                                       float* lse, int64_t bh, int64_t n, int64_t d, float scale,
                                       int64_t b, void* workspace, hipStream_t stream) {
   switch (d * 1000 + b) {
-    case 64 * 1000 + 64: return launch<64, 64>(Q, K, V, O, lse, bh, n, scale, workspace, stream);
-    case 64 * 1000 + 128: return launch<64, 128>(Q, K, V, O, lse, bh, n, scale, workspace, stream);
     case 128 * 1000 + 64: return launch<128, 64>(Q, K, V, O, lse, bh, n, scale, workspace, stream);
     case 128 * 1000 + 128:
       return launch<128, 128>(Q, K, V, O, lse, bh, n, scale, workspace, stream);

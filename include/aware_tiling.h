@@ -219,7 +219,8 @@ attn_status attn_fwd_blocksparse(const void* Q, const void* K, const void* V,
  *   workspace, workspace_bytes : device scratch of at least
  *             attn_fwd_smallcache_workspace_size(bh, n, d, m_elems) bytes,
  *             256-byte aligned.  Its contents on return are unspecified.
- *   Other arguments as attn_fwd; bf16 only, d in {64, 128, 256}.
+ *   Other arguments as attn_fwd; bf16 only, d in {128, 256} (at d = 64 no
+ *             tile fits below d^2: ATTN_ERR_UNSUPPORTED).
  */
 size_t attn_fwd_smallcache_workspace_size(int64_t bh, int64_t n, int64_t d,
                                           int64_t m_elems);
