@@ -30,8 +30,10 @@
 //     deterministic.
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 #include "device_common.h"
+#include "lds_dma.h"
 #include "launch.h"
 
 namespace at {
@@ -416,7 +418,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq(
 // ---------------------------------------------------------------------------
 // Second-generation kernels (default).  Tiles of Q and dO (dK/dV kernel) and
 // of K and V (dQ kernel) go global -> LDS with global_load_lds_dwordx4 and
-// stay row-major; the transposed operands (Q^T, dO^T, K^T) come from
+// stay row-major.  In the default kernels these copies are issued from
+// inline assembly (dma16), so that the next tile's copies stay in flight
+// while the current tile is read and are waited for only at the end of the
+// step.  The transposed operands (Q^T, dO^T, K^T) come from
 // ds_read_b64_tr_b16 on the same tiles, whose swizzle (dual_swizzle) keeps
 // both the row-wise and the transposed reads free of bank conflicts.  No
 // staging registers and no vector-ALU transposition, so two waves fit per
@@ -425,7 +430,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq(
 
 namespace {
 
-template <int D>
+template <int D, bool ASM = false>
 __device__ __forceinline__ void tile_load_lds(const bf16* src, bf16* dst, int t, int rows_per_tile,
                                               int n, int wave, int lane, int wave_chunks,
                                               int insts, bool dual) {
@@ -437,7 +442,10 @@ __device__ __forceinline__ void tile_load_lds(const bf16* src, bf16* dst, int t,
     const int row = p / CPR, phys = p % CPR;
     const int logical = phys ^ (dual ? dual_swizzle<D * 2>(row) : chunk_swizzle<D * 2>(row));
     const int grow = min(rbase + row, n - 1);
-    load_lds_16(src + (size_t)grow * D + logical * 8, dst + p0 * 8);
+    if constexpr (ASM)
+      dma16(src + (size_t)grow * D + logical * 8, dst + p0 * 8);
+    else
+      load_lds_16(src + (size_t)grow * D + logical * 8, dst + p0 * 8);
   }
 }
 
@@ -477,7 +485,7 @@ struct Dkdv2Cfg {
   static_assert(CHUNKS % (NW * 64) == 0, "tile must split into whole wave loads");
 };
 
-template <int D, int NW>
+template <int D, int NW, bool PF, bool VL>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv2(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ Dg,
@@ -499,13 +507,31 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv2(
   const float* Dh = Dg + (size_t)head * n;
   const int key = kblk * C::BKV + wave * 32 + li;
 
-  bf16x8 kreg[D / 16], vreg[D / 16];
+  // K rows of the wave's 32 keys stay in registers (B operand of S).  V rows
+  // (B operand of dP) stay in registers too, or with VL in a wave-private
+  // LDS region, which frees 32 registers per lane at d = 128 for reading
+  // operands ahead.  Keys past n: K = 0 in registers, V rows clamped to n-1
+  // in LDS; either way only the unstored dK/dV rows of those keys see them.
+  __shared__ __attribute__((aligned(1024))) bf16 vtile[VL ? NW * 32 * D : 8];
+  bf16* Vw = vtile + (VL ? wave * 32 * D : 0);
+  bf16x8 kreg[D / 16], vreg[VL ? 1 : D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
     kreg[kk] = key < n ? *reinterpret_cast<const bf16x8*>(Kh + (size_t)key * D + 16 * kk + 8 * h)
                        : bf16x8{};
-    vreg[kk] = key < n ? *reinterpret_cast<const bf16x8*>(Vh + (size_t)key * D + 16 * kk + 8 * h)
-                       : bf16x8{};
+    if constexpr (!VL)
+      vreg[kk] = key < n ? *reinterpret_cast<const bf16x8*>(Vh + (size_t)key * D + 16 * kk + 8 * h)
+                         : bf16x8{};
+  }
+  if constexpr (VL) {
+    constexpr int RC = D / 8;  // 16-byte chunks per row
+#pragma unroll
+    for (int it = 0; it < 32 * RC / 64; ++it) {
+      const int p = it * 64 + lane, row = p / RC, phys = p % RC;
+      const int logical = phys ^ chunk_swizzle<D * 2>(row);
+      const int vrow = min(kblk * C::BKV + wave * 32 + row, n - 1);
+      load_lds_16(Vh + (size_t)vrow * D + logical * 8, Vw + it * 64 * 8);
+    }
   }
   f32x16 dkt[D / 32], dvt[D / 32];
 #pragma unroll
@@ -529,18 +555,33 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv2(
 #pragma unroll
       for (int it = 0; it < C::INSTS; ++it) {
         const int p0 = wave * C::WAVE_CHUNKS + it * 64;
-        load_lds_16(qb + toff[it], tiles[buf] + p0 * 8);
-        load_lds_16(gb + toff[it], tiles[buf] + C::TILE + p0 * 8);
+        if constexpr (PF) {
+          dma16(qb + toff[it], tiles[buf] + p0 * 8);
+          dma16(gb + toff[it], tiles[buf] + C::TILE + p0 * 8);
+        } else {
+          load_lds_16(qb + toff[it], tiles[buf] + p0 * 8);
+          load_lds_16(gb + toff[it], tiles[buf] + C::TILE + p0 * 8);
+        }
       }
     } else {
-      tile_load_lds<D>(Qh, tiles[buf], i, BQ, n, wave, lane, C::WAVE_CHUNKS, C::INSTS, true);
-      tile_load_lds<D>(dOh, tiles[buf] + C::TILE, i, BQ, n, wave, lane, C::WAVE_CHUNKS, C::INSTS,
-                       true);
+      tile_load_lds<D, PF>(Qh, tiles[buf], i, BQ, n, wave, lane, C::WAVE_CHUNKS, C::INSTS, true);
+      tile_load_lds<D, PF>(dOh, tiles[buf] + C::TILE, i, BQ, n, wave, lane, C::WAVE_CHUNKS,
+                           C::INSTS, true);
     }
     if (wave * 64 < 2 * BQ) {  // whole waves: 2 BQ is a multiple of 64
+      // A query row past n (a clamped copy of row n-1) gets lse2 = +inf,
+      // so its weights 2^(S c - lse2) are exactly 0 and it adds nothing to
+      // dV or dK, with no per-element mask in the loop.  Its D stays the
+      // clamped row's (finite), and 0 x finite = 0 in dS.
       const int which = tid / BQ, r = tid - which * BQ;
       const int qrow = min(i * BQ + r, n - 1);
-      load_lds_4((which == 0 ? lseh : Dh) + qrow, &stats[buf][wave * 64]);
+      if (which == 0 && i * BQ + r >= n) {
+        stats[buf][tid] = __builtin_inff();
+      } else if constexpr (PF) {
+        dma4((which == 0 ? lseh : Dh) + qrow, &stats[buf][wave * 64]);
+      } else {
+        load_lds_4((which == 0 ? lseh : Dh) + qrow, &stats[buf][wave * 64]);
+      }
     }
   };
 
@@ -553,7 +594,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv2(
     if (i + 1 < nqt) load(i + 1, buf ^ 1);
     const bf16* Qs = tiles[buf];
     const bf16* dOs = tiles[buf] + C::TILE;
-    const bool tailq = (i + 1) * BQ > n;  // rows past n (clamped copies) get P = 0
     // Opaque copies of the lane index: the LDS addresses derived from them
     // are recomputed each iteration (a few integer ops) rather than held in
     // registers across the loop, which would not fit.
@@ -564,20 +604,47 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv2(
       // S = Q K^T (32 queries x 32 keys per wave), P in bf16, dV^T += dO^T P;
       // then dP = dO V^T, dS = P o (dP - D) from the same bf16 P, and
       // dK^T += Q^T dS.  Only one score-sized accumulator is live at a time.
+      // With PF the LDS operands of the 2 (D/16 + D/16) MFMAs are read AH
+      // MFMAs ahead of their use, in one sequence across the four products,
+      // so an MFMA does not wait for the read that feeds it.
+      constexpr int NKK = D / 16, NDB = D / 32;
+      constexpr int NA = 2 * NKK + 4 * NDB;
+      constexpr int AH = PF ? 2 : 0;
+      bf16x8 a[NA];
+      auto fetch = [&](int t) {
+        if (t < NKK) {
+          a[t] = row_operand<D>(Qs, qb * 32 + lio, 2 * t + h, true);
+        } else if (t < NKK + 2 * NDB) {
+          const int u = t - NKK;
+          a[t] = tr_operand<D>(dOs, 2 * qb + u / NDB, u % NDB, laneo);
+        } else if (t < 2 * NKK + 2 * NDB) {
+          const int u = t - NKK - 2 * NDB;
+          a[t] = row_operand<D>(dOs, qb * 32 + lio, 2 * u + h, true);
+        } else {
+          const int u = t - 2 * NKK - 2 * NDB;
+          a[t] = tr_operand<D>(Qs, 2 * qb + u / NDB, u % NDB, laneo);
+        }
+      };
+      auto use = [&](int t) -> bf16x8 {
+        if constexpr (PF) {
+          if (t + AH < NA) fetch(t + AH);
+        } else {
+          fetch(t);
+        }
+        return a[t];
+      };
+#pragma unroll
+      for (int t = 0; t < AH; ++t) fetch(t);
       f32x16 s = {};
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
-        s = mfma_bf16_32x32x16(row_operand<D>(Qs, qb * 32 + lio, 2 * kk + h, true), kreg[kk], s);
+      for (int kk = 0; kk < NKK; ++kk) s = mfma_bf16_32x32x16(use(kk), kreg[kk], s);
       uint32_t pk[8];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x4 l2 = *reinterpret_cast<const f32x4*>(&stats[buf][qb * 32 + 8 * g + 4 * h]);
         float p[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p[e] = fast_exp2(__builtin_fmaf(s[4 * g + e], c, -l2[e]));
-          if (tailq && i * BQ + qb * 32 + 8 * g + 4 * h + e >= n) p[e] = 0.f;
-        }
+        for (int e = 0; e < 4; ++e) p[e] = fast_exp2(__builtin_fmaf(s[4 * g + e], c, -l2[e]));
         pk[2 * g] = pack_bf16x2(p[0], p[1]);
         pk[2 * g + 1] = pack_bf16x2(p[2], p[3]);
       }
@@ -586,14 +653,19 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv2(
         const bf16x8 bp = __builtin_bit_cast(
             bf16x8, (u32x4{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]}));
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-          dvt[db] = mfma_bf16_32x32x16(tr_operand<D>(dOs, 2 * qb + ks, db, laneo), bp, dvt[db]);
+        for (int db = 0; db < NDB; ++db)
+          dvt[db] = mfma_bf16_32x32x16(use(NKK + ks * NDB + db), bp, dvt[db]);
       }
       f32x16 dp = {};
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
-        dp = mfma_bf16_32x32x16(row_operand<D>(dOs, qb * 32 + lio, 2 * kk + h, true), vreg[kk],
-                                dp);
+      for (int kk = 0; kk < NKK; ++kk) {
+        if constexpr (VL) {
+          const bf16x8 vb = row_operand<D>(Vw, lio, 2 * kk + h, false);
+          dp = mfma_bf16_32x32x16(use(NKK + 2 * NDB + kk), vb, dp);
+        } else {
+          dp = mfma_bf16_32x32x16(use(NKK + 2 * NDB + kk), vreg[kk], dp);
+        }
+      }
       uint32_t dsk[8];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -609,8 +681,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv2(
         const bf16x8 bs = __builtin_bit_cast(
             bf16x8, (u32x4{dsk[4 * ks], dsk[4 * ks + 1], dsk[4 * ks + 2], dsk[4 * ks + 3]}));
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-          dkt[db] = mfma_bf16_32x32x16(tr_operand<D>(Qs, 2 * qb + ks, db, laneo), bs, dkt[db]);
+        for (int db = 0; db < NDB; ++db)
+          dkt[db] = mfma_bf16_32x32x16(use(2 * NKK + 2 * NDB + ks * NDB + db), bs, dkt[db]);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -622,6 +694,243 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv2(
     float* dVr = dV + hoff + (size_t)key * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = db * 32 + 8 * g + 4 * h;
+        f32x4 a = {dkt[db][4 * g] * scale, dkt[db][4 * g + 1] * scale, dkt[db][4 * g + 2] * scale,
+                   dkt[db][4 * g + 3] * scale};
+        f32x4 b = {dvt[db][4 * g], dvt[db][4 * g + 1], dvt[db][4 * g + 2], dvt[db][4 * g + 3]};
+        *reinterpret_cast<f32x4*>(dKr + col) = a;
+        *reinterpret_cast<f32x4*>(dVr + col) = b;
+      }
+  }
+}
+
+// dK/dV kernel with every LDS address fixed before the loop.  Same
+// products and order as bwd_dkdv2, with V in LDS and the operands read two
+// MFMAs ahead; in addition each lane's byte offsets into a tile (row-wise
+// reads per k-step, transposed reads per 32-column block and half) are
+// computed once: the dual swizzle mixes only the low four bits of a row,
+// which the lane fixes, so the query sub-block, the k-step of the transposed
+// reads and the tile (Q or dO) only add constants, and the step is unrolled
+// by two so that the stage is a constant as well.  The loop then forms no
+// LDS address with vector instructions.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv3(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ Dg,
+    float* __restrict__ dK, float* __restrict__ dV, int n, int nkb, int total, float c,
+    float scale) {
+  using C = Dkdv2Cfg<D, NW>;
+  constexpr int BQ = C::BQ;
+  constexpr int NKK = D / 16, NDB = D / 32;
+  constexpr int TILE_B = C::TILE * 2;               // bytes of one Q or dO tile
+  constexpr int VT_B = NW * 32 * D * 2;             // bytes of the V rows
+  // [stage][Q | dO] tiles first (so every tile offset fits a read's
+  // immediate), then the waves' V rows, then [stage][lse2 | D].
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_B + VT_B + 2 * 2 * BQ * 4];
+  char* const tiles = smem;
+  bf16* const vtile = reinterpret_cast<bf16*>(smem + 4 * TILE_B);
+  float* const stats = reinterpret_cast<float*>(smem + 4 * TILE_B + VT_B);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, li = lane & 31;
+  const int tile = xcd_remap(blockIdx.x, total);
+  const int head = tile / nkb, kblk = tile - head * nkb;
+  const size_t hoff = (size_t)head * n * D;
+  const bf16 *Qh = Q + hoff, *Kh = K + hoff, *Vh = V + hoff, *dOh = dO + hoff;
+  const float* lseh = lse2 + (size_t)head * n;
+  const float* Dh = Dg + (size_t)head * n;
+  const int key = kblk * C::BKV + wave * 32 + li;
+
+  // K rows of the wave's 32 keys in registers (zero past n); V rows in the
+  // wave's LDS region (clamped to n-1): only the unstored dK/dV rows of
+  // keys past n see either.
+  bf16* const Vw = vtile + wave * 32 * D;
+  bf16x8 kreg[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk)
+    kreg[kk] = key < n ? *reinterpret_cast<const bf16x8*>(Kh + (size_t)key * D + 16 * kk + 8 * h)
+                       : bf16x8{};
+  {
+    constexpr int RC = D / 8;
+#pragma unroll
+    for (int it = 0; it < 32 * RC / 64; ++it) {
+      const int p = it * 64 + lane, row = p / RC, phys = p % RC;
+      const int logical = phys ^ chunk_swizzle<D * 2>(row);
+      const int vrow = min(kblk * C::BKV + wave * 32 + row, n - 1);
+      load_lds_16(Vh + (size_t)vrow * D + logical * 8, Vw + it * 64 * 8);
+    }
+  }
+  f32x16 dkt[NDB], dvt[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dkt[db] = dvt[db] = f32x16{};
+
+  // Copy offsets (global side) and read offsets (LDS side), per lane.
+  uint32_t toff[C::INSTS];
+#pragma unroll
+  for (int it = 0; it < C::INSTS; ++it) {
+    const int p = wave * C::WAVE_CHUNKS + it * 64 + lane;
+    const int row = p / (D / 8), phys = p % (D / 8);
+    toff[it] = (uint32_t)(row * D + (phys ^ dual_swizzle<D * 2>(row)) * 8) * 2u;
+  }
+  uint32_t roff[NKK], voff[NKK], troff[NDB][2];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    roff[kk] = (uint32_t)(li * D + ((2 * kk + h) ^ dual_swizzle<D * 2>(li)) * 8) * 2u;
+    voff[kk] = (uint32_t)(li * D + ((2 * kk + h) ^ chunk_swizzle<D * 2>(li)) * 8) * 2u;
+  }
+  {
+    const int G = lane >> 4, sl = lane & 15, hh = G >> 1;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int piece = 0; piece < 2; ++piece) {
+        const int row = 8 * piece + 4 * hh + (sl >> 2);
+        const int d0 = db * 32 + 16 * (G & 1) + 4 * (sl & 3);
+        troff[db][piece] =
+            (uint32_t)(row * D + ((d0 >> 3) ^ dual_swizzle<D * 2>(row)) * 8 + (d0 & 7)) * 2u;
+      }
+  }
+
+  auto load = [&](int i, int stage) {
+    char* qdst = tiles + stage * 2 * TILE_B;
+    if ((i + 1) * BQ <= n) {
+      const char* qb = reinterpret_cast<const char*>(Qh) + (size_t)i * BQ * D * 2;
+      const char* gb = reinterpret_cast<const char*>(dOh) + (size_t)i * BQ * D * 2;
+#pragma unroll
+      for (int it = 0; it < C::INSTS; ++it) {
+        const int p0 = wave * C::WAVE_CHUNKS + it * 64;
+        dma16(qb + toff[it], qdst + p0 * 16);
+        dma16(gb + toff[it], qdst + TILE_B + p0 * 16);
+      }
+    } else {
+      tile_load_lds<D, true>(Qh, reinterpret_cast<bf16*>(qdst), i, BQ, n, wave, lane,
+                             C::WAVE_CHUNKS, C::INSTS, true);
+      tile_load_lds<D, true>(dOh, reinterpret_cast<bf16*>(qdst + TILE_B), i, BQ, n, wave, lane,
+                             C::WAVE_CHUNKS, C::INSTS, true);
+    }
+    if (wave * 64 < 2 * BQ) {  // whole waves: 2 BQ is a multiple of 64
+      // A query row past n (a clamped copy of row n-1) gets lse2 = +inf, so
+      // its weights are exactly 0; its D stays finite.
+      float* st = stats + stage * 2 * BQ;
+      const int which = tid / BQ, r = tid - which * BQ;
+      const int qrow = min(i * BQ + r, n - 1);
+      if (which == 0 && i * BQ + r >= n)
+        st[tid] = __builtin_inff();
+      else
+        dma4((which == 0 ? lseh : Dh) + qrow, st + wave * 64);
+    }
+  };
+
+  const int nqt = (n + BQ - 1) / BQ;
+  auto step = [&](auto stage_c, int i) {
+    constexpr int P = decltype(stage_c)::value;
+    if (i + 1 < nqt) load(i + 1, P ^ 1);
+    const char* Qs = tiles + P * 2 * TILE_B;
+    const char* Gs = Qs + TILE_B;
+    const float* st = stats + P * 2 * BQ;
+#pragma unroll
+    for (int qb = 0; qb < BQ / 32; ++qb) {
+      constexpr int NA = 2 * NKK + 4 * NDB, AH = 2;
+      bf16x8 a[NA];
+      auto row_rd = [&](const char* t, int kk) {
+        return *reinterpret_cast<const bf16x8*>(t + roff[kk] + qb * 32 * D * 2);
+      };
+      auto tr_rd = [&](const char* t, int ksp, int db) {
+        const u32x2 p0 =
+            lds_read_tr16(reinterpret_cast<const bf16*>(t + troff[db][0] + ksp * 16 * D * 2));
+        const u32x2 p1 =
+            lds_read_tr16(reinterpret_cast<const bf16*>(t + troff[db][1] + ksp * 16 * D * 2));
+        return __builtin_bit_cast(bf16x8, (u32x4{p0[0], p0[1], p1[0], p1[1]}));
+      };
+      auto fetch = [&](int t) {
+        if (t < NKK) {
+          a[t] = row_rd(Qs, t);
+        } else if (t < NKK + 2 * NDB) {
+          const int u = t - NKK;
+          a[t] = tr_rd(Gs, 2 * qb + u / NDB, u % NDB);
+        } else if (t < 2 * NKK + 2 * NDB) {
+          a[t] = row_rd(Gs, t - NKK - 2 * NDB);
+        } else {
+          const int u = t - 2 * NKK - 2 * NDB;
+          a[t] = tr_rd(Qs, 2 * qb + u / NDB, u % NDB);
+        }
+      };
+      auto use = [&](int t) -> bf16x8 {
+        if (t + AH < NA) fetch(t + AH);
+        return a[t];
+      };
+#pragma unroll
+      for (int t = 0; t < AH; ++t) fetch(t);
+      // S = Q K^T, P = 2^(S c - lse2) in bf16, dV^T += dO^T P.
+      f32x16 s = {};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) s = mfma_bf16_32x32x16(use(kk), kreg[kk], s);
+      uint32_t pk[8];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(st + qb * 32 + 8 * g + 4 * h);
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = fast_exp2(__builtin_fmaf(s[4 * g + e], c, -l2[e]));
+        pk[2 * g] = pack_bf16x2(p[0], p[1]);
+        pk[2 * g + 1] = pack_bf16x2(p[2], p[3]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 bp = __builtin_bit_cast(
+            bf16x8, (u32x4{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]}));
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          dvt[db] = mfma_bf16_32x32x16(use(NKK + ks * NDB + db), bp, dvt[db]);
+      }
+      // dP = dO V^T, dS = P o (dP - D) from the same bf16 P, dK^T += Q^T dS.
+      f32x16 dp = {};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const bf16x8 vb =
+            *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(Vw) + voff[kk]);
+        dp = mfma_bf16_32x32x16(use(NKK + 2 * NDB + kk), vb, dp);
+      }
+      uint32_t dsk[8];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 dd = *reinterpret_cast<const f32x4*>(st + BQ + qb * 32 + 8 * g + 4 * h);
+        const float p0 = bf_lo(pk[2 * g]), p1 = bf_hi(pk[2 * g]);
+        const float p2 = bf_lo(pk[2 * g + 1]), p3 = bf_hi(pk[2 * g + 1]);
+        dsk[2 * g] = pack_bf16x2(p0 * (dp[4 * g] - dd[0]), p1 * (dp[4 * g + 1] - dd[1]));
+        dsk[2 * g + 1] = pack_bf16x2(p2 * (dp[4 * g + 2] - dd[2]), p3 * (dp[4 * g + 3] - dd[3]));
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 bs = __builtin_bit_cast(
+            bf16x8, (u32x4{dsk[4 * ks], dsk[4 * ks + 1], dsk[4 * ks + 2], dsk[4 * ks + 3]}));
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          dkt[db] = mfma_bf16_32x32x16(use(2 * NKK + 2 * NDB + ks * NDB + db), bs, dkt[db]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the next tile's copies, before the barrier
+    __syncthreads();
+  };
+
+  load(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int i = 0;
+  for (; i + 1 < nqt; i += 2) {
+    step(std::integral_constant<int, 0>{}, i);
+    step(std::integral_constant<int, 1>{}, i + 1);
+  }
+  if (i < nqt) step(std::integral_constant<int, 0>{}, i);
+
+  if (key < n) {
+    float* dKr = dK + hoff + (size_t)key * D;
+    float* dVr = dV + hoff + (size_t)key * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int col = db * 32 + 8 * g + 4 * h;
@@ -693,13 +1002,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq2(
 #pragma unroll
       for (int it = 0; it < C::INSTS; ++it) {
         const int p0 = wave * C::WAVE_CHUNKS + it * 64;
-        load_lds_16(kb + koff[it], tiles[buf] + p0 * 8);
-        load_lds_16(vb + voff[it], tiles[buf] + C::TILE + p0 * 8);
+        dma16(kb + koff[it], tiles[buf] + p0 * 8);
+        dma16(vb + voff[it], tiles[buf] + C::TILE + p0 * 8);
       }
     } else {
-      tile_load_lds<D>(Kh, tiles[buf], j, BC, n, wave, lane, C::WAVE_CHUNKS, C::INSTS, true);
-      tile_load_lds<D>(Vh, tiles[buf] + C::TILE, j, BC, n, wave, lane, C::WAVE_CHUNKS, C::INSTS,
-                       false);
+      tile_load_lds<D, true>(Kh, tiles[buf], j, BC, n, wave, lane, C::WAVE_CHUNKS, C::INSTS, true);
+      tile_load_lds<D, true>(Vh, tiles[buf] + C::TILE, j, BC, n, wave, lane, C::WAVE_CHUNKS,
+                             C::INSTS, false);
     }
   };
 
@@ -777,7 +1086,10 @@ struct IntK {
   static constexpr int value = V;
 };
 
-// Kernel generation: "v2" (default) or "v1" via ATTN_BWD_VARIANT, and the
+// Kernel generation via ATTN_BWD_VARIANT: "v2" (default: bwd_dkdv3 and
+// bwd_dq2), or bwd_dkdv2 with "v2l" (V in LDS, operands read ahead), "v2r"
+// (V in registers, operands read ahead), "v2s" (V in registers, each LDS
+// operand read just before its MFMA), or "v1" (first-generation kernels); and the
 // waves per workgroup of the v2 kernels via ATTN_BWD_WAVES ("4" or "8").
 template <int D>
 hipError_t launch(const void* Q, const void* K, const void* V, const float* O, const void* dO,
@@ -799,6 +1111,9 @@ hipError_t launch(const void* Q, const void* K, const void* V, const float* O, c
   if (e != hipSuccess) return e;
   const char* var = getenv("ATTN_BWD_VARIANT");
   const bool v1 = var && strcmp(var, "v1") == 0;
+  const bool serial = var && strcmp(var, "v2s") == 0;
+  const bool vreg = var && strcmp(var, "v2r") == 0;
+  const bool vlds = var && strcmp(var, "v2l") == 0;
   const char* wv = getenv("ATTN_BWD_WAVES");
   const bool w4 = wv && strcmp(wv, "4") == 0;
   if (v1) {
@@ -819,8 +1134,18 @@ hipError_t launch(const void* Q, const void* K, const void* V, const float* O, c
     using Cf = Dkdv2Cfg<D, NW>;
     const int nkb = (int)((n + Cf::BKV - 1) / Cf::BKV);
     const int total_kv = (int)(bh * nkb);
-    hipLaunchKernelGGL((bwd_dkdv2<D, NW>), dim3(total_kv), dim3(NW * 64), 0, stream, q, k, v, g,
-                       lse2, Dbuf, dK, dV, (int)n, nkb, total_kv, c, scale);
+    if (serial)
+      hipLaunchKernelGGL((bwd_dkdv2<D, NW, false, false>), dim3(total_kv), dim3(NW * 64), 0,
+                         stream, q, k, v, g, lse2, Dbuf, dK, dV, (int)n, nkb, total_kv, c, scale);
+    else if (vreg)
+      hipLaunchKernelGGL((bwd_dkdv2<D, NW, true, false>), dim3(total_kv), dim3(NW * 64), 0,
+                         stream, q, k, v, g, lse2, Dbuf, dK, dV, (int)n, nkb, total_kv, c, scale);
+    else if (vlds)
+      hipLaunchKernelGGL((bwd_dkdv2<D, NW, true, true>), dim3(total_kv), dim3(NW * 64), 0,
+                         stream, q, k, v, g, lse2, Dbuf, dK, dV, (int)n, nkb, total_kv, c, scale);
+    else
+      hipLaunchKernelGGL((bwd_dkdv3<D, NW>), dim3(total_kv), dim3(NW * 64), 0, stream, q, k, v,
+                         g, lse2, Dbuf, dK, dV, (int)n, nkb, total_kv, c, scale);
   };
   auto dqk = [&](auto nwc) {
     constexpr int NW = decltype(nwc)::value;

@@ -39,6 +39,7 @@
 // the dQ product b/16 contiguous pieces of 512 bytes, and a b x b tile of
 // the scores kernel 2 b^2 contiguous bytes.
 #include "device_common.h"
+#include "lds_dma.h"
 #include "launch.h"
 
 namespace at {
@@ -90,55 +91,6 @@ __device__ __forceinline__ bf16x8 tr_panel(const bf16* panel, int col0, int lane
   return __builtin_bit_cast(bf16x8, (u32x4{part[0][0], part[0][1], part[1][0], part[1][1]}));
 }
 
-// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4)
-// from inline assembly: lane l's 16 bytes land at lds_wave_base + 16 l
-// (lds_wave_base uniform across the wave).  The compiler does not see these
-// as LDS writes, so it does not make every LDS read wait for all copies in
-// flight (it cannot tell the ring slots apart); the kernels wait for the
-// copies they need with an exact vmcnt before a barrier without a fence.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // m0: only LDS copies use it here
-__device__ __forceinline__ void sb_copy16(const void* gsrc, bf16* lds_wave_base) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
-      __attribute__((address_space(3))) char*)(reinterpret_cast<char*>(lds_wave_base)));
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(gsrc), "s"(lds)
-      : "memory", "m0");
-}
-// The same with 4 bytes per lane (global_load_lds_dword).
-__device__ __forceinline__ void sb_copy4(const void* gsrc, float* lds_wave_base) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
-      __attribute__((address_space(3))) char*)(reinterpret_cast<char*>(lds_wave_base)));
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dword %0, off"
-      :
-      : "v"(gsrc), "s"(lds)
-      : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// s_waitcnt with vmcnt = N and the other counters left at their maxima.
-template <int N>
-__device__ __forceinline__ void sb_wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-// Workgroup barrier without a memory fence (a fence would wait for the
-// later panels' copies); the empty asm statements keep the compiler from
-// moving memory accesses across it.
-__device__ __forceinline__ void sb_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // Direct load of one 16-row x W-column panel (row stride `stride` elements,
 // rows clamped to rmax) into LDS with vtr_swizzle, by one wave-load of 64
 // lanes per 64 chunks: part `part` covers chunks 64 part .. +63.
@@ -151,7 +103,7 @@ __device__ __forceinline__ void load_tr_panel(const bf16* src, int64_t stride, i
   const int row = p / CPR, phys = p % CPR;
   const int logical = phys ^ vtr_swizzle<W * 2>(row);
   const int grow = min(r0 + row, rmax);
-  sb_copy16(src + (size_t)grow * stride + c0 + logical * 8, dst + p0 * 8);
+  dma16(src + (size_t)grow * stride + c0 + logical * 8, dst + p0 * 8);
 }
 
 // ---------------------------------------------------------------------------
@@ -216,7 +168,7 @@ __global__ __launch_bounds__(B * 4) void sb_scores_grads(
     const int row = p >> 1, hf = p & 1;
     const int grow = min((side == 0 ? I * B : J * B) + row, n - 1);
     const bf16* src = side == 0 ? (second ? dO : Q) : (second ? V : K);
-    sb_copy16(src + hoff + (size_t)grow * D + kp * SKP + hf * 8, &sm[t % R][side][p0 * 8]);
+    dma16(src + hoff + (size_t)grow * D + kp * SKP + hf * 8, &sm[t % R][side][p0 * 8]);
   };
 
   f32x16 s[CB], dp[CB];
@@ -228,7 +180,7 @@ __global__ __launch_bounds__(B * 4) void sb_scores_grads(
   if (wave < 2 * B / 64) {
     const int which = wave / (B / 64), r0 = (wave % (B / 64)) * 64;
     const int i = min(I * B + r0 + lane, n - 1);
-    sb_copy4((which == 0 ? lse : Dv) + (size_t)head * n + i, &rowstat[which][r0]);
+    dma4((which == 0 ? lse : Dv) + (size_t)head * n + i, &rowstat[which][r0]);
   }
   auto compute = [&](int t) {
     const bf16* qs = sm[t % R][0];
@@ -259,14 +211,14 @@ __global__ __launch_bounds__(B * 4) void sb_scores_grads(
 #pragma unroll
   for (int i = 0; i < AHEAD; ++i) issue(i);
   for (int t = 0; t < T; t += PPS) {
-    sb_wait_vm<AHEAD - PPS>();  // steps t .. t+PPS-1 are done; later ones may be in flight
-    sb_barrier();               // every lane's copies; the slots of steps t-PPS.. are free
+    wait_vm<AHEAD - PPS>();  // steps t .. t+PPS-1 are done; later ones may be in flight
+    slot_barrier();               // every lane's copies; the slots of steps t-PPS.. are free
 #pragma unroll
     for (int p = 0; p < PPS; ++p) issue(t + AHEAD + p);
 #pragma unroll
     for (int p = 0; p < PPS; ++p) compute(t + p);
   }
-  sb_wait_vm<0>();  // no copy into LDS may outlive the workgroup
+  wait_vm<0>();  // no copy into LDS may outlive the workgroup
 
   // Epilogue.  Accumulator register r of a lane holds query row
   // i0 + 8 (r/4) + 4 h + r%4 and key column j of the lane.  P and dS are
@@ -317,7 +269,7 @@ __global__ __launch_bounds__(B * 4) void sb_scores_grads(
   bf16* tileb = &sm[0][0][0];
   constexpr int CPT = B / 8;  // 16-byte chunks per tile row
   auto to_global = [&](const uint32_t (&v)[CB][4][2], bf16* dst) {
-    sb_barrier();  // the slots (or the previous tile) are no longer read
+    slot_barrier();  // the slots (or the previous tile) are no longer read
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -329,7 +281,7 @@ __global__ __launch_bounds__(B * 4) void sb_scores_grads(
             u32x2{v[cb][g][0], v[cb][g][1]};
       }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this lane's tile writes are done
-    sb_barrier();
+    slot_barrier();
     // the tile is one contiguous region [16-query panel q][key r][16
     // queries]: 16-byte chunk x holds panel q = x / 2b, key r, half c
     bf16* region = dst + pt_offset<B>(head, J * B, I * B, nt, npad);
@@ -412,12 +364,12 @@ __global__ __launch_bounds__(B * 4) void sb_product(const SbJobs jobs, int n, in
         const int p0 = wave * 64, p = p0 + lane;
         const int row = p / CPR, phys = p % CPR;
         const int logical = phys ^ vtr_swizzle<B * 2>(row);
-        sb_copy16(A + pt_offset<B>(head, k0 + row, R0 + logical * 8, nt, npad),
+        dma16(A + pt_offset<B>(head, k0 + row, R0 + logical * 8, nt, npad),
                   &sm[st][0][p0 * 8]);
       } else {
         // keys R0 .. R0+b-1 x queries k0 .. k0+15: one contiguous 4 KB panel
         const int p0 = wave * 64, p = p0 + lane;
-        sb_copy16(A + pt_offset<B>(head, R0, k0, nt, npad) + (size_t)p * 8, &sm[st][0][p0 * 8]);
+        dma16(A + pt_offset<B>(head, R0, k0, nt, npad) + (size_t)p * 8, &sm[st][0][p0 * 8]);
       }
     } else {
       load_tr_panel<B>(Bh, D, k0, n - 1, C0, sm[st][1], wave - RB, lane);
@@ -445,12 +397,12 @@ __global__ __launch_bounds__(B * 4) void sb_product(const SbJobs jobs, int n, in
 #pragma unroll
   for (int i = 0; i < DIST; ++i) issue(i);
   for (int kp = 0; kp < NP; ++kp) {
-    sb_wait_vm<DIST - 1>();  // panel kp is done; the later DIST - 1 may be in flight
-    sb_barrier();            // every lane's copy of panel kp; slot (kp - 1) % R is free
+    wait_vm<DIST - 1>();  // panel kp is done; the later DIST - 1 may be in flight
+    slot_barrier();            // every lane's copy of panel kp; slot (kp - 1) % R is free
     issue(kp + DIST);
     compute(kp % R);
   }
-  sb_wait_vm<0>();  // no copy into LDS may outlive the workgroup
+  wait_vm<0>();  // no copy into LDS may outlive the workgroup
 
   // acc[cb] register r: column C0 + ch B/2 + 32 cb + 8 (r/4) + 4 h + r%4,
   // output row R0 + rb*32 + l%32.

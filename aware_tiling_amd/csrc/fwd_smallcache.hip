@@ -43,6 +43,7 @@
 // discarded rows or are multiplied by 0), then m_IJ [bh][n][nt] and
 // l_IJ [bh][n][nt] fp32 with nt = ceil(n/b).
 #include "device_common.h"
+#include "lds_dma.h"
 #include "launch.h"
 
 namespace at {
@@ -87,60 +88,6 @@ struct ScDist {
   static constexpr int DIST = B >= 128 ? 2 : 1;
   static constexpr int R = DIST + 1;
 };
-
-// s_waitcnt with vmcnt = N and the other counters left at their maxima.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4),
-// issued from inline assembly: lane l's 16 bytes land at lds_wave_base +
-// 16 l (lds_wave_base uniform across the wave).  The compiler does not see
-// this as an LDS write, so it does not make every later LDS read wait for
-// all such copies in flight (it cannot tell the ring slots apart); the
-// kernels wait for exactly the copies they need with wait_vm before the
-// slot barrier.  Its own waits for ordinary loads stay correct: copies it
-// does not count only lengthen them.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // m0: only LDS copies use it here
-__device__ __forceinline__ void dma16(const void* gsrc, bf16* lds_wave_base) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
-      __attribute__((address_space(3))) char*)(reinterpret_cast<char*>(lds_wave_base)));
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(gsrc), "s"(lds)
-      : "memory", "m0");
-}
-// The same with 4 bytes per lane (global_load_lds_dword): lane l's 4 bytes
-// land at lds_wave_base + 4 l.
-__device__ __forceinline__ void dma4(const void* gsrc, float* lds_wave_base) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
-      __attribute__((address_space(3))) char*)(reinterpret_cast<char*>(lds_wave_base)));
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dword %0, off"
-      :
-      : "v"(gsrc), "s"(lds)
-      : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// Workgroup barrier without a memory fence: the LDS slots are filled by
-// direct loads whose completion each lane has already waited for with an
-// exact vmcnt, and later panels' loads must stay in flight across it (a
-// fence would wait for them).  The empty asm statements keep the compiler
-// from moving memory accesses across the barrier.
-__device__ __forceinline__ void slot_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // ---------------------------------------------------------------------------
 // 1. Scores and exponentials of b x b tiles.

@@ -1,0 +1,68 @@
+// Direct global -> LDS copies issued from inline assembly, exact vmcnt
+// waits, and a workgroup barrier without a memory fence (gfx950).
+//
+// The compiler treats its own global_load_lds builtins as LDS writes it
+// cannot tell apart, and makes every later LDS read wait for all of them
+// (s_waitcnt vmcnt(0)), which serialises a prefetch of the next tile with
+// the reads of the current one.  Copies issued from inline assembly are
+// invisible to it: the kernels wait for exactly the copies they need with
+// wait_vm<N> before a barrier without a fence.  The compiler's own waits for
+// ordinary loads stay correct, since copies it does not count only lengthen
+// them.  A kernel that issues these copies ends with wait_vm<0>() so that no
+// copy into LDS outlives its workgroup.
+#pragma once
+
+#include <cstdint>
+
+#include "device_common.h"
+
+namespace at {
+
+// s_waitcnt with vmcnt = N and the other counters left at their maxima.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0: only LDS copies use it here
+// 16 bytes per lane (global_load_lds_dwordx4): lane l's 16 bytes land at
+// lds_wave_base + 16 l; lds_wave_base must be uniform across the wave.
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
+      __attribute__((address_space(3))) char*)(reinterpret_cast<char*>(lds_wave_base)));
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(gsrc), "s"(lds)
+      : "memory", "m0");
+}
+// 4 bytes per lane (global_load_lds_dword): lane l's 4 bytes land at
+// lds_wave_base + 4 l.
+__device__ __forceinline__ void dma4(const void* gsrc, void* lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
+      __attribute__((address_space(3))) char*)(reinterpret_cast<char*>(lds_wave_base)));
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, off"
+      :
+      : "v"(gsrc), "s"(lds)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Workgroup barrier without a memory fence: every lane has already waited
+// for its own copies with an exact vmcnt, and later copies stay in flight
+// across it (a fence would wait for them).  The empty asm statements keep
+// the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void slot_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+}  // namespace at
