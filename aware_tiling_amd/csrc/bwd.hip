@@ -1076,6 +1076,181 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq2(
   }
 }
 
+// dQ kernel with every LDS address fixed before the loop (as bwd_dkdv3):
+// each lane's byte offsets for the row-wise K and V reads per k-step and the
+// transposed K reads per 32-column block and half are computed once, the
+// key sub-block and the k-step only add constants, and the step is unrolled
+// by two so that the stage is a constant.  Operands are read two MFMAs
+// ahead.  Products, order and masking as bwd_dq2.
+template <int D, int NW, int BC>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq3(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dg,
+    float* __restrict__ dQ, int n, int nqb, int total, float c, float scale) {
+  using C = Dq2Cfg<D, NW, BC>;
+  constexpr int NKK = D / 16, NDB = D / 32;
+  constexpr int TILE_B = C::TILE * 2;
+  __shared__ __attribute__((aligned(1024))) char tiles[4 * TILE_B];  // [stage][K | V]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, li = lane & 31;
+  const int tile = xcd_remap(blockIdx.x, total);
+  const int head = tile / nqb, qblk = tile - head * nqb;
+  const size_t hoff = (size_t)head * n * D;
+  const bf16 *Qh = Q + hoff, *Kh = K + hoff, *Vh = V + hoff, *dOh = dO + hoff;
+  const int q = qblk * C::BQB + wave * 32 + li;
+
+  bf16x8 qreg[NKK], dogreg[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    qreg[kk] = q < n ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)q * D + 16 * kk + 8 * h)
+                     : bf16x8{};
+    dogreg[kk] = q < n ? *reinterpret_cast<const bf16x8*>(dOh + (size_t)q * D + 16 * kk + 8 * h)
+                       : bf16x8{};
+  }
+  const float l2 = q < n ? lse[(size_t)head * n + q] * kLog2e : 0.f;
+  const float dq_d = q < n ? Dg[(size_t)head * n + q] : 0.f;
+  f32x16 dqt[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dqt[db] = f32x16{};
+
+  uint32_t koff[C::INSTS], voff[C::INSTS];
+#pragma unroll
+  for (int it = 0; it < C::INSTS; ++it) {
+    const int p = wave * C::WAVE_CHUNKS + it * 64 + lane;
+    const int row = p / (D / 8), phys = p % (D / 8);
+    koff[it] = (uint32_t)(row * D + (phys ^ dual_swizzle<D * 2>(row)) * 8) * 2u;
+    voff[it] = (uint32_t)(row * D + (phys ^ chunk_swizzle<D * 2>(row)) * 8) * 2u;
+  }
+  uint32_t rk[NKK], rv[NKK], tk[NDB][2];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    rk[kk] = (uint32_t)(li * D + ((2 * kk + h) ^ dual_swizzle<D * 2>(li)) * 8) * 2u;
+    rv[kk] = (uint32_t)(li * D + ((2 * kk + h) ^ chunk_swizzle<D * 2>(li)) * 8) * 2u;
+  }
+  {
+    const int G = lane >> 4, sl = lane & 15, hh = G >> 1;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int piece = 0; piece < 2; ++piece) {
+        const int row = 8 * piece + 4 * hh + (sl >> 2);
+        const int d0 = db * 32 + 16 * (G & 1) + 4 * (sl & 3);
+        tk[db][piece] =
+            (uint32_t)(row * D + ((d0 >> 3) ^ dual_swizzle<D * 2>(row)) * 8 + (d0 & 7)) * 2u;
+      }
+  }
+  auto load = [&](int j, int stage) {
+    char* kdst = tiles + stage * 2 * TILE_B;
+    if ((j + 1) * BC <= n) {
+      const char* kb = reinterpret_cast<const char*>(Kh) + (size_t)j * BC * D * 2;
+      const char* vb = reinterpret_cast<const char*>(Vh) + (size_t)j * BC * D * 2;
+#pragma unroll
+      for (int it = 0; it < C::INSTS; ++it) {
+        const int p0 = wave * C::WAVE_CHUNKS + it * 64;
+        dma16(kb + koff[it], kdst + p0 * 16);
+        dma16(vb + voff[it], kdst + TILE_B + p0 * 16);
+      }
+    } else {
+      tile_load_lds<D, true>(Kh, reinterpret_cast<bf16*>(kdst), j, BC, n, wave, lane,
+                             C::WAVE_CHUNKS, C::INSTS, true);
+      tile_load_lds<D, true>(Vh, reinterpret_cast<bf16*>(kdst + TILE_B), j, BC, n, wave, lane,
+                             C::WAVE_CHUNKS, C::INSTS, false);
+    }
+  };
+
+  const int nkt = (n + BC - 1) / BC;
+  auto step = [&](auto stage_c, int j) {
+    constexpr int P = decltype(stage_c)::value;
+    if (j + 1 < nkt) load(j + 1, P ^ 1);
+    const char* Ks = tiles + P * 2 * TILE_B;
+    const char* Vs = Ks + TILE_B;
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb) {
+      // Operand sequence: K and V rows alternating over the k-steps of S^T
+      // and dP^T, then the transposed K blocks of dQ^T.
+      constexpr int NA = 2 * NKK + 2 * NDB, AH = 2;
+      bf16x8 a[NA];
+      auto fetch = [&](int t) {
+        if (t < 2 * NKK) {
+          const int kk = t >> 1;
+          const char* base = (t & 1) ? Vs : Ks;
+          const uint32_t off = (t & 1) ? rv[kk] : rk[kk];
+          a[t] = *reinterpret_cast<const bf16x8*>(base + off + kb * 32 * D * 2);
+        } else {
+          const int u = t - 2 * NKK, ksp = 2 * kb + u / NDB, db = u % NDB;
+          const u32x2 p0 =
+              lds_read_tr16(reinterpret_cast<const bf16*>(Ks + tk[db][0] + ksp * 16 * D * 2));
+          const u32x2 p1 =
+              lds_read_tr16(reinterpret_cast<const bf16*>(Ks + tk[db][1] + ksp * 16 * D * 2));
+          a[t] = __builtin_bit_cast(bf16x8, (u32x4{p0[0], p0[1], p1[0], p1[1]}));
+        }
+      };
+      auto use = [&](int t) -> bf16x8 {
+        if (t + AH < NA) fetch(t + AH);
+        return a[t];
+      };
+#pragma unroll
+      for (int t = 0; t < AH; ++t) fetch(t);
+      // S^T = K Q^T and dP^T = V dO^T (32 keys x 32 queries per wave).
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        s = mfma_bf16_32x32x16(use(2 * kk), qreg[kk], s);
+        dp = mfma_bf16_32x32x16(use(2 * kk + 1), dogreg[kk], dp);
+      }
+      const int kbase = j * BC + kb * 32;
+      const bool tail = kbase + 32 > n;
+      uint32_t dsk[8];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float p0 = fast_exp2(__builtin_fmaf(s[r], c, -l2));
+        float p1 = fast_exp2(__builtin_fmaf(s[r + 1], c, -l2));
+        if (tail) {
+          const int k0 = kbase + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (k0 >= n) p0 = 0.f;
+          if (k0 + 1 >= n) p1 = 0.f;
+        }
+        dsk[r >> 1] = pack_bf16x2(p0 * (dp[r] - dq_d), p1 * (dp[r + 1] - dq_d));
+      }
+      // dQ^T += K^T dS^T over these 32 keys.
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 bs = __builtin_bit_cast(
+            bf16x8, (u32x4{dsk[4 * ks], dsk[4 * ks + 1], dsk[4 * ks + 2], dsk[4 * ks + 3]}));
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          dqt[db] = mfma_bf16_32x32x16(use(2 * NKK + ks * NDB + db), bs, dqt[db]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the next tile's copies, before the barrier
+    __syncthreads();
+  };
+
+  load(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int j = 0;
+  for (; j + 1 < nkt; j += 2) {
+    step(std::integral_constant<int, 0>{}, j);
+    step(std::integral_constant<int, 1>{}, j + 1);
+  }
+  if (j < nkt) step(std::integral_constant<int, 0>{}, j);
+
+  if (q < n) {
+    float* dQr = dQ + hoff + (size_t)q * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 a = {dqt[db][4 * g] * scale, dqt[db][4 * g + 1] * scale, dqt[db][4 * g + 2] * scale,
+                   dqt[db][4 * g + 3] * scale};
+        *reinterpret_cast<f32x4*>(dQr + db * 32 + 8 * g + 4 * h) = a;
+      }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Host side.
 
@@ -1087,9 +1262,10 @@ struct IntK {
 };
 
 // Kernel generation via ATTN_BWD_VARIANT: "v2" (default: bwd_dkdv3 and
-// bwd_dq2), or bwd_dkdv2 with "v2l" (V in LDS, operands read ahead), "v2r"
-// (V in registers, operands read ahead), "v2s" (V in registers, each LDS
-// operand read just before its MFMA), or "v1" (first-generation kernels); and the
+// bwd_dq3), or bwd_dq2 with bwd_dkdv2 in one of three forms: "v2l" (V in
+// LDS, operands read ahead), "v2r" (V in registers, operands read ahead),
+// "v2s" (V in registers, each LDS operand read just before its MFMA); or
+// "v1" (first-generation kernels); and the
 // waves per workgroup of the v2 kernels via ATTN_BWD_WAVES ("4" or "8").
 template <int D>
 hipError_t launch(const void* Q, const void* K, const void* V, const float* O, const void* dO,
@@ -1152,8 +1328,12 @@ hipError_t launch(const void* Q, const void* K, const void* V, const float* O, c
     using Cf = Dq2Cfg<D, NW, 64>;
     const int nqb = (int)((n + Cf::BQB - 1) / Cf::BQB);
     const int total_q = (int)(bh * nqb);
-    hipLaunchKernelGGL((bwd_dq2<D, NW, 64>), dim3(total_q), dim3(NW * 64), 0, stream, q, k, v, g,
-                       lse, Dbuf, dQ, (int)n, nqb, total_q, c, scale);
+    if (serial || vreg || vlds)
+      hipLaunchKernelGGL((bwd_dq2<D, NW, 64>), dim3(total_q), dim3(NW * 64), 0, stream, q, k, v,
+                         g, lse, Dbuf, dQ, (int)n, nqb, total_q, c, scale);
+    else
+      hipLaunchKernelGGL((bwd_dq3<D, NW, 64>), dim3(total_q), dim3(NW * 64), 0, stream, q, k, v,
+                         g, lse, Dbuf, dQ, (int)n, nqb, total_q, c, scale);
   };
   if (w4) {
     dkdv(IntK<4>{});
