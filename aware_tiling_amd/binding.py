@@ -31,6 +31,7 @@ SIGNATURES = {
     "attn_fwd_query_block": (_i64, [_i64, _int]),
     "attn_fwd_budget": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _int, _i64, _vp]),
     "attn_fwd_budget_onchip_elems": (_i64, [_i64]),
+    "attn_calib_mfma_loop": (_int, [_vp, _i64, ctypes.c_int32, _f32, _vp]),
     "attn_fwd_splitk_splits": (_i64, [_i64, _i64, _i64, _i64, _i64]),
     "attn_fwd_splitk_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "attn_fwd_splitk": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _int, _i64,
@@ -169,6 +170,18 @@ def attn_fwd_budget(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, m_elems: 
                                _dtype_code(q), int(m_elems), _stream(q, stream))
     _check("attn_fwd_budget", rc)
     return out, lse
+
+
+def calib_mfma_loop(out: torch.Tensor, iters: int, amp: float = 1.0, stream=None) -> int:
+    """Calibration matrix-core loop (no memory traffic) over out.numel() // 256
+    workgroups; returns the flops it issues. out: float32 CUDA tensor."""
+    if out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 CUDA tensor")
+    wgs = out.numel() // 256
+    rc = lib().attn_calib_mfma_loop(out.data_ptr(), wgs, int(iters), float(amp),
+                                    _stream(out, stream))
+    _check("attn_calib_mfma_loop", rc)
+    return wgs * int(iters) * 4 * 4 * 2 * 32 * 32 * 16
 
 
 def splitk_splits(bh: int, nq: int, nk: int, d: int, splits: int = 0) -> int:

@@ -283,4 +283,13 @@ attn_status attn_bwd_smallcache(const void* Q, const void* K, const void* V, con
                                                       static_cast<hipStream_t>(stream)));
 }
 
+attn_status attn_calib_mfma_loop(float* out, int64_t workgroups, int32_t iters, float amp,
+                                 void* stream) {
+  if (!out || !aligned16(out) || workgroups < 1 || workgroups > INT32_MAX || iters < 1 ||
+      !std::isfinite(amp))
+    return ATTN_ERR_INVALID_ARG;
+  return launch_status(
+      at::launch_calib_mfma_loop(out, workgroups, iters, amp, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -101,4 +101,8 @@ hipError_t launch_bwd_smallcache_bf16(const void* Q, const void* K, const void* 
                                       int64_t d, float scale, SmallBwdTile t, void* workspace,
                                       hipStream_t stream);
 
+// Matrix-core loop for the reachable bf16 MFMA rate (calib.hip).
+hipError_t launch_calib_mfma_loop(float* out, int64_t workgroups, int iters, float amp,
+                                  hipStream_t stream);
+
 }  // namespace at

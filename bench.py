@@ -22,7 +22,8 @@ Reported (one JSON line on stdout):
                measured L2-miss bytes (traffic) / launch time;
   launch_ms_*  min, median, p90, max over the timed launches, and
                cold_launch_ms with L2 and MALL flushed by a 512 MB write;
-  measured_peaks  a library bf16 GEMM and a device copy on the same GPU,
+  measured_peaks  a library bf16 GEMM, a device copy and the library's
+               matrix-core loop (random and zero operands) on the same GPU,
                the reachable rates beside the published peaks;
   cpu_baseline the float64 oracle on the host cores, on a bounded sample of
                rows of the same workload (about 15 s of CPU work);
@@ -114,9 +115,22 @@ def cold_launch_ms(fn, torch, dev, reps: int = 5) -> float:
     return percentile(times, 50)
 
 
-def measured_peaks(torch, dev) -> dict:
+def measured_peaks(torch, dev, at=None) -> dict:
     """Reference rates measured on this device: a library bf16 GEMM
-    (8192^3, torch.matmul) and a 1 GiB device-to-device copy."""
+    (8192^3, torch.matmul), a 1 GiB device-to-device copy and, when the
+    library is built, its matrix-core loop (the attention kernels' MFMA
+    instruction on register operands, no memory traffic) with random bf16
+    operands and with zero operands, at two waves per SIMD."""
+    loops = {}
+    if at is not None:
+        out = torch.empty(512 * 256, dtype=torch.float32, device=dev)
+        for name, amp in (("mfma_loop_bf16_tflops", 1.0), ("mfma_loop_zero_data_bf16_tflops", 0.0)):
+            flops = [0]
+            def run():
+                flops[0] = at.calib_mfma_loop(out, 100000, amp)
+            ms, _, _ = time_launches(run, 5, 2)
+            loops[name] = round(flops[0] / (ms * 1e-3) / 1e12, 1)
+        del out
     a = torch.randn((8192, 8192), device=dev).to(torch.bfloat16)
     b = torch.randn((8192, 8192), device=dev).to(torch.bfloat16)
     gemm_ms, _, _ = time_launches(lambda: torch.matmul(a, b), 10, 3)
@@ -127,7 +141,7 @@ def measured_peaks(torch, dev) -> dict:
     del src, dst
     torch.cuda.empty_cache()
     return {"gemm_bf16_tflops": round(2 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
-            "copy_gbps": round(2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9, 1)}
+            "copy_gbps": round(2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9, 1), **loops}
 
 
 def traffic_for_launch():
@@ -381,8 +395,10 @@ def main():
     out["cold_launch_ms"] = round(cold_launch_ms(fn, torch, dev), 4)
     del q, k, v, o, lse
     torch.cuda.empty_cache()
-    out["measured_peaks"] = measured_peaks(torch, dev)
+    out["measured_peaks"] = measured_peaks(torch, dev, at)
     out["frac_of_measured_gemm"] = round(achieved / out["measured_peaks"]["gemm_bf16_tflops"], 4)
+    out["frac_of_measured_mfma_loop"] = round(
+        achieved / out["measured_peaks"]["mfma_loop_bf16_tflops"], 4)
 
     if not args.no_secondary:
         out["secondary"] = secondary(args, at, torch, dev)

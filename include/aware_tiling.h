@@ -301,6 +301,23 @@ attn_status attn_bwd_smallcache(const void* Q, const void* K, const void* V,
                                 void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/*
+ * attn_calib_mfma_loop -- calibration, not part of the attention method: a
+ * matrix-core loop with no memory traffic, timed by the caller for the bf16
+ * MFMA rate this device reaches (the published dense peak assumes the top
+ * clock; the card lowers its clock with the matrix core's switching load).
+ * Each of `workgroups` workgroups of four waves runs `iters` rounds of four
+ * independent v_mfma_f32_32x32x16_bf16 chains on register operands drawn
+ * in [-amp, amp) (all zero when amp = 0): 4 * 4 * 2 * 32 * 32 * 16 flops
+ * per workgroup per round.
+ *
+ *   out : workgroups * 256 floats (device, written; 16-byte aligned).
+ *   ATTN_ERR_INVALID_ARG for a null or unaligned out, workgroups outside
+ *   [1, 2^31), iters < 1 or a non-finite amp.  Asynchronous on `stream`.
+ */
+attn_status attn_calib_mfma_loop(float* out, int64_t workgroups, int32_t iters, float amp,
+                                 void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -273,3 +273,15 @@ def test_blocksparse_validation_and_sizes(lib):
     assert call(w=FAKE * 256 + 64) == WORKSPACE
     assert lib.attn_fwd_blocksparse(None, None, None, None, None, 0, n, d, 0.088, BF16, None, 1,
                                     None, 0, None) == OK  # empty batch
+
+
+def test_calib_mfma_loop_validation(lib):
+    call = lambda out=FAKE, wgs=512, iters=10, amp=1.0: lib.attn_calib_mfma_loop(
+        out, wgs, iters, amp, None)
+    assert call(out=None) == INVALID
+    assert call(out=FAKE + 4) == INVALID
+    assert call(wgs=0) == INVALID
+    assert call(wgs=1 << 31) == INVALID
+    assert call(iters=0) == INVALID
+    assert call(amp=float("nan")) == INVALID
+    assert call(amp=float("inf")) == INVALID
