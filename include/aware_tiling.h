@@ -30,7 +30,11 @@
  *  - Errors: validation happens before any HIP call; on an error nothing is
  *    enqueued and no output is touched.  ATTN_ERR_LAUNCH reports a HIP error
  *    seen right after enqueueing (its text is in attn_last_hip_error()).
- *  - Non-finite inputs propagate to the outputs; they are not detected.
+ *  - Non-finite inputs propagate to the outputs; they are not detected.  For
+ *    the forward entry points a NaN in query row i gives NaN in O row i and
+ *    lse i; in key row j, NaN in every row of that head; in V[j][c], NaN in
+ *    column c of every row of that head, lse unchanged.  Other rows, columns
+ *    and heads are computed as if the NaN were absent.
  */
 #ifndef AWARE_TILING_H_
 #define AWARE_TILING_H_
