@@ -23,11 +23,10 @@
 //     b.  It first merges its rows' statistics: m = max_J m_IJ,
 //     l = sum_J 2^(m_IJ - m) l_IJ (the streaming rescale rule applied across
 //     tiles), lse = (m + log2 l) ln 2.  Then for each key tile J it
-//     accumulates A_J = V_J^T E_IJ^T over 32-key panels (V panel global ->
-//     LDS with direct loads and read transposed, E straight from global
-//     memory into registers as the MFMA B operand) and adds
-//     f_IJ A_J with f_IJ = 2^(m_IJ - m) / l, a per-lane scalar (one query per
-//     lane).
+//     accumulates A_J = V_J^T E_IJ^T over 32-key panels (V and E panels
+//     global -> LDS with direct copies; V read transposed, E as stored as
+//     the MFMA B operand) and adds f_IJ A_J with f_IJ = 2^(m_IJ - m) / l, a
+//     per-lane scalar (one query per lane), in fp32 once per key tile.
 //
 // E is stored in the score kernel's accumulator order, so both kernels move
 // it with 16-byte lane accesses that are contiguous per wave: unit
@@ -42,6 +41,8 @@
 // unit order above (tiles past n hold finite values that only reach
 // discarded rows or are multiplied by 0), then m_IJ [bh][n][nt] and
 // l_IJ [bh][n][nt] fp32 with nt = ceil(n/b).
+#include <type_traits>
+
 #include "device_common.h"
 #include "lds_dma.h"
 #include "launch.h"
@@ -226,18 +227,6 @@ __global__ __launch_bounds__(B * 2) void sc_scores_exp(const bf16* __restrict__ 
 // ---------------------------------------------------------------------------
 // 2. Statistics merge and second product with per-tile row factors.
 
-// (E * f) in bf16 for 8 packed bf16 values and one fp32 factor.
-__device__ __forceinline__ bf16x8 scale_bf16x8(const u32x4& e, float f) {
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float lo = __builtin_bit_cast(float, e[i] << 16);
-    const float hi = __builtin_bit_cast(float, e[i] & 0xFFFF0000u);
-    r[i] = pack_bf16x2(lo * f, hi * f);
-  }
-  return __builtin_bit_cast(bf16x8, r);
-}
-
 template <int D, int B>
 __global__ __launch_bounds__(B * 2) void sc_value_product(const bf16* __restrict__ V,
                                                           const u32x4* __restrict__ E,
@@ -316,38 +305,75 @@ __global__ __launch_bounds__(B * 2) void sc_value_product(const bf16* __restrict
 
   // transposed V reads: lane group G = lane / 16 covers d rows 16 (G & 1)
   // .. +15 of a 32-row block and key half hh = G / 2; source lane sl points
-  // at key K0 + sl / 4, d D0 + 4 (sl % 4)
+  // at key K0 + sl / 4, d D0 + 4 (sl % 4).  The swizzle depends only on the
+  // low row bits, which the lane fixes, so each lane's byte offset of a
+  // 32-column block is computed once; the 16-key half, the 8-row piece and
+  // the ring slot add constants.
   const int G = lane >> 4, sl = lane & 15, hh = G >> 1;
-  float f = 0.f;
+  uint32_t vt_off[BD / 32];
+#pragma unroll
+  for (int db = 0; db < BD / 32; ++db) {
+    const int row0 = 4 * hh + (sl >> 2);
+    const int d0 = db * 32 + 16 * (G & 1) + 4 * (sl & 3);
+    vt_off[db] =
+        (uint32_t)(row0 * BD + ((d0 >> 3) ^ vtr_swizzle<BD * 2>(row0)) * 8 + (d0 & 7)) * 2u;
+  }
+  const uint32_t e_off = (uint32_t)(((wave * 2) * 64 + lane) * 8) * 2u;
+
+  // Key tile J: A_J = V_J^T E_IJ^T over its PPT panels, then out += f_IJ A_J.
+  // E enters the MFMA as stored (bf16); the row factor is applied in fp32
+  // once per tile.  P = (J PPT) % R is the ring slot of the tile's first
+  // panel, a constant in each instance.
+  auto key_tile = [&](auto phase_c, int J) {
+    constexpr int P = decltype(phase_c)::value;
+    f32x16 acc[BD / 32];
+    float f = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < PPT; ++kb) {
+      const int t = J * PPT + kb;
+      const int slot_rt = (P + kb) % R;  // constant after unrolling
+      // panel t's copies are complete once at most the later DIST - 1
+      // panels' copies are outstanding (vector-memory operations complete
+      // in issue order)
+      wait_vm<(DIST - 1) * OPS>();
+      slot_barrier();  // every lane's part of panel t; slot (t - 1) % R is free
+      issue(t + DIST);
+      if (kb == 0) f = qok ? fast_exp2(Ms[slot_rt][wave * 64 + lane] - m) * inv : 0.f;  // f_IJ
+      const char* Vs = reinterpret_cast<const char*>(Vp[slot_rt]);
+      const char* Es = reinterpret_cast<const char*>(Ep[slot_rt]);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const bf16x8 pb = *reinterpret_cast<const bf16x8*>(Es + e_off + half * 64 * 8 * 2);
+#pragma unroll
+        for (int db = 0; db < BD / 32; ++db) {
+          u32x2 part[2];
+#pragma unroll
+          for (int piece = 0; piece < 2; ++piece)
+            part[piece] = lds_read_tr16(reinterpret_cast<const bf16*>(
+                Vs + vt_off[db] + (16 * half + 8 * piece) * BD * 2));
+          const bf16x8 a =
+              __builtin_bit_cast(bf16x8, (u32x4{part[0][0], part[0][1], part[1][0], part[1][1]}));
+          acc[db] = mfma_bf16_32x32x16(a, pb, (kb == 0 && half == 0) ? f32x16{} : acc[db]);
+        }
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < BD / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) out[db][r] = __builtin_fmaf(f, acc[db][r], out[db][r]);
+  };
+
 #pragma unroll
   for (int s = 0; s < DIST; ++s) issue(s);
-  for (int t = 0; t < T; ++t) {
-    // panel t's copies are complete once at most the later DIST - 1 panels'
-    // copies are outstanding (vector-memory operations complete in issue
-    // order)
-    wait_vm<(DIST - 1) * OPS>();
-    slot_barrier();  // every lane's part of panel t; slot (t - 1) % R is free
-    issue(t + DIST);
-    const int slot = t % R;
-    if (t % PPT == 0) f = qok ? fast_exp2(Ms[slot][wave * 64 + lane] - m) * inv : 0.f;  // f_IJ
-    const bf16* Vs = Vp[slot];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const u32x4 e = *reinterpret_cast<const u32x4*>(&Ep[slot][((wave * 2 + half) * 64 + lane) * 8]);
-      const bf16x8 pb = scale_bf16x8(e, f);
-#pragma unroll
-      for (int db = 0; db < BD / 32; ++db) {
-        u32x2 part[2];
-#pragma unroll
-        for (int piece = 0; piece < 2; ++piece) {
-          const int row = 16 * half + 8 * piece + 4 * hh + (sl >> 2);
-          const int d0 = db * 32 + 16 * (G & 1) + 4 * (sl & 3);
-          const int phys = (d0 >> 3) ^ vtr_swizzle<BD * 2>(row);
-          part[piece] = lds_read_tr16(Vs + row * BD + phys * 8 + (d0 & 7));
-        }
-        const bf16x8 a =
-            __builtin_bit_cast(bf16x8, (u32x4{part[0][0], part[0][1], part[1][0], part[1][1]}));
-        out[db] = mfma_bf16_32x32x16(a, pb, out[db]);
+  for (int J = 0; J < nt; ++J) {
+    const int P = (J * PPT) % R;
+    if (P == 0) {
+      key_tile(std::integral_constant<int, 0>{}, J);
+    } else if constexpr (R > 1) {
+      if (P == 1) {
+        key_tile(std::integral_constant<int, 1 % R>{}, J);
+      } else if constexpr (R > 2) {
+        key_tile(std::integral_constant<int, 2 % R>{}, J);
       }
     }
   }
