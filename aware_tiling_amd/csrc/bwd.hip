@@ -707,15 +707,17 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv2(
 }
 
 // dK/dV kernel with every LDS address fixed before the loop.  Same
-// products and order as bwd_dkdv2, with V in LDS and the operands read two
-// MFMAs ahead; in addition each lane's byte offsets into a tile (row-wise
-// reads per k-step, transposed reads per 32-column block and half) are
-// computed once: the dual swizzle mixes only the low four bits of a row,
-// which the lane fixes, so the query sub-block, the k-step of the transposed
-// reads and the tile (Q or dO) only add constants, and the step is unrolled
-// by two so that the stage is a constant as well.  The loop then forms no
-// LDS address with vector instructions.
-template <int D, int NW>
+// products as bwd_dkdv2, with V in LDS and the operands read two MFMAs
+// ahead; in addition each lane's byte offsets into a tile (row-wise reads
+// per k-step, transposed reads per 32-column block and half) are computed
+// once: the dual swizzle mixes only the low four bits of a row, which the
+// lane fixes, so the query sub-block, the k-step of the transposed reads and
+// the tile (Q, dO, or the wave's V rows, stored with the same swizzle under
+// REORDER) only add constants, and the step is unrolled by two so that the
+// stage is a constant as well.  The loop then forms no LDS address with
+// vector instructions.  REORDER issues S, dP, dV, dK (instead of S, dV, dP,
+// dK) so that the exponentials overlap the dP MFMAs and dS the dV MFMAs.
+template <int D, int NW, bool REORDER = true>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv3(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ Dg,
@@ -758,7 +760,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv3(
 #pragma unroll
     for (int it = 0; it < 32 * RC / 64; ++it) {
       const int p = it * 64 + lane, row = p / RC, phys = p % RC;
-      const int logical = phys ^ chunk_swizzle<D * 2>(row);
+      const int logical = phys ^ (REORDER ? dual_swizzle<D * 2>(row) : chunk_swizzle<D * 2>(row));
       const int vrow = min(kblk * C::BKV + wave * 32 + row, n - 1);
       load_lds_16(Vh + (size_t)vrow * D + logical * 8, Vw + it * 64 * 8);
     }
@@ -845,16 +847,21 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv3(
             lds_read_tr16(reinterpret_cast<const bf16*>(t + troff[db][1] + ksp * 16 * D * 2));
         return __builtin_bit_cast(bf16x8, (u32x4{p0[0], p0[1], p1[0], p1[1]}));
       };
+      // operand sequence: S (Q rows), then with REORDER dP (dO rows), dV
+      // (dO^T), dK (Q^T); without it dV, dP, dK
+      constexpr int T_DV = REORDER ? 2 * NKK : NKK;
+      constexpr int T_DP = REORDER ? NKK : NKK + 2 * NDB;
+      constexpr int T_DK = 2 * NKK + 2 * NDB;
       auto fetch = [&](int t) {
         if (t < NKK) {
           a[t] = row_rd(Qs, t);
-        } else if (t < NKK + 2 * NDB) {
-          const int u = t - NKK;
+        } else if (t >= T_DV && t < T_DV + 2 * NDB) {
+          const int u = t - T_DV;
           a[t] = tr_rd(Gs, 2 * qb + u / NDB, u % NDB);
-        } else if (t < 2 * NKK + 2 * NDB) {
-          a[t] = row_rd(Gs, t - NKK - 2 * NDB);
+        } else if (t >= T_DP && t < T_DP + NKK) {
+          a[t] = row_rd(Gs, t - T_DP);
         } else {
-          const int u = t - 2 * NKK - 2 * NDB;
+          const int u = t - T_DK;
           a[t] = tr_rd(Qs, 2 * qb + u / NDB, u % NDB);
         }
       };
@@ -864,35 +871,57 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv3(
       };
 #pragma unroll
       for (int t = 0; t < AH; ++t) fetch(t);
-      // S = Q K^T, P = 2^(S c - lse2) in bf16, dV^T += dO^T P.
-      f32x16 s = {};
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) s = mfma_bf16_32x32x16(use(kk), kreg[kk], s);
+      // S = Q K^T, P = 2^(S c - lse2) in bf16, dV^T += dO^T P; dP = dO V^T,
+      // dS = P o (dP - D) from the same bf16 P, dK^T += Q^T dS.  With
+      // REORDER the dP MFMAs follow the S MFMAs directly, so the
+      // exponentials run while they execute and dS while the dV MFMAs do
+      // (two score-sized accumulators live instead of one).
+      f32x16 s = {}, dp = {};
       uint32_t pk[8];
+      auto scores = [&]() {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 l2 = *reinterpret_cast<const f32x4*>(st + qb * 32 + 8 * g + 4 * h);
-        float p[4];
+        for (int kk = 0; kk < NKK; ++kk) s = mfma_bf16_32x32x16(use(kk), kreg[kk], s);
+      };
+      auto exps = [&]() {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = fast_exp2(__builtin_fmaf(s[4 * g + e], c, -l2[e]));
-        pk[2 * g] = pack_bf16x2(p[0], p[1]);
-        pk[2 * g + 1] = pack_bf16x2(p[2], p[3]);
-      }
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 l2 = *reinterpret_cast<const f32x4*>(st + qb * 32 + 8 * g + 4 * h);
+          float p[4];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 bp = __builtin_bit_cast(
-            bf16x8, (u32x4{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]}));
+          for (int e = 0; e < 4; ++e) p[e] = fast_exp2(__builtin_fmaf(s[4 * g + e], c, -l2[e]));
+          pk[2 * g] = pack_bf16x2(p[0], p[1]);
+          pk[2 * g + 1] = pack_bf16x2(p[2], p[3]);
+        }
+      };
+      auto dv_update = [&]() {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          dvt[db] = mfma_bf16_32x32x16(use(NKK + ks * NDB + db), bp, dvt[db]);
-      }
-      // dP = dO V^T, dS = P o (dP - D) from the same bf16 P, dK^T += Q^T dS.
-      f32x16 dp = {};
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 bp = __builtin_bit_cast(
+              bf16x8, (u32x4{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]}));
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const bf16x8 vb =
-            *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(Vw) + voff[kk]);
-        dp = mfma_bf16_32x32x16(use(NKK + 2 * NDB + kk), vb, dp);
+          for (int db = 0; db < NDB; ++db)
+            dvt[db] = mfma_bf16_32x32x16(use(T_DV + ks * NDB + db), bp, dvt[db]);
+        }
+      };
+      auto dprod = [&]() {
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          const uint32_t vo = REORDER ? roff[kk] : voff[kk];
+          const bf16x8 vb =
+              *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(Vw) + vo);
+          dp = mfma_bf16_32x32x16(use(T_DP + kk), vb, dp);
+        }
+      };
+      if constexpr (REORDER) {
+        scores();
+        dprod();
+        exps();
+        dv_update();
+      } else {
+        scores();
+        exps();
+        dv_update();
+        dprod();
       }
       uint32_t dsk[8];
 #pragma unroll
@@ -909,7 +938,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv3(
             bf16x8, (u32x4{dsk[4 * ks], dsk[4 * ks + 1], dsk[4 * ks + 2], dsk[4 * ks + 3]}));
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-          dkt[db] = mfma_bf16_32x32x16(use(2 * NKK + 2 * NDB + ks * NDB + db), bs, dkt[db]);
+          dkt[db] = mfma_bf16_32x32x16(use(T_DK + ks * NDB + db), bs, dkt[db]);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);  // the next tile's copies, before the barrier
@@ -1261,11 +1290,12 @@ struct IntK {
   static constexpr int value = V;
 };
 
-// Kernel generation via ATTN_BWD_VARIANT: "v2" (default: bwd_dkdv3 and
-// bwd_dq3), or bwd_dq2 with bwd_dkdv2 in one of three forms: "v2l" (V in
-// LDS, operands read ahead), "v2r" (V in registers, operands read ahead),
-// "v2s" (V in registers, each LDS operand read just before its MFMA); or
-// "v1" (first-generation kernels); and the
+// Kernel generation via ATTN_BWD_VARIANT: "v2" (default: bwd_dkdv3 with
+// the dP MFMAs right after the S MFMAs, and bwd_dq3); "v3o" (bwd_dkdv3 in
+// the order S, dV, dP, dK); bwd_dq2 with bwd_dkdv2 in one of three forms:
+// "v2l" (V in LDS, operands read ahead), "v2r" (V in registers, operands
+// read ahead), "v2s" (V in registers, each LDS operand read just before its
+// MFMA); or "v1" (first-generation kernels); and the
 // waves per workgroup of the v2 kernels via ATTN_BWD_WAVES ("4" or "8").
 template <int D>
 hipError_t launch(const void* Q, const void* K, const void* V, const float* O, const void* dO,
@@ -1290,6 +1320,7 @@ hipError_t launch(const void* Q, const void* K, const void* V, const float* O, c
   const bool serial = var && strcmp(var, "v2s") == 0;
   const bool vreg = var && strcmp(var, "v2r") == 0;
   const bool vlds = var && strcmp(var, "v2l") == 0;
+  const bool first_order = var && strcmp(var, "v3o") == 0;
   const char* wv = getenv("ATTN_BWD_WAVES");
   const bool w4 = wv && strcmp(wv, "4") == 0;
   if (v1) {
@@ -1319,9 +1350,12 @@ hipError_t launch(const void* Q, const void* K, const void* V, const float* O, c
     else if (vlds)
       hipLaunchKernelGGL((bwd_dkdv2<D, NW, true, true>), dim3(total_kv), dim3(NW * 64), 0,
                          stream, q, k, v, g, lse2, Dbuf, dK, dV, (int)n, nkb, total_kv, c, scale);
+    else if (first_order)
+      hipLaunchKernelGGL((bwd_dkdv3<D, NW, false>), dim3(total_kv), dim3(NW * 64), 0, stream, q,
+                         k, v, g, lse2, Dbuf, dK, dV, (int)n, nkb, total_kv, c, scale);
     else
-      hipLaunchKernelGGL((bwd_dkdv3<D, NW>), dim3(total_kv), dim3(NW * 64), 0, stream, q, k, v,
-                         g, lse2, Dbuf, dK, dV, (int)n, nkb, total_kv, c, scale);
+      hipLaunchKernelGGL((bwd_dkdv3<D, NW, true>), dim3(total_kv), dim3(NW * 64), 0, stream, q, k,
+                         v, g, lse2, Dbuf, dK, dV, (int)n, nkb, total_kv, c, scale);
   };
   auto dqk = [&](auto nwc) {
     constexpr int NW = decltype(nwc)::value;
