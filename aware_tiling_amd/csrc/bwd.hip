@@ -45,47 +45,6 @@ __device__ __forceinline__ float bf_hi(uint32_t w) {
   return __builtin_bit_cast(float, w & 0xffff0000u);
 }
 
-// Write one 4-row x 8-column bf16 block (v[e] holds row row0+e, columns
-// col0..col0+7) into a transposed tile dst[col][ROWS]: row col0+2w(+1) of
-// the destination receives the four source rows as four contiguous elements
-// at position vt_key_pos(row0) (row0 a multiple of 4), with the 16-byte
-// chunk swizzle of the destination rows.
-template <int ROWS>
-__device__ __forceinline__ void store_transposed_4x8(bf16* dst, int row0, int col0,
-                                                     const u32x4 (&v)[4]) {
-  const int pos = vt_key_pos(row0);
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const int r0 = col0 + 2 * w, r1 = r0 + 1;
-    u32x2 lo = {pair_lo(v[0][w], v[1][w]), pair_lo(v[2][w], v[3][w])};
-    u32x2 hi = {pair_hi(v[0][w], v[1][w]), pair_hi(v[2][w], v[3][w])};
-    *reinterpret_cast<u32x2*>(dst + r0 * ROWS + (((pos >> 3) ^ chunk_swizzle<ROWS * 2>(r0)) * 8) +
-                              (pos & 7)) = lo;
-    *reinterpret_cast<u32x2*>(dst + r1 * ROWS + (((pos >> 3) ^ chunk_swizzle<ROWS * 2>(r1)) * 8) +
-                              (pos & 7)) = hi;
-  }
-}
-
-// Write the same block row-major into dst[row][COLS] with swizzled chunks.
-template <int COLS>
-__device__ __forceinline__ void store_rows_4x8(bf16* dst, int row0, int col0,
-                                               const u32x4 (&v)[4]) {
-  const int cc = col0 >> 3;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int r = row0 + e;
-    *reinterpret_cast<u32x4*>(dst + r * COLS + ((cc ^ chunk_swizzle<COLS * 2>(r)) * 8)) = v[e];
-  }
-}
-
-// A operand (32 rows x 16 k) from a row-major swizzled tile: row `row`,
-// logical 16-byte chunk `chunk`.
-template <int COLS>
-__device__ __forceinline__ bf16x8 lds_operand(const bf16* tile, int row, int chunk) {
-  return *reinterpret_cast<const bf16x8*>(tile + row * COLS +
-                                          ((chunk ^ chunk_swizzle<COLS * 2>(row)) * 8));
-}
-
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -121,307 +80,14 @@ __global__ __launch_bounds__(256) void bwd_preprocess(const float* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// 2. dK, dV
-
-template <int D>
-struct DkdvCfg {
-  static constexpr int NW = 4, NT = 256, BKV = NW * 32, BQ = 32;
-  static constexpr int ITEMS = (BQ / 4) * (D / 8);  // 4x8 blocks per tile (per tensor)
-  static constexpr int ITERS = (2 * ITEMS + NT - 1) / NT;
-  static constexpr int TILE = BQ * D;               // bf16 elements per tile
-  // per buffer: Q rows, dO rows, Q^T, dO^T, then lse2 and D (floats)
-  static constexpr int BUF_BF16 = 4 * TILE;
-};
-
-template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dg,
-    float* __restrict__ dK, float* __restrict__ dV, int n, int nkb, int total, float c,
-    float scale) {
-  using C = DkdvCfg<D>;
-  constexpr int BQ = C::BQ;
-  __shared__ __attribute__((aligned(16))) bf16 tiles[2][C::BUF_BF16];
-  __shared__ __attribute__((aligned(16))) float stats[2][2 * BQ];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = lane >> 5, li = lane & 31;
-  const int tile = xcd_remap(blockIdx.x, total);
-  const int head = tile / nkb, kblk = tile - head * nkb;
-  const size_t hoff = (size_t)head * n * D;
-  const bf16 *Qh = Q + hoff, *Kh = K + hoff, *Vh = V + hoff, *dOh = dO + hoff;
-  const float* lseh = lse + (size_t)head * n;
-  const float* Dh = Dg + (size_t)head * n;
-  const int key = kblk * C::BKV + wave * 32 + li;
-
-  // K and V rows of this wave's keys as B operands (lane: row `key`).
-  bf16x8 kreg[D / 16], vreg[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    kreg[kk] = key < n ? *reinterpret_cast<const bf16x8*>(Kh + (size_t)key * D + 16 * kk + 8 * h)
-                       : bf16x8{};
-    vreg[kk] = key < n ? *reinterpret_cast<const bf16x8*>(Vh + (size_t)key * D + 16 * kk + 8 * h)
-                       : bf16x8{};
-  }
-  f32x16 dkt[D / 32], dvt[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) dkt[db] = dvt[db] = f32x16{};
-
-  // Staging registers: item x < ITEMS is a 4x8 block of Q, else of dO.
-  u32x4 st[C::ITERS][4];
-  float sl = 0.f;
-  auto load = [&](int i) {
-#pragma unroll
-    for (int it = 0; it < C::ITERS; ++it) {
-      const int x = tid + it * C::NT;
-      const int y = x % C::ITEMS;
-      const int g = y % (BQ / 4), cc = y / (BQ / 4);
-      const bf16* src = x < C::ITEMS ? Qh : dOh;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int q = i * BQ + 4 * g + e;
-        st[it][e] = (x < 2 * C::ITEMS && q < n)
-                        ? *reinterpret_cast<const u32x4*>(src + (size_t)q * D + cc * 8)
-                        : u32x4{};
-      }
-    }
-    if (tid < 2 * BQ) {
-      const int q = i * BQ + (tid % BQ);
-      if (tid < BQ)
-        sl = q < n ? lseh[q] * kLog2e : INFINITY;  // +inf: rows past n get P = 0
-      else
-        sl = q < n ? Dh[q] : 0.f;
-    }
-  };
-  auto store = [&](int buf) {
-    bf16* base = tiles[buf];
-#pragma unroll
-    for (int it = 0; it < C::ITERS; ++it) {
-      const int x = tid + it * C::NT;
-      if (x < 2 * C::ITEMS) {
-        const int y = x % C::ITEMS;
-        const int g = y % (BQ / 4), cc = y / (BQ / 4);
-        const int which = x < C::ITEMS ? 0 : 1;  // 0: Q, 1: dO
-        store_rows_4x8<D>(base + which * C::TILE, 4 * g, 8 * cc, st[it]);
-        store_transposed_4x8<BQ>(base + (2 + which) * C::TILE, 4 * g, 8 * cc, st[it]);
-      }
-    }
-    if (tid < 2 * BQ) stats[buf][tid] = sl;
-  };
-
-  const int nqt = (n + BQ - 1) / BQ;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int i = 0; i < nqt; ++i) {
-    const int buf = i & 1;
-    if (i + 1 < nqt) load(i + 1);
-    const bf16* Qs = tiles[buf];
-    const bf16* dOs = tiles[buf] + C::TILE;
-    const bf16* Qt = tiles[buf] + 2 * C::TILE;
-    const bf16* dOt = tiles[buf] + 3 * C::TILE;
-
-    // S = Q K^T and dP = dO V^T (32 queries x 32 keys per wave).
-    f32x16 s = {}, dp = {};
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      s = mfma_bf16_32x32x16(lds_operand<D>(Qs, li, 2 * kk + h), kreg[kk], s);
-      dp = mfma_bf16_32x32x16(lds_operand<D>(dOs, li, 2 * kk + h), vreg[kk], dp);
-    }
-    // Lane holds column `key`, rows (queries) 8(r/4) + 4h + r%4.
-    uint32_t pk[8], dsk[8];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 l2 = *reinterpret_cast<const f32x4*>(&stats[buf][8 * g + 4 * h]);
-      const f32x4 dd = *reinterpret_cast<const f32x4*>(&stats[buf][BQ + 8 * g + 4 * h]);
-      float p[4], ds[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p[e] = fast_exp2(__builtin_fmaf(s[4 * g + e], c, -l2[e]));
-        ds[e] = p[e] * (dp[4 * g + e] - dd[e]);
-      }
-      pk[2 * g] = pack_bf16x2(p[0], p[1]);
-      pk[2 * g + 1] = pack_bf16x2(p[2], p[3]);
-      dsk[2 * g] = pack_bf16x2(ds[0], ds[1]);
-      dsk[2 * g + 1] = pack_bf16x2(ds[2], ds[3]);
-    }
-    // dV^T += dO^T P, dK^T += Q^T dS (contraction over the tile's queries).
-#pragma unroll
-    for (int ks = 0; ks < BQ / 16; ++ks) {
-      const bf16x8 bp = __builtin_bit_cast(
-          bf16x8, (u32x4{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]}));
-      const bf16x8 bs = __builtin_bit_cast(
-          bf16x8, (u32x4{dsk[4 * ks], dsk[4 * ks + 1], dsk[4 * ks + 2], dsk[4 * ks + 3]}));
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        dvt[db] = mfma_bf16_32x32x16(lds_operand<BQ>(dOt, db * 32 + li, 2 * ks + h), bp, dvt[db]);
-        dkt[db] = mfma_bf16_32x32x16(lds_operand<BQ>(Qt, db * 32 + li, 2 * ks + h), bs, dkt[db]);
-      }
-    }
-    if (i + 1 < nqt) store(buf ^ 1);
-    __syncthreads();
-  }
-
-  if (key < n) {
-    float* dKr = dK + hoff + (size_t)key * D;
-    float* dVr = dV + hoff + (size_t)key * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = db * 32 + 8 * g + 4 * h;
-        f32x4 a = {dkt[db][4 * g] * scale, dkt[db][4 * g + 1] * scale, dkt[db][4 * g + 2] * scale,
-                   dkt[db][4 * g + 3] * scale};
-        f32x4 b = {dvt[db][4 * g], dvt[db][4 * g + 1], dvt[db][4 * g + 2], dvt[db][4 * g + 3]};
-        *reinterpret_cast<f32x4*>(dKr + col) = a;
-        *reinterpret_cast<f32x4*>(dVr + col) = b;
-      }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// 3. dQ
-
-template <int D>
-struct DqCfg {
-  static constexpr int NW = 4, NT = 256, BQB = NW * 32, BC = 32;
-  static constexpr int ITEMS = (BC / 4) * (D / 8);
-  static constexpr int ITERS = (2 * ITEMS + NT - 1) / NT;
-  static constexpr int TILE = BC * D;
-  static constexpr int BUF_BF16 = 3 * TILE;  // K rows, V rows, K^T
-};
-
-template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dq(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dg,
-    float* __restrict__ dQ, int n, int nqb, int total, float c, float scale) {
-  using C = DqCfg<D>;
-  constexpr int BC = C::BC;
-  __shared__ __attribute__((aligned(16))) bf16 tiles[2][C::BUF_BF16];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = lane >> 5, li = lane & 31;
-  const int tile = xcd_remap(blockIdx.x, total);
-  const int head = tile / nqb, qblk = tile - head * nqb;
-  const size_t hoff = (size_t)head * n * D;
-  const bf16 *Qh = Q + hoff, *Kh = K + hoff, *Vh = V + hoff, *dOh = dO + hoff;
-  const int q = qblk * C::BQB + wave * 32 + li;
-
-  bf16x8 qreg[D / 16], dogreg[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    qreg[kk] = q < n ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)q * D + 16 * kk + 8 * h)
-                     : bf16x8{};
-    dogreg[kk] = q < n ? *reinterpret_cast<const bf16x8*>(dOh + (size_t)q * D + 16 * kk + 8 * h)
-                       : bf16x8{};
-  }
-  const float l2 = q < n ? lse[(size_t)head * n + q] * kLog2e : 0.f;
-  const float dq_d = q < n ? Dg[(size_t)head * n + q] : 0.f;
-  f32x16 dqt[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) dqt[db] = f32x16{};
-
-  u32x4 st[C::ITERS][4];
-  auto load = [&](int j) {
-#pragma unroll
-    for (int it = 0; it < C::ITERS; ++it) {
-      const int x = tid + it * C::NT;
-      const int y = x % C::ITEMS;
-      const int g = y % (BC / 4), cc = y / (BC / 4);
-      const bf16* src = x < C::ITEMS ? Kh : Vh;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = j * BC + 4 * g + e;
-        st[it][e] = (x < 2 * C::ITEMS && key < n)
-                        ? *reinterpret_cast<const u32x4*>(src + (size_t)key * D + cc * 8)
-                        : u32x4{};
-      }
-    }
-  };
-  auto store = [&](int buf) {
-    bf16* base = tiles[buf];
-#pragma unroll
-    for (int it = 0; it < C::ITERS; ++it) {
-      const int x = tid + it * C::NT;
-      if (x < 2 * C::ITEMS) {
-        const int y = x % C::ITEMS;
-        const int g = y % (BC / 4), cc = y / (BC / 4);
-        if (x < C::ITEMS) {
-          store_rows_4x8<D>(base, 4 * g, 8 * cc, st[it]);
-          store_transposed_4x8<BC>(base + 2 * C::TILE, 4 * g, 8 * cc, st[it]);
-        } else {
-          store_rows_4x8<D>(base + C::TILE, 4 * g, 8 * cc, st[it]);
-        }
-      }
-    }
-  };
-
-  const int nkt = (n + BC - 1) / BC;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int j = 0; j < nkt; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < nkt) load(j + 1);
-    const bf16* Ks = tiles[buf];
-    const bf16* Vs = tiles[buf] + C::TILE;
-    const bf16* Kt = tiles[buf] + 2 * C::TILE;
-
-    // S^T = K Q^T and dP^T = V dO^T (32 keys x 32 queries per wave).
-    f32x16 s = {}, dp = {};
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      s = mfma_bf16_32x32x16(lds_operand<D>(Ks, li, 2 * kk + h), qreg[kk], s);
-      dp = mfma_bf16_32x32x16(lds_operand<D>(Vs, li, 2 * kk + h), dogreg[kk], dp);
-    }
-    // Lane holds query column q, rows (keys) 8(r/4) + 4h + r%4.
-    const bool tail = j == nkt - 1 && (n % BC) != 0;
-    uint32_t dsk[8];
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      float p0 = fast_exp2(__builtin_fmaf(s[r], c, -l2));
-      float p1 = fast_exp2(__builtin_fmaf(s[r + 1], c, -l2));
-      if (tail) {
-        const int k0 = j * BC + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (k0 >= n) p0 = 0.f;
-        if (k0 + 1 >= n) p1 = 0.f;
-      }
-      dsk[r >> 1] = pack_bf16x2(p0 * (dp[r] - dq_d), p1 * (dp[r + 1] - dq_d));
-    }
-    // dQ^T += K^T dS^T (contraction over the tile's keys).
-#pragma unroll
-    for (int ks = 0; ks < BC / 16; ++ks) {
-      const bf16x8 bs = __builtin_bit_cast(
-          bf16x8, (u32x4{dsk[4 * ks], dsk[4 * ks + 1], dsk[4 * ks + 2], dsk[4 * ks + 3]}));
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-        dqt[db] = mfma_bf16_32x32x16(lds_operand<BC>(Kt, db * 32 + li, 2 * ks + h), bs, dqt[db]);
-    }
-    if (j + 1 < nkt) store(buf ^ 1);
-    __syncthreads();
-  }
-
-  if (q < n) {
-    float* dQr = dQ + hoff + (size_t)q * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 a = {dqt[db][4 * g] * scale, dqt[db][4 * g + 1] * scale, dqt[db][4 * g + 2] * scale,
-                   dqt[db][4 * g + 3] * scale};
-        *reinterpret_cast<f32x4*>(dQr + db * 32 + 8 * g + 4 * h) = a;
-      }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Second-generation kernels (default).  Tiles of Q and dO (dK/dV kernel) and
-// of K and V (dQ kernel) go global -> LDS with global_load_lds_dwordx4 and
-// stay row-major.  In the default kernels these copies are issued from
-// inline assembly (dma16), so that the next tile's copies stay in flight
-// while the current tile is read and are waited for only at the end of the
-// step.  The transposed operands (Q^T, dO^T, K^T) come from
+// dK/dV and dQ kernels.  Tiles of Q and dO (dK/dV kernel) and of K and V
+// (dQ kernel) go global -> LDS with global_load_lds_dwordx4 and stay
+// row-major.  In the default kernels (bwd_dkdv3, bwd_dq3) these copies are
+// issued from inline assembly (dma16), so that the next tile's copies stay
+// in flight while the current tile is read (with compiler-visible copies in
+// flight every wait for an LDS read becomes lgkmcnt(0)) and are waited for
+// only at the end of the step; bwd_dkdv2 and bwd_dq2 are the previous
+// generation.  The transposed operands (Q^T, dO^T, K^T) come from
 // ds_read_b64_tr_b16 on the same tiles, whose swizzle (dual_swizzle) keeps
 // both the row-wise and the transposed reads free of bank conflicts.  No
 // staging registers and no vector-ALU transposition, so two waves fit per
@@ -485,7 +151,7 @@ struct Dkdv2Cfg {
   static_assert(CHUNKS % (NW * 64) == 0, "tile must split into whole wave loads");
 };
 
-template <int D, int NW, bool PF, bool VL>
+template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv2(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ Dg,
@@ -507,31 +173,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv2(
   const float* Dh = Dg + (size_t)head * n;
   const int key = kblk * C::BKV + wave * 32 + li;
 
-  // K rows of the wave's 32 keys stay in registers (B operand of S).  V rows
-  // (B operand of dP) stay in registers too, or with VL in a wave-private
-  // LDS region, which frees 32 registers per lane at d = 128 for reading
-  // operands ahead.  Keys past n: K = 0 in registers, V rows clamped to n-1
-  // in LDS; either way only the unstored dK/dV rows of those keys see them.
-  __shared__ __attribute__((aligned(1024))) bf16 vtile[VL ? NW * 32 * D : 8];
-  bf16* Vw = vtile + (VL ? wave * 32 * D : 0);
-  bf16x8 kreg[D / 16], vreg[VL ? 1 : D / 16];
+  bf16x8 kreg[D / 16], vreg[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
     kreg[kk] = key < n ? *reinterpret_cast<const bf16x8*>(Kh + (size_t)key * D + 16 * kk + 8 * h)
                        : bf16x8{};
-    if constexpr (!VL)
-      vreg[kk] = key < n ? *reinterpret_cast<const bf16x8*>(Vh + (size_t)key * D + 16 * kk + 8 * h)
-                         : bf16x8{};
-  }
-  if constexpr (VL) {
-    constexpr int RC = D / 8;  // 16-byte chunks per row
-#pragma unroll
-    for (int it = 0; it < 32 * RC / 64; ++it) {
-      const int p = it * 64 + lane, row = p / RC, phys = p % RC;
-      const int logical = phys ^ chunk_swizzle<D * 2>(row);
-      const int vrow = min(kblk * C::BKV + wave * 32 + row, n - 1);
-      load_lds_16(Vh + (size_t)vrow * D + logical * 8, Vw + it * 64 * 8);
-    }
+    vreg[kk] = key < n ? *reinterpret_cast<const bf16x8*>(Vh + (size_t)key * D + 16 * kk + 8 * h)
+                       : bf16x8{};
   }
   f32x16 dkt[D / 32], dvt[D / 32];
 #pragma unroll
@@ -555,18 +203,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv2(
 #pragma unroll
       for (int it = 0; it < C::INSTS; ++it) {
         const int p0 = wave * C::WAVE_CHUNKS + it * 64;
-        if constexpr (PF) {
-          dma16(qb + toff[it], tiles[buf] + p0 * 8);
-          dma16(gb + toff[it], tiles[buf] + C::TILE + p0 * 8);
-        } else {
-          load_lds_16(qb + toff[it], tiles[buf] + p0 * 8);
-          load_lds_16(gb + toff[it], tiles[buf] + C::TILE + p0 * 8);
-        }
+        load_lds_16(qb + toff[it], tiles[buf] + p0 * 8);
+        load_lds_16(gb + toff[it], tiles[buf] + C::TILE + p0 * 8);
       }
     } else {
-      tile_load_lds<D, PF>(Qh, tiles[buf], i, BQ, n, wave, lane, C::WAVE_CHUNKS, C::INSTS, true);
-      tile_load_lds<D, PF>(dOh, tiles[buf] + C::TILE, i, BQ, n, wave, lane, C::WAVE_CHUNKS,
-                           C::INSTS, true);
+      tile_load_lds<D>(Qh, tiles[buf], i, BQ, n, wave, lane, C::WAVE_CHUNKS, C::INSTS, true);
+      tile_load_lds<D>(dOh, tiles[buf] + C::TILE, i, BQ, n, wave, lane, C::WAVE_CHUNKS, C::INSTS,
+                       true);
     }
     if (wave * 64 < 2 * BQ) {  // whole waves: 2 BQ is a multiple of 64
       // A query row past n (a clamped copy of row n-1) gets lse2 = +inf,
@@ -575,13 +218,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv2(
       // clamped row's (finite), and 0 x finite = 0 in dS.
       const int which = tid / BQ, r = tid - which * BQ;
       const int qrow = min(i * BQ + r, n - 1);
-      if (which == 0 && i * BQ + r >= n) {
+      if (which == 0 && i * BQ + r >= n)
         stats[buf][tid] = __builtin_inff();
-      } else if constexpr (PF) {
-        dma4((which == 0 ? lseh : Dh) + qrow, &stats[buf][wave * 64]);
-      } else {
+      else
         load_lds_4((which == 0 ? lseh : Dh) + qrow, &stats[buf][wave * 64]);
-      }
     }
   };
 
@@ -604,40 +244,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv2(
       // S = Q K^T (32 queries x 32 keys per wave), P in bf16, dV^T += dO^T P;
       // then dP = dO V^T, dS = P o (dP - D) from the same bf16 P, and
       // dK^T += Q^T dS.  Only one score-sized accumulator is live at a time.
-      // With PF the LDS operands of the 2 (D/16 + D/16) MFMAs are read AH
-      // MFMAs ahead of their use, in one sequence across the four products,
-      // so an MFMA does not wait for the read that feeds it.
-      constexpr int NKK = D / 16, NDB = D / 32;
-      constexpr int NA = 2 * NKK + 4 * NDB;
-      constexpr int AH = PF ? 2 : 0;
-      bf16x8 a[NA];
-      auto fetch = [&](int t) {
-        if (t < NKK) {
-          a[t] = row_operand<D>(Qs, qb * 32 + lio, 2 * t + h, true);
-        } else if (t < NKK + 2 * NDB) {
-          const int u = t - NKK;
-          a[t] = tr_operand<D>(dOs, 2 * qb + u / NDB, u % NDB, laneo);
-        } else if (t < 2 * NKK + 2 * NDB) {
-          const int u = t - NKK - 2 * NDB;
-          a[t] = row_operand<D>(dOs, qb * 32 + lio, 2 * u + h, true);
-        } else {
-          const int u = t - 2 * NKK - 2 * NDB;
-          a[t] = tr_operand<D>(Qs, 2 * qb + u / NDB, u % NDB, laneo);
-        }
-      };
-      auto use = [&](int t) -> bf16x8 {
-        if constexpr (PF) {
-          if (t + AH < NA) fetch(t + AH);
-        } else {
-          fetch(t);
-        }
-        return a[t];
-      };
-#pragma unroll
-      for (int t = 0; t < AH; ++t) fetch(t);
       f32x16 s = {};
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) s = mfma_bf16_32x32x16(use(kk), kreg[kk], s);
+      for (int kk = 0; kk < D / 16; ++kk)
+        s = mfma_bf16_32x32x16(row_operand<D>(Qs, qb * 32 + lio, 2 * kk + h, true), kreg[kk], s);
       uint32_t pk[8];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -653,19 +263,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv2(
         const bf16x8 bp = __builtin_bit_cast(
             bf16x8, (u32x4{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]}));
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          dvt[db] = mfma_bf16_32x32x16(use(NKK + ks * NDB + db), bp, dvt[db]);
+        for (int db = 0; db < D / 32; ++db)
+          dvt[db] = mfma_bf16_32x32x16(tr_operand<D>(dOs, 2 * qb + ks, db, laneo), bp, dvt[db]);
       }
       f32x16 dp = {};
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        if constexpr (VL) {
-          const bf16x8 vb = row_operand<D>(Vw, lio, 2 * kk + h, false);
-          dp = mfma_bf16_32x32x16(use(NKK + 2 * NDB + kk), vb, dp);
-        } else {
-          dp = mfma_bf16_32x32x16(use(NKK + 2 * NDB + kk), vreg[kk], dp);
-        }
-      }
+      for (int kk = 0; kk < D / 16; ++kk)
+        dp = mfma_bf16_32x32x16(row_operand<D>(dOs, qb * 32 + lio, 2 * kk + h, true), vreg[kk],
+                                dp);
       uint32_t dsk[8];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -681,8 +286,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv2(
         const bf16x8 bs = __builtin_bit_cast(
             bf16x8, (u32x4{dsk[4 * ks], dsk[4 * ks + 1], dsk[4 * ks + 2], dsk[4 * ks + 3]}));
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          dkt[db] = mfma_bf16_32x32x16(use(2 * NKK + 2 * NDB + ks * NDB + db), bs, dkt[db]);
+        for (int db = 0; db < D / 32; ++db)
+          dkt[db] = mfma_bf16_32x32x16(tr_operand<D>(Qs, 2 * qb + ks, db, laneo), bs, dkt[db]);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -1290,13 +895,12 @@ struct IntK {
   static constexpr int value = V;
 };
 
-// Kernel generation via ATTN_BWD_VARIANT: "v2" (default: bwd_dkdv3 with
-// the dP MFMAs right after the S MFMAs, and bwd_dq3); "v3o" (bwd_dkdv3 in
-// the order S, dV, dP, dK); bwd_dq2 with bwd_dkdv2 in one of three forms:
-// "v2l" (V in LDS, operands read ahead), "v2r" (V in registers, operands
-// read ahead), "v2s" (V in registers, each LDS operand read just before its
-// MFMA); or "v1" (first-generation kernels); and the
-// waves per workgroup of the v2 kernels via ATTN_BWD_WAVES ("4" or "8").
+// Kernel generation via ATTN_BWD_VARIANT: unset or "v3" (default:
+// bwd_dkdv3 with the dP MFMAs right after the S MFMAs, and bwd_dq3), "v3o"
+// (bwd_dkdv3 in the order S, dV, dP, dK, and bwd_dq3), or "v2" (the
+// previous generation, bwd_dkdv2 and bwd_dq2: V in registers, every LDS
+// address recomputed and every operand read just before its MFMA); the
+// waves per workgroup via ATTN_BWD_WAVES ("4" or "8", default 8).
 template <int D>
 hipError_t launch(const void* Q, const void* K, const void* V, const float* O, const void* dO,
                   const float* lse, float* dQ, float* dK, float* dV, int64_t bh, int64_t n,
@@ -1316,40 +920,18 @@ hipError_t launch(const void* Q, const void* K, const void* V, const float* O, c
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const char* var = getenv("ATTN_BWD_VARIANT");
-  const bool v1 = var && strcmp(var, "v1") == 0;
-  const bool serial = var && strcmp(var, "v2s") == 0;
-  const bool vreg = var && strcmp(var, "v2r") == 0;
-  const bool vlds = var && strcmp(var, "v2l") == 0;
+  const bool gen2 = var && strcmp(var, "v2") == 0;
   const bool first_order = var && strcmp(var, "v3o") == 0;
   const char* wv = getenv("ATTN_BWD_WAVES");
   const bool w4 = wv && strcmp(wv, "4") == 0;
-  if (v1) {
-    const int nkb = (int)((n + DkdvCfg<D>::BKV - 1) / DkdvCfg<D>::BKV);
-    const int total_kv = (int)(bh * nkb);
-    hipLaunchKernelGGL(bwd_dkdv<D>, dim3(total_kv), dim3(256), 0, stream, q, k, v, g, lse, Dbuf,
-                       dK, dV, (int)n, nkb, total_kv, c, scale);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int nqb = (int)((n + DqCfg<D>::BQB - 1) / DqCfg<D>::BQB);
-    const int total_q = (int)(bh * nqb);
-    hipLaunchKernelGGL(bwd_dq<D>, dim3(total_q), dim3(256), 0, stream, q, k, v, g, lse, Dbuf, dQ,
-                       (int)n, nqb, total_q, c, scale);
-    return hipGetLastError();
-  }
   auto dkdv = [&](auto nwc) {
     constexpr int NW = decltype(nwc)::value;
     using Cf = Dkdv2Cfg<D, NW>;
     const int nkb = (int)((n + Cf::BKV - 1) / Cf::BKV);
     const int total_kv = (int)(bh * nkb);
-    if (serial)
-      hipLaunchKernelGGL((bwd_dkdv2<D, NW, false, false>), dim3(total_kv), dim3(NW * 64), 0,
-                         stream, q, k, v, g, lse2, Dbuf, dK, dV, (int)n, nkb, total_kv, c, scale);
-    else if (vreg)
-      hipLaunchKernelGGL((bwd_dkdv2<D, NW, true, false>), dim3(total_kv), dim3(NW * 64), 0,
-                         stream, q, k, v, g, lse2, Dbuf, dK, dV, (int)n, nkb, total_kv, c, scale);
-    else if (vlds)
-      hipLaunchKernelGGL((bwd_dkdv2<D, NW, true, true>), dim3(total_kv), dim3(NW * 64), 0,
-                         stream, q, k, v, g, lse2, Dbuf, dK, dV, (int)n, nkb, total_kv, c, scale);
+    if (gen2)
+      hipLaunchKernelGGL((bwd_dkdv2<D, NW>), dim3(total_kv), dim3(NW * 64), 0, stream, q, k, v,
+                         g, lse2, Dbuf, dK, dV, (int)n, nkb, total_kv, c, scale);
     else if (first_order)
       hipLaunchKernelGGL((bwd_dkdv3<D, NW, false>), dim3(total_kv), dim3(NW * 64), 0, stream, q,
                          k, v, g, lse2, Dbuf, dK, dV, (int)n, nkb, total_kv, c, scale);
@@ -1362,7 +944,7 @@ hipError_t launch(const void* Q, const void* K, const void* V, const float* O, c
     using Cf = Dq2Cfg<D, NW, 64>;
     const int nqb = (int)((n + Cf::BQB - 1) / Cf::BQB);
     const int total_q = (int)(bh * nqb);
-    if (serial || vreg || vlds)
+    if (gen2)
       hipLaunchKernelGGL((bwd_dq2<D, NW, 64>), dim3(total_q), dim3(NW * 64), 0, stream, q, k, v,
                          g, lse, Dbuf, dQ, (int)n, nqb, total_q, c, scale);
     else

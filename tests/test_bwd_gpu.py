@@ -90,9 +90,8 @@ def test_bwd_rejects_unsupported_head_dim():
         at.attn_bwd(q, k, v, o, do, lse)
 
 
-@pytest.mark.parametrize("variant,waves", [("v1", None), ("v2", "4"), ("v2", "8"), ("v2l", "8"),
-                                           ("v2r", "8"), ("v2s", "8"), ("v2l", "4"),
-                                           ("v3o", "8"), ("v3o", "4")])
+@pytest.mark.parametrize("variant,waves", [("v3", "8"), ("v3", "4"), ("v3o", "8"), ("v3o", "4"),
+                                           ("v2", "8"), ("v2", "4")])
 def test_bwd_every_kernel_variant(variant, waves, monkeypatch):
     monkeypatch.setenv("ATTN_BWD_VARIANT", variant)
     if waves:
