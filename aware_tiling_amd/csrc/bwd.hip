@@ -382,11 +382,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv3(
     const int row = p / (D / 8), phys = p % (D / 8);
     toff[it] = (uint32_t)(row * D + (phys ^ dual_swizzle<D * 2>(row)) * 8) * 2u;
   }
+  // roff: Q, dO (and, under REORDER, V) rows; voff: V rows stored with the
+  // row swizzle (order S, dV, dP, dK)
   uint32_t roff[NKK], voff[NKK], troff[NDB][2];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
     roff[kk] = (uint32_t)(li * D + ((2 * kk + h) ^ dual_swizzle<D * 2>(li)) * 8) * 2u;
-    voff[kk] = (uint32_t)(li * D + ((2 * kk + h) ^ chunk_swizzle<D * 2>(li)) * 8) * 2u;
+    voff[kk] = REORDER ? roff[kk]
+                       : (uint32_t)(li * D + ((2 * kk + h) ^ chunk_swizzle<D * 2>(li)) * 8) * 2u;
   }
   {
     const int G = lane >> 4, sl = lane & 15, hh = G >> 1;
@@ -511,9 +514,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv3(
       auto dprod = [&]() {
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          const uint32_t vo = REORDER ? roff[kk] : voff[kk];
           const bf16x8 vb =
-              *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(Vw) + vo);
+              *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(Vw) + voff[kk]);
           dp = mfma_bf16_32x32x16(use(T_DP + kk), vb, dp);
         }
       };
