@@ -37,6 +37,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-seco
        python bench.py --summarize-counters DIR  (write the traffic summary)
        python bench.py --tile-sweep [--steps K]   (fused forward at B_r x B_c shapes)
        python bench.py --summarize-sweep DIR TIMING.jsonl OUT.md  (sweep table)
+       python bench.py --smallcache-sweep [--steps K]   (square tiles at each b, d = 256)
+       python bench.py --summarize-smallcache-sweep DIR TIMING.jsonl OUT.md
 """
 from __future__ import annotations
 
@@ -230,44 +232,82 @@ def summarize_counters(pmc_dir: str, out_path: str = TRAFFIC_FILE):
     print(json.dumps(summary))
 
 
+def counter_means(path: str, counter: str, key_of) -> dict:
+    """Per-dispatch mean of `counter` in a rocprofv3 counter_collection.csv,
+    grouped by key_of(kernel name) (rows whose key is None are skipped)."""
+    import csv
+    import statistics
+
+    vals = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            key = key_of(r["Kernel_Name"])
+            if key is not None:
+                vals.setdefault(key, []).append(float(r["Counter_Value"]))
+    return {k: statistics.mean(v) for k, v in vals.items()}
+
+
+def copy_counter(path: str, counter: str) -> float:
+    """Mean of `counter` over the calibration copies (--calibrate-copy)."""
+    return counter_means(path, counter, lambda n: "copy" if "copyBuffer" in n else None)["copy"]
+
+
+def fused_sweep_key(name: str):
+    """(B_r, B_c) of a d = 128 direct fused-forward kernel name, else None."""
+    import re
+
+    m = re.search(r"fwd_fused_bf16_direct_kernel<128, (\d+), (\d+),", name)
+    return (32 * int(m.group(1)), int(m.group(2))) if m else None
+
+
+def mfma_busy(pmc_dir: str, fname: str, key_of) -> dict:
+    """Matrix-core utilisation per key: SQ_VALU_MFMA_BUSY_CYCLES over the
+    SIMD-cycles of the dispatch (1024 SIMDs; GRBM_GUI_ACTIVE sums the 8
+    XCDs' cycles, so SIMD-cycles = 128 x GRBM_GUI_ACTIVE).  Kernels sharing a
+    key (the two launches of one path) are summed before dividing.  Empty
+    when the counter file is absent."""
+    path = os.path.join(pmc_dir, fname)
+    if not os.path.exists(path):
+        return {}
+    b = counter_means(path, "SQ_VALU_MFMA_BUSY_CYCLES", lambda n: (key_of(n), n) if key_of(n) else None)
+    g = counter_means(path, "GRBM_GUI_ACTIVE", lambda n: (key_of(n), n) if key_of(n) else None)
+    out = {}
+    for (key, name), v in b.items():
+        acc = out.setdefault(key, [0.0, 0.0])
+        acc[0] += v
+        acc[1] += g[(key, name)]
+    return {k: bv / (128.0 * gv) for k, (bv, gv) in out.items() if gv > 0}
+
+
+def fmt_busy(x) -> str:
+    return "n/a" if x is None else f"{x:.2f}"
+
+
 def summarize_sweep(pmc_dir: str, timing_path: str, out_path: str):
     """Combine the tile sweep's timing lines with its counter runs into a
     markdown table: CU<->L2 read bytes (TCC_READ_SECTORS) and L2-miss read
     bytes (FETCH_SIZE), each scaled by what the counter reads for a plain
     copy of COPY_BYTES, against the schedule-exact and the page's models.
     Expects <dir>/sweepread_, sweepfetch_, copyread_ and copyfetch_
-    counter_collection.csv."""
-    import csv
-    import re
-    import statistics
-
+    counter_collection.csv, and optionally sweepmfma_ (matrix-core busy)."""
     def per_tile(fname, counter):
-        vals = {}
-        with open(os.path.join(pmc_dir, fname)) as f:
-            for r in csv.DictReader(f):
-                if r["Counter_Name"] != counter:
-                    continue
-                m = re.search(r"fwd_fused_bf16_direct_kernel<128, (\d+), (\d+),", r["Kernel_Name"])
-                if m:
-                    key = (32 * int(m.group(1)), int(m.group(2)))
-                    vals.setdefault(key, []).append(float(r["Counter_Value"]))
-        return {k: statistics.mean(v) for k, v in vals.items()}
+        return counter_means(os.path.join(pmc_dir, fname), counter, fused_sweep_key)
 
     def copy_value(fname, counter):
-        with open(os.path.join(pmc_dir, fname)) as f:
-            v = [float(r["Counter_Value"]) for r in csv.DictReader(f)
-                 if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"]]
-        return statistics.mean(v)
+        return copy_counter(os.path.join(pmc_dir, fname), counter)
 
     rd = per_tile("sweepread_counter_collection.csv", "TCC_READ_SECTORS_sum")
     fe = per_tile("sweepfetch_counter_collection.csv", "FETCH_SIZE")
+    busy = mfma_busy(pmc_dir, "sweepmfma_counter_collection.csv", fused_sweep_key)
     rd_unit = COPY_BYTES / copy_value("copyread_counter_collection.csv", "TCC_READ_SECTORS_sum")
     fe_unit = COPY_BYTES / copy_value("copyfetch_counter_collection.csv", "FETCH_SIZE")
     rows = [json.loads(line) for line in open(timing_path) if line.startswith("{")]
     compulsory = 402653184  # Q, K, V once (bf16)
     lines = ["| tile | B_r | B_c | M (elements) | ms | TFLOP/s | CU->L2 read bytes | "
              "schedule 2N^2d/B_r+Nd | ratio | page N^2d^2/M+Nd | ratio | L2-miss read bytes "
-             "| / compulsory |", "|" + "---|" * 13]
+             "| / compulsory | matrix core busy |", "|" + "---|" * 14]
     for r in rows:
         key = (r["block_rows"], r["key_tile"])
         cu = rd.get(key, float("nan")) * rd_unit
@@ -276,7 +316,8 @@ def summarize_sweep(pmc_dir: str, timing_path: str, out_path: str):
             f"| {r['tile']} | {r['block_rows']} | {r['key_tile']} | {r['onchip_elems']:,} | "
             f"{r['ms']} | {r['tflops']} | {cu / 1e9:.2f} GB | {r['sched_read_bytes'] / 1e9:.2f} GB | "
             f"{cu / r['sched_read_bytes']:.3f} | {r['page_model_bytes'] / 1e9:.2f} GB | "
-            f"{cu / r['page_model_bytes']:.3f} | {miss / 1e9:.3f} GB | {miss / compulsory:.2f} |")
+            f"{cu / r['page_model_bytes']:.3f} | {miss / 1e9:.3f} GB | {miss / compulsory:.2f} | "
+            f"{fmt_busy(busy.get(key))} |")
     text = "\n".join(lines) + "\n"
     text += (f"\nCounter scaling: one TCC_READ_SECTORS unit = {rd_unit:.2f} bytes and one "
              f"FETCH_SIZE unit = {fe_unit:.1f} bytes (a plain copy of {COPY_BYTES} bytes).\n")
@@ -285,7 +326,69 @@ def summarize_sweep(pmc_dir: str, timing_path: str, out_path: str):
     print(text)
 
 
+def smallcache_sweep_key(name: str):
+    """Tile b of a d = 256 small-cache forward kernel name (demangled or
+    mangled), else None."""
+    import re
+
+    m = re.search(r"sc_(?:scores_exp|value_product)(?:<256, (\d+)>|ILi256ELi(\d+)E)", name)
+    return int(m.group(1) or m.group(2)) if m else None
+
+
+def summarize_smallcache_sweep(pmc_dir: str, timing_path: str, out_path: str):
+    """Markdown table of the small-cache tile sweep: per tile b, the two
+    kernels' CU->L2 read bytes (TCC_READ_SECTORS), L2-miss read and write
+    bytes (FETCH_SIZE, WRITE_SIZE) and matrix-core busy, against the
+    square-tile schedule's exact panel count and the page's N^2 d / sqrt(M)
+    model.  Expects <dir>/scread_, scfetch_, scwrite_, scmfma_, copyread_,
+    copyfetch_ and copywrite_ counter_collection.csv."""
+    def sums(fname, counter):
+        # mean per dispatch of each kernel, summed over the two kernels of a b
+        per = counter_means(os.path.join(pmc_dir, fname), counter,
+                            lambda n: (smallcache_sweep_key(n), "value" in n)
+                            if smallcache_sweep_key(n) else None)
+        out = {}
+        for (b, _), v in per.items():
+            out[b] = out.get(b, 0.0) + v
+        return out
+
+    cu = sums("scread_counter_collection.csv", "TCC_READ_SECTORS_sum")
+    fe = sums("scfetch_counter_collection.csv", "FETCH_SIZE")
+    wr = sums("scwrite_counter_collection.csv", "WRITE_SIZE")
+    busy = mfma_busy(pmc_dir, "scmfma_counter_collection.csv", smallcache_sweep_key)
+    rd_unit = COPY_BYTES / copy_counter(os.path.join(pmc_dir, "copyread_counter_collection.csv"),
+                                        "TCC_READ_SECTORS_sum")
+    fe_unit = COPY_BYTES / copy_counter(os.path.join(pmc_dir, "copyfetch_counter_collection.csv"),
+                                        "FETCH_SIZE")
+    wr_unit = COPY_BYTES / copy_counter(os.path.join(pmc_dir, "copywrite_counter_collection.csv"),
+                                        "WRITE_SIZE")
+    rows = [json.loads(line) for line in open(timing_path) if line.startswith("{")]
+    lines = ["| b | M (elements) | ms | TFLOP/s | CU->L2 read bytes | schedule 4N^2d/b | ratio | "
+             "page N^2d/sqrt(M)+Nd | ratio | L2-miss read bytes | L2-miss write bytes | "
+             "E round trip 2N^2 | matrix core busy |", "|" + "---|" * 13]
+    for r in rows:
+        b = r["tile_b"]
+        c = cu.get(b, float("nan")) * rd_unit
+        lines.append(
+            f"| {b} | {r['onchip_elems']:,} | {r['ms']} | {r['tflops']} | {c / 1e9:.2f} GB | "
+            f"{r['sched_read_bytes'] / 1e9:.2f} GB | {c / r['sched_read_bytes']:.3f} | "
+            f"{r['page_model_bytes'] / 1e9:.3f} GB | {c / r['page_model_bytes']:.2f} | "
+            f"{fe.get(b, float('nan')) * fe_unit / 1e9:.3f} GB | "
+            f"{wr.get(b, float('nan')) * wr_unit / 1e9:.3f} GB | {r['exp_matrix_bytes'] / 1e9:.3f} GB | "
+            f"{fmt_busy(busy.get(b))} |")
+    text = "\n".join(lines) + "\n"
+    text += (f"\nCounter scaling: one TCC_READ_SECTORS unit = {rd_unit:.2f} bytes, one FETCH_SIZE "
+             f"unit = {fe_unit:.1f} bytes, one WRITE_SIZE unit = {wr_unit:.1f} bytes (a plain "
+             f"copy of {COPY_BYTES} bytes).\n")
+    with open(out_path, "w") as f:
+        f.write(text)
+    print(text)
+
+
 def main():
+    if len(sys.argv) >= 5 and sys.argv[1] == "--summarize-smallcache-sweep":
+        summarize_smallcache_sweep(sys.argv[2], sys.argv[3], sys.argv[4])
+        return
     if len(sys.argv) >= 3 and sys.argv[1] == "--summarize-counters":
         summarize_counters(sys.argv[2])
         return
@@ -306,6 +409,9 @@ def main():
     ap.add_argument("--tile-sweep", action="store_true",
                     help="time every query-block x key-tile shape of the fused forward on the "
                          "headline workload (one JSON line per shape) and exit")
+    ap.add_argument("--smallcache-sweep", action="store_true",
+                    help="time the square-tile forward at every tile b on the d = 256 "
+                         "small-cache workload (one JSON line per tile) and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB three times (to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -333,6 +439,9 @@ def main():
         return
     if args.tile_sweep:
         tile_sweep(args, at, torch, dev)
+        return
+    if args.smallcache_sweep:
+        smallcache_sweep(args, at, torch, dev)
         return
     if args.secondary_only:
         print(json.dumps({"secondary": secondary(args, at, torch, dev)}), flush=True)
@@ -439,6 +548,41 @@ def tile_sweep(args, at, torch, dev):
                           "tflops": round(w.fwd_flops / (ms * 1e-3) / 1e12, 1),
                           "sched_read_bytes": sched, "page_model_bytes": model}), flush=True)
     os.environ.pop("ATTN_FWD_TILE", None)
+
+
+SC_SWEEP_B = (128, 64)
+
+
+def smallcache_sweep(args, at, torch, dev):
+    """The square-tile forward at each tile b, with M set to that tile's
+    exact on-chip footprint, on the d = 256 small-cache workload: time and
+    the byte models (counters from rocprofv3 runs of this same mode; see
+    --summarize-smallcache-sweep)."""
+    from aware_tiling_amd.inputs import WORKLOADS, workload_inputs
+
+    w = WORKLOADS["smallcache_bf16_b1h8_n4096_d256"]
+    q, k, v = (t.to(dev) for t in workload_inputs(w))
+    o = torch.empty((w.bh, w.n, w.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.bh, w.n), dtype=torch.float32, device=dev)
+    for b in SC_SWEEP_B:
+        m_elems = int(at.lib().attn_smallcache_onchip_elems(b))
+        if m_elems <= 0 or at.smallcache_tile(w.d, m_elems) != b:
+            raise RuntimeError(f"tile b={b} is not selected at its own footprint {m_elems}")
+        need = int(at.lib().attn_fwd_smallcache_workspace_size(w.bh, w.n, w.d, m_elems))
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        print(f"[bench] small-cache tile b={b} M={m_elems}", file=sys.stderr, flush=True)
+        ms, _, _ = time_launches(lambda: at.attn_fwd_smallcache(
+            q, k, v, m_elems, w.scale, out=o, lse=lse, workspace=ws), args.steps, args.warmup)
+        # per launch, bytes: every (query tile, key tile) reads a b x d panel of Q
+        # and of K; every (query tile, b-wide output column block) reads a
+        # b x N panel of E and an N x b panel of V -- 4 N^2 d / b bf16 elements
+        sched = w.bh * 4 * w.n * w.n * w.d / b * 2
+        model = w.bh * (w.n * w.n * w.d / math.sqrt(m_elems) + w.n * w.d) * 2
+        print(json.dumps({"tile_b": b, "onchip_elems": m_elems, "ms": round(ms, 4),
+                          "tflops": round(w.fwd_flops / (ms * 1e-3) / 1e12, 1),
+                          "sched_read_bytes": sched, "page_model_bytes": model,
+                          "exp_matrix_bytes": w.bh * 2 * w.n * w.n * 2}), flush=True)
+        del ws
 
 
 def secondary(args, at, torch, dev):
