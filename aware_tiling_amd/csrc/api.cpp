@@ -29,12 +29,15 @@ attn_status launch_status(hipError_t e) {
 }
 
 // Shapes: bh, n >= 0; per-head element count and the grid must fit the
-// kernels' 32-bit in-head indexing.
+// kernels' 32-bit in-head indexing.  bh * n <= 2^29 rows keeps every
+// one-workgroup-per-block grid inside 32 bits; at d >= 64 that many rows of
+// Q, K, V and O would not fit in HBM anyway.
 bool shape_ok(int64_t bh, int64_t n, int64_t d) {
   if (bh < 0 || n < 0 || d <= 0) return false;
   if (n > (int64_t(1) << 24)) return false;
   if (n * d >= (int64_t(1) << 31)) return false;
   if (bh > (int64_t(1) << 20)) return false;
+  if (bh * n > (int64_t(1) << 29)) return false;
   return true;
 }
 

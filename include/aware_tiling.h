@@ -27,6 +27,9 @@
  *  - stream: a hipStream_t passed as void*; NULL means the null stream.
  *    Calls only enqueue work and return without synchronising the host.
  *  - scale must be finite and > 0 (callers pass 1/sqrt(d)).
+ *  - Sizes: n <= 2^24, n * d < 2^31, bh <= 2^20 and bh * n <= 2^29 (more
+ *    rows than Q, K, V and an fp32 O take in the 288 GB of one GPU at
+ *    d >= 64); a larger size is ATTN_ERR_INVALID_ARG.
  *  - Errors: validation happens before any HIP call; on an error nothing is
  *    enqueued and no output is touched.  ATTN_ERR_LAUNCH reports a HIP error
  *    seen right after enqueueing (its text is in attn_last_hip_error()).

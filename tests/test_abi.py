@@ -73,6 +73,7 @@ def test_fwd_validation(lib):
     assert fwd(lib, bh=-1) == INVALID
     assert fwd(lib, n=-5) == INVALID
     assert fwd(lib, n=1 << 25) == INVALID
+    assert fwd(lib, bh=(1 << 9) + 1, n=1 << 20, d=64) == INVALID  # bh * n above 2^29 rows
     # empty problems are a no-op even with null pointers
     assert fwd(lib, q=None, k=None, v=None, o=None, n=0) == OK
     assert fwd(lib, q=None, k=None, v=None, o=None, bh=0) == OK
@@ -125,6 +126,7 @@ def test_budget_forward_validation(lib):
     assert call(scale=-1.0) == INVALID
     assert call(q=None) == INVALID
     assert call(bh=1 << 20, n=1 << 20) == INVALID  # more workgroups than a grid holds
+    assert call(bh=(1 << 9) + 1, n=1 << 20) == INVALID  # bh * n above 2^29 rows
     assert call(q=None, n=0) == OK  # empty: no launch, no pointer needed
 
 
