@@ -39,8 +39,10 @@
 //
 // Workspace layout (256-byte aligned pieces): E, bh nt^2 b^2 bf16 in the
 // unit order above (tiles past n hold finite values that only reach
-// discarded rows or are multiplied by 0), then m_IJ [bh][n][nt] and
-// l_IJ [bh][n][nt] fp32 with nt = ceil(n/b).
+// discarded rows or are multiplied by 0), then m_IJ [bh][nt][n] and
+// l_IJ [bh][nt][n] fp32 with nt = ceil(n/b): key tile major, so the
+// statistics of one key tile for consecutive query rows are contiguous
+// (each wave writes, merges and stages them as whole 256-byte rows).
 #include <type_traits>
 
 #include "device_common.h"
@@ -215,7 +217,7 @@ __global__ __launch_bounds__(B * 2) void sc_scores_exp(const bf16* __restrict__ 
       }
       lsum += __shfl_xor(lsum, 32);
       if (qok && h == 0) {
-        const size_t sidx = ((size_t)head * n + q) * nt + J;
+        const size_t sidx = ((size_t)head * nt + J) * n + q;
         mst[sidx] = m;
         lst[sidx] = lsum;
       }
@@ -261,12 +263,14 @@ __global__ __launch_bounds__(B * 2) void sc_value_product(const bf16* __restrict
   const bool qok = q < n;
 
   // merged statistics of this lane's query row
-  const float* mr = mst + ((size_t)head * n + (qok ? q : 0)) * nt;
-  const float* lr = lst + ((size_t)head * n + (qok ? q : 0)) * nt;
+  // statistics are [head][key tile][row]: a wave's 64 rows of one key tile
+  // are 256 contiguous bytes
+  const float* mr = mst + (size_t)head * nt * n + (qok ? q : 0);
+  const float* lr = lst + (size_t)head * nt * n + (qok ? q : 0);
   float m = -INFINITY;
-  for (int t = 0; t < nt; ++t) m = fmaxf(m, mr[t]);
+  for (int t = 0; t < nt; ++t) m = fmaxf(m, mr[(size_t)t * n]);
   float l = 0.f;
-  for (int t = 0; t < nt; ++t) l += fast_exp2(mr[t] - m) * lr[t];
+  for (int t = 0; t < nt; ++t) l += fast_exp2(mr[(size_t)t * n] - m) * lr[(size_t)t * n];
   const float inv = 1.0f / l;
   if (ct == 0 && lse != nullptr && qok && h == 0)
     lse[(size_t)head * n + q] = (m + __log2f(l)) * kLn2;
@@ -296,7 +300,7 @@ __global__ __launch_bounds__(B * 2) void sc_value_product(const bf16* __restrict
     const u32x4* p = Ew + ((size_t)J * NW * PPT * 2 + kb * 2) * 64;
     dma16(p, &Ep[slot][(wave * 2 + 0) * 64 * 8]);
     dma16(p + 64, &Ep[slot][(wave * 2 + 1) * 64 * 8]);
-    dma4(mr + J, &Ms[slot][wave * 64]);
+    dma4(mr + (size_t)J * n, &Ms[slot][wave * 64]);
   };
 
   f32x16 out[BD / 32];
