@@ -9,7 +9,6 @@ two identities that hold at any size: sum_j dK_j = 0 (a common shift of all
 keys changes no weight) and sum_j dV_j = sum_i dO_i (each row of weights
 sums to one).  Tolerance: max-abs 2e-2 (bf16 inputs, fp32 accumulation).
 """
-import numpy as np
 import pytest
 import torch
 
@@ -48,10 +47,10 @@ def test_bwd_matches_oracle(bh, n, d, seed, q_mult):
     say(f"attn_bwd bh={bh} n={n} d={d} seed={seed} qx{q_mult}")
     (qc, kc, vc, doc), _, (dq, dk, dv), scale = _grads(bh, n, d, seed, q_mult)
     rq, rk, rv, _, _ = oracle.attn_bwd(f64(qc), f64(kc), f64(vc), f64(doc), scale)
-    scaled = q_mult > 1.0  # gradients grow with the scaled queries
-    check(f64(dq), rq, TOL["bf16"], f"dQ {bh}x{n}x{d}", scaled)
-    check(f64(dk), rk, TOL["bf16"], f"dK {bh}x{n}x{d}", scaled)
-    check(f64(dv), rv, TOL["bf16"], f"dV {bh}x{n}x{d}", scaled)
+    gs = q_mult > 1.0  # gradients grow with the scaled queries
+    check(f64(dq), rq, TOL["bf16"], f"dQ {bh}x{n}x{d}", grad_scaled=gs)
+    check(f64(dk), rk, TOL["bf16"], f"dK {bh}x{n}x{d}", grad_scaled=gs)
+    check(f64(dv), rv, TOL["bf16"], f"dV {bh}x{n}x{d}", grad_scaled=gs)
 
 
 def test_bwd_full_size_sampled_heads_and_identities():
@@ -65,13 +64,13 @@ def test_bwd_full_size_sampled_heads_and_identities():
     sv = (dv.double().sum(dim=1) - do.double().sum(dim=1)).abs().max().item()
     say(f"  max |sum_j dK_j| {sk:.3e}, max |sum_j dV_j - sum_i dO_i| {sv:.3e}")
     assert sk <= 5e-2 and sv <= 5e-2
-    # whole sampled heads against the oracle
-    for h in (0, w.bh - 1):
-        rq, rk, rv, _, _ = oracle.attn_bwd(f64(qc[h:h + 1]), f64(kc[h:h + 1]), f64(vc[h:h + 1]),
-                                           f64(doc[h:h + 1]), scale)
-        check(f64(dq[h:h + 1]), rq, TOL["bf16"], f"dQ head {h}")
-        check(f64(dk[h:h + 1]), rk, TOL["bf16"], f"dK head {h}")
-        check(f64(dv[h:h + 1]), rv, TOL["bf16"], f"dV head {h}")
+    # every head against the oracle (dK and dV of a key need every query, so
+    # whole heads are compared; all of them, i.e. every workgroup's output)
+    say(f"  oracle gradients for all {w.bh} heads")
+    rq, rk, rv, _, _ = oracle.attn_bwd(f64(qc), f64(kc), f64(vc), f64(doc), scale)
+    check(f64(dq), rq, TOL["bf16"], "dQ all heads")
+    check(f64(dk), rk, TOL["bf16"], "dK all heads")
+    check(f64(dv), rv, TOL["bf16"], "dV all heads")
 
 
 def test_bwd_deterministic():

@@ -2,21 +2,22 @@
 
 Small shapes are compared element by element over all of O and lse; they
 span several query blocks and key tiles and end in ragged tails.  The
-full-size workloads are compared on sampled rows (the oracle computes those
-rows one by one over all keys) and, over every element, against the
+full-size workloads are compared on rows drawn from every (head, query
+block), so every workgroup of the launch is checked (the oracle computes
+those rows one by one over all keys), and, over every element, against the
 convex-hull property that holds at any size (each output row is a weighted
 average of value rows, so it lies between their column minima and maxima).
 Tolerances: max-abs 1e-5 for fp32 inputs, 2e-2 for bf16 inputs.
 """
-import os
 
 import numpy as np
 import pytest
 import torch
 
 import aware_tiling_amd as at
-from aware_tiling_amd.inputs import WORKLOADS
-from tests.gpu_util import TOL, check, f64, inputs, oracle_fwd_rows, sample_rows, say
+from aware_tiling_amd.inputs import TORCH_DTYPES, WORKLOADS
+from tests.gpu_util import (TOL, check, f64, gather_rows, inputs, oracle_fwd_head_rows,
+                            oracle_fwd_rows, rows_every_block, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -71,7 +72,7 @@ def test_fwd_every_tile_shape(d, tile, monkeypatch):
     _run_full(2, 333, d, "bf16", 40 + d, 2.0)
 
 
-def _full_workload(name, nrows):
+def _full_workload(name, per_block=2):
     w = WORKLOADS[name]
     say(f"attn_fwd full workload {name}")
     (qc, kc, vc), (q, k, v) = inputs(w.bh, w.n, w.d, w.dtype, w.seed, w.q_mult)
@@ -84,27 +85,28 @@ def _full_workload(name, nrows):
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
     slack = 1e-3
     assert bool(((o >= lo - slack) & (o <= hi + slack)).all()), "O outside the hull of V"
-    # sampled rows against the oracle
-    heads = np.unique(np.clip(np.array([0, w.bh // 2 + 1, w.bh - 1]), 0, w.bh - 1))
-    rows = sample_rows(w.n, nrows, w.seed)
-    ro, rl = oracle_fwd_rows(qc, kc, vc, w.scale, heads, rows)
-    got_o = f64(o[heads][:, rows])
-    got_l = f64(lse[heads][:, rows])
-    check(got_o, ro, TOL[w.dtype], f"O sampled {name}")
-    check(got_l, rl, TOL[w.dtype], f"lse sampled {name}")
+    # rows from every (head, query block), i.e. from every workgroup of the
+    # launch, against the oracle
+    block = at.fwd_query_block(w.d, TORCH_DTYPES[w.dtype])
+    rows = rows_every_block(w.bh, w.n, block, per_block, w.seed)
+    say(f"  oracle on {rows.size} rows: {per_block} from each of {w.bh} heads x "
+        f"{-(-w.n // block)} query blocks of {block}")
+    ro, rl = oracle_fwd_head_rows(qc, kc, vc, w.scale, rows)
+    check(gather_rows(o, rows), ro, TOL[w.dtype], f"O every block {name}")
+    check(gather_rows(lse, rows), rl, TOL[w.dtype], f"lse every block {name}")
     return o, lse, (q, k, v)
 
 
 def test_fwd_full_f32_workload():
-    _full_workload("fwd_f32_h1_n256_d64", 256)
+    _full_workload("fwd_f32_h1_n256_d64", 64)
 
 
 def test_fwd_full_teaching_shape():
-    _full_workload("fwd_bf16_b4h16_n4096_d64", 160)
+    _full_workload("fwd_bf16_b4h16_n4096_d64")
 
 
 def test_fwd_full_long_sequence_large_scores():
-    o, lse, (q, k, v) = _full_workload("fwd_bf16_b1h32_n16384_d128_qx4", 96)
+    o, lse, (q, k, v) = _full_workload("fwd_bf16_b1h32_n16384_d128_qx4")
     # bitwise determinism at full size
     o2, lse2 = at.attn_fwd(q, k, v, WORKLOADS["fwd_bf16_b1h32_n16384_d128_qx4"].scale)
     torch.cuda.synchronize()
@@ -112,7 +114,7 @@ def test_fwd_full_long_sequence_large_scores():
 
 
 def test_fwd_d256_fused_on_small_cache_shape():
-    _full_workload("smallcache_bf16_b1h8_n4096_d256", 96)
+    _full_workload("smallcache_bf16_b1h8_n4096_d256")
 
 
 def test_fwd_deterministic_repeat():

@@ -3,7 +3,8 @@
 The square-tile schedule reaches the same function as the definition (it only
 keeps the exponentiated score matrix in device memory), so it is compared
 with the float64 oracle of the definition: in full on small ragged shapes,
-on sampled rows at the full batch 1 x 8 heads, N 4096, d 256 size, and
+on rows from every (head, query tile) at the full batch 1 x 8 heads,
+N 4096, d 256 size, and
 against the fused path on the same inputs.  Tolerance: max-abs 2e-2 (bf16).
 """
 import numpy as np
@@ -12,7 +13,8 @@ import torch
 
 import aware_tiling_amd as at
 from aware_tiling_amd.inputs import WORKLOADS
-from tests.gpu_util import TOL, check, f64, inputs, oracle_fwd_rows, sample_rows, say
+from tests.gpu_util import (TOL, check, f64, gather_rows, inputs, oracle_fwd_head_rows,
+                            oracle_fwd_rows, rows_every_block, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -53,12 +55,15 @@ def test_smallcache_full_size_against_oracle_and_fused():
     of, lf = at.attn_fwd(q, k, v, w.scale)
     torch.cuda.synchronize()
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
-    heads = np.array([0, 5, 7])
-    rows = sample_rows(w.n, 96, w.seed)
-    ro, rl = oracle_fwd_rows(qc, kc, vc, w.scale, heads, rows)
-    check(f64(o[heads][:, rows]), ro, TOL["bf16"], "O smallcache sampled")
-    check(f64(lse[heads][:, rows]), rl, TOL["bf16"], "lse smallcache sampled")
-    check(f64(of[heads][:, rows]), ro, TOL["bf16"], "O fused sampled (same inputs)")
+    # rows from every (head, query tile of b rows): every output tile of the
+    # value product and every query block of the fused kernel
+    b = at.smallcache_tile(w.d, m_elems)
+    rows = rows_every_block(w.bh, w.n, b, 2, w.seed)
+    say(f"  oracle on {rows.size} rows: 2 from each of {w.bh} heads x {w.n // b} tiles of {b}")
+    ro, rl = oracle_fwd_head_rows(qc, kc, vc, w.scale, rows)
+    check(gather_rows(o, rows), ro, TOL["bf16"], "O smallcache every tile")
+    check(gather_rows(lse, rows), rl, TOL["bf16"], "lse smallcache every tile")
+    check(gather_rows(of, rows), ro, TOL["bf16"], "O fused every tile (same inputs)")
     # both paths compute the same function: compare them everywhere
     diff = float((o - of).abs().max())
     say(f"  max |O_smallcache - O_fused| over all elements: {diff:.3e}")
