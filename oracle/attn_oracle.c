@@ -12,8 +12,8 @@
  *     s_ij = scale * <q_i, k_j>,
  *     p_ij = exp(s_ij) / sum_t exp(s_it),
  *     o_i  = sum_j p_ij v_j.
- * The page leaves out the 1/sqrt(d) factor ("Actual models usually divide
- * this score by sqrt d"); here it is the explicit `scale` argument.
+ * The page writes the score without the 1/sqrt(d) factor, noting only that
+ * practical models apply it; here it is the explicit `scale` argument.
  *
  * All arithmetic is IEEE double with libm exp/log, no fast-math.  Batches of
  * heads are independent; `bh` heads are laid out back to back, each row-major
