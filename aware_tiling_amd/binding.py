@@ -29,6 +29,10 @@ SIGNATURES = {
     "attn_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _int, _vp]),
     "attn_fwd_onchip_elems": (_i64, [_i64, _int]),
     "attn_fwd_query_block": (_i64, [_i64, _int]),
+    "attn_fwd_tiles": (ctypes.c_char_p, [_i64]),
+    "attn_fwd_tile_info": (_int, [ctypes.c_char_p, _i64, _vp, _vp, _vp]),
+    "attn_fwd_tile": (_int, [ctypes.c_char_p, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32,
+                             _int, _vp]),
     "attn_fwd_budget": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _int, _i64, _vp]),
     "attn_fwd_budget_onchip_elems": (_i64, [_i64]),
     "attn_calib_mfma_loop": (_int, [_vp, _i64, ctypes.c_int32, _f32, _vp]),
@@ -100,10 +104,19 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _on_gpu(t: torch.Tensor) -> bool:
+    """Whether ``t`` lives in GPU memory (the kernels read and write it)."""
+    return t.is_cuda
+
+
 def _check_inputs(*ts: torch.Tensor):
+    """Q, K, V (and dO) style inputs: tensors on one GPU, contiguous,
+    [bh, n, d], bf16 or fp32."""
     ref = ts[0]
     for t in ts:
-        if not t.is_cuda:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("inputs must be torch tensors")
+        if not _on_gpu(t):
             raise ValueError("tensors must be on the GPU")
         if t.device != ref.device:
             raise ValueError("tensors must be on one device")
@@ -111,6 +124,76 @@ def _check_inputs(*ts: torch.Tensor):
             raise ValueError("tensors must be contiguous")
         if t.dim() != 3:
             raise ValueError("tensors must be [bh, n, d]")
+        if t.dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _check_buffer(t, name: str, shape, dtype: torch.dtype, device: torch.device):
+    """A caller-supplied output or auxiliary tensor the kernels read or write
+    in full: it must have exactly ``shape`` and ``dtype``, be contiguous and
+    sit on ``device``; anything else could send a kernel past its end."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not _on_gpu(t) or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_workspace(t, device: torch.device):
+    """Workspace: contiguous device memory of any dtype on ``device`` (the
+    library checks its byte size and alignment)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("workspace must be a torch tensor")
+    if not _on_gpu(t) or t.device != device:
+        raise ValueError(f"workspace must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+
+
+def _out_lse(out, lse, bh: int, n: int, d: int, device):
+    """Allocate or check the forward's O [bh, n, d] fp32 and lse [bh, n] fp32
+    (lse=True allocates, False or None means no lse)."""
+    if out is None:
+        out = torch.empty((bh, n, d), dtype=torch.float32, device=device)
+    else:
+        _check_buffer(out, "out", (bh, n, d), torch.float32, device)
+    if lse is True:
+        lse = torch.empty((bh, n), dtype=torch.float32, device=device)
+    elif lse is False or lse is None:
+        lse = None
+    else:
+        _check_buffer(lse, "lse", (bh, n), torch.float32, device)
+    return out, lse
+
+
+def _grads(grads, bh: int, n: int, d: int, device):
+    if grads is None:
+        return tuple(torch.empty((bh, n, d), dtype=torch.float32, device=device)
+                     for _ in range(3))
+    if len(grads) != 3:
+        raise ValueError("grads must be (dQ, dK, dV)")
+    for name, g in zip(("dQ", "dK", "dV"), grads):
+        _check_buffer(g, name, (bh, n, d), torch.float32, device)
+    return tuple(grads)
+
+
+def _bwd_operands(q, k, v, o, do, lse):
+    """Backward inputs: Q, K, V, dO of one shape and dtype; O fp32 and lse
+    fp32 as written by the forward."""
+    _check_inputs(q, k, v, do)
+    if not (q.shape == k.shape == v.shape == do.shape):
+        raise ValueError("Q, K, V and dO must share one shape")
+    if not (q.dtype == k.dtype == v.dtype == do.dtype):
+        raise ValueError("Q, K, V and dO must share one dtype")
+    bh, n, d = q.shape
+    _check_buffer(o, "O", (bh, n, d), torch.float32, q.device)
+    _check_buffer(lse, "lse", (bh, n), torch.float32, q.device)
+    return bh, n, d
 
 
 def _stream(t: torch.Tensor, stream=None) -> int:
@@ -131,16 +214,44 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | N
         raise ValueError("Q, K, V must share shape and dtype")
     bh, n, d = q.shape
     scale = default_scale(d) if scale is None else float(scale)
-    if out is None:
-        out = torch.empty((bh, n, d), dtype=torch.float32, device=q.device)
-    if lse is True:
-        lse = torch.empty((bh, n), dtype=torch.float32, device=q.device)
-    elif lse is False:
-        lse = None
+    out, lse = _out_lse(out, lse, bh, n, d, q.device)
     rc = lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                         lse.data_ptr() if lse is not None else None, bh, n, d, scale,
                         _dtype_code(q), _stream(q, stream))
     _check("attn_fwd", rc)
+    return out, lse
+
+
+def fwd_tiles(d: int) -> list[str]:
+    """Names of the fused forward's compiled tile shapes for head dimension
+    d, the default (the one attn_fwd uses) first."""
+    return lib().attn_fwd_tiles(d).decode().split()
+
+
+def fwd_tile_info(tile: str, d: int) -> dict:
+    """Query-block rows, keys per tile and on-chip elements of a named
+    tile shape at head dimension d."""
+    vals = [ctypes.c_int64(0) for _ in range(3)]
+    rc = lib().attn_fwd_tile_info(tile.encode(), d, *(ctypes.byref(x) for x in vals))
+    _check("attn_fwd_tile_info", rc)
+    return {"block_rows": vals[0].value, "key_tile": vals[1].value, "onchip_elems": vals[2].value}
+
+
+def attn_fwd_tile(tile: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  scale: float | None = None, out: torch.Tensor | None = None,
+                  lse: torch.Tensor | bool = True, stream=None):
+    """attn_fwd with the named tile shape (tile sweeps and tests).
+    Returns (O, lse)."""
+    _check_inputs(q, k, v)
+    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("Q, K, V must share shape and dtype")
+    bh, n, d = q.shape
+    scale = default_scale(d) if scale is None else float(scale)
+    out, lse = _out_lse(out, lse, bh, n, d, q.device)
+    rc = lib().attn_fwd_tile(tile.encode(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                             out.data_ptr(), lse.data_ptr() if lse is not None else None, bh, n,
+                             d, scale, _dtype_code(q), _stream(q, stream))
+    _check("attn_fwd_tile", rc)
     return out, lse
 
 
@@ -159,12 +270,7 @@ def attn_fwd_budget(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, m_elems: 
         raise ValueError("Q, K, V must share shape and dtype")
     bh, n, d = q.shape
     scale = default_scale(d) if scale is None else float(scale)
-    if out is None:
-        out = torch.empty((bh, n, d), dtype=torch.float32, device=q.device)
-    if lse is True:
-        lse = torch.empty((bh, n), dtype=torch.float32, device=q.device)
-    elif lse is False:
-        lse = None
+    out, lse = _out_lse(out, lse, bh, n, d, q.device)
     rc = lib().attn_fwd_budget(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                lse.data_ptr() if lse is not None else None, bh, n, d, scale,
                                _dtype_code(q), int(m_elems), _stream(q, stream))
@@ -175,7 +281,7 @@ def attn_fwd_budget(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, m_elems: 
 def calib_mfma_loop(out: torch.Tensor, iters: int, amp: float = 1.0, stream=None) -> int:
     """Calibration matrix-core loop (no memory traffic) over out.numel() // 256
     workgroups; returns the flops it issues. out: float32 CUDA tensor."""
-    if out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous():
+    if out.dtype != torch.float32 or not _on_gpu(out) or not out.is_contiguous():
         raise ValueError("out must be a contiguous float32 CUDA tensor")
     wgs = out.numel() // 256
     rc = lib().attn_calib_mfma_loop(out.data_ptr(), wgs, int(iters), float(amp),
@@ -202,15 +308,12 @@ def attn_fwd_splitk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, splits: i
     bh, nq, d = q.shape
     nk = k.shape[1]
     scale = default_scale(d) if scale is None else float(scale)
-    need = int(lib().attn_fwd_splitk_workspace_size(bh, nq, nk, d, int(splits)))
+    out, lse = _out_lse(out, lse, bh, nq, d, q.device)
     if workspace is None:
+        need = int(lib().attn_fwd_splitk_workspace_size(bh, nq, nk, d, int(splits)))
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty((bh, nq, d), dtype=torch.float32, device=q.device)
-    if lse is True:
-        lse = torch.empty((bh, nq), dtype=torch.float32, device=q.device)
-    elif lse is False:
-        lse = None
+    else:
+        _check_workspace(workspace, q.device)
     rc = lib().attn_fwd_splitk(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                lse.data_ptr() if lse is not None else None, bh, nq, nk, d, scale,
                                _dtype_code(q), int(splits), workspace.data_ptr(),
@@ -234,23 +337,24 @@ def attn_fwd_blocksparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise ValueError("Q, K, V must share shape and dtype")
     bh, n, d = q.shape
     nb = -(-n // SPARSE_BLOCK)
+    if not isinstance(block_mask, torch.Tensor):
+        raise TypeError("block_mask must be a torch tensor")
     if block_mask.dtype == torch.bool:
         block_mask = block_mask.to(torch.uint8)
-    if (block_mask.dtype != torch.uint8 or not block_mask.is_cuda or block_mask.dim() != 3
-            or tuple(block_mask.shape[1:]) != (nb, nb) or block_mask.shape[0] not in (1, bh)):
-        raise ValueError(f"block_mask must be uint8 [1 or {bh}, {nb}, {nb}] on the GPU")
+    if (not isinstance(block_mask, torch.Tensor) or block_mask.dtype != torch.uint8
+            or not _on_gpu(block_mask) or block_mask.device != q.device
+            or block_mask.dim() != 3 or tuple(block_mask.shape[1:]) != (nb, nb)
+            or block_mask.shape[0] not in (1, bh)):
+        raise ValueError(f"block_mask must be uint8 [1 or {bh}, {nb}, {nb}] on {q.device}")
     block_mask = block_mask.contiguous()
     mh = block_mask.shape[0]
     scale = default_scale(d) if scale is None else float(scale)
-    need = int(lib().attn_fwd_blocksparse_workspace_size(bh, n, mh))
+    out, lse = _out_lse(out, lse, bh, n, d, q.device)
     if workspace is None:
+        need = int(lib().attn_fwd_blocksparse_workspace_size(bh, n, mh))
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty((bh, n, d), dtype=torch.float32, device=q.device)
-    if lse is True:
-        lse = torch.empty((bh, n), dtype=torch.float32, device=q.device)
-    elif lse is False:
-        lse = None
+    else:
+        _check_workspace(workspace, q.device)
     rc = lib().attn_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                     lse.data_ptr() if lse is not None else None, bh, n, d, scale,
                                     _dtype_code(q), block_mask.data_ptr(), mh,
@@ -275,15 +379,12 @@ def attn_fwd_smallcache(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, m_ele
         raise ValueError("Q, K, V must share shape and dtype")
     bh, n, d = q.shape
     scale = default_scale(d) if scale is None else float(scale)
-    need = int(lib().attn_fwd_smallcache_workspace_size(bh, n, d, m_elems))
+    out, lse = _out_lse(out, lse, bh, n, d, q.device)
     if workspace is None:
+        need = int(lib().attn_fwd_smallcache_workspace_size(bh, n, d, m_elems))
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty((bh, n, d), dtype=torch.float32, device=q.device)
-    if lse is True:
-        lse = torch.empty((bh, n), dtype=torch.float32, device=q.device)
-    elif lse is False:
-        lse = None
+    else:
+        _check_workspace(workspace, q.device)
     rc = lib().attn_fwd_smallcache(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                    lse.data_ptr() if lse is not None else None, bh, n, d, scale,
                                    _dtype_code(q), int(m_elems), workspace.data_ptr(),
@@ -296,16 +397,14 @@ def attn_fwd_smallcache(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, m_ele
 def attn_bwd(q, k, v, o, do, lse, scale: float | None = None, workspace=None, grads=None,
              stream=None):
     """Gradients (dQ, dK, dV) in fp32 from the forward's O and lse."""
-    _check_inputs(q, k, v, o, do)
-    bh, n, d = q.shape
+    bh, n, d = _bwd_operands(q, k, v, o, do, lse)
     scale = default_scale(d) if scale is None else float(scale)
-    need = int(lib().attn_bwd_workspace_size(bh, n, d))
+    dq, dk, dv = _grads(grads, bh, n, d, q.device)
     if workspace is None:
+        need = int(lib().attn_bwd_workspace_size(bh, n, d))
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    if grads is None:
-        grads = tuple(torch.empty((bh, n, d), dtype=torch.float32, device=q.device)
-                      for _ in range(3))
-    dq, dk, dv = grads
+    else:
+        _check_workspace(workspace, q.device)
     rc = lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                         lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), bh, n, d,
                         scale, _dtype_code(q), workspace.data_ptr(),
@@ -318,16 +417,14 @@ def attn_bwd_smallcache(q, k, v, o, do, lse, m_elems: int, scale: float | None =
                         workspace=None, grads=None, stream=None):
     """Square-tile (small-cache) gradients (dQ, dK, dV) in fp32; the n x n
     P^T and dS^T live in the workspace."""
-    _check_inputs(q, k, v, o, do)
-    bh, n, d = q.shape
+    bh, n, d = _bwd_operands(q, k, v, o, do, lse)
     scale = default_scale(d) if scale is None else float(scale)
-    need = int(lib().attn_bwd_smallcache_workspace_size(bh, n, d, int(m_elems)))
+    dq, dk, dv = _grads(grads, bh, n, d, q.device)
     if workspace is None:
+        need = int(lib().attn_bwd_smallcache_workspace_size(bh, n, d, int(m_elems)))
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    if grads is None:
-        grads = tuple(torch.empty((bh, n, d), dtype=torch.float32, device=q.device)
-                      for _ in range(3))
-    dq, dk, dv = grads
+    else:
+        _check_workspace(workspace, q.device)
     rc = lib().attn_bwd_smallcache(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                    do.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                                    dv.data_ptr(), bh, n, d, scale, _dtype_code(q), int(m_elems),

@@ -87,11 +87,39 @@ attn_status attn_fwd(const void* Q, const void* K, const void* V, float* O, floa
   if (lse && !aligned16(lse)) return ATTN_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == ATTN_BF16)
-    return launch_status(at::launch_fwd_fused_bf16(Q, K, V, O, lse, bh, n, d, scale, s));
+    return launch_status(at::launch_fwd_fused_bf16(Q, K, V, O, lse, bh, n, d, scale, nullptr, s));
   return launch_status(at::launch_fwd_fused_f32(static_cast<const float*>(Q),
                                                 static_cast<const float*>(K),
                                                 static_cast<const float*>(V), O, lse, bh, n, d,
                                                 scale, s));
+}
+
+const char* attn_fwd_tiles(int64_t d) { return at::fused_bf16_tile_names(d); }
+
+attn_status attn_fwd_tile_info(const char* tile, int64_t d, int64_t* block_rows,
+                               int64_t* key_tile, int64_t* onchip_elems) {
+  if (!tile) return ATTN_ERR_INVALID_ARG;
+  const at::FusedTileInfo t = at::fused_bf16_tile_info(d, tile);
+  if (t.block_rows == 0) return ATTN_ERR_UNSUPPORTED;
+  if (block_rows) *block_rows = t.block_rows;
+  if (key_tile) *key_tile = t.key_tile;
+  if (onchip_elems) *onchip_elems = t.onchip;
+  return ATTN_OK;
+}
+
+attn_status attn_fwd_tile(const char* tile, const void* Q, const void* K, const void* V,
+                          float* O, float* lse, int64_t bh, int64_t n, int64_t d, float scale,
+                          attn_dtype dtype, void* stream) {
+  if (!tile) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (!shape_ok(bh, n, d) || !scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
+  if (at::fused_bf16_tile_info(d, tile).block_rows == 0) return ATTN_ERR_UNSUPPORTED;
+  if (bh * n == 0) return ATTN_OK;
+  if (!Q || !K || !V || !O) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return ATTN_ERR_INVALID_ARG;
+  if (lse && !aligned16(lse)) return ATTN_ERR_INVALID_ARG;
+  return launch_status(at::launch_fwd_fused_bf16(Q, K, V, O, lse, bh, n, d, scale, tile,
+                                                 static_cast<hipStream_t>(stream)));
 }
 
 int64_t attn_fwd_budget_onchip_elems(int64_t d) { return at::fused_budget_onchip(d); }

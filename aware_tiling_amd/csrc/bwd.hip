@@ -13,23 +13,23 @@
 // is stored.
 //
 // Three kernels, stream ordered:
-//  1. bwd_preprocess: D_i = <dO_i, O_i> into the workspace.
-//  2. bwd_dkdv: one workgroup per (head, block of 128 keys), one wave per 32
-//     keys.  Each wave keeps K and V of its keys as MFMA B operands and the
-//     transposed accumulators dK^T, dV^T (d x 32 keys) in registers, and
-//     streams 32-query tiles of Q, dO, lse, D through double-buffered LDS.
-//     Scores are computed as S = Q K^T so that a lane owns one key: the
-//     bf16 P and dS tiles then feed dV^T += dO^T P and dK^T += Q^T dS
-//     straight from registers, with Q and dO also stored transposed in LDS.
-//  3. bwd_dq: one workgroup per (head, block of 128 queries), one wave per
+//  1. bwd_preprocess: D_i = <dO_i, O_i> and lse_i log2(e) into the
+//     workspace.
+//  2. bwd_dkdv3: one workgroup per (head, block of 256 keys), one wave per
+//     32 keys.  Each wave keeps its K rows as MFMA B operands and the
+//     transposed accumulators dK^T, dV^T (d x 32 keys) in registers, its V
+//     rows in LDS, and streams query tiles of Q, dO, lse, D through
+//     double-buffered LDS.  Scores are computed as S = Q K^T so that a lane
+//     owns one key: the bf16 P and dS tiles then feed dV^T += dO^T P and
+//     dK^T += Q^T dS straight from registers, with Q^T and dO^T read from
+//     the same row-major LDS tiles by transposing reads.
+//  3. bwd_dq3: one workgroup per (head, block of 256 queries), one wave per
 //     32 queries.  Each wave keeps Q and dO as B operands, lse and D as
-//     per-lane scalars, and dQ^T in registers, and streams 32-key tiles of
-//     K, V (row-major) and K^T through LDS: S^T = K Q^T, dP^T = V dO^T,
-//     dS^T, dQ^T += K^T dS^T.  Recomputing S and dP here costs 4 N^2 d more
-//     flops than accumulating dQ with atomics, and keeps the result
-//     deterministic.
-#include <cstdlib>
-#include <cstring>
+//     per-lane scalars, and dQ^T in registers, and streams 64-key tiles of
+//     K and V through LDS: S^T = K Q^T, dP^T = V dO^T, dS^T, and
+//     dQ^T += K^T dS^T with K^T read transposed.  Recomputing S and dP here
+//     costs 4 N^2 d more flops than accumulating dQ with atomics, and keeps
+//     the result deterministic.
 #include <type_traits>
 
 #include "device_common.h"
@@ -82,12 +82,11 @@ __global__ __launch_bounds__(256) void bwd_preprocess(const float* __restrict__ 
 // ---------------------------------------------------------------------------
 // dK/dV and dQ kernels.  Tiles of Q and dO (dK/dV kernel) and of K and V
 // (dQ kernel) go global -> LDS with global_load_lds_dwordx4 and stay
-// row-major.  In the default kernels (bwd_dkdv3, bwd_dq3) these copies are
-// issued from inline assembly (dma16), so that the next tile's copies stay
-// in flight while the current tile is read (with compiler-visible copies in
-// flight every wait for an LDS read becomes lgkmcnt(0)) and are waited for
-// only at the end of the step; bwd_dkdv2 and bwd_dq2 are the previous
-// generation.  The transposed operands (Q^T, dO^T, K^T) come from
+// row-major.  These copies are issued from inline assembly (dma16), so that
+// the next tile's copies stay in flight while the current tile is read (with
+// compiler-visible copies in flight every wait for an LDS read becomes
+// lgkmcnt(0)) and are waited for only at the end of the step.  The
+// transposed operands (Q^T, dO^T, K^T) come from
 // ds_read_b64_tr_b16 on the same tiles, whose swizzle (dual_swizzle) keeps
 // both the row-wise and the transposed reads free of bank conflicts.  No
 // staging registers and no vector-ALU transposition, so two waves fit per
@@ -141,7 +140,7 @@ __device__ __forceinline__ bf16x8 row_operand(const bf16* tile, int row, int chu
 }  // namespace
 
 template <int D, int NW>
-struct Dkdv2Cfg {
+struct DkdvCfg {
   static constexpr int NT = NW * 64, BKV = NW * 32;
   static constexpr int BQ = (32 * D / 8) % (NW * 64) == 0 ? 32 : 64;  // whole-wave loads
   static constexpr int CHUNKS = BQ * D / 8;
@@ -151,184 +150,27 @@ struct Dkdv2Cfg {
   static_assert(CHUNKS % (NW * 64) == 0, "tile must split into whole wave loads");
 };
 
+// dK/dV kernel: one workgroup per block of NW * 32 keys, one wave per 32
+// keys.  The wave keeps its K rows in registers (the B operand of S^T) and
+// its V rows in LDS, and streams Q and dO tiles through LDS; per 32 queries
+// it forms S = Q K^T, P = exp(S - lse), dV^T += dO^T P, dP = dO V^T,
+// dS = P o (dP - D) and dK^T += Q^T dS.  Every LDS address is fixed before
+// the loop: each lane's byte offsets into a tile (row-wise reads per
+// k-step, transposed reads per 32-column block and half) are computed once,
+// since the dual swizzle mixes only the low four bits of a row, which the
+// lane fixes; the query sub-block, the k-step of the transposed reads and
+// the tile (Q, dO, or the wave's V rows, stored with the same swizzle) only
+// add constants, and the step is unrolled by two so that the stage is a
+// constant as well.  Operands are read two MFMAs ahead.  The products are
+// issued S, dP, dV, dK, so that the exponentials overlap the dP MFMAs and
+// dS the dV MFMAs.
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv2(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ Dg,
-    float* __restrict__ dK, float* __restrict__ dV, int n, int nkb, int total, float c,
-    float scale) {
-  using C = Dkdv2Cfg<D, NW>;
-  constexpr int BQ = C::BQ;
-  __shared__ __attribute__((aligned(1024))) bf16 tiles[2][2 * C::TILE];  // [stage][Q | dO]
-  __shared__ __attribute__((aligned(16))) float stats[2][2 * BQ];          // [stage][lse2 | D]
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = lane >> 5, li = lane & 31;
-  const int tile = xcd_remap(blockIdx.x, total);
-  const int head = tile / nkb, kblk = tile - head * nkb;
-  const size_t hoff = (size_t)head * n * D;
-  const bf16 *Qh = Q + hoff, *Kh = K + hoff, *Vh = V + hoff, *dOh = dO + hoff;
-  const float* lseh = lse2 + (size_t)head * n;
-  const float* Dh = Dg + (size_t)head * n;
-  const int key = kblk * C::BKV + wave * 32 + li;
-
-  bf16x8 kreg[D / 16], vreg[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    kreg[kk] = key < n ? *reinterpret_cast<const bf16x8*>(Kh + (size_t)key * D + 16 * kk + 8 * h)
-                       : bf16x8{};
-    vreg[kk] = key < n ? *reinterpret_cast<const bf16x8*>(Vh + (size_t)key * D + 16 * kk + 8 * h)
-                       : bf16x8{};
-  }
-  f32x16 dkt[D / 32], dvt[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) dkt[db] = dvt[db] = f32x16{};
-
-  // Tiles of Q and dO and the rows' lse2 and D go global -> LDS with direct
-  // loads (no registers, one wait): full tiles from a wave-uniform base plus
-  // per-lane offsets computed once; a partial last tile clamps its rows to
-  // n-1, and those rows are masked after the exponentials.
-  uint32_t toff[C::INSTS];
-#pragma unroll
-  for (int it = 0; it < C::INSTS; ++it) {
-    const int p = wave * C::WAVE_CHUNKS + it * 64 + lane;
-    const int row = p / (D / 8), phys = p % (D / 8);
-    toff[it] = (uint32_t)(row * D + (phys ^ dual_swizzle<D * 2>(row)) * 8) * 2u;
-  }
-  auto load = [&](int i, int buf) {
-    if ((i + 1) * BQ <= n) {
-      const char* qb = reinterpret_cast<const char*>(Qh) + (size_t)i * BQ * D * 2;
-      const char* gb = reinterpret_cast<const char*>(dOh) + (size_t)i * BQ * D * 2;
-#pragma unroll
-      for (int it = 0; it < C::INSTS; ++it) {
-        const int p0 = wave * C::WAVE_CHUNKS + it * 64;
-        load_lds_16(qb + toff[it], tiles[buf] + p0 * 8);
-        load_lds_16(gb + toff[it], tiles[buf] + C::TILE + p0 * 8);
-      }
-    } else {
-      tile_load_lds<D>(Qh, tiles[buf], i, BQ, n, wave, lane, C::WAVE_CHUNKS, C::INSTS, true);
-      tile_load_lds<D>(dOh, tiles[buf] + C::TILE, i, BQ, n, wave, lane, C::WAVE_CHUNKS, C::INSTS,
-                       true);
-    }
-    if (wave * 64 < 2 * BQ) {  // whole waves: 2 BQ is a multiple of 64
-      // A query row past n (a clamped copy of row n-1) gets lse2 = +inf,
-      // so its weights 2^(S c - lse2) are exactly 0 and it adds nothing to
-      // dV or dK, with no per-element mask in the loop.  Its D stays the
-      // clamped row's (finite), and 0 x finite = 0 in dS.
-      const int which = tid / BQ, r = tid - which * BQ;
-      const int qrow = min(i * BQ + r, n - 1);
-      if (which == 0 && i * BQ + r >= n)
-        stats[buf][tid] = __builtin_inff();
-      else
-        load_lds_4((which == 0 ? lseh : Dh) + qrow, &stats[buf][wave * 64]);
-    }
-  };
-
-  const int nqt = (n + BQ - 1) / BQ;
-  load(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int i = 0; i < nqt; ++i) {
-    const int buf = i & 1;
-    if (i + 1 < nqt) load(i + 1, buf ^ 1);
-    const bf16* Qs = tiles[buf];
-    const bf16* dOs = tiles[buf] + C::TILE;
-    // Opaque copies of the lane index: the LDS addresses derived from them
-    // are recomputed each iteration (a few integer ops) rather than held in
-    // registers across the loop, which would not fit.
-    int lio = li, laneo = lane;
-    asm volatile("" : "+v"(lio), "+v"(laneo));
-#pragma unroll
-    for (int qb = 0; qb < BQ / 32; ++qb) {
-      // S = Q K^T (32 queries x 32 keys per wave), P in bf16, dV^T += dO^T P;
-      // then dP = dO V^T, dS = P o (dP - D) from the same bf16 P, and
-      // dK^T += Q^T dS.  Only one score-sized accumulator is live at a time.
-      f32x16 s = {};
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
-        s = mfma_bf16_32x32x16(row_operand<D>(Qs, qb * 32 + lio, 2 * kk + h, true), kreg[kk], s);
-      uint32_t pk[8];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 l2 = *reinterpret_cast<const f32x4*>(&stats[buf][qb * 32 + 8 * g + 4 * h]);
-        float p[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = fast_exp2(__builtin_fmaf(s[4 * g + e], c, -l2[e]));
-        pk[2 * g] = pack_bf16x2(p[0], p[1]);
-        pk[2 * g + 1] = pack_bf16x2(p[2], p[3]);
-      }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 bp = __builtin_bit_cast(
-            bf16x8, (u32x4{pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]}));
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-          dvt[db] = mfma_bf16_32x32x16(tr_operand<D>(dOs, 2 * qb + ks, db, laneo), bp, dvt[db]);
-      }
-      f32x16 dp = {};
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk)
-        dp = mfma_bf16_32x32x16(row_operand<D>(dOs, qb * 32 + lio, 2 * kk + h, true), vreg[kk],
-                                dp);
-      uint32_t dsk[8];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 dd =
-            *reinterpret_cast<const f32x4*>(&stats[buf][BQ + qb * 32 + 8 * g + 4 * h]);
-        const float p0 = bf_lo(pk[2 * g]), p1 = bf_hi(pk[2 * g]);
-        const float p2 = bf_lo(pk[2 * g + 1]), p3 = bf_hi(pk[2 * g + 1]);
-        dsk[2 * g] = pack_bf16x2(p0 * (dp[4 * g] - dd[0]), p1 * (dp[4 * g + 1] - dd[1]));
-        dsk[2 * g + 1] = pack_bf16x2(p2 * (dp[4 * g + 2] - dd[2]), p3 * (dp[4 * g + 3] - dd[3]));
-      }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 bs = __builtin_bit_cast(
-            bf16x8, (u32x4{dsk[4 * ks], dsk[4 * ks + 1], dsk[4 * ks + 2], dsk[4 * ks + 3]}));
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-          dkt[db] = mfma_bf16_32x32x16(tr_operand<D>(Qs, 2 * qb + ks, db, laneo), bs, dkt[db]);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-
-  if (key < n) {
-    float* dKr = dK + hoff + (size_t)key * D;
-    float* dVr = dV + hoff + (size_t)key * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = db * 32 + 8 * g + 4 * h;
-        f32x4 a = {dkt[db][4 * g] * scale, dkt[db][4 * g + 1] * scale, dkt[db][4 * g + 2] * scale,
-                   dkt[db][4 * g + 3] * scale};
-        f32x4 b = {dvt[db][4 * g], dvt[db][4 * g + 1], dvt[db][4 * g + 2], dvt[db][4 * g + 3]};
-        *reinterpret_cast<f32x4*>(dKr + col) = a;
-        *reinterpret_cast<f32x4*>(dVr + col) = b;
-      }
-  }
-}
-
-// dK/dV kernel with every LDS address fixed before the loop.  Same
-// products as bwd_dkdv2, with V in LDS and the operands read two MFMAs
-// ahead; in addition each lane's byte offsets into a tile (row-wise reads
-// per k-step, transposed reads per 32-column block and half) are computed
-// once: the dual swizzle mixes only the low four bits of a row, which the
-// lane fixes, so the query sub-block, the k-step of the transposed reads and
-// the tile (Q, dO, or the wave's V rows, stored with the same swizzle under
-// REORDER) only add constants, and the step is unrolled by two so that the
-// stage is a constant as well.  The loop then forms no LDS address with
-// vector instructions.  REORDER issues S, dP, dV, dK (instead of S, dV, dP,
-// dK) so that the exponentials overlap the dP MFMAs and dS the dV MFMAs.
-template <int D, int NW, bool REORDER = true>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv3(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ Dg,
     float* __restrict__ dK, float* __restrict__ dV, int n, int nkb, int total, float c,
     float scale) {
-  using C = Dkdv2Cfg<D, NW>;
+  using C = DkdvCfg<D, NW>;
   constexpr int BQ = C::BQ;
   constexpr int NKK = D / 16, NDB = D / 32;
   constexpr int TILE_B = C::TILE * 2;               // bytes of one Q or dO tile
@@ -365,7 +207,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv3(
 #pragma unroll
     for (int it = 0; it < 32 * RC / 64; ++it) {
       const int p = it * 64 + lane, row = p / RC, phys = p % RC;
-      const int logical = phys ^ (REORDER ? dual_swizzle<D * 2>(row) : chunk_swizzle<D * 2>(row));
+      const int logical = phys ^ dual_swizzle<D * 2>(row);
       const int vrow = min(kblk * C::BKV + wave * 32 + row, n - 1);
       load_lds_16(Vh + (size_t)vrow * D + logical * 8, Vw + it * 64 * 8);
     }
@@ -382,15 +224,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv3(
     const int row = p / (D / 8), phys = p % (D / 8);
     toff[it] = (uint32_t)(row * D + (phys ^ dual_swizzle<D * 2>(row)) * 8) * 2u;
   }
-  // roff: Q, dO (and, under REORDER, V) rows; voff: V rows stored with the
-  // row swizzle (order S, dV, dP, dK)
-  uint32_t roff[NKK], voff[NKK], troff[NDB][2];
+  // roff: row-wise reads of Q, dO and the wave's V rows (one swizzle)
+  uint32_t roff[NKK], troff[NDB][2];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
+  for (int kk = 0; kk < NKK; ++kk)
     roff[kk] = (uint32_t)(li * D + ((2 * kk + h) ^ dual_swizzle<D * 2>(li)) * 8) * 2u;
-    voff[kk] = REORDER ? roff[kk]
-                       : (uint32_t)(li * D + ((2 * kk + h) ^ chunk_swizzle<D * 2>(li)) * 8) * 2u;
-  }
   {
     const int G = lane >> 4, sl = lane & 15, hh = G >> 1;
 #pragma unroll
@@ -455,10 +293,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv3(
             lds_read_tr16(reinterpret_cast<const bf16*>(t + troff[db][1] + ksp * 16 * D * 2));
         return __builtin_bit_cast(bf16x8, (u32x4{p0[0], p0[1], p1[0], p1[1]}));
       };
-      // operand sequence: S (Q rows), then with REORDER dP (dO rows), dV
-      // (dO^T), dK (Q^T); without it dV, dP, dK
-      constexpr int T_DV = REORDER ? 2 * NKK : NKK;
-      constexpr int T_DP = REORDER ? NKK : NKK + 2 * NDB;
+      // operand sequence: S (Q rows), dP (dO rows), dV (dO^T), dK (Q^T)
+      constexpr int T_DP = NKK, T_DV = 2 * NKK;
       constexpr int T_DK = 2 * NKK + 2 * NDB;
       auto fetch = [&](int t) {
         if (t < NKK) {
@@ -480,10 +316,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv3(
 #pragma unroll
       for (int t = 0; t < AH; ++t) fetch(t);
       // S = Q K^T, P = 2^(S c - lse2) in bf16, dV^T += dO^T P; dP = dO V^T,
-      // dS = P o (dP - D) from the same bf16 P, dK^T += Q^T dS.  With
-      // REORDER the dP MFMAs follow the S MFMAs directly, so the
-      // exponentials run while they execute and dS while the dV MFMAs do
-      // (two score-sized accumulators live instead of one).
+      // dS = P o (dP - D) from the same bf16 P, dK^T += Q^T dS.  The dP
+      // MFMAs follow the S MFMAs directly, so the exponentials run while
+      // they execute and dS while the dV MFMAs do (two score-sized
+      // accumulators live instead of one).
       f32x16 s = {}, dp = {};
       uint32_t pk[8];
       auto scores = [&]() {
@@ -515,21 +351,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv3(
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
           const bf16x8 vb =
-              *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(Vw) + voff[kk]);
+              *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(Vw) + roff[kk]);
           dp = mfma_bf16_32x32x16(use(T_DP + kk), vb, dp);
         }
       };
-      if constexpr (REORDER) {
-        scores();
-        dprod();
-        exps();
-        dv_update();
-      } else {
-        scores();
-        exps();
-        dv_update();
-        dprod();
-      }
+      scores();
+      dprod();
+      exps();
+      dv_update();
       uint32_t dsk[8];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -580,7 +409,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv3(
 }
 
 template <int D, int NW, int BC>
-struct Dq2Cfg {
+struct DqCfg {
   static constexpr int NT = NW * 64, BQB = NW * 32;
   static constexpr int CHUNKS = BC * D / 8;
   static constexpr int WAVE_CHUNKS = CHUNKS / NW;
@@ -589,141 +418,22 @@ struct Dq2Cfg {
   static_assert(CHUNKS % (NW * 64) == 0, "tile must split into whole wave loads");
 };
 
-template <int D, int NW, int BC>
-__global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq2(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dg,
-    float* __restrict__ dQ, int n, int nqb, int total, float c, float scale) {
-  using C = Dq2Cfg<D, NW, BC>;
-  __shared__ __attribute__((aligned(1024))) bf16 tiles[2][2 * C::TILE];  // [stage][K | V]
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = lane >> 5, li = lane & 31;
-  const int tile = xcd_remap(blockIdx.x, total);
-  const int head = tile / nqb, qblk = tile - head * nqb;
-  const size_t hoff = (size_t)head * n * D;
-  const bf16 *Qh = Q + hoff, *Kh = K + hoff, *Vh = V + hoff, *dOh = dO + hoff;
-  const int q = qblk * C::BQB + wave * 32 + li;
-
-  bf16x8 qreg[D / 16], dogreg[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    qreg[kk] = q < n ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)q * D + 16 * kk + 8 * h)
-                     : bf16x8{};
-    dogreg[kk] = q < n ? *reinterpret_cast<const bf16x8*>(dOh + (size_t)q * D + 16 * kk + 8 * h)
-                       : bf16x8{};
-  }
-  const float l2 = q < n ? lse[(size_t)head * n + q] * kLog2e : 0.f;
-  const float dq_d = q < n ? Dg[(size_t)head * n + q] : 0.f;
-  f32x16 dqt[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) dqt[db] = f32x16{};
-
-  // Full tiles from a wave-uniform base plus per-lane offsets computed once
-  // (K with the dual swizzle, V with the row swizzle); a partial last tile
-  // clamps its rows to n-1 (those keys are masked below).
-  uint32_t koff[C::INSTS], voff[C::INSTS];
-#pragma unroll
-  for (int it = 0; it < C::INSTS; ++it) {
-    const int p = wave * C::WAVE_CHUNKS + it * 64 + lane;
-    const int row = p / (D / 8), phys = p % (D / 8);
-    koff[it] = (uint32_t)(row * D + (phys ^ dual_swizzle<D * 2>(row)) * 8) * 2u;
-    voff[it] = (uint32_t)(row * D + (phys ^ chunk_swizzle<D * 2>(row)) * 8) * 2u;
-  }
-  auto load = [&](int j, int buf) {
-    if ((j + 1) * BC <= n) {
-      const char* kb = reinterpret_cast<const char*>(Kh) + (size_t)j * BC * D * 2;
-      const char* vb = reinterpret_cast<const char*>(Vh) + (size_t)j * BC * D * 2;
-#pragma unroll
-      for (int it = 0; it < C::INSTS; ++it) {
-        const int p0 = wave * C::WAVE_CHUNKS + it * 64;
-        dma16(kb + koff[it], tiles[buf] + p0 * 8);
-        dma16(vb + voff[it], tiles[buf] + C::TILE + p0 * 8);
-      }
-    } else {
-      tile_load_lds<D, true>(Kh, tiles[buf], j, BC, n, wave, lane, C::WAVE_CHUNKS, C::INSTS, true);
-      tile_load_lds<D, true>(Vh, tiles[buf] + C::TILE, j, BC, n, wave, lane, C::WAVE_CHUNKS,
-                             C::INSTS, false);
-    }
-  };
-
-  const int nkt = (n + BC - 1) / BC;
-  load(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int j = 0; j < nkt; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < nkt) load(j + 1, buf ^ 1);
-    const bf16* Ks = tiles[buf];
-    const bf16* Vs = tiles[buf] + C::TILE;
-    // Opaque copies of the lane index: LDS addresses derived from them are
-    // recomputed each iteration instead of being held across the loop.
-    int lio = li, laneo = lane;
-    asm volatile("" : "+v"(lio), "+v"(laneo));
-#pragma unroll
-    for (int kb = 0; kb < BC / 32; ++kb) {
-      // S^T = K Q^T and dP^T = V dO^T (32 keys x 32 queries per wave).
-      f32x16 s = {}, dp = {};
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        s = mfma_bf16_32x32x16(row_operand<D>(Ks, kb * 32 + lio, 2 * kk + h, true), qreg[kk], s);
-        dp = mfma_bf16_32x32x16(row_operand<D>(Vs, kb * 32 + lio, 2 * kk + h, false), dogreg[kk],
-                                dp);
-      }
-      const int kbase = j * BC + kb * 32;
-      const bool tail = kbase + 32 > n;
-      uint32_t dsk[8];
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float p0 = fast_exp2(__builtin_fmaf(s[r], c, -l2));
-        float p1 = fast_exp2(__builtin_fmaf(s[r + 1], c, -l2));
-        if (tail) {
-          const int k0 = kbase + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (k0 >= n) p0 = 0.f;
-          if (k0 + 1 >= n) p1 = 0.f;
-        }
-        dsk[r >> 1] = pack_bf16x2(p0 * (dp[r] - dq_d), p1 * (dp[r + 1] - dq_d));
-      }
-      // dQ^T += K^T dS^T over these 32 keys.
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 bs = __builtin_bit_cast(
-            bf16x8, (u32x4{dsk[4 * ks], dsk[4 * ks + 1], dsk[4 * ks + 2], dsk[4 * ks + 3]}));
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-          dqt[db] = mfma_bf16_32x32x16(tr_operand<D>(Ks, 2 * kb + ks, db, laneo), bs, dqt[db]);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-
-  if (q < n) {
-    float* dQr = dQ + hoff + (size_t)q * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 a = {dqt[db][4 * g] * scale, dqt[db][4 * g + 1] * scale, dqt[db][4 * g + 2] * scale,
-                   dqt[db][4 * g + 3] * scale};
-        *reinterpret_cast<f32x4*>(dQr + db * 32 + 8 * g + 4 * h) = a;
-      }
-  }
-}
-
-// dQ kernel with every LDS address fixed before the loop (as bwd_dkdv3):
-// each lane's byte offsets for the row-wise K and V reads per k-step and the
-// transposed K reads per 32-column block and half are computed once, the
-// key sub-block and the k-step only add constants, and the step is unrolled
-// by two so that the stage is a constant.  Operands are read two MFMAs
-// ahead.  Products, order and masking as bwd_dq2.
+// dQ kernel: one workgroup per block of NW * 32 queries, one wave per 32
+// queries, K and V tiles of BC keys streamed through LDS.  Per key tile the
+// wave recomputes S = Q K^T and P = exp(S - lse), forms dP = dO V^T and
+// dS = P o (dP - D), and accumulates dQ^T += K^T dS^T; keys past n are
+// masked.  Every LDS address is fixed before the loop (as in bwd_dkdv3):
+// each lane's byte offsets for the row-wise K and V reads per k-step and
+// the transposed K reads per 32-column block and half are computed once,
+// the key sub-block and the k-step only add constants, and the step is
+// unrolled by two so that the stage is a constant.  Operands are read two
+// MFMAs ahead.
 template <int D, int NW, int BC>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq3(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dg,
     float* __restrict__ dQ, int n, int nqb, int total, float c, float scale) {
-  using C = Dq2Cfg<D, NW, BC>;
+  using C = DqCfg<D, NW, BC>;
   constexpr int NKK = D / 16, NDB = D / 32;
   constexpr int TILE_B = C::TILE * 2;
   __shared__ __attribute__((aligned(1024))) char tiles[4 * TILE_B];  // [stage][K | V]
@@ -892,17 +602,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq3(
 
 namespace {
 
-template <int V>
-struct IntK {
-  static constexpr int value = V;
-};
-
-// Kernel generation via ATTN_BWD_VARIANT: unset or "v3" (default:
-// bwd_dkdv3 with the dP MFMAs right after the S MFMAs, and bwd_dq3), "v3o"
-// (bwd_dkdv3 in the order S, dV, dP, dK, and bwd_dq3), or "v2" (the
-// previous generation, bwd_dkdv2 and bwd_dq2: V in registers, every LDS
-// address recomputed and every operand read just before its MFMA); the
-// waves per workgroup via ATTN_BWD_WAVES ("4" or "8", default 8).
+// Eight waves per workgroup in both kernels: bwd_dkdv3 (one wave per 32
+// keys; per 32 queries S, then dP, then dV and dK) and bwd_dq3.
 template <int D>
 hipError_t launch(const void* Q, const void* K, const void* V, const float* O, const void* dO,
                   const float* lse, float* dQ, float* dK, float* dV, int64_t bh, int64_t n,
@@ -921,49 +622,19 @@ hipError_t launch(const void* Q, const void* K, const void* V, const float* O, c
                      stream, O, g, Dbuf, rows, lse, lse2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const char* var = getenv("ATTN_BWD_VARIANT");
-  const bool gen2 = var && strcmp(var, "v2") == 0;
-  const bool first_order = var && strcmp(var, "v3o") == 0;
-  const char* wv = getenv("ATTN_BWD_WAVES");
-  const bool w4 = wv && strcmp(wv, "4") == 0;
-  auto dkdv = [&](auto nwc) {
-    constexpr int NW = decltype(nwc)::value;
-    using Cf = Dkdv2Cfg<D, NW>;
-    const int nkb = (int)((n + Cf::BKV - 1) / Cf::BKV);
-    const int total_kv = (int)(bh * nkb);
-    if (gen2)
-      hipLaunchKernelGGL((bwd_dkdv2<D, NW>), dim3(total_kv), dim3(NW * 64), 0, stream, q, k, v,
-                         g, lse2, Dbuf, dK, dV, (int)n, nkb, total_kv, c, scale);
-    else if (first_order)
-      hipLaunchKernelGGL((bwd_dkdv3<D, NW, false>), dim3(total_kv), dim3(NW * 64), 0, stream, q,
-                         k, v, g, lse2, Dbuf, dK, dV, (int)n, nkb, total_kv, c, scale);
-    else
-      hipLaunchKernelGGL((bwd_dkdv3<D, NW, true>), dim3(total_kv), dim3(NW * 64), 0, stream, q, k,
-                         v, g, lse2, Dbuf, dK, dV, (int)n, nkb, total_kv, c, scale);
-  };
-  auto dqk = [&](auto nwc) {
-    constexpr int NW = decltype(nwc)::value;
-    using Cf = Dq2Cfg<D, NW, 64>;
-    const int nqb = (int)((n + Cf::BQB - 1) / Cf::BQB);
-    const int total_q = (int)(bh * nqb);
-    if (gen2)
-      hipLaunchKernelGGL((bwd_dq2<D, NW, 64>), dim3(total_q), dim3(NW * 64), 0, stream, q, k, v,
-                         g, lse, Dbuf, dQ, (int)n, nqb, total_q, c, scale);
-    else
-      hipLaunchKernelGGL((bwd_dq3<D, NW, 64>), dim3(total_q), dim3(NW * 64), 0, stream, q, k, v,
-                         g, lse, Dbuf, dQ, (int)n, nqb, total_q, c, scale);
-  };
-  if (w4) {
-    dkdv(IntK<4>{});
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    dqk(IntK<4>{});
-  } else {
-    dkdv(IntK<8>{});
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    dqk(IntK<8>{});
-  }
+  constexpr int NW = 8;
+  using Ckv = DkdvCfg<D, NW>;
+  const int nkb = (int)((n + Ckv::BKV - 1) / Ckv::BKV);
+  const int total_kv = (int)(bh * nkb);
+  hipLaunchKernelGGL((bwd_dkdv3<D, NW>), dim3(total_kv), dim3(NW * 64), 0, stream, q, k, v, g,
+                     lse2, Dbuf, dK, dV, (int)n, nkb, total_kv, c, scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  using Cq = DqCfg<D, NW, 64>;
+  const int nqb = (int)((n + Cq::BQB - 1) / Cq::BQB);
+  const int total_q = (int)(bh * nqb);
+  hipLaunchKernelGGL((bwd_dq3<D, NW, 64>), dim3(total_q), dim3(NW * 64), 0, stream, q, k, v, g,
+                     lse, Dbuf, dQ, (int)n, nqb, total_q, c, scale);
   return hipGetLastError();
 }
 

@@ -7,21 +7,17 @@
 // FlashAttention's I/O comes from" (keep a block of B queries and their
 // output state on chip, scan all of K and V once per query block).
 //
-// Work split: one workgroup per (head, block of B query rows); B = NW * QB *
-// 32.  Each wave owns QB*32 query rows and keeps, in registers, its Q rows
-// (as MFMA B operands), the transposed output accumulator U^T (d x rows) and
-// per row (m, l).  K/V are streamed in tiles of BC keys through
-// double-buffered LDS; the tile for step j+1 is fetched into registers while
-// step j computes.
+// Work split: one workgroup per (head, block of B query rows).  Each wave
+// owns 32 query rows and keeps, in registers, its Q rows (as MFMA B
+// operands), the transposed output accumulator U^T (d x rows) and per row
+// (m, l).  K/V are streamed in tiles of BC keys through LDS.
 //
 // Orientation.  The score tile is computed transposed, S^T = K Q^T, so the
 // MFMA result puts one query per lane column: a query's scores sit in one
 // lane pair (l, l^32), row maxima need only one cross-lane exchange, and the
 // rescale factor of a query is a per-lane scalar.  The exponentiated tile
 // P^T is converted to bf16 in registers and used directly as the B operand
-// of U^T += V^T P^T; the value tile is therefore stored transposed in LDS
-// (d rows x BC keys), with the key order permuted (vt_key_pos) to match the
-// MFMA accumulator layout, so that each lane's A operand is one 16-byte read.
+// of U^T += V^T P^T.
 //
 // Exponent base.  Scores are turned into base-2 exponents with one FMA,
 // t = s * c - m with c = scale * log2(e), and exponentiated with v_exp_f32.
@@ -34,7 +30,6 @@
 // The row sum l is accumulated from the bf16-rounded P values (the ones the
 // MFMA multiplies), so the normalisation matches the weights used.
 #include <algorithm>
-#include <cstdlib>
 #include <cstring>
 
 #include "device_common.h"
@@ -44,551 +39,10 @@ namespace at {
 
 constexpr float kTau = 8.0f;
 
-template <int D, int QB, int NW, int BC>
-struct FusedCfg {
-  static constexpr int NT = NW * 64;
-  static constexpr int BR = NW * QB * 32;
-  static constexpr int KEYS = BC;
-  static constexpr int CPR = D / 8;                  // 16-byte chunks per K row
-  static constexpr int K_CHUNKS = BC * CPR;          // chunks per K tile
-  static constexpr int K_ITERS = (K_CHUNKS + NT - 1) / NT;
-  static constexpr int V_ITEMS = (BC / 4) * CPR;     // (4 keys x 8 d) blocks per V tile
-  static constexpr int V_ITERS = (V_ITEMS + NT - 1) / NT;
-  static constexpr int KS = BC * D;                  // bf16 elements per K buffer
-  static constexpr int VT = D * BC;                  // bf16 elements per V^T buffer
-  static constexpr int LDS_ELEMS = 2 * (KS + VT);
-  // Elements held on chip per workgroup: Q block, U block, (m, l) per row,
-  // one K tile, one V tile and the score tile (the double buffer is a
-  // latency device and is not counted).
-  static constexpr int64_t ONCHIP = (int64_t)BR * D * 2 + 2 * BR + 2 * BC * D + (int64_t)BR * BC;
-  static_assert(D % 32 == 0 && BC % 32 == 0, "tile shape");
-};
-
-template <int D, int QB, int NW, int BC>
-__global__ __launch_bounds__(NW * 64, 1) void fwd_fused_bf16_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    float* __restrict__ O, float* __restrict__ lse, int n, int nqb, int total, float c) {
-  using C = FusedCfg<D, QB, NW, BC>;
-  __shared__ __attribute__((aligned(16))) bf16 smem[C::LDS_ELEMS];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int h = lane >> 5;
-  const int li = lane & 31;
-
-  const int tile = xcd_remap(blockIdx.x, total);
-  const int head = tile / nqb;
-  const int qblk = tile - head * nqb;
-  const size_t hoff = (size_t)head * (size_t)n * D;
-  const bf16* Qh = Q + hoff;
-  const bf16* Kh = K + hoff;
-  const bf16* Vh = V + hoff;
-  const int qw0 = qblk * C::BR + wave * (QB * 32);
-
-  // Q rows of this wave as B operands: lane holds Q[q][16kk + 8h .. +7].
-  bf16x8 qreg[QB][D / 16];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int q = qw0 + qb * 32 + li;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      if (q < n)
-        qreg[qb][kk] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)q * D + kk * 16 + 8 * h);
-      else
-        qreg[qb][kk] = bf16x8{};
-    }
-  }
-
-  f32x16 uacc[D / 32][QB];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) uacc[db][qb] = f32x16{};
-  float m[QB], l[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = -INFINITY;
-    l[qb] = 0.f;
-  }
-
-  const int nt = (n + BC - 1) / BC;
-  u32x4 kreg[C::K_ITERS];
-  u32x4 vreg[C::V_ITERS][4];
-
-  // Global -> registers for key tile j (rows past n read as zero).
-  auto load_tile = [&](int j) {
-    const int kbase = j * BC;
-#pragma unroll
-    for (int it = 0; it < C::K_ITERS; ++it) {
-      const int x = tid + it * C::NT;
-      const int row = x / C::CPR, cc = x % C::CPR;
-      const int key = kbase + row;
-      if (x < C::K_CHUNKS && key < n)
-        kreg[it] = *reinterpret_cast<const u32x4*>(Kh + (size_t)key * D + cc * 8);
-      else
-        kreg[it] = u32x4{};
-    }
-#pragma unroll
-    for (int it = 0; it < C::V_ITERS; ++it) {
-      const int x = tid + it * C::NT;
-      const int g = x % (BC / 4), cc = x / (BC / 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = kbase + 4 * g + e;
-        if (x < C::V_ITEMS && key < n)
-          vreg[it][e] = *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + cc * 8);
-        else
-          vreg[it][e] = u32x4{};
-      }
-    }
-  };
-
-  // Registers -> LDS buffer `buf`: K row-major with swizzled chunks; V
-  // transposed (d rows x BC keys) with permuted key positions.
-  auto store_tile = [&](int buf) {
-    bf16* Ks = smem + buf * C::KS;
-    bf16* Vt = smem + 2 * C::KS + buf * C::VT;
-#pragma unroll
-    for (int it = 0; it < C::K_ITERS; ++it) {
-      const int x = tid + it * C::NT;
-      if (x < C::K_CHUNKS) {
-        const int row = x / C::CPR, cc = x % C::CPR;
-        *reinterpret_cast<u32x4*>(Ks + row * D + ((cc ^ chunk_swizzle<D * 2>(row)) * 8)) =
-            kreg[it];
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < C::V_ITERS; ++it) {
-      const int x = tid + it * C::NT;
-      if (x < C::V_ITEMS) {
-        const int g = x % (BC / 4), cc = x / (BC / 4);
-        const int pos = vt_key_pos(4 * g);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int r0 = cc * 8 + 2 * w;
-          const int r1 = r0 + 1;
-          u32x2 lo = {pair_lo(vreg[it][0][w], vreg[it][1][w]),
-                      pair_lo(vreg[it][2][w], vreg[it][3][w])};
-          u32x2 hi = {pair_hi(vreg[it][0][w], vreg[it][1][w]),
-                      pair_hi(vreg[it][2][w], vreg[it][3][w])};
-          *reinterpret_cast<u32x2*>(Vt + r0 * BC +
-                                    (((pos >> 3) ^ chunk_swizzle<BC * 2>(r0)) * 8) + (pos & 7)) = lo;
-          *reinterpret_cast<u32x2*>(Vt + r1 * BC +
-                                    (((pos >> 3) ^ chunk_swizzle<BC * 2>(r1)) * 8) + (pos & 7)) = hi;
-        }
-      }
-    }
-  };
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < nt; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < nt) load_tile(j + 1);
-    const bf16* Ks = smem + buf * C::KS;
-    const bf16* Vt = smem + 2 * C::KS + buf * C::VT;
-
-    // S^T = K_j Q^T: BC x (QB*32), contraction over d.
-    f32x16 s[BC / 32][QB];
-#pragma unroll
-    for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb) {
-        const int row = kb * 32 + li;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            Ks + row * D + (((2 * kk + h) ^ chunk_swizzle<D * 2>(row)) * 8));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma_bf16_32x32x16(a, qreg[qb][kk], s[kb][qb]);
-      }
-    }
-
-    // Keys past n in the last tile do not exist: their scores are -inf.
-    if (j == nt - 1 && (n % BC) != 0) {
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j * BC + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key >= n) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) s[kb][qb][r] = -INFINITY;
-          }
-        }
-    }
-
-    // Online softmax: running maximum, rescale factor, exponentials, sums.
-    uint32_t pk[BC / 32][QB][8];
-    float alpha[QB];
-    bool need_any = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mc = mx * c;
-      const bool need = mc > m[qb] + kTau;
-      const float mn = need ? mc : m[qb];
-      alpha[qb] = need ? fast_exp2(m[qb] - mn) : 1.0f;
-      need_any |= need;
-      m[qb] = mn;
-      float lsum = l[qb] * alpha[qb];
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(__builtin_fmaf(s[kb][qb][r], c, -mn));
-          const float p1 = fast_exp2(__builtin_fmaf(s[kb][qb][r + 1], c, -mn));
-          const uint32_t pp = pack_bf16x2(p0, p1);
-          pk[kb][qb][r >> 1] = pp;
-          lsum = add_bf16x2(pp, lsum);
-        }
-      l[qb] = lsum;
-    }
-    if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) uacc[db][qb] *= alpha[qb];
-    }
-
-    // U^T += V_j^T P^T: contraction over the BC keys in steps of 16.
-#pragma unroll
-    for (int ks = 0; ks < BC / 16; ++ks) {
-      const int kb = ks >> 1, half = ks & 1;
-      bf16x8 pb[QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        u32x4 t = {pk[kb][qb][4 * half + 0], pk[kb][qb][4 * half + 1], pk[kb][qb][4 * half + 2],
-                   pk[kb][qb][4 * half + 3]};
-        pb[qb] = __builtin_bit_cast(bf16x8, t);
-      }
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int row = db * 32 + li;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            Vt + row * BC + (((4 * kb + 2 * half + h) ^ chunk_swizzle<BC * 2>(row)) * 8));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) uacc[db][qb] = mfma_bf16_32x32x16(a, pb[qb], uacc[db][qb]);
-      }
-    }
-
-    if (j + 1 < nt) store_tile(buf ^ 1);
-    __syncthreads();
-  }
-
-  // Epilogue: o = u / l, lse = (m + log2 l) ln 2.
-  float* Oh = O + hoff;
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = l[qb] + __shfl_xor(l[qb], 32);
-    const float inv = 1.0f / lt;
-    const int q = qw0 + qb * 32 + li;
-    if (q < n) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 v = {uacc[db][qb][4 * g + 0] * inv, uacc[db][qb][4 * g + 1] * inv,
-                     uacc[db][qb][4 * g + 2] * inv, uacc[db][qb][4 * g + 3] * inv};
-          *reinterpret_cast<f32x4*>(Oh + (size_t)q * D + db * 32 + 8 * g + 4 * h) = v;
-        }
-      if (h == 0 && lse != nullptr) lse[(size_t)head * n + q] = (m[qb] + __log2f(lt)) * kLn2;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Software-pipelined variant (one 32-row query block per wave).  Within each
-// wave the score tile of step j+1 is issued on the matrix cores before the
-// softmax of step j runs on the vector ALUs, so the two overlap:
-//
-//   step j:  global -> registers: K tile j+2, V tile j+1
-//            S_{j+1} = K_{j+1} Q^T        (MFMA, LDS K buffer (j+1)%2)
-//            softmax(S_j) -> P_j          (VALU)
-//            U^T += V_j^T P_j^T           (MFMA, LDS V buffer j%2)
-//            registers -> LDS: K_{j+2} into K buffer j%2, V_{j+1} into V
-//            buffer (j+1)%2;  barrier
-//
-// K runs two tiles ahead of V, so two buffers of each still need only one
-// barrier per step: the K buffer written in step j held K_j, last read in
-// step j-1, and the V buffer written held V_{j-1}, also last read in step
-// j-1.  Steps are unrolled in pairs so every LDS offset is a compile-time
-// constant; only the last tile takes the guarded loads and the key mask.
-
 template <int V>
 struct IntC {
   static constexpr int value = V;
 };
-
-template <int D, int NW, int BC>
-struct PipeCfg {
-  static constexpr int NT = NW * 64;
-  static constexpr int BR = NW * 32;
-  static constexpr int KEYS = BC;
-  static constexpr int CPR = D / 8;
-  static constexpr int K_CHUNKS = BC * CPR;
-  static constexpr int K_ITERS = (K_CHUNKS + NT - 1) / NT;
-  static constexpr int V_ITEMS = (BC / 4) * CPR;
-  static constexpr int V_ITERS = (V_ITEMS + NT - 1) / NT;
-  static constexpr int KS = BC * D;
-  static constexpr int VT = D * BC;
-  static constexpr int LDS_ELEMS = 2 * (KS + VT);
-  static constexpr int MINB = NW >= 8 ? 1 : 8 / NW;  // two waves per SIMD
-  static constexpr int64_t ONCHIP = (int64_t)BR * D * 2 + 2 * BR + 2 * BC * D + (int64_t)BR * BC;
-};
-
-template <int D, int NW, int BC>
-__global__ __launch_bounds__(NW * 64, (NW >= 8 ? 1 : 8 / NW)) void fwd_fused_bf16_pipe_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    float* __restrict__ O, float* __restrict__ lse, int n, int nqb, int total, float c) {
-  using C = PipeCfg<D, NW, BC>;
-  __shared__ __attribute__((aligned(16))) bf16 smem[C::LDS_ELEMS];
-  bf16* const Ksb = smem;                 // [2][KS]
-  bf16* const Vtb = smem + 2 * C::KS;     // [2][VT]
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int h = lane >> 5;
-  const int li = lane & 31;
-
-  const int tile = xcd_remap(blockIdx.x, total);
-  const int head = tile / nqb;
-  const int qblk = tile - head * nqb;
-  const size_t hoff = (size_t)head * (size_t)n * D;
-  const bf16* Qh = Q + hoff;
-  const bf16* Kh = K + hoff;
-  const bf16* Vh = V + hoff;
-  const int q = qblk * C::BR + wave * 32 + li;
-
-  bf16x8 qreg[D / 16];
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk)
-    qreg[kk] = q < n ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)q * D + kk * 16 + 8 * h)
-                     : bf16x8{};
-
-  f32x16 uacc[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) uacc[db] = f32x16{};
-  float m = -INFINITY, l = 0.f;
-  const int nt = (n + BC - 1) / BC;
-
-  u32x4 kreg[C::K_ITERS];
-  u32x4 vreg[C::V_ITERS][4];
-
-  auto load_k = [&](int t) {
-    const int kbase = t * BC;
-    const bool full = kbase + BC <= n;
-#pragma unroll
-    for (int it = 0; it < C::K_ITERS; ++it) {
-      const int x = tid + it * C::NT;
-      const int row = x / C::CPR, cc = x % C::CPR;
-      const bool ok = (C::K_CHUNKS % C::NT == 0 || x < C::K_CHUNKS) && (full || kbase + row < n);
-      kreg[it] = ok ? *reinterpret_cast<const u32x4*>(Kh + (size_t)(kbase + row) * D + cc * 8)
-                    : u32x4{};
-    }
-  };
-  auto load_v = [&](int t) {
-    const int kbase = t * BC;
-    const bool full = kbase + BC <= n;
-#pragma unroll
-    for (int it = 0; it < C::V_ITERS; ++it) {
-      const int x = tid + it * C::NT;
-      const int g = x % (BC / 4), cc = x / (BC / 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool ok =
-            (C::V_ITEMS % C::NT == 0 || x < C::V_ITEMS) && (full || kbase + 4 * g + e < n);
-        vreg[it][e] =
-            ok ? *reinterpret_cast<const u32x4*>(Vh + (size_t)(kbase + 4 * g + e) * D + cc * 8)
-               : u32x4{};
-      }
-    }
-  };
-  auto store_k = [&](bf16* Ks) {
-#pragma unroll
-    for (int it = 0; it < C::K_ITERS; ++it) {
-      const int x = tid + it * C::NT;
-      if (C::K_CHUNKS % C::NT == 0 || x < C::K_CHUNKS) {
-        const int row = x / C::CPR, cc = x % C::CPR;
-        *reinterpret_cast<u32x4*>(Ks + row * D + ((cc ^ chunk_swizzle<D * 2>(row)) * 8)) =
-            kreg[it];
-      }
-    }
-  };
-  auto store_v = [&](bf16* Vt) {
-#pragma unroll
-    for (int it = 0; it < C::V_ITERS; ++it) {
-      const int x = tid + it * C::NT;
-      if (C::V_ITEMS % C::NT == 0 || x < C::V_ITEMS) {
-        const int g = x % (BC / 4), cc = x / (BC / 4);
-        const int pos = vt_key_pos(4 * g);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int r0 = cc * 8 + 2 * w;
-          const int r1 = r0 + 1;
-          u32x2 lo = {pair_lo(vreg[it][0][w], vreg[it][1][w]),
-                      pair_lo(vreg[it][2][w], vreg[it][3][w])};
-          u32x2 hi = {pair_hi(vreg[it][0][w], vreg[it][1][w]),
-                      pair_hi(vreg[it][2][w], vreg[it][3][w])};
-          *reinterpret_cast<u32x2*>(Vt + r0 * BC +
-                                    (((pos >> 3) ^ chunk_swizzle<BC * 2>(r0)) * 8) + (pos & 7)) = lo;
-          *reinterpret_cast<u32x2*>(Vt + r1 * BC +
-                                    (((pos >> 3) ^ chunk_swizzle<BC * 2>(r1)) * 8) + (pos & 7)) = hi;
-        }
-      }
-    }
-  };
-  auto compute_s = [&](const bf16* Ks, f32x16 (&s)[BC / 32]) {
-#pragma unroll
-    for (int kb = 0; kb < BC / 32; ++kb) s[kb] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb) {
-        const int row = kb * 32 + li;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            Ks + row * D + (((2 * kk + h) ^ chunk_swizzle<D * 2>(row)) * 8));
-        s[kb] = mfma_bf16_32x32x16(a, qreg[kk], s[kb]);
-      }
-  };
-  // Online softmax, part 1: row maximum, the new reference m and the
-  // rescale of l and U (the only branch; taken when some row's maximum rose
-  // by more than kTau).  Returns m.
-  auto softmax_max = [&](f32x16 (&s)[BC / 32], bool mask, int kbase) {
-    if (mask) {
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kbase + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3) >= n) s[kb][r] = -INFINITY;
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mc = mx * c;
-    const bool need = mc > m + kTau;
-    const float mn = need ? mc : m;
-    const float alpha = need ? fast_exp2(m - mn) : 1.0f;
-    m = mn;
-    l *= alpha;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) uacc[db] *= alpha;
-    }
-  };
-  // Online softmax, part 2: exponentials in bf16 and their row sum
-  // (branch-free, so it can interleave with the matrix-core work).
-  auto softmax_exp = [&](const f32x16 (&s)[BC / 32], uint32_t (&pk)[BC / 32][8]) {
-    float lsum = l;
-#pragma unroll
-    for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(__builtin_fmaf(s[kb][r], c, -m));
-        const float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], c, -m));
-        const uint32_t pp = pack_bf16x2(p0, p1);
-        pk[kb][r >> 1] = pp;
-        lsum = add_bf16x2(pp, lsum);
-      }
-    l = lsum;
-  };
-  auto pv = [&](const bf16* Vt, const uint32_t (&pk)[BC / 32][8]) {
-#pragma unroll
-    for (int ks = 0; ks < BC / 16; ++ks) {
-      const int kb = ks >> 1, half = ks & 1;
-      u32x4 t = {pk[kb][4 * half + 0], pk[kb][4 * half + 1], pk[kb][4 * half + 2],
-                 pk[kb][4 * half + 3]};
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, t);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const int row = db * 32 + li;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            Vt + row * BC + (((4 * kb + 2 * half + h) ^ chunk_swizzle<BC * 2>(row)) * 8));
-        uacc[db] = mfma_bf16_32x32x16(a, pb, uacc[db]);
-      }
-    }
-  };
-
-  // Prologue: K_0, K_1, V_0 into LDS; S_0.
-  load_k(0);
-  load_v(0);
-  store_k(Ksb);
-  store_v(Vtb);
-  if (nt > 1) {
-    load_k(1);
-    store_k(Ksb + C::KS);
-  }
-  __syncthreads();
-  f32x16 s_cur[BC / 32];
-  compute_s(Ksb, s_cur);
-  __syncthreads();  // every wave has read K_0 before step 0 overwrites it
-
-  // Steady state: step j < nt-1, parity P = j % 2.
-  auto step = [&](auto par, int j) {
-    constexpr int P = decltype(par)::value;
-    const bool has2 = j + 2 < nt;
-    if (has2) load_k(j + 2);
-    load_v(j + 1);
-    softmax_max(s_cur, false, 0);
-    // one straight-line block: S_{j+1} on the matrix cores while the
-    // exponentials of S_j run, then U += V_j P_j
-    f32x16 s_next[BC / 32];
-    compute_s(Ksb + (P ^ 1) * C::KS, s_next);
-    uint32_t pk[BC / 32][8];
-    softmax_exp(s_cur, pk);
-    pv(Vtb + P * C::VT, pk);
-    if (has2) store_k(Ksb + P * C::KS);
-    store_v(Vtb + (P ^ 1) * C::VT);
-    __syncthreads();
-#pragma unroll
-    for (int kb = 0; kb < BC / 32; ++kb) s_cur[kb] = s_next[kb];
-  };
-  int j = 0;
-  for (; j + 2 < nt; j += 2) {
-    step(IntC<0>{}, j);
-    step(IntC<1>{}, j + 1);
-  }
-  if (j + 1 < nt) {
-    step(IntC<0>{}, j);
-    ++j;
-  }
-  // Last step (j = nt-1): no next tile; mask keys past n.
-  {
-    uint32_t pk[BC / 32][8];
-    softmax_max(s_cur, (n % BC) != 0, j * BC);
-    softmax_exp(s_cur, pk);
-    pv(Vtb + (j & 1) * C::VT, pk);
-  }
-
-  const float lt = l + __shfl_xor(l, 32);
-  const float inv = 1.0f / lt;
-  if (q < n) {
-    float* Oh = O + hoff;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 v = {uacc[db][4 * g + 0] * inv, uacc[db][4 * g + 1] * inv,
-                   uacc[db][4 * g + 2] * inv, uacc[db][4 * g + 3] * inv};
-        *reinterpret_cast<f32x4*>(Oh + (size_t)q * D + db * 32 + 8 * g + 4 * h) = v;
-      }
-    if (h == 0 && lse != nullptr) lse[(size_t)head * n + q] = (m + __log2f(lt)) * kLn2;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Direct-load variant for gfx950.  K and V tiles travel global -> LDS with
@@ -600,11 +54,22 @@ __global__ __launch_bounds__(NW * 64, (NW >= 8 ? 1 : 8 / NW)) void fwd_fused_bf1
 // k-slots, and K0 of each read follows the key order of the score
 // accumulator, so P^T still feeds the MFMA straight from registers.
 //
-// The schedule is the software-pipelined one above (S_{j+1} on the matrix
-// cores while the softmax of S_j runs; K two tiles ahead, V one tile ahead,
-// two LDS buffers each, one barrier per step).  Rows past n are clamped to
-// row n-1 when loading (finite data; those keys are masked in the last
-// tile), so no load leaves the tensor.
+// The schedule is software-pipelined within each wave:
+//
+//   step j:  issue global -> LDS: K tile j+2, V tile j+1
+//            S_{j+1} = K_{j+1} Q^T        (MFMA, LDS K buffer (j+1)%2)
+//            softmax(S_j) -> P_j          (VALU)
+//            U^T += V_j^T P_j^T           (MFMA, LDS V buffer j%2)
+//            wait for this step's copies; barrier
+//
+// so S_{j+1} runs on the matrix cores while the softmax of S_j runs on the
+// vector ALUs.  K runs two tiles ahead of V, so two buffers of each still
+// need only one barrier per step: the K buffer written in step j held K_j,
+// last read in step j-1, and the V buffer written held V_{j-1}, also last
+// read in step j-1.  Steps are unrolled in pairs so every LDS offset is a
+// compile-time constant; only the last tile takes the key mask.  Rows past
+// n are clamped to row n-1 when loading (finite data; those keys are masked
+// in the last tile), so no load leaves the tensor.
 
 // Arguments of the direct-load forward body.  Queries [bh, nq, d], keys and
 // values [bh, nk, d]; outputs [splits, bh, nq, d] and [splits, bh, nq].
@@ -636,8 +101,7 @@ struct VTileSwizzle {
   __device__ int operator()(int row) const { return vtr_swizzle<ROW_BYTES>(row); }
 };
 
-template <int D, int NW, int BC, bool PIPE = true, int WPS = 2, bool SCHED = false,
-          int STAGES = 2>
+template <int D, int NW, int BC>
 struct DirectCfg {
   static constexpr int NT = NW * 64;
   static constexpr int BR = NW * 32;
@@ -647,38 +111,27 @@ struct DirectCfg {
   static constexpr int WAVE_CHUNKS = CHUNKS / NW;  // per wave, per tensor
   static constexpr int INSTS = WAVE_CHUNKS / 64;   // load instructions per wave per tensor
   static constexpr int TILE = BC * D;              // bf16 elements per tile
-  static constexpr int LDS_ELEMS = 2 * STAGES * TILE;  // K[STAGES], V[STAGES]
+  static constexpr int LDS_ELEMS = 4 * TILE;       // K[2], V[2]
   static constexpr int64_t ONCHIP = (int64_t)BR * D * 2 + 2 * BR + 2 * BC * D + (int64_t)BR * BC;
   static_assert(CHUNKS % (NW * 64) == 0, "tile must split into whole wave loads");
 };
 
-// PIPE selects the cross-tile pipelining of S; WPS is the number of waves
-// per SIMD the register budget is sized for (without PIPE each wave holds
-// one score tile, so more waves fit and the hardware interleaves them).
-// With SKIP (two-stage PIPE only) a wave whose 32 query rows all lie past
-// nq still loads its share of every tile but does no arithmetic; short query
-// blocks (decoding) then cost little beyond the key/value stream.
-// With LIST (two-stage PIPE only) the workgroup visits only the key tiles of
-// its tile list, in ascending order; a workgroup with an empty list writes
-// O = 0 and lse = -inf (no kept key, no softmax).
-// PRIO (two-stage PIPE only) sets wave issue priorities: 1 = the first half
-// of the waves (one per SIMD pair) at priority 1 throughout, so the two
-// waves that share a SIMD drift into opposite phases instead of competing
-// for the same unit; 2 = every wave at priority 1 while it issues its score
-// MFMAs and back to 0 for the rest of the step.
+// With SKIP a wave whose 32 query rows all lie past nq still loads its share
+// of every tile but does no arithmetic; short query blocks (decoding) then
+// cost little beyond the key/value stream.
+// With LIST the workgroup visits only the key tiles of its tile list, in
+// ascending order; a workgroup with an empty list writes O = 0 and
+// lse = -inf (no kept key, no softmax).
 // BUF loads full K/V tiles with buffer instructions (buffer_load ... lds):
 // the tile base goes into a per-tile buffer resource (scalar arithmetic), so
 // no per-lane 64-bit address arithmetic is needed.
-template <int D, int NW, int BC, bool PIPE, int WPS, bool SCHED, int STAGES, bool SKIP = false,
-          bool LIST = false, int PRIO = 0, bool BUF = false>
+template <int D, int NW, int BC, bool SKIP = false, bool LIST = false, bool BUF = false>
 __device__ __forceinline__ void direct_body(const DirectArgs& A) {
-  static_assert(!SKIP || (PIPE && STAGES == 2), "SKIP is built for the two-stage pipeline");
-  static_assert(!LIST || (PIPE && STAGES == 2), "LIST is built for the two-stage pipeline");
-  using C = DirectCfg<D, NW, BC, PIPE, WPS, SCHED, STAGES>;
+  using C = DirectCfg<D, NW, BC>;
   const float c = A.c;
   __shared__ __attribute__((aligned(1024))) bf16 smem[C::LDS_ELEMS];
-  bf16* const Kb = smem;                     // [STAGES][TILE]
-  bf16* const Vb = smem + STAGES * C::TILE;  // [STAGES][TILE]
+  bf16* const Kb = smem;                // [2][TILE]
+  bf16* const Vb = smem + 2 * C::TILE;  // [2][TILE]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -704,9 +157,6 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
   float* const lseh = A.lse ? A.lse + ((size_t)split * A.bh + head) * nq : nullptr;
   const int q = qblk * C::BR + wave * 32 + li;
   const bool active = !SKIP || qblk * C::BR + wave * 32 < nq;  // wave-uniform
-  if constexpr (PRIO == 1) {
-    if (wave < NW / 2) __builtin_amdgcn_s_setprio(1);
-  }
 
   bf16x8 qreg[D / 16];
 #pragma unroll
@@ -877,146 +327,39 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
 
   f32x16 s_cur[BC / 32];
   int j = 0;
-  if constexpr (PIPE && STAGES == 3) {
-    // Three-slot ring: step j issues K_{j+3} and V_{j+2}, so every load has
-    // two steps to land, and the wait before each barrier leaves the
-    // current step's loads in flight (vmcnt = loads issued this step).
-    load_tile(Kh, Kb, 0, kswz);
-    load_tile(Vh, Vb, 0, vswz);
-    if (nt > 1) {
-      load_tile(Kh, Kb + C::TILE, 1, kswz);
-      load_tile(Vh, Vb + C::TILE, 1, vswz);
-    }
-    if (nt > 2) load_tile(Kh, Kb + 2 * C::TILE, 2, kswz);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    compute_s(Kb, s_cur);
-    __syncthreads();  // every wave has read K_0 before step 0 overwrites it
+  // Prologue: K_0, V_0, K_1 into LDS; S_0.
+  load_tile(Kh, Kb, 0, kswz);
+  load_tile(Vh, Vb, 0, vswz);
+  if (nt > 1) load_tile(Kh, Kb + C::TILE, 1, kswz);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (active) compute_s(Kb, s_cur);
+  __syncthreads();  // every wave has read K_0 before step 0 overwrites it
 
-    auto step = [&](auto par, int j) {
-      constexpr int P = decltype(par)::value;  // j % 3
-      constexpr int P1 = (P + 1) % 3, P2 = (P + 2) % 3;
-      const bool k3 = j + 3 < nt, v2 = j + 2 < nt;
-      if (k3) load_tile(Kh, Kb + P * C::TILE, j + 3, kswz);
-      if (v2) load_tile(Vh, Vb + P2 * C::TILE, j + 2, vswz);
+  auto step = [&](auto par, int j) {
+    constexpr int P = decltype(par)::value;
+    if (j + 2 < nt) load_tile(Kh, Kb + P * C::TILE, j + 2, kswz);
+    load_tile(Vh, Vb + (P ^ 1) * C::TILE, j + 1, vswz);
+    f32x16 s_next[BC / 32];
+    if (active) {
       softmax_max(s_cur, false, 0);
-      f32x16 s_next[BC / 32];
-      compute_s(Kb + P1 * C::TILE, s_next);
+      compute_s(Kb + (P ^ 1) * C::TILE, s_next);
       uint32_t pk[BC / 32][8];
       softmax_exp(s_cur, pk);
       pv(Vb + P * C::TILE, pk);
-      // vmcnt(x): expcnt and lgkmcnt fields left at their maxima
-      static_assert(C::INSTS <= 4, "wait counts below assume at most 4 loads per tensor");
-      if (k3 && v2)
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * C::INSTS));
-      else if (k3 || v2)
-        __builtin_amdgcn_s_waitcnt(0x0F70 | C::INSTS);
-      else
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb) s_cur[kb] = s_next[kb];
-    };
-    for (; j + 3 < nt; j += 3) {
-      step(IntC<0>{}, j);
-      step(IntC<1>{}, j + 1);
-      step(IntC<2>{}, j + 2);
     }
-    if (j + 1 < nt) {
-      step(IntC<0>{}, j);
-      ++j;
-    }
-    if (j + 1 < nt) {
-      step(IntC<1>{}, j);
-      ++j;
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-  } else if constexpr (PIPE) {
-    // Prologue: K_0, V_0, K_1 into LDS; S_0.
-    load_tile(Kh, Kb, 0, kswz);
-    load_tile(Vh, Vb, 0, vswz);
-    if (nt > 1) load_tile(Kh, Kb + C::TILE, 1, kswz);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (active) compute_s(Kb, s_cur);
-    __syncthreads();  // every wave has read K_0 before step 0 overwrites it
-
-    auto step = [&](auto par, int j) {
-      constexpr int P = decltype(par)::value;
-      if (j + 2 < nt) load_tile(Kh, Kb + P * C::TILE, j + 2, kswz);
-      load_tile(Vh, Vb + (P ^ 1) * C::TILE, j + 1, vswz);
-      f32x16 s_next[BC / 32];
-      if (active) {
-        softmax_max(s_cur, false, 0);
-        if constexpr (PRIO == 2) __builtin_amdgcn_s_setprio(1);
-        compute_s(Kb + (P ^ 1) * C::TILE, s_next);
-        if constexpr (PRIO == 2) __builtin_amdgcn_s_setprio(0);
-        uint32_t pk[BC / 32][8];
-        softmax_exp(s_cur, pk);
-        pv(Vb + P * C::TILE, pk);
-      }
-      if constexpr (SCHED) {
-        // Interleave: each S_{j+1} MFMA with ~7 softmax instructions and
-        // the K operand read of the MFMA two places later; then each PV
-        // MFMA with the two transposed V reads of the MFMA two places later.
-        constexpr int NS = (D / 16) * (BC / 32);  // S MFMAs
-        constexpr int NPV = (BC / 16) * (D / 32);  // PV MFMAs
-        constexpr int AHEAD = 2;
-        __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // DS read
 #pragma unroll
-        for (int i = 0; i < NS; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          if (i + AHEAD < NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          else if (i + AHEAD - NS < AHEAD) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // VALU
-        }
-#pragma unroll
-        for (int i = 0; i < NPV; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (i + AHEAD < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
-        }
-      }
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb) s_cur[kb] = s_next[kb];
-    };
-    for (; j + 2 < nt; j += 2) {
-      step(IntC<0>{}, j);
-      step(IntC<1>{}, j + 1);
-    }
-    if (j + 1 < nt) {
-      step(IntC<0>{}, j);
-      ++j;
-    }
-  } else {
-    // Tile j+1 is fetched into the other buffer while tile j is used.
-    load_tile(Kh, Kb, 0, kswz);
-    load_tile(Vh, Vb, 0, vswz);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    auto step = [&](auto par, int j) {
-      constexpr int P = decltype(par)::value;
-      load_tile(Kh, Kb + (P ^ 1) * C::TILE, j + 1, kswz);
-      load_tile(Vh, Vb + (P ^ 1) * C::TILE, j + 1, vswz);
-      compute_s(Kb + P * C::TILE, s_cur);
-      softmax_max(s_cur, false, 0);
-      uint32_t pk[BC / 32][8];
-      softmax_exp(s_cur, pk);
-      pv(Vb + P * C::TILE, pk);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    };
-    for (; j + 2 < nt; j += 2) {
-      step(IntC<0>{}, j);
-      step(IntC<1>{}, j + 1);
-    }
-    if (j + 1 < nt) {
-      step(IntC<0>{}, j);
-      ++j;
-    }
-    compute_s(Kb + (j & 1) * C::TILE, s_cur);
+    for (int kb = 0; kb < BC / 32; ++kb) s_cur[kb] = s_next[kb];
+  };
+  for (; j + 2 < nt; j += 2) {
+    step(IntC<0>{}, j);
+    step(IntC<1>{}, j + 1);
+  }
+  if (j + 1 < nt) {
+    step(IntC<0>{}, j);
+    ++j;
   }
   if (active) {
     uint32_t pk[BC / 32][8];
@@ -1025,7 +368,7 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
     else
       softmax_max(s_cur, (n % BC) != 0, j * BC);
     softmax_exp(s_cur, pk);
-    pv(Vb + (j % STAGES) * C::TILE, pk);
+    pv(Vb + (j & 1) * C::TILE, pk);
   }
 
   const float lt = l + __shfl_xor(l, 32);
@@ -1043,13 +386,13 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
   }
 }
 
-template <int D, int NW, int BC, bool PIPE, int WPS, bool SCHED, int STAGES, int PRIO = 0,
-          bool BUF = false>
+// WPS is the number of waves per SIMD the register budget is sized for.
+template <int D, int NW, int BC, int WPS, bool BUF>
 __global__ __launch_bounds__(NW * 64, (WPS * 4 / NW > 0 ? WPS * 4 / NW : 1)) void
 fwd_fused_bf16_direct_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                              const bf16* __restrict__ V, float* __restrict__ O,
                              float* __restrict__ lse, int n, int nqb, int total, float c) {
-  direct_body<D, NW, BC, PIPE, WPS, SCHED, STAGES, false, false, PRIO, BUF>(
+  direct_body<D, NW, BC, false, false, BUF>(
       DirectArgs{Q, K, V, O, lse, n, n, nqb, total, total / nqb, n, c});
 }
 
@@ -1059,7 +402,7 @@ fwd_fused_bf16_direct_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
 template <int D, int NW, int BC>
 __global__ __launch_bounds__(NW * 64, (8 / NW > 0 ? 8 / NW : 1)) void fwd_split_bf16_kernel(
     const DirectArgs A) {
-  direct_body<D, NW, BC, true, 2, false, 2, true, false, 0, true>(A);
+  direct_body<D, NW, BC, true, false, true>(A);
 }
 
 // Block-sparse entry: one workgroup per (head, 128-query block), visiting
@@ -1067,7 +410,7 @@ __global__ __launch_bounds__(NW * 64, (8 / NW > 0 ? 8 / NW : 1)) void fwd_split_
 template <int D, int NW, int BC>
 __global__ __launch_bounds__(NW * 64, (8 / NW > 0 ? 8 / NW : 1)) void fwd_sparse_bf16_kernel(
     const DirectArgs A) {
-  direct_body<D, NW, BC, true, 2, false, 2, false, true, 0, true>(A);
+  direct_body<D, NW, BC, false, true, true>(A);
 }
 
 // Compacts one row of the block mask (mask head, query block) into the
@@ -1127,282 +470,6 @@ __global__ __launch_bounds__(256) void fwd_split_merge_kernel(const float* __res
 }
 
 // ---------------------------------------------------------------------------
-// Wide variant: QB 32-row query blocks per wave (64 rows for QB = 2).  Every
-// K operand read from LDS and every transposed V operand read then feeds QB
-// MFMAs instead of one, which halves LDS instructions per MFMA and doubles
-// the independent matrix-core work each wave has in flight.  The price is
-// register space (Q, U, two score tiles and P for 64 rows), so QB = 2 runs
-// one wave per SIMD with the U accumulators in AGPRs, and hides latency with
-// the same schedule as the direct variant: direct global -> LDS tiles, K two
-// tiles ahead of V in two LDS buffers each, S_{j+1} issued before the
-// softmax of S_j, and operand reads two MFMAs ahead.
-
-template <int D, int QB, int NW, int BC>
-struct WideCfg {
-  static constexpr int NT = NW * 64;
-  static constexpr int BR = NW * QB * 32;
-  static constexpr int KEYS = BC;
-  static constexpr int CPR = D / 8;
-  static constexpr int CHUNKS = BC * CPR;
-  static constexpr int WAVE_CHUNKS = CHUNKS / NW;
-  static constexpr int INSTS = WAVE_CHUNKS / 64;
-  static constexpr int TILE = BC * D;
-  static constexpr int LDS_ELEMS = 4 * TILE;
-  static constexpr int WPS = QB >= 2 ? 1 : 2;  // waves per SIMD the registers allow
-  static constexpr int64_t ONCHIP = (int64_t)BR * D * 2 + 2 * BR + 2 * BC * D + (int64_t)BR * BC;
-  static_assert(CHUNKS % (NW * 64) == 0, "tile must split into whole wave loads");
-};
-
-template <int D, int QB, int NW, int BC>
-__global__ __launch_bounds__(NW * 64, ((QB >= 2 ? 1 : 2) * 4 / NW > 0 ? (QB >= 2 ? 1 : 2) * 4 / NW
-                                                                       : 1)) void
-fwd_fused_bf16_wide_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
-                           const bf16* __restrict__ V, float* __restrict__ O,
-                           float* __restrict__ lse, int n, int nqb, int total, float c) {
-  using C = WideCfg<D, QB, NW, BC>;
-  __shared__ __attribute__((aligned(1024))) bf16 smem[C::LDS_ELEMS];
-  bf16* const Kb = smem;                // [2][TILE]
-  bf16* const Vb = smem + 2 * C::TILE;  // [2][TILE]
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = lane >> 5;
-  const int li = lane & 31;
-
-  const int tile = xcd_remap(blockIdx.x, total);
-  const int head = tile / nqb;
-  const int qblk = tile - head * nqb;
-  const size_t hoff = (size_t)head * (size_t)n * D;
-  const bf16* Qh = Q + hoff;
-  const bf16* Kh = K + hoff;
-  const bf16* Vh = V + hoff;
-  const int qw0 = qblk * C::BR + wave * (QB * 32);
-
-  bf16x8 qreg[QB][D / 16];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int q = qw0 + qb * 32 + li;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-      qreg[qb][kk] = q < n ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)q * D + kk * 16 + 8 * h)
-                           : bf16x8{};
-  }
-
-  f32x16 uacc[D / 32][QB];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) uacc[db][qb] = f32x16{};
-  float m[QB], l[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = -INFINITY;
-    l[qb] = 0.f;
-  }
-  const int nt = (n + BC - 1) / BC;
-
-  auto load_tile = [&](const bf16* src, bf16* dst, int t, auto swz) {
-    const int kbase = t * BC;
-#pragma unroll
-    for (int it = 0; it < C::INSTS; ++it) {
-      const int p0 = wave * C::WAVE_CHUNKS + it * 64;
-      const int p = p0 + lane;
-      const int row = p / C::CPR, phys = p % C::CPR;
-      const int logical = phys ^ swz(row);
-      const int grow = min(kbase + row, n - 1);
-      load_lds_16(src + (size_t)grow * D + logical * 8, dst + p0 * 8);
-    }
-  };
-  auto kswz = [](int row) { return chunk_swizzle<D * 2>(row); };
-  auto vswz = [](int row) { return vtr_swizzle<D * 2>(row); };
-
-  typedef f32x16 STile[BC / 32][QB];
-  auto compute_s = [&](const bf16* Ks, STile& s) {
-#pragma unroll
-    for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb) {
-        const int row = kb * 32 + li;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            Ks + row * D + (((2 * kk + h) ^ chunk_swizzle<D * 2>(row)) * 8));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma_bf16_32x32x16(a, qreg[qb][kk], s[kb][qb]);
-      }
-  };
-  auto softmax_max = [&](STile& s, bool mask, int kbase) {
-    if (mask) {
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kbase + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3) >= n) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) s[kb][qb][r] = -INFINITY;
-          }
-    }
-    bool need_any = false;
-    float alpha[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mc = mx * c;
-      const bool need = mc > m[qb] + kTau;
-      const float mn = need ? mc : m[qb];
-      alpha[qb] = need ? fast_exp2(m[qb] - mn) : 1.0f;
-      m[qb] = mn;
-      l[qb] *= alpha[qb];
-      need_any |= need;
-    }
-    if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) uacc[db][qb] *= alpha[qb];
-    }
-  };
-  typedef uint32_t PTile[BC / 32][QB][8];
-  auto softmax_exp = [&](const STile& s, PTile& pk) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float lsum = l[qb];
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(__builtin_fmaf(s[kb][qb][r], c, -m[qb]));
-          const float p1 = fast_exp2(__builtin_fmaf(s[kb][qb][r + 1], c, -m[qb]));
-          const uint32_t pp = pack_bf16x2(p0, p1);
-          pk[kb][qb][r >> 1] = pp;
-          lsum = add_bf16x2(pp, lsum);
-        }
-      l[qb] = lsum;
-    }
-  };
-  const int G = lane >> 4, sl = lane & 15;
-  const int hh = G >> 1;
-  auto pv = [&](const bf16* Vs, const PTile& pk) {
-#pragma unroll
-    for (int ks = 0; ks < BC / 16; ++ks) {
-      const int kb = ks >> 1, half = ks & 1;
-      bf16x8 pb[QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        u32x4 t = {pk[kb][qb][4 * half + 0], pk[kb][qb][4 * half + 1], pk[kb][qb][4 * half + 2],
-                   pk[kb][qb][4 * half + 3]};
-        pb[qb] = __builtin_bit_cast(bf16x8, t);
-      }
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        u32x2 part[2];
-#pragma unroll
-        for (int piece = 0; piece < 2; ++piece) {
-          const int row = kb * 32 + 16 * half + 8 * piece + 4 * hh + (sl >> 2);
-          const int d0 = db * 32 + 16 * (G & 1) + 4 * (sl & 3);
-          const int phys = (d0 >> 3) ^ vtr_swizzle<D * 2>(row);
-          part[piece] = lds_read_tr16(Vs + row * D + phys * 8 + (d0 & 7));
-        }
-        const bf16x8 a =
-            __builtin_bit_cast(bf16x8, (u32x4{part[0][0], part[0][1], part[1][0], part[1][1]}));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) uacc[db][qb] = mfma_bf16_32x32x16(a, pb[qb], uacc[db][qb]);
-      }
-    }
-  };
-
-  load_tile(Kh, Kb, 0, kswz);
-  load_tile(Vh, Vb, 0, vswz);
-  if (nt > 1) load_tile(Kh, Kb + C::TILE, 1, kswz);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  STile s_cur;
-  compute_s(Kb, s_cur);
-  __syncthreads();
-
-  auto step = [&](auto par, int j) {
-    constexpr int P = decltype(par)::value;
-    if (j + 2 < nt) load_tile(Kh, Kb + P * C::TILE, j + 2, kswz);
-    load_tile(Vh, Vb + (P ^ 1) * C::TILE, j + 1, vswz);
-    softmax_max(s_cur, false, 0);
-    STile s_next;
-    compute_s(Kb + (P ^ 1) * C::TILE, s_next);
-    PTile pk;
-    softmax_exp(s_cur, pk);
-    pv(Vb + P * C::TILE, pk);
-    {
-      constexpr int NK = (D / 16) * (BC / 32);   // K operand reads
-      constexpr int NS = NK * QB;                // S MFMAs
-      constexpr int NV = (BC / 16) * (D / 32);   // V operand read pairs
-      constexpr int NPV = NV * QB;               // PV MFMAs
-      constexpr int VALU_PER = 180 * QB / NS + 1;
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i % QB == QB - 1 && i / QB + 2 < NK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int i = 0; i < NPV; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i % QB == QB - 1 && i / QB + 2 < NV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-#pragma unroll
-    for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s_cur[kb][qb] = s_next[kb][qb];
-  };
-  int j = 0;
-  for (; j + 2 < nt; j += 2) {
-    step(IntC<0>{}, j);
-    step(IntC<1>{}, j + 1);
-  }
-  if (j + 1 < nt) {
-    step(IntC<0>{}, j);
-    ++j;
-  }
-  {
-    PTile pk;
-    softmax_max(s_cur, (n % BC) != 0, j * BC);
-    softmax_exp(s_cur, pk);
-    pv(Vb + (j & 1) * C::TILE, pk);
-  }
-
-  float* Oh = O + hoff;
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = l[qb] + __shfl_xor(l[qb], 32);
-    const float inv = 1.0f / lt;
-    const int q = qw0 + qb * 32 + li;
-    if (q < n) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 v = {uacc[db][qb][4 * g + 0] * inv, uacc[db][qb][4 * g + 1] * inv,
-                     uacc[db][qb][4 * g + 2] * inv, uacc[db][qb][4 * g + 3] * inv};
-          *reinterpret_cast<f32x4*>(Oh + (size_t)q * D + db * 32 + 8 * g + 4 * h) = v;
-        }
-      if (h == 0 && lse != nullptr) lse[(size_t)head * n + q] = (m[qb] + __log2f(lt)) * kLn2;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Ping-pong variant.  The 8 waves form two groups of four (one wave of each
 // group per SIMD) that run one phase apart.  Each tile j has a matrix phase
 // X_j (S_{j+1} = K_{j+1} Q^T and U^T += V_j^T P_j^T, operands from LDS) and a
@@ -1414,6 +481,8 @@ fwd_fused_bf16_wide_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ 
 // softmax arithmetic.  Direct loads of K_{j+2} and V_{j+1} are issued at the
 // start of slot 2j into the buffers K_j and V_{j-1} left (both groups
 // finished X_{j-1} before slot 2j) and waited for at the end of slot 2j+1.
+// A wave issues its matrix phase at priority 1 and its vector phase at 0,
+// so when both waves of a SIMD are ready the MFMAs go first.
 
 template <int D, int QB, int BC>
 struct PingCfg {
@@ -1430,7 +499,7 @@ struct PingCfg {
   static_assert(CHUNKS % (NW * 64) == 0, "tile must split into whole wave loads");
 };
 
-template <int D, int QB, int BC, bool PRIO>
+template <int D, int QB, int BC>
 __global__ __launch_bounds__(512, 1) void fwd_fused_bf16_pingpong_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     float* __restrict__ O, float* __restrict__ lse, int n, int nqb, int total, float c) {
@@ -1613,10 +682,10 @@ __global__ __launch_bounds__(512, 1) void fwd_fused_bf16_pingpong_kernel(
   };
   // Matrix phase X_j and vector phase Y_j.
   auto phase_x = [&](int j) {
-    if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_s_setprio(1);
     if (j + 1 < nt) compute_s(Kb + ((j + 1) & 1) * C::TILE);
     pv(Vb + (j & 1) * C::TILE);
-    if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_setprio(0);
   };
   auto phase_y = [&](int j) {  // softmax of S_{j+1}
     softmax((j + 2 == nt) && (n % BC) != 0, (j + 1) * BC);
@@ -1790,12 +859,11 @@ __global__ __launch_bounds__(256, 1) void fwd_fused_f32_kernel(
 // ---------------------------------------------------------------------------
 // Host launchers.
 //
-// Several kernels and tile shapes are compiled per head dimension; the first
-// entry for a head dimension is its default.  The environment variable
-// ATTN_FWD_TILE selects another compiled entry by name, for tile sweeps:
-// "QBxNWxBC" (e.g. "1x8x64") names the basic kernel with QB 32-row query
-// blocks per wave, NW waves and BC-key tiles; "pNWxBC" (e.g. "p8x64") names
-// the software-pipelined kernel.  An unknown name falls back to the default.
+// The registry lists the compiled tile shapes per head dimension; the first
+// entry for a head dimension is the one attn_fwd uses.  The others are the
+// query-block x key-tile shapes of the d = 128 tile sweep (B_r = 32 x waves
+// query rows, B_c keys per tile), reachable only through the explicitly
+// named entry point attn_fwd_tile.
 
 namespace {
 
@@ -1809,96 +877,48 @@ struct FusedEntry {
   FusedKernel kernel;
 };
 
-template <int D, int QB, int NW, int BC>
-FusedEntry basic(const char* name) {
-  using C = FusedCfg<D, QB, NW, BC>;
-  return FusedEntry{name, D, NW, FusedTileInfo{C::BR, C::KEYS, C::ONCHIP},
-                    &fwd_fused_bf16_kernel<D, QB, NW, BC>};
-}
-
-template <int D, int NW, int BC, bool PIPE = true, int WPS = 2, bool SCHED = false,
-          int STAGES = 2, int PRIO = 0, bool BUF = false>
+template <int D, int NW, int BC, int WPS = 2, bool BUF = false>
 FusedEntry direct(const char* name) {
-  using C = DirectCfg<D, NW, BC, PIPE, WPS, SCHED, STAGES>;
-  return FusedEntry{
-      name, D, NW, FusedTileInfo{C::BR, C::KEYS, C::ONCHIP},
-      &fwd_fused_bf16_direct_kernel<D, NW, BC, PIPE, WPS, SCHED, STAGES, PRIO, BUF>};
-}
-
-template <int D, int QB, int NW, int BC>
-FusedEntry wide(const char* name) {
-  using C = WideCfg<D, QB, NW, BC>;
+  using C = DirectCfg<D, NW, BC>;
   return FusedEntry{name, D, NW, FusedTileInfo{C::BR, C::KEYS, C::ONCHIP},
-                    &fwd_fused_bf16_wide_kernel<D, QB, NW, BC>};
+                    &fwd_fused_bf16_direct_kernel<D, NW, BC, WPS, BUF>};
 }
 
-template <int D, int QB, int BC, bool PRIO = false>
+template <int D, int QB, int BC>
 FusedEntry pingpong(const char* name) {
   using C = PingCfg<D, QB, BC>;
   return FusedEntry{name, D, C::NW, FusedTileInfo{C::BR, C::KEYS, C::ONCHIP},
-                    &fwd_fused_bf16_pingpong_kernel<D, QB, BC, PRIO>};
-}
-
-template <int D, int NW, int BC>
-FusedEntry piped(const char* name) {
-  using C = PipeCfg<D, NW, BC>;
-  return FusedEntry{name, D, NW, FusedTileInfo{C::BR, C::KEYS, C::ONCHIP},
-                    &fwd_fused_bf16_pipe_kernel<D, NW, BC>};
+                    &fwd_fused_bf16_pingpong_kernel<D, QB, BC>};
 }
 
 const FusedEntry* registry(int& count) {
   static const FusedEntry table[] = {
-      // head dimension 64 (first entry is the default)
-      pingpong<64, 2, 64, true>("g2x64p"),
-      pingpong<64, 2, 64>("g2x64"),
-      pingpong<64, 1, 64>("g1x64"),
-      direct<64, 8, 64, true, 2, false, 3>("t8x64"),
-      direct<64, 8, 64, true, 2, false, 2, 0, true>("d8x64"),
-      basic<64, 2, 8, 32>("2x8x32"),
-      // head dimension 128
-      direct<128, 8, 64, true, 2, false, 2, 0, true>("d8x64"),
-      direct<128, 8, 64>("d8x64g"),  // 64-bit per-lane addresses instead of buffer loads
-      direct<128, 8, 64, true, 2, false, 2, 1>("d8x64q1"),
-      direct<128, 8, 64, true, 2, false, 2, 2>("d8x64q2"),
-      // query-block x key-tile sweep (B_r = 32 x waves, B_c = keys per tile;
-      // 128-key tiles spill registers at d = 128 and are left out)
+      // head dimension 64: two 4-wave groups offset by half a tile
+      pingpong<64, 2, 64>("g2x64p"),
+      // head dimension 128: 8 waves, 64-key tiles, buffer-resource copies
+      direct<128, 8, 64, 2, true>("d8x64"),
+      // d = 128 tile sweep (128-key tiles spill registers at d = 128)
       direct<128, 2, 32>("r64c32"),
       direct<128, 2, 64>("r64c64"),
       direct<128, 4, 32>("r128c32"),
-      direct<128, 4, 64, true, 1>("r128c64"),
+      direct<128, 4, 64, 1>("r128c64"),
       direct<128, 8, 32>("r256c32"),
       direct<128, 8, 64>("r256c64"),
-      pingpong<128, 1, 64, true>("g1x64p"),
-      pingpong<128, 1, 64>("g1x64"),
-      wide<128, 1, 8, 64>("w1x8x64"),
-      direct<128, 8, 64, true, 2, true>("s8x64"),
-      direct<128, 8, 32, false, 3>("n8x32w3"),
-      basic<128, 1, 8, 64>("1x8x64"),
-      // head dimension 256
-      direct<256, 4, 32, true, 1, false, 2, 0, true>("d4x32b"),
-      direct<256, 4, 32, true, 1>("d4x32"),
-      direct<256, 2, 32, true, 1, false, 2, 0, true>("d2x32b"),
-      basic<256, 1, 4, 32>("1x4x32"),
+      // head dimension 256: 4 waves (one per SIMD), 32-key tiles
+      direct<256, 4, 32, 1, true>("d4x32b"),
   };
   count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
 }
 
-const FusedEntry* pick(int64_t d) {
+// The default entry for head dimension d, or, with a name, the entry of
+// that name for d; nullptr if there is none.
+const FusedEntry* pick(int64_t d, const char* name = nullptr) {
   int count = 0;
   const FusedEntry* t = registry(count);
-  const FusedEntry* def = nullptr;
   for (int i = 0; i < count; ++i)
-    if (t[i].d == d) {
-      def = &t[i];
-      break;
-    }
-  if (!def) return nullptr;
-  const char* env = getenv("ATTN_FWD_TILE");
-  if (env)
-    for (int i = 0; i < count; ++i)
-      if (t[i].d == d && strcmp(t[i].name, env) == 0) return &t[i];
-  return def;
+    if (t[i].d == d && (name == nullptr || std::strcmp(t[i].name, name) == 0)) return &t[i];
+  return nullptr;
 }
 
 template <int D>
@@ -2047,9 +1067,35 @@ hipError_t launch_fwd_sparse_bf16(const void* Q, const void* K, const void* V, f
 bool fused_bf16_supported(int64_t d) { return pick(d) != nullptr; }
 bool fused_f32_supported(int64_t d) { return d == 64 || d == 128; }
 
-FusedTileInfo fused_bf16_tile_info(int64_t d) {
-  const FusedEntry* e = pick(d);
+FusedTileInfo fused_bf16_tile_info(int64_t d, const char* tile) {
+  const FusedEntry* e = pick(d, tile);
   return e ? e->info : FusedTileInfo{0, 0, 0};
+}
+
+const char* fused_bf16_tile_names(int64_t d) {
+  // Space-separated names per head dimension, built once (function-local
+  // static: thread-safe initialisation).
+  struct Names {
+    char s[3][160] = {};
+    Names() {
+      int count = 0;
+      const FusedEntry* t = registry(count);
+      const int dims[3] = {64, 128, 256};
+      for (int k = 0; k < 3; ++k) {
+        size_t len = 0;
+        for (int i = 0; i < count; ++i) {
+          if (t[i].d != dims[k]) continue;
+          const size_t w = std::strlen(t[i].name);
+          if (len + w + 2 > sizeof(s[k])) break;
+          if (len) s[k][len++] = ' ';
+          std::memcpy(s[k] + len, t[i].name, w);
+          len += w;
+        }
+      }
+    }
+  };
+  static const Names names;
+  return d == 64 ? names.s[0] : d == 128 ? names.s[1] : d == 256 ? names.s[2] : "";
 }
 
 FusedTileInfo fused_f32_tile_info(int64_t d) {
@@ -2062,8 +1108,8 @@ FusedTileInfo fused_f32_tile_info(int64_t d) {
 
 hipError_t launch_fwd_fused_bf16(const void* Q, const void* K, const void* V, float* O,
                                  float* lse, int64_t bh, int64_t n, int64_t d, float scale,
-                                 hipStream_t stream) {
-  const FusedEntry* e = pick(d);
+                                 const char* tile, hipStream_t stream) {
+  const FusedEntry* e = pick(d, tile);
   if (!e) return hipErrorInvalidValue;
   const int nqb = (int)((n + e->info.block_rows - 1) / e->info.block_rows);
   const int total = (int)(bh * nqb);

@@ -16,14 +16,18 @@ struct FusedTileInfo {
   int64_t onchip;    // elements held on chip per workgroup (M)
 };
 
+// bf16 tile shapes: `tile` names a compiled shape for d, nullptr the
+// default one.  fused_bf16_tile_names(d) lists the names (default first,
+// space separated; "" for an unsupported d).
 bool fused_bf16_supported(int64_t d);
 bool fused_f32_supported(int64_t d);
-FusedTileInfo fused_bf16_tile_info(int64_t d);
+FusedTileInfo fused_bf16_tile_info(int64_t d, const char* tile = nullptr);
+const char* fused_bf16_tile_names(int64_t d);
 FusedTileInfo fused_f32_tile_info(int64_t d);
 
 hipError_t launch_fwd_fused_bf16(const void* Q, const void* K, const void* V, float* O,
                                  float* lse, int64_t bh, int64_t n, int64_t d, float scale,
-                                 hipStream_t stream);
+                                 const char* tile, hipStream_t stream);
 // Fused forward with 32-row query blocks and 32-key tiles, four waves each
 // owning a quarter of d (fwd_budget.hip): the fused schedule held to a
 // budget below d^2.
@@ -51,7 +55,6 @@ hipError_t launch_fwd_splitk_bf16(const void* Q, const void* K, const void* V, f
                                   float* lse, int64_t bh, int64_t nq, int64_t nk, int64_t d,
                                   float scale, int64_t splits, void* workspace,
                                   hipStream_t stream);
-
 // Block-sparse forward: a byte mask [mask_heads][nb][nb] over square blocks
 // of kSparseBlock queries x kSparseBlock keys (nb = ceil(n / kSparseBlock));
 // mask_heads is 1 (shared) or bh.  The workspace holds per-row tile counts

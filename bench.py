@@ -487,7 +487,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.n,
                    "head_dim": w.d, "q_scale": w.q_mult, "query_block": br,
-                   "onchip_elems": m_elems, "tile": os.environ.get("ATTN_FWD_TILE", "default")},
+                   "onchip_elems": m_elems, "tile": at.fwd_tiles(w.d)[0]},
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "hbm_gbps": round(compulsory / (wall_ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(compulsory / (wall_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
@@ -535,19 +535,18 @@ def tile_sweep(args, at, torch, dev):
     o = torch.empty((w.bh, w.n, w.d), dtype=torch.float32, device=dev)
     lse = torch.empty((w.bh, w.n), dtype=torch.float32, device=dev)
     for name in SWEEP_TILES:
-        os.environ["ATTN_FWD_TILE"] = name
-        br, m_elems = at.fwd_query_block(w.d), at.fwd_onchip_elems(w.d)
+        info = at.fwd_tile_info(name, w.d)
+        br, m_elems = info["block_rows"], info["onchip_elems"]
         print(f"[bench] tile {name}", file=sys.stderr, flush=True)
-        ms, _, _ = time_launches(lambda: at.attn_fwd(q, k, v, w.scale, out=o, lse=lse),
+        ms, _, _ = time_launches(lambda: at.attn_fwd_tile(name, q, k, v, w.scale, out=o, lse=lse),
                                  args.steps, args.warmup)
         # per launch, in bytes (bf16 K/V stream + Q once); elements x 2
         sched = w.bh * (2 * w.n * w.n * w.d / br + w.n * w.d) * 2
         model = w.bh * (w.n * w.n * w.d * w.d / m_elems + w.n * w.d) * 2
-        print(json.dumps({"tile": name, "block_rows": br, "key_tile": int(name.split("c")[1]),
+        print(json.dumps({"tile": name, "block_rows": br, "key_tile": info["key_tile"],
                           "onchip_elems": m_elems, "ms": round(ms, 4),
                           "tflops": round(w.fwd_flops / (ms * 1e-3) / 1e12, 1),
                           "sched_read_bytes": sched, "page_model_bytes": model}), flush=True)
-    os.environ.pop("ATTN_FWD_TILE", None)
 
 
 SC_SWEEP_B = (128, 64)

@@ -6,8 +6,9 @@
  * for a batch of independent heads, as defined on the page "The I/O
  * Complexity of Attention, or How Optimal is Flash Attention?" (exposition),
  * section "Attention as a mathematical problem": the score of query i and key
- * j is scale * <q_i, k_j>, softmax turns each row of scores into weights, and
- * the output row is the weighted average of the value rows.  That page omits
+ * j is scale * <q_i, k_j>, each row of scores is normalised by a row-wise
+ * softmax into weights summing to one, and output row i is the average of
+ * the value rows under row i's weights.  That page omits
  * the 1/sqrt(d) factor; here it is the explicit `scale` argument.
  *
  * Conventions shared by every entry point
@@ -100,6 +101,34 @@ attn_status attn_fwd(const void* Q, const void* K, const void* V, float* O,
  */
 int64_t attn_fwd_onchip_elems(int64_t d, attn_dtype dtype);
 int64_t attn_fwd_query_block(int64_t d, attn_dtype dtype);
+
+/*
+ * attn_fwd_tile -- attn_fwd with the bf16 kernel's tile shape named
+ * explicitly, for tile sweeps and tests of every compiled shape.  The
+ * fast-memory size M of the exposition's section "Large caches: where
+ * FlashAttention's I/O comes from" is set by the query-block rows B and
+ * the key tile; this call lets a caller measure the schedule's traffic at
+ * each compiled (B, key tile) pair.  attn_fwd itself always uses the first
+ * (default) shape for d and reads no environment.
+ *
+ *   attn_fwd_tiles(d) : space-separated names of the shapes compiled for
+ *             head dimension d, the default first; "" if none (static
+ *             storage).
+ *   attn_fwd_tile_info : query-block rows, keys per tile and on-chip
+ *             elements (as attn_fwd_onchip_elems) of shape `tile` at d;
+ *             any output pointer may be NULL.  ATTN_ERR_UNSUPPORTED for an
+ *             unknown (tile, d), ATTN_ERR_INVALID_ARG for a NULL name.
+ *   attn_fwd_tile : same arguments, result and errors as attn_fwd (bf16
+ *             only), computed with shape `tile`; ATTN_ERR_UNSUPPORTED for
+ *             an unknown (tile, d).
+ */
+const char* attn_fwd_tiles(int64_t d);
+attn_status attn_fwd_tile_info(const char* tile, int64_t d, int64_t* block_rows,
+                               int64_t* key_tile, int64_t* onchip_elems);
+attn_status attn_fwd_tile(const char* tile, const void* Q, const void* K,
+                          const void* V, float* O, float* lse, int64_t bh,
+                          int64_t n, int64_t d, float scale, attn_dtype dtype,
+                          void* stream);
 
 /*
  * attn_fwd_budget -- the fused streaming forward held to an on-chip budget

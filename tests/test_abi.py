@@ -50,7 +50,43 @@ def test_status_strings_and_version(lib):
     assert re.fullmatch(r"\d+\.\d+\.\d+", lib.attn_version().decode())
 
 
+def test_tile_listing(lib):
+    """attn_fwd_tiles lists the compiled shapes, the default first, and
+    attn_fwd_tile_info of the default agrees with attn_fwd's query block and
+    on-chip count; unknown names are refused."""
+    expect = {64: ["g2x64p"],
+              128: ["d8x64", "r64c32", "r64c64", "r128c32", "r128c64", "r256c32", "r256c64"],
+              256: ["d4x32b"]}
+    for d, names in expect.items():
+        assert binding.fwd_tiles(d) == names
+        info = binding.fwd_tile_info(names[0], d)
+        assert info["block_rows"] == lib.attn_fwd_query_block(d, BF16)
+        assert info["onchip_elems"] == lib.attn_fwd_onchip_elems(d, BF16)
+    for name in expect[128][1:]:  # sweep shapes: B_r = 32 x waves, B_c keys per tile
+        info = binding.fwd_tile_info(name, 128)
+        br, bc = (int(x) for x in name[1:].split("c"))
+        assert (info["block_rows"], info["key_tile"]) == (br, bc)
+    assert binding.fwd_tiles(96) == []
+    z = ctypes.c_int64(0)
+    assert lib.attn_fwd_tile_info(b"nope", 128, ctypes.byref(z), None, None) == UNSUPPORTED
+    assert lib.attn_fwd_tile_info(b"d8x64", 64, None, None, None) == UNSUPPORTED
+    assert lib.attn_fwd_tile_info(None, 128, None, None, None) == INVALID
+
+
 FAKE = 0x1000  # aligned, never dereferenced: every call below fails validation first
+
+
+def test_fwd_tile_validation(lib):
+    def call(tile=b"r128c32", q=FAKE, o=FAKE, n=128, d=128, dtype=BF16, scale=0.125):
+        return lib.attn_fwd_tile(tile, q, FAKE, FAKE, o, None, 1, n, d, scale, dtype, None)
+    assert call(tile=None) == INVALID
+    assert call(tile=b"nope") == UNSUPPORTED
+    assert call(d=64) == UNSUPPORTED
+    assert call(dtype=F32) == UNSUPPORTED
+    assert call(q=None) == INVALID
+    assert call(o=FAKE + 8) == INVALID
+    assert call(scale=0.0) == INVALID
+    assert call(q=None, o=None, n=0) == OK
 
 
 def fwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, bh=1, n=128, d=64, scale=0.125,

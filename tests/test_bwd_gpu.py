@@ -87,18 +87,3 @@ def test_bwd_rejects_unsupported_head_dim():
     o, lse = at.attn_fwd(q, k, v)
     with pytest.raises(at.AttnError):
         at.attn_bwd(q, k, v, o, do, lse)
-
-
-@pytest.mark.parametrize("variant,waves", [("v3", "8"), ("v3", "4"), ("v3o", "8"), ("v3o", "4"),
-                                           ("v2", "8"), ("v2", "4")])
-def test_bwd_every_kernel_variant(variant, waves, monkeypatch):
-    monkeypatch.setenv("ATTN_BWD_VARIANT", variant)
-    if waves:
-        monkeypatch.setenv("ATTN_BWD_WAVES", waves)
-    say(f"attn_bwd variant {variant} waves {waves}")
-    for (bh, n, d, seed) in ((2, 300, 128, 91), (1, 257, 64, 92)):
-        (qc, kc, vc, doc), _, (dq, dk, dv), scale = _grads(bh, n, d, seed, 1.0)
-        rq, rk, rv, _, _ = oracle.attn_bwd(f64(qc), f64(kc), f64(vc), f64(doc), scale)
-        check(f64(dq), rq, TOL["bf16"], f"dQ {variant} {bh}x{n}x{d}")
-        check(f64(dk), rk, TOL["bf16"], f"dK {variant} {bh}x{n}x{d}")
-        check(f64(dv), rv, TOL["bf16"], f"dV {variant} {bh}x{n}x{d}")
