@@ -40,6 +40,8 @@ SIGNATURES = {
     "attn_fwd_splitk_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "attn_fwd_splitk": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _int, _i64,
                                _vp, _sz, _vp]),
+    "attn_fwd_splitk_noalloc": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _int,
+                                       _i64, _vp]),
     "attn_fwd_blocksparse_workspace_size": (_sz, [_i64, _i64, _i64]),
     "attn_fwd_blocksparse": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _int, _vp,
                                     _i64, _vp, _sz, _vp]),
@@ -319,6 +321,34 @@ def attn_fwd_splitk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, splits: i
                                _dtype_code(q), int(splits), workspace.data_ptr(),
                                workspace.numel() * workspace.element_size(), _stream(q, stream))
     _check("attn_fwd_splitk", rc)
+    return out, lse
+
+
+SPLITK_NOALLOC_SCRATCH_BYTES = 16 << 20  # ATTN_SPLITK_NOALLOC_SCRATCH_BYTES
+
+
+def attn_fwd_splitk_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                            out: torch.Tensor, lse: torch.Tensor | None = None, splits: int = 0,
+                            scale: float | None = None, stream=None):
+    """attn_fwd_splitk with the chunk partials in the library's own device
+    array: neither the library nor this wrapper allocates (the caller passes
+    O, and lse or None).  Returns (out, lse)."""
+    _check_inputs(q, k, v)
+    if k.shape != v.shape or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2] \
+            or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("Q [bh,nq,d], K and V [bh,nk,d] must agree in bh, d and dtype")
+    bh, nq, d = q.shape
+    nk = k.shape[1]
+    if out is None:
+        raise ValueError("out is required: this entry point allocates nothing")
+    _check_buffer(out, "out", (bh, nq, d), torch.float32, q.device)
+    if lse is not None:
+        _check_buffer(lse, "lse", (bh, nq), torch.float32, q.device)
+    scale = default_scale(d) if scale is None else float(scale)
+    rc = lib().attn_fwd_splitk_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                       lse.data_ptr() if lse is not None else None, bh, nq, nk, d,
+                                       scale, _dtype_code(q), int(splits), _stream(q, stream))
+    _check("attn_fwd_splitk_noalloc", rc)
     return out, lse
 
 

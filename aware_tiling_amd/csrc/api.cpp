@@ -13,6 +13,9 @@
 
 namespace {
 
+static_assert(ATTN_SPLITK_NOALLOC_SCRATCH_BYTES == at::kSplitkScratchBytes,
+              "header and library agree on the no-allocation scratch size");
+
 thread_local char g_last_hip_error[256] = "";
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -186,6 +189,28 @@ attn_status attn_fwd_splitk(const void* Q, const void* K, const void* V, float* 
     return ATTN_ERR_WORKSPACE;
   return launch_status(at::launch_fwd_splitk_bf16(Q, K, V, O, lse, bh, nq, nk, d, scale, req,
                                                   workspace, static_cast<hipStream_t>(stream)));
+}
+
+attn_status attn_fwd_splitk_noalloc(const void* Q, const void* K, const void* V, float* O,
+                                    float* lse, int64_t bh, int64_t nq, int64_t nk, int64_t d,
+                                    float scale, attn_dtype dtype, int64_t splits, void* stream) {
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (!shape_ok(bh, nq, d) || !shape_ok(bh, nk, d) || !scale_ok(scale))
+    return ATTN_ERR_INVALID_ARG;
+  if (!at::splitk_supported(d)) return ATTN_ERR_UNSUPPORTED;
+  if (splits < 0 || splits > 256) return ATTN_ERR_INVALID_ARG;
+  if (bh * nq == 0) return ATTN_OK;
+  if (nk == 0) return ATTN_ERR_INVALID_ARG;
+  const int64_t req = splitk_count(bh, nq, nk, splits);
+  const int64_t eff = at::splitk_effective_splits(nk, req);
+  if (eff * bh * ((nq + 127) / 128) >= (int64_t(1) << 31)) return ATTN_ERR_INVALID_ARG;
+  if (!Q || !K || !V || !O) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return ATTN_ERR_INVALID_ARG;
+  if (lse && !aligned16(lse)) return ATTN_ERR_INVALID_ARG;
+  if (at::splitk_workspace_bytes(bh, nq, nk, d, req) > at::kSplitkScratchBytes)
+    return ATTN_ERR_WORKSPACE;
+  return launch_status(at::launch_fwd_splitk_noalloc_bf16(Q, K, V, O, lse, bh, nq, nk, d, scale,
+                                                          req, static_cast<hipStream_t>(stream)));
 }
 
 size_t attn_fwd_blocksparse_workspace_size(int64_t bh, int64_t n, int64_t mask_heads) {

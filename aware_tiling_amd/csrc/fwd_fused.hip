@@ -31,6 +31,7 @@
 // MFMA multiplies), so the normalisation matches the weights used.
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 
 #include "device_common.h"
 #include "launch.h"
@@ -1020,6 +1021,52 @@ hipError_t launch_fwd_splitk_bf16(const void* Q, const void* K, const void* V, f
     case 128: return launch_split<128>(Q, K, V, O, lse, bh, nq, nk, c, splits, workspace, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Scratch of the allocation-free key-split forward: the per-chunk partial
+// O and lse live in this file-scope device array (one copy per GPU the
+// library is loaded on, kept until the process ends) instead of a caller's
+// workspace.  In host code `scratch` names a host-side stand-in, never the
+// device memory: its device address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and only that address is
+// passed to kernels.
+static __device__ __align__(256) unsigned char scratch[kSplitkScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device.
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_fwd_splitk_noalloc_bf16(const void* Q, const void* K, const void* V, float* O,
+                                          float* lse, int64_t bh, int64_t nq, int64_t nk,
+                                          int64_t d, float scale, int64_t splits,
+                                          hipStream_t stream) {
+  void* ws = nullptr;
+  if (splitk_workspace_bytes(bh, nq, nk, d, splits) > 0) {
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return e;
+  }
+  return launch_fwd_splitk_bf16(Q, K, V, O, lse, bh, nq, nk, d, scale, splits, ws, stream);
 }
 
 size_t sparse_workspace_bytes(int64_t n, int64_t mask_heads) {

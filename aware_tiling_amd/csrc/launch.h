@@ -55,6 +55,15 @@ hipError_t launch_fwd_splitk_bf16(const void* Q, const void* K, const void* V, f
                                   float* lse, int64_t bh, int64_t nq, int64_t nk, int64_t d,
                                   float scale, int64_t splits, void* workspace,
                                   hipStream_t stream);
+// The same with the partials in the library's own device array of
+// kSplitkScratchBytes (no workspace, no allocation); the caller checks
+// splitk_workspace_bytes(...) <= kSplitkScratchBytes.
+constexpr size_t kSplitkScratchBytes = size_t(16) << 20;
+hipError_t launch_fwd_splitk_noalloc_bf16(const void* Q, const void* K, const void* V, float* O,
+                                          float* lse, int64_t bh, int64_t nq, int64_t nk,
+                                          int64_t d, float scale, int64_t splits,
+                                          hipStream_t stream);
+
 // Block-sparse forward: a byte mask [mask_heads][nb][nb] over square blocks
 // of kSparseBlock queries x kSparseBlock keys (nb = ceil(n / kSparseBlock));
 // mask_heads is 1 (shared) or bh.  The workspace holds per-row tile counts

@@ -199,6 +199,35 @@ attn_status attn_fwd_splitk(const void* Q, const void* K, const void* V,
                             size_t workspace_bytes, void* stream);
 
 /*
+ * attn_fwd_splitk_noalloc -- attn_fwd_splitk for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * (decoding) loops, harnesses that forbid allocation.  Same arguments,
+ * result and errors as attn_fwd_splitk, without the workspace: the
+ * per-chunk partial outputs live in a device array inside the library of
+ * ATTN_SPLITK_NOALLOC_SCRATCH_BYTES bytes (16 MiB), one per GPU, held from
+ * the library's load until the process ends.  The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine); its first call on
+ * a device looks up that device's array address once.
+ *
+ *   Requests whose partials need more than the array holds, i.e.
+ *   attn_fwd_splitk_workspace_size(bh, nq, nk, d, splits) >
+ *   ATTN_SPLITK_NOALLOC_SCRATCH_BYTES, return ATTN_ERR_WORKSPACE (pass a
+ *   smaller `splits`, or use attn_fwd_splitk).  With one chunk the array
+ *   is not used.
+ *   Every call on one GPU shares that GPU's array: calls that overlap in
+ *   time on one GPU (different streams, or host threads without stream
+ *   order between them) race and give undefined results.  Calls ordered on
+ *   one stream are safe; the array's contents between calls are
+ *   unspecified and nothing in it needs clearing.
+ */
+#define ATTN_SPLITK_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+attn_status attn_fwd_splitk_noalloc(const void* Q, const void* K, const void* V,
+                                    float* O, float* lse, int64_t bh,
+                                    int64_t nq, int64_t nk, int64_t d,
+                                    float scale, attn_dtype dtype,
+                                    int64_t splits, void* stream);
+
+/*
  * attn_fwd_blocksparse -- fused forward restricted to the query/key blocks a
  * block mask keeps (block-sparse attention).
  *

@@ -76,6 +76,24 @@ def test_tile_listing(lib):
 FAKE = 0x1000  # aligned, never dereferenced: every call below fails validation first
 
 
+def test_splitk_noalloc_validation(lib):
+    """The allocation-free key-split call refuses, before any HIP call, a
+    request whose partials exceed its device array, as well as the usual
+    bad arguments."""
+    def call(q=FAKE, bh=1, nq=4, nk=1000, d=128, splits=0, scale=0.125, dtype=BF16):
+        return lib.attn_fwd_splitk_noalloc(q, FAKE, FAKE, FAKE, None, bh, nq, nk, d, scale,
+                                           dtype, splits, None)
+    assert call(bh=64, nq=200, nk=4096, splits=16) == WORKSPACE  # 64 MiB of partials
+    assert lib.attn_fwd_splitk_workspace_size(64, 200, 4096, 128, 16) > \
+        binding.SPLITK_NOALLOC_SCRATCH_BYTES
+    assert call(q=None) == INVALID
+    assert call(d=256) == UNSUPPORTED
+    assert call(dtype=F32) == UNSUPPORTED
+    assert call(splits=300) == INVALID
+    assert call(nk=0) == INVALID
+    assert call(q=None, nq=0) == OK
+
+
 def test_fwd_tile_validation(lib):
     def call(tile=b"r128c32", q=FAKE, o=FAKE, n=128, d=128, dtype=BF16, scale=0.125):
         return lib.attn_fwd_tile(tile, q, FAKE, FAKE, o, None, 1, n, d, scale, dtype, None)
