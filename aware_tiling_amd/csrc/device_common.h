@@ -65,6 +65,19 @@ __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max(x, x of lane l ^ 32) in every lane, with one v_permlane32_swap_b32
+// (which exchanges lanes 32..63 of its first operand with lanes 0..31 of
+// its second) instead of a ds_bpermute round trip through the LDS unit.
+// With both operands holding x, lane i < 32 ends with {x[i], x[i + 32]}
+// and lane i >= 32 with {x[i - 32], x[i]}, so one fmaxf finishes the pair.
+// Issued from inline assembly (two wait states before and after it) since
+// the compiler builtin returns the same register for both results here.
+__device__ __forceinline__ float pair_max_xor32(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
+
 // XOR swizzle of the 16-byte chunk index inside an LDS row, chosen so that
 // when consecutive rows are read at the same logical chunk (one row per
 // lane), the lanes of one ds_read_b128 phase land on distinct banks, whether

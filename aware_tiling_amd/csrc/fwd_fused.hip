@@ -271,14 +271,15 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
     for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = pair_max_xor32(mx);
     const float mc = mx * c;
     const bool need = mc > m + kTau;
-    const float mn = need ? mc : m;
-    const float alpha = need ? fast_exp2(m - mn) : 1.0f;
-    m = mn;
-    l *= alpha;
+    // rare: some lane's maximum moved; lanes that keep m get alpha = 1
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float mn = need ? mc : m;
+      const float alpha = fast_exp2(m - mn);
+      m = mn;
+      l *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) uacc[db] *= alpha;
     }
@@ -643,7 +644,7 @@ __global__ __launch_bounds__(512, 1) void fwd_fused_bf16_pingpong_kernel(
           }
     }
     bool need_any = false;
-    float alpha[QB];
+    float mn[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = -INFINITY;
@@ -651,23 +652,26 @@ __global__ __launch_bounds__(512, 1) void fwd_fused_bf16_pingpong_kernel(
       for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = pair_max_xor32(mx);
       const float mc = mx * c;
       const bool need = mc > m[qb] + kTau;
-      const float mn = need ? mc : m[qb];
-      alpha[qb] = need ? fast_exp2(m[qb] - mn) : 1.0f;
-      m[qb] = mn;
+      mn[qb] = need ? mc : m[qb];
       need_any |= need;
     }
+    // rare: some lane's maximum moved; lanes that keep m get alpha = 1
     if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int qb = 0; qb < QB; ++qb) {
+        const float alpha = fast_exp2(m[qb] - mn[qb]);
+        m[qb] = mn[qb];
+        l[qb] *= alpha;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) uacc[db][qb] *= alpha[qb];
+        for (int db = 0; db < D / 32; ++db) uacc[db][qb] *= alpha;
+      }
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float lsum = l[qb] * alpha[qb];
+      float lsum = l[qb];
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
