@@ -35,6 +35,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace at {
 
@@ -123,10 +124,7 @@ struct DirectCfg {
 // With LIST the workgroup visits only the key tiles of its tile list, in
 // ascending order; a workgroup with an empty list writes O = 0 and
 // lse = -inf (no kept key, no softmax).
-// BUF loads full K/V tiles with buffer instructions (buffer_load ... lds):
-// the tile base goes into a per-tile buffer resource (scalar arithmetic), so
-// no per-lane 64-bit address arithmetic is needed.
-template <int D, int NW, int BC, bool SKIP = false, bool LIST = false, bool BUF = false>
+template <int D, int NW, int BC, bool SKIP = false, bool LIST = false>
 __device__ __forceinline__ void direct_body(const DirectArgs& A) {
   using C = DirectCfg<D, NW, BC>;
   const float c = A.c;
@@ -196,11 +194,16 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
       return t * BC;
   };
 
-  // Issue the direct loads of tile t of `src` into the LDS tile `dst`.  Lane
+  // Issue the copies of tile t of K or V into the LDS tile `dst`.  Lane
   // chunk p of this wave is LDS chunk (row, phys); it fetches logical chunk
-  // phys ^ swizzle(row) of that row.  Full tiles use a wave-uniform tile base
-  // plus a per-lane byte offset computed once; only a partial last tile
-  // clamps its rows to n-1.
+  // phys ^ swizzle(row) of that row, at a per-lane byte offset computed once.
+  // One buffer resource spans this workgroup's keys of the head and the tile
+  // start goes in the scalar offset, so a tile costs no address arithmetic;
+  // rows of a partial last tile past n fail the resource's range check and
+  // land as zeros (their scores are masked, their values weigh 0).  The
+  // copies are issued from inline assembly, so the compiler adds no wait for
+  // them before the transposed V reads; each step waits for them before its
+  // barrier.
   const KTileSwizzle<D * 2> kswz;
   const VTileSwizzle<D * 2> vswz;
   uint32_t koff[C::INSTS], voff[C::INSTS];
@@ -211,38 +214,15 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
     koff[it] = (uint32_t)(row * D + (phys ^ kswz(row)) * 8) * 2u;
     voff[it] = (uint32_t)(row * D + (phys ^ vswz(row)) * 8) * 2u;
   }
-  auto load_tile = [&](const bf16* src, bf16* dst, int t, auto swz) {
-    const int kbase = kbase_of(t);
-    const uint32_t* offs = decltype(swz)::is_v ? voff : koff;
-    if (BUF && kbase + BC <= n) {
-      // one buffer resource per tile: scalar base arithmetic only
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<bf16*>(src + (size_t)kbase * D), (short)0, BC * D * 2, 0x00020000);
+  const rsrc_t rsK = buffer_rsrc(Kh, (uint32_t)n * (D * 2));
+  const rsrc_t rsV = buffer_rsrc(Vh, (uint32_t)n * (D * 2));
+  auto load_tile = [&](bf16* dst, int t, auto swz) {
+    const bool is_v = decltype(swz)::is_v;
+    const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane(kbase_of(t)) * (D * 2);
 #pragma unroll
-      for (int it = 0; it < C::INSTS; ++it) {
-        const int p0 = wave * C::WAVE_CHUNKS + it * 64;  // wave-uniform
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (__attribute__((address_space(3))) void*)(dst + p0 * 8), 16, (int)offs[it], 0, 0,
-            0);
-      }
-    } else if (kbase + BC <= n) {
-      const char* tb = reinterpret_cast<const char*>(src) + (size_t)kbase * (D * 2);
-#pragma unroll
-      for (int it = 0; it < C::INSTS; ++it) {
-        const int p0 = wave * C::WAVE_CHUNKS + it * 64;  // wave-uniform
-        load_lds_16(tb + offs[it], dst + p0 * 8);
-      }
-    } else {
-#pragma unroll
-      for (int it = 0; it < C::INSTS; ++it) {
-        const int p0 = wave * C::WAVE_CHUNKS + it * 64;
-        const int p = p0 + lane;
-        const int row = p / C::CPR, phys = p % C::CPR;
-        const int logical = phys ^ swz(row);
-        const int grow = min(kbase + row, n - 1);
-        load_lds_16(src + (size_t)grow * D + logical * 8, dst + p0 * 8);
-      }
-    }
+    for (int it = 0; it < C::INSTS; ++it)
+      dma16_buf(is_v ? rsV : rsK, is_v ? voff[it] : koff[it], so,
+                dst + (wave * C::WAVE_CHUNKS + it * 64) * 8);
   };
 
   auto compute_s = [&](const bf16* Ks, f32x16 (&s)[BC / 32]) {
@@ -330,26 +310,32 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
   f32x16 s_cur[BC / 32];
   int j = 0;
   // Prologue: K_0, V_0, K_1 into LDS; S_0.
-  load_tile(Kh, Kb, 0, kswz);
-  load_tile(Vh, Vb, 0, vswz);
-  if (nt > 1) load_tile(Kh, Kb + C::TILE, 1, kswz);
+  load_tile(Kb, 0, kswz);
+  load_tile(Vb, 0, vswz);
+  if (nt > 1) load_tile(Kb + C::TILE, 1, kswz);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (active) compute_s(Kb, s_cur);
   __syncthreads();  // every wave has read K_0 before step 0 overwrites it
 
+  // The next tiles' copies are issued between the score MFMAs and the
+  // softmax, not at the top of the step, so that their data returns while
+  // the PV MFMAs run instead of during the burst of K operand reads.
   auto step = [&](auto par, int j) {
     constexpr int P = decltype(par)::value;
-    if (j + 2 < nt) load_tile(Kh, Kb + P * C::TILE, j + 2, kswz);
-    load_tile(Vh, Vb + (P ^ 1) * C::TILE, j + 1, vswz);
     f32x16 s_next[BC / 32];
     if (active) {
       softmax_max(s_cur, false, 0);
       compute_s(Kb + (P ^ 1) * C::TILE, s_next);
+    }
+    if (j + 2 < nt) load_tile(Kb + P * C::TILE, j + 2, kswz);
+    load_tile(Vb + (P ^ 1) * C::TILE, j + 1, vswz);
+    if (active) {
       uint32_t pk[BC / 32][8];
       softmax_exp(s_cur, pk);
       pv(Vb + P * C::TILE, pk);
     }
+    // this step's copies and LDS reads complete before any wave moves on
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #pragma unroll
@@ -389,12 +375,12 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
 }
 
 // WPS is the number of waves per SIMD the register budget is sized for.
-template <int D, int NW, int BC, int WPS, bool BUF>
+template <int D, int NW, int BC, int WPS>
 __global__ __launch_bounds__(NW * 64, (WPS * 4 / NW > 0 ? WPS * 4 / NW : 1)) void
 fwd_fused_bf16_direct_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                              const bf16* __restrict__ V, float* __restrict__ O,
                              float* __restrict__ lse, int n, int nqb, int total, float c) {
-  direct_body<D, NW, BC, false, false, BUF>(
+  direct_body<D, NW, BC, false, false>(
       DirectArgs{Q, K, V, O, lse, n, n, nqb, total, total / nqb, n, c});
 }
 
@@ -404,7 +390,7 @@ fwd_fused_bf16_direct_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
 template <int D, int NW, int BC>
 __global__ __launch_bounds__(NW * 64, (8 / NW > 0 ? 8 / NW : 1)) void fwd_split_bf16_kernel(
     const DirectArgs A) {
-  direct_body<D, NW, BC, true, false, true>(A);
+  direct_body<D, NW, BC, true, false>(A);
 }
 
 // Block-sparse entry: one workgroup per (head, 128-query block), visiting
@@ -412,7 +398,7 @@ __global__ __launch_bounds__(NW * 64, (8 / NW > 0 ? 8 / NW : 1)) void fwd_split_
 template <int D, int NW, int BC>
 __global__ __launch_bounds__(NW * 64, (8 / NW > 0 ? 8 / NW : 1)) void fwd_sparse_bf16_kernel(
     const DirectArgs A) {
-  direct_body<D, NW, BC, false, true, true>(A);
+  direct_body<D, NW, BC, false, true>(A);
 }
 
 // Compacts one row of the block mask (mask head, query block) into the
@@ -882,11 +868,11 @@ struct FusedEntry {
   FusedKernel kernel;
 };
 
-template <int D, int NW, int BC, int WPS = 2, bool BUF = false>
+template <int D, int NW, int BC, int WPS = 2>
 FusedEntry direct(const char* name) {
   using C = DirectCfg<D, NW, BC>;
   return FusedEntry{name, D, NW, FusedTileInfo{C::BR, C::KEYS, C::ONCHIP},
-                    &fwd_fused_bf16_direct_kernel<D, NW, BC, WPS, BUF>};
+                    &fwd_fused_bf16_direct_kernel<D, NW, BC, WPS>};
 }
 
 template <int D, int QB, int BC>
@@ -900,8 +886,8 @@ const FusedEntry* registry(int& count) {
   static const FusedEntry table[] = {
       // head dimension 64: two 4-wave groups offset by half a tile
       pingpong<64, 2, 64>("g2x64p"),
-      // head dimension 128: 8 waves, 64-key tiles, buffer-resource copies
-      direct<128, 8, 64, 2, true>("d8x64"),
+      // head dimension 128: 8 waves, 64-key tiles
+      direct<128, 8, 64>("d8x64"),
       // d = 128 tile sweep (128-key tiles spill registers at d = 128)
       direct<128, 2, 32>("r64c32"),
       direct<128, 2, 64>("r64c64"),
@@ -910,7 +896,7 @@ const FusedEntry* registry(int& count) {
       direct<128, 8, 32>("r256c32"),
       direct<128, 8, 64>("r256c64"),
       // head dimension 256: 4 waves (one per SIMD), 32-key tiles
-      direct<256, 4, 32, 1, true>("d4x32b"),
+      direct<256, 4, 32, 1>("d4x32b"),
   };
   count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

@@ -53,6 +53,35 @@ __device__ __forceinline__ void dma4(const void* gsrc, void* lds_wave_base) {
       : "v"(gsrc), "s"(lds)
       : "memory", "m0");
 }
+// Buffer resource (V#) for `bytes` bytes from `base`: raw addressing, no
+// stride, the range check against `bytes` turning every read past the end
+// into zeros.  Built with scalar instructions from a wave-uniform base.
+typedef int rsrc_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  rsrc_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);
+  r[2] = (int)bytes;
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane through a buffer resource (buffer_load_dwordx4 ... lds):
+// lane l reads bytes [voff + soff, +16) of the resource (zeros past its end)
+// into lds_wave_base + 16 l; soff is wave-uniform (an SGPR).
+__device__ __forceinline__ void dma16_buf(rsrc_t rs, uint32_t voff, uint32_t soff,
+                                          const void* lds_wave_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
+      __attribute__((address_space(3))) const char*)(reinterpret_cast<const char*>(lds_wave_base)));
+  asm volatile(
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, %2 offen lds"
+      :
+      : "v"(voff), "s"(rs), "s"(soff), "s"(lds)
+      : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // Workgroup barrier without a memory fence: every lane has already waited
