@@ -72,10 +72,18 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // and lane i >= 32 with {x[i - 32], x[i]}, so one fmaxf finishes the pair.
 // Issued from inline assembly (two wait states before and after it) since
 // the compiler builtin returns the same register for both results here.
+// The max is taken in the same assembly block (v_max_f32: the larger
+// operand, the other one if one is a quiet NaN), which spares the compiler's
+// NaN canonicalisation of two values it cannot see into.
 __device__ __forceinline__ float pair_max_xor32(float x) {
   float a = x, b = x;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-  return fmaxf(a, b);
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_permlane32_swap_b32 %0, %1\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32 %0, %0, %1"
+      : "+v"(a), "+v"(b));
+  return a;
 }
 
 // XOR swizzle of the 16-byte chunk index inside an LDS row, chosen so that

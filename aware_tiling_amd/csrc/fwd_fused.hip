@@ -327,8 +327,18 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
     if (active) {
       softmax_max(s_cur, false, 0);
       compute_s(Kb + (P ^ 1) * C::TILE, s_next);
+      // issue each score MFMA's K read four MFMAs ahead of it
+      constexpr int NS = (D / 16) * (BC / 32);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // LDS reads
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        if (i + 4 < NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
-    if (j + 2 < nt) load_tile(Kb + P * C::TILE, j + 2, kswz);
+    // Consecutive tiles need no test: a tile past the end reads zeros into
+    // the free slot.  A tile list cannot be read past its length.
+    if (!LIST || j + 2 < nt) load_tile(Kb + P * C::TILE, j + 2, kswz);
     load_tile(Vb + (P ^ 1) * C::TILE, j + 1, vswz);
     if (active) {
       uint32_t pk[BC / 32][8];
