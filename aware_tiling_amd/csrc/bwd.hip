@@ -104,9 +104,9 @@ __device__ __forceinline__ void tile_load_lds(const bf16* src, bf16* dst, int t,
   for (int it = 0; it < insts; ++it) {
     const int p0 = wave * wave_chunks + it * 64;
     const int p = p0 + lane;
-    const int row = p / CPR, phys = p % CPR;
-    const int logical = phys ^ (dual ? dual_swizzle<D * 2>(row) : chunk_swizzle<D * 2>(row));
-    const int grow = min(rbase + row, n - 1);
+    const int logical = dual ? tile_copy_chunk<D, dual_swizzle<D * 2>>(p)
+                             : tile_copy_chunk<D, chunk_swizzle<D * 2>>(p);
+    const int grow = min(rbase + p / CPR, n - 1);
     if constexpr (ASM)
       dma16(src + (size_t)grow * D + logical * 8, dst + p0 * 8);
     else
@@ -119,22 +119,20 @@ __device__ __forceinline__ void tile_load_lds(const bf16* src, bf16* dst, int t,
 // accumulator's row order (tile rows 16 ks + 8 (j/4) + 4 h + j%4).
 template <int D>
 __device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int ks, int db, int lane) {
-  const int G = lane >> 4, sl = lane & 15, hh = G >> 1;
   u32x2 part[2];
 #pragma unroll
-  for (int piece = 0; piece < 2; ++piece) {
-    const int row = 16 * ks + 8 * piece + 4 * hh + (sl >> 2);
-    const int d0 = db * 32 + 16 * (G & 1) + 4 * (sl & 3);
-    const int phys = (d0 >> 3) ^ dual_swizzle<D * 2>(row);
-    part[piece] = lds_read_tr16(tile + row * D + phys * 8 + (d0 & 7));
-  }
+  for (int piece = 0; piece < 2; ++piece)
+    part[piece] = lds_read_tr16(tile + tile_elem<D, dual_swizzle<D * 2>>(
+                                           16 * ks + tr_read_row(lane, piece),
+                                           db * 32 + tr_read_col(lane)));
   return __builtin_bit_cast(bf16x8, (u32x4{part[0][0], part[0][1], part[1][0], part[1][1]}));
 }
 
 template <int D>
 __device__ __forceinline__ bf16x8 row_operand(const bf16* tile, int row, int chunk, bool dual) {
-  const int sw = dual ? dual_swizzle<D * 2>(row) : chunk_swizzle<D * 2>(row);
-  return *reinterpret_cast<const bf16x8*>(tile + row * D + ((chunk ^ sw) * 8));
+  return *reinterpret_cast<const bf16x8*>(
+      tile + (dual ? row_chunk_elem<D, dual_swizzle<D * 2>>(row, chunk)
+                   : row_chunk_elem<D, chunk_swizzle<D * 2>>(row, chunk)));
 }
 
 }  // namespace
@@ -206,9 +204,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv3(
     constexpr int RC = D / 8;
 #pragma unroll
     for (int it = 0; it < 32 * RC / 64; ++it) {
-      const int p = it * 64 + lane, row = p / RC, phys = p % RC;
-      const int logical = phys ^ dual_swizzle<D * 2>(row);
-      const int vrow = min(kblk * C::BKV + wave * 32 + row, n - 1);
+      const int p = it * 64 + lane;
+      const int logical = tile_copy_chunk<D, dual_swizzle<D * 2>>(p);
+      const int vrow = min(kblk * C::BKV + wave * 32 + p / RC, n - 1);
       load_lds_16(Vh + (size_t)vrow * D + logical * 8, Vw + it * 64 * 8);
     }
   }
@@ -220,27 +218,21 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv3(
   uint32_t toff[C::INSTS];
 #pragma unroll
   for (int it = 0; it < C::INSTS; ++it) {
-    const int p = wave * C::WAVE_CHUNKS + it * 64 + lane;
-    const int row = p / (D / 8), phys = p % (D / 8);
-    toff[it] = (uint32_t)(row * D + (phys ^ dual_swizzle<D * 2>(row)) * 8) * 2u;
+    toff[it] = tile_copy_src<D, dual_swizzle<D * 2>>(wave * C::WAVE_CHUNKS + it * 64 + lane);
   }
-  // roff: row-wise reads of Q, dO and the wave's V rows (one swizzle)
+  // roff: row-wise reads of Q, dO and the wave's V rows (one swizzle);
+  // troff: transposed reads.  The dual swizzle depends only on the low four
+  // row bits, so further rows (query sub-block, k-step) add whole rows.
   uint32_t roff[NKK], troff[NDB][2];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk)
-    roff[kk] = (uint32_t)(li * D + ((2 * kk + h) ^ dual_swizzle<D * 2>(li)) * 8) * 2u;
-  {
-    const int G = lane >> 4, sl = lane & 15, hh = G >> 1;
+    roff[kk] = (uint32_t)row_chunk_elem<D, dual_swizzle<D * 2>>(li, 2 * kk + h) * 2u;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int piece = 0; piece < 2; ++piece) {
-        const int row = 8 * piece + 4 * hh + (sl >> 2);
-        const int d0 = db * 32 + 16 * (G & 1) + 4 * (sl & 3);
-        troff[db][piece] =
-            (uint32_t)(row * D + ((d0 >> 3) ^ dual_swizzle<D * 2>(row)) * 8 + (d0 & 7)) * 2u;
-      }
-  }
+    for (int piece = 0; piece < 2; ++piece)
+      troff[db][piece] = (uint32_t)tile_elem<D, dual_swizzle<D * 2>>(
+                             tr_read_row(lane, piece), db * 32 + tr_read_col(lane)) * 2u;
 
   auto load = [&](int i, int stage) {
     char* qdst = tiles + stage * 2 * TILE_B;
@@ -465,28 +457,21 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq3(
 #pragma unroll
   for (int it = 0; it < C::INSTS; ++it) {
     const int p = wave * C::WAVE_CHUNKS + it * 64 + lane;
-    const int row = p / (D / 8), phys = p % (D / 8);
-    koff[it] = (uint32_t)(row * D + (phys ^ dual_swizzle<D * 2>(row)) * 8) * 2u;
-    voff[it] = (uint32_t)(row * D + (phys ^ chunk_swizzle<D * 2>(row)) * 8) * 2u;
+    koff[it] = tile_copy_src<D, dual_swizzle<D * 2>>(p);
+    voff[it] = tile_copy_src<D, chunk_swizzle<D * 2>>(p);
   }
   uint32_t rk[NKK], rv[NKK], tk[NDB][2];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
-    rk[kk] = (uint32_t)(li * D + ((2 * kk + h) ^ dual_swizzle<D * 2>(li)) * 8) * 2u;
-    rv[kk] = (uint32_t)(li * D + ((2 * kk + h) ^ chunk_swizzle<D * 2>(li)) * 8) * 2u;
+    rk[kk] = (uint32_t)row_chunk_elem<D, dual_swizzle<D * 2>>(li, 2 * kk + h) * 2u;
+    rv[kk] = (uint32_t)row_chunk_elem<D, chunk_swizzle<D * 2>>(li, 2 * kk + h) * 2u;
   }
-  {
-    const int G = lane >> 4, sl = lane & 15, hh = G >> 1;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int piece = 0; piece < 2; ++piece) {
-        const int row = 8 * piece + 4 * hh + (sl >> 2);
-        const int d0 = db * 32 + 16 * (G & 1) + 4 * (sl & 3);
-        tk[db][piece] =
-            (uint32_t)(row * D + ((d0 >> 3) ^ dual_swizzle<D * 2>(row)) * 8 + (d0 & 7)) * 2u;
-      }
-  }
+    for (int piece = 0; piece < 2; ++piece)
+      tk[db][piece] = (uint32_t)tile_elem<D, dual_swizzle<D * 2>>(
+                          tr_read_row(lane, piece), db * 32 + tr_read_col(lane)) * 2u;
   auto load = [&](int j, int stage) {
     char* kdst = tiles + stage * 2 * TILE_B;
     if ((j + 1) * BC <= n) {

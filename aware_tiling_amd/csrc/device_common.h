@@ -1,5 +1,6 @@
 // Device-side helpers shared by the gfx950 attention kernels: vector types,
-// MFMA wrappers, bf16 packing, and the LDS swizzles.
+// MFMA wrappers, bf16 packing, LDS reads and copies.  The integer index maps
+// (swizzles, offsets) are in index_maps.h.
 //
 // MFMA operand layouts used throughout (wave64, lane l, h = l / 32, i = l % 32):
 //   v_mfma_f32_32x32x16_bf16  D[32x32] += A[32x16] * B[16x32]
@@ -12,6 +13,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "index_maps.h"
 
 namespace at {
 
@@ -86,53 +89,6 @@ __device__ __forceinline__ float pair_max_xor32(float x) {
   return a;
 }
 
-// XOR swizzle of the 16-byte chunk index inside an LDS row, chosen so that
-// when consecutive rows are read at the same logical chunk (one row per
-// lane), the lanes of one ds_read_b128 phase land on distinct banks, whether
-// a phase spans 128 bytes (8 lanes) or 256 bytes (16 lanes).  Rows of 256
-// bytes or more use the low four row bits; 128-byte rows alternate bank
-// halves between even and odd rows, so they fold bit 3 into bit 0; 64-byte
-// rows put four rows in 256 bytes and mix bits 1 and 2.
-template <int ROW_BYTES>
-__device__ __forceinline__ int chunk_swizzle(int row) {
-  static_assert(ROW_BYTES >= 64, "rows shorter than 64 bytes are not swizzled");
-  if constexpr (ROW_BYTES >= 256)
-    return row & 15;
-  else if constexpr (ROW_BYTES == 128)
-    return (row & 7) ^ ((row >> 3) & 1);
-  else
-    return ((row >> 1) ^ (row >> 2)) & 3;
-}
-
-// Swizzle of the 16-byte chunk index for a row-major value tile read with
-// ds_read_b64_tr_b16 (rows of ROW_BYTES).  One such read touches 4
-// consecutive rows at the same 4-chunk group per half wave; flipping bits 2-3
-// of the chunk index by the row (d >= 128) or by row bit 1 (d = 64, two rows
-// per 256 bytes) spreads those 4 rows over all 64 banks.
-template <int ROW_BYTES>
-__device__ __forceinline__ int vtr_swizzle(int row) {
-  if constexpr (ROW_BYTES >= 256)
-    return 4 * (row & 3);
-  else
-    return 4 * ((row >> 1) & 1);
-}
-
-// Swizzle for a row-major tile that is read both ways: row-wise with
-// ds_read_b128 (16 consecutive rows at one logical chunk per phase) and
-// transposed with ds_read_b64_tr_b16 (4 consecutive rows x 4 consecutive
-// chunks per half wave).  The XOR value is a bijection of the low 4 row bits
-// (distinct for any 16 consecutive rows) whose bits 2-3 are the row's low
-// bits (distinct 64-byte chunk groups for any 4 consecutive rows).  For
-// 128-byte rows (two rows per 256-byte bank window) bit 2 follows row bit 1
-// instead.
-template <int ROW_BYTES>
-__device__ __forceinline__ int dual_swizzle(int row) {
-  if constexpr (ROW_BYTES >= 256)
-    return ((row & 3) << 2) | ((row >> 2) & 3);
-  else
-    return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-}
-
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
 // lane l's 16 bytes land at lds_wave_base + 16 l.  lds_wave_base must be
 // uniform across the wave.
@@ -157,22 +113,6 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const bf16* p) {
       (__attribute__((address_space(3))) i16x4*)(
           (__attribute__((address_space(3))) char*)(const_cast<bf16*>(p))));
   return __builtin_bit_cast(u32x2, v);
-}
-
-// Position of key k inside a transposed value tile: within each group of 16
-// keys, bits 2 and 3 of the key index are swapped, so that the 8 keys one
-// lane feeds to the P*V product (see the fused kernel) are contiguous.
-__device__ __forceinline__ int vt_key_pos(int k) {
-  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
-}
-
-// Map the hardware workgroup id to a logical tile id so that consecutive
-// logical tiles run on the same XCD (workgroups are dispatched round robin
-// over the 8 XCDs); tiles that share K/V then share that XCD's L2.
-__device__ __forceinline__ int xcd_remap(int w, int total) {
-  const int per = total >> 3;
-  if (w < (per << 3)) return (w & 7) * per + (w >> 3);
-  return w;
 }
 
 }  // namespace at

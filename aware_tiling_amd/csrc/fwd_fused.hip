@@ -90,8 +90,9 @@ struct DirectArgs {
   int tile_cap = 0, mask_heads = 1;
 };
 
-// Swizzle functors for the K tile (row-wise reads) and the V tile
-// (transposed reads), tagged so a loader can pick the matching offsets.
+// Tags for the K tile (row-wise reads, chunk_swizzle) and the V tile
+// (transposed reads, vtr_swizzle), so a loader can pick the matching
+// offsets.
 template <int ROW_BYTES>
 struct KTileSwizzle {
   static constexpr bool is_v = false;
@@ -210,9 +211,8 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
 #pragma unroll
   for (int it = 0; it < C::INSTS; ++it) {
     const int p = wave * C::WAVE_CHUNKS + it * 64 + lane;
-    const int row = p / C::CPR, phys = p % C::CPR;
-    koff[it] = (uint32_t)(row * D + (phys ^ kswz(row)) * 8) * 2u;
-    voff[it] = (uint32_t)(row * D + (phys ^ vswz(row)) * 8) * 2u;
+    koff[it] = tile_copy_src<D, chunk_swizzle<D * 2>>(p);
+    voff[it] = tile_copy_src<D, vtr_swizzle<D * 2>>(p);
   }
   const rsrc_t rsK = buffer_rsrc(Kh, (uint32_t)n * (D * 2));
   const rsrc_t rsV = buffer_rsrc(Vh, (uint32_t)n * (D * 2));
@@ -232,9 +232,8 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
     for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb) {
-        const int row = kb * 32 + li;
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            Ks + row * D + (((2 * kk + h) ^ chunk_swizzle<D * 2>(row)) * 8));
+            Ks + row_chunk_elem<D, chunk_swizzle<D * 2>>(kb * 32 + li, 2 * kk + h));
         s[kb] = mfma_bf16_32x32x16(a, qreg[kk], s[kb]);
       }
   };
@@ -278,11 +277,9 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
       }
     l = lsum;
   };
-  // U^T += V^T P^T with the V^T operand from transposed LDS reads.  Lane
-  // group G = lane/16 covers d rows 16(G&1)..+15 of the 32-row block and
-  // key half hh = G/2; source lane s points at key K0 + s/4, d D0 + 4(s%4).
-  const int G = lane >> 4, sl = lane & 15;
-  const int hh = G >> 1;
+  // U^T += V^T P^T with the V^T operand from transposed LDS reads
+  // (tr_read_row / tr_read_col: each lane gets one d column across 4 keys,
+  // in the score accumulator's key order).
   auto pv = [&](const bf16* Vs, const uint32_t (&pk)[BC / 32][8]) {
 #pragma unroll
     for (int ks = 0; ks < BC / 16; ++ks) {
@@ -294,12 +291,10 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
       for (int db = 0; db < D / 32; ++db) {
         u32x2 part[2];
 #pragma unroll
-        for (int piece = 0; piece < 2; ++piece) {
-          const int row = kb * 32 + 16 * half + 8 * piece + 4 * hh + (sl >> 2);
-          const int d0 = db * 32 + 16 * (G & 1) + 4 * (sl & 3);
-          const int phys = (d0 >> 3) ^ vtr_swizzle<D * 2>(row);
-          part[piece] = lds_read_tr16(Vs + row * D + phys * 8 + (d0 & 7));
-        }
+        for (int piece = 0; piece < 2; ++piece)
+          part[piece] = lds_read_tr16(Vs + tile_elem<D, vtr_swizzle<D * 2>>(
+                                               kb * 32 + 16 * half + tr_read_row(lane, piece),
+                                               db * 32 + tr_read_col(lane)));
         const bf16x8 a =
             __builtin_bit_cast(bf16x8, (u32x4{part[0][0], part[0][1], part[1][0], part[1][1]}));
         uacc[db] = mfma_bf16_32x32x16(a, pb, uacc[db]);
@@ -551,9 +546,8 @@ __global__ __launch_bounds__(512, 1) void fwd_fused_bf16_pingpong_kernel(
 #pragma unroll
   for (int it = 0; it < C::INSTS; ++it) {
     const int p = wave * C::WAVE_CHUNKS + it * 64 + lane;
-    const int row = p / C::CPR, phys = p % C::CPR;
-    koff[it] = (uint32_t)(row * D + (phys ^ kswz(row)) * 8) * 2u;
-    voff[it] = (uint32_t)(row * D + (phys ^ vswz(row)) * 8) * 2u;
+    koff[it] = tile_copy_src<D, chunk_swizzle<D * 2>>(p);
+    voff[it] = tile_copy_src<D, vtr_swizzle<D * 2>>(p);
   }
   // Full tiles: wave-uniform tile base + per-lane offsets; a partial last
   // tile clamps its rows to n-1.
@@ -590,15 +584,12 @@ __global__ __launch_bounds__(512, 1) void fwd_fused_bf16_pingpong_kernel(
     for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb) {
-        const int row = kb * 32 + li;
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            Ks + row * D + (((2 * kk + h) ^ chunk_swizzle<D * 2>(row)) * 8));
+            Ks + row_chunk_elem<D, chunk_swizzle<D * 2>>(kb * 32 + li, 2 * kk + h));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma_bf16_32x32x16(a, qreg[qb][kk], s[kb][qb]);
       }
   };
-  const int G = lane >> 4, sl = lane & 15;
-  const int hh = G >> 1;
   auto pv = [&](const bf16* Vs) {
 #pragma unroll
     for (int ks = 0; ks < BC / 16; ++ks) {
@@ -614,12 +605,10 @@ __global__ __launch_bounds__(512, 1) void fwd_fused_bf16_pingpong_kernel(
       for (int db = 0; db < D / 32; ++db) {
         u32x2 part[2];
 #pragma unroll
-        for (int piece = 0; piece < 2; ++piece) {
-          const int row = kb * 32 + 16 * half + 8 * piece + 4 * hh + (sl >> 2);
-          const int d0 = db * 32 + 16 * (G & 1) + 4 * (sl & 3);
-          const int phys = (d0 >> 3) ^ vtr_swizzle<D * 2>(row);
-          part[piece] = lds_read_tr16(Vs + row * D + phys * 8 + (d0 & 7));
-        }
+        for (int piece = 0; piece < 2; ++piece)
+          part[piece] = lds_read_tr16(Vs + tile_elem<D, vtr_swizzle<D * 2>>(
+                                               kb * 32 + 16 * half + tr_read_row(lane, piece),
+                                               db * 32 + tr_read_col(lane)));
         const bf16x8 a =
             __builtin_bit_cast(bf16x8, (u32x4{part[0][0], part[0][1], part[1][0], part[1][1]}));
 #pragma unroll
