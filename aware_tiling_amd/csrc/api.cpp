@@ -35,11 +35,12 @@ attn_status launch_status(hipError_t e) {
 // kernels' 32-bit in-head indexing.  bh * n <= 2^29 rows keeps every
 // one-workgroup-per-block grid inside 32 bits; at d >= 64 that many rows of
 // Q, K, V and O would not fit in HBM anyway.
+// Every factor is bounded before any product is formed, so no check can
+// overflow whatever the caller passes.
 bool shape_ok(int64_t bh, int64_t n, int64_t d) {
   if (bh < 0 || n < 0 || d <= 0) return false;
-  if (n > (int64_t(1) << 24)) return false;
+  if (n > (int64_t(1) << 24) || d > (int64_t(1) << 16) || bh > (int64_t(1) << 20)) return false;
   if (n * d >= (int64_t(1) << 31)) return false;
-  if (bh > (int64_t(1) << 20)) return false;
   if (bh * n > (int64_t(1) << 29)) return false;
   return true;
 }
@@ -57,6 +58,7 @@ const char* attn_status_string(attn_status s) {
     case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
     case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE";
     case ATTN_ERR_LAUNCH: return "ATTN_ERR_LAUNCH";
+    default: break;
   }
   return "ATTN_STATUS_UNKNOWN";
 }

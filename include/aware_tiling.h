@@ -50,15 +50,26 @@
 extern "C" {
 #endif
 
+/* Both enums carry two range sentinels (never returned or accepted) so that
+ * every 32-bit integer is a representable value: a caller may pass any int
+ * as a dtype and get ATTN_ERR_UNSUPPORTED, and attn_status_string accepts
+ * any int. */
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size or scale */
   ATTN_ERR_UNSUPPORTED = 2, /* head dimension or dtype not built */
   ATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
-  ATTN_ERR_LAUNCH = 4       /* HIP reported an error when enqueueing */
+  ATTN_ERR_LAUNCH = 4,      /* HIP reported an error when enqueueing */
+  ATTN_STATUS_RANGE_MIN_ = -2147483647 - 1,
+  ATTN_STATUS_RANGE_MAX_ = 2147483647
 } attn_status;
 
-typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+typedef enum {
+  ATTN_F32 = 0,
+  ATTN_BF16 = 1,
+  ATTN_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  ATTN_DTYPE_RANGE_MAX_ = 2147483647
+} attn_dtype;
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* attn_status_string(attn_status s);
