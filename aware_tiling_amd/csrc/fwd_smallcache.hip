@@ -11,10 +11,11 @@
 // Two kernels, stream ordered:
 //  1. sc_scores_exp: one workgroup per (head, query tile I, run of jc key
 //     tiles J), b x b tiles.  S^T = K_J Q_I^T is accumulated over d in
-//     panels of KP = 32 columns: the K panel goes global -> LDS with direct
-//     loads (two stages), the Q panel goes straight into registers as the
-//     MFMA B operand (two stages), and the panel pipeline runs on across tile
-//     boundaries.  The epilogue takes each query row's maximum over the tile,
+//     panels of KS columns (64 at b = 128: whole 128-byte lines of the
+//     row-major rows; 32 at b = 64): the K and Q panels go global -> LDS
+//     with direct copies into a two-slot ring, the next panel's copies run
+//     while the current one is multiplied, and the panel pipeline runs on
+//     across tile boundaries.  The epilogue takes each query row's maximum over the tile,
 //     m_IJ (base-2 units, c = scale log2 e), writes E = exp2(c S - m_IJ) in
 //     bf16, and the tile sum l_IJ of the stored bf16 values.  The page does
 //     not say how the exponentials are kept in range; the per-tile shift is
@@ -53,7 +54,7 @@ namespace at {
 
 namespace {
 
-constexpr int KP = 32;  // contraction panel width (elements)
+constexpr int KP = 32;  // value product: keys per panel (one 32-key block of E)
 
 __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -81,15 +82,24 @@ __device__ __forceinline__ size_t e_unit(int head, int I, int J, int nt, int wav
 
 }  // namespace
 
-// Prefetch distance: every operand panel is copied global -> LDS DIST
-// panels ahead of the one being multiplied, into a ring of R = DIST + 1
-// slots.  The on-chip footprint is then b^2 + 2 R b KP for the scores (K and
-// Q panels, b x KP each) and b bd + R (KP bd + b KP) for the value product
-// (V panels KP x bd, E panels b x KP).
+// Panel pipelines: every operand panel is copied global -> LDS DIST panels
+// ahead of the one being multiplied, into a ring of R = DIST + 1 slots.  The
+// on-chip footprint is then b^2 + 2 R_s b KS for the scores (K and Q panels,
+// b x KS each) and b bd + R_v (KP bd + b KP) for the value product (V panels
+// KP x bd, E panels b x KP).
+template <int B>
+struct ScScoreCfg {
+  // contraction columns per panel: at b = 128 each panel row is one whole
+  // 128-byte line of a row-major Q or K row, so no line crosses into the CU
+  // twice (two 64-byte strips of a line, a panel apart, would each fetch it)
+  static constexpr int KS = B >= 128 ? 64 : 32;
+  static constexpr int R = 2;
+  static constexpr int DIST = R - 1;
+};
 template <int B>
 struct ScDist {
-  static constexpr int DIST = B >= 128 ? 2 : 1;
-  static constexpr int R = DIST + 1;
+  static constexpr int R = B >= 128 ? 4 : 2;
+  static constexpr int DIST = R - 1;
 };
 
 // ---------------------------------------------------------------------------
@@ -102,15 +112,17 @@ __global__ __launch_bounds__(B * 2) void sc_scores_exp(const bf16* __restrict__ 
                                                        float* __restrict__ mst,
                                                        float* __restrict__ lst, int n, int nt,
                                                        int jc, int njc, int total, float c) {
+  constexpr int KS = ScScoreCfg<B>::KS;
   constexpr int NW = B / 32, NT = NW * 64;
-  constexpr int CPR = KP / 8;       // 16-byte chunks per panel row
+  constexpr int CPR = KS / 8;       // 16-byte chunks per panel row
   constexpr int PCH = B * CPR;      // chunks per panel
   constexpr int LI = PCH / NT;      // copies per lane per panel and operand
-  constexpr int NP = D / KP;        // panels per tile
-  constexpr int DIST = ScDist<B>::DIST, R = ScDist<B>::R;
+  constexpr int NP = D / KS;        // panels per tile
+  constexpr int DIST = ScScoreCfg<B>::DIST, R = ScScoreCfg<B>::R;
   static_assert(PCH % NT == 0, "panel chunks must split evenly over the lanes");
-  __shared__ __attribute__((aligned(16))) bf16 Kp[R][B * KP];
-  __shared__ __attribute__((aligned(16))) bf16 Qp[R][B * KP];
+  static_assert(NP % R == 0 && DIST < NP, "ring slots must repeat with every tile");
+  __shared__ __attribute__((aligned(16))) bf16 Kp[R][B * KS];
+  __shared__ __attribute__((aligned(16))) bf16 Qp[R][B * KS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, li = lane & 31;
@@ -119,108 +131,115 @@ __global__ __launch_bounds__(B * 2) void sc_scores_exp(const bf16* __restrict__ 
   const int rem = tile - head * nt * njc;
   const int I = rem / njc, jr = rem - (rem / njc) * njc;
   const int J0 = jr * jc, J1 = min(nt, J0 + jc);
-  const int T = (J1 - J0) * NP;
-  const bf16* Qh = Q + (size_t)head * n * D;
-  const bf16* Kh = K + (size_t)head * n * D;
   const int q = I * B + wave * 32 + li;
   const bool qok = q < n;
 
-  // lane chunk p = (wave LI + it) 64 + lane of a panel: row p / CPR,
-  // physical chunk p % CPR, which holds logical chunk phys ^ swizzle(row);
-  // rows past n are clamped (their scores are masked, or belong to rows
-  // that are not stored)
-  int prow[LI], pcol[LI];
+  // Head-wide buffer resources: rows past n read as zeros (their scores
+  // are masked, or belong to query rows that are not stored).  Lane chunk
+  // p = (wave LI + it) 64 + lane of a panel is row p / CPR, physical chunk
+  // p % CPR, which holds logical chunk phys ^ swizzle(row); its byte offset
+  // within a panel is per-lane constant, the panel's own offset is scalar.
+  const rsrc_t rq = buffer_rsrc(Q + (size_t)head * n * D, (uint32_t)n * (D * 2));
+  const rsrc_t rk = buffer_rsrc(K + (size_t)head * n * D, (uint32_t)n * (D * 2));
+  uint32_t voff[LI];
 #pragma unroll
   for (int it = 0; it < LI; ++it) {
     const int p = (wave * LI + it) * 64 + lane;
-    const int row = p / CPR, phys = p % CPR;
-    prow[it] = row;
-    pcol[it] = (phys ^ chunk_swizzle<KP * 2>(row)) * 8;
+    voff[it] = (uint32_t)((p / CPR) * D * 2 + tile_copy_chunk<KS, chunk_swizzle<KS * 2>>(p) * 16);
   }
-  // Copy panel t's K and Q into slot t % R.  Panels past the end copy the
-  // last one again, so every step issues the same number of copies.
-  auto issue = [&](int t) {
-    t = min(t, T - 1);
-    const int J = J0 + t / NP, pan = t - (t / NP) * NP, slot = t % R;
+  // LDS destinations: this wave's part of slot 0 of each ring (scalar)
+  const uint32_t wlds = (uint32_t)__builtin_amdgcn_readfirstlane(wave) * (LI * 1024u);
+  const uint32_t kl = lds_addr(&Kp[0][0]) + wlds, ql = lds_addr(&Qp[0][0]) + wlds;
+  // Copy panel pan of key tile J (and of query tile I) into ring slot `slot`.
+  auto issue = [&](int J, int pan, int slot) {
+    const uint32_t sk = (uint32_t)(J * B * D + pan * KS) * 2u;
+    const uint32_t sq = (uint32_t)(I * B * D + pan * KS) * 2u;
+    const uint32_t so = (uint32_t)slot * (B * KS * 2);
 #pragma unroll
     for (int it = 0; it < LI; ++it) {
-      const int key = min(J * B + prow[it], n - 1);
-      const int qrow = min(I * B + prow[it], n - 1);
-      dma16(Kh + (size_t)key * D + pan * KP + pcol[it], &Kp[slot][(wave * LI + it) * 64 * 8]);
-      dma16(Qh + (size_t)qrow * D + pan * KP + pcol[it], &Qp[slot][(wave * LI + it) * 64 * 8]);
+      dma16_buf_at(rk, voff[it], sk, kl + so + it * 1024u);
+      dma16_buf_at(rq, voff[it], sq, ql + so + it * 1024u);
     }
   };
 
-  f32x16 acc[B / 32];
 #pragma unroll
-  for (int kb = 0; kb < B / 32; ++kb) acc[kb] = f32x16{};
-
+  for (int s = 0; s < DIST; ++s) issue(J0, s, s);
+  for (int J = J0; J < J1; ++J) {
+    f32x16 acc[B / 32];
 #pragma unroll
-  for (int s = 0; s < DIST; ++s) issue(s);
-  for (int t = 0; t < T; ++t) {
-    // panel t is complete once at most the later DIST - 1 panels' copies
-    // are outstanding (vector-memory operations complete in issue order; an
-    // E store in between only makes this wait longer)
-    wait_vm<(DIST - 1) * 2 * LI>();
-    slot_barrier();  // every lane's part of panel t; slot (t - 1) % R is free
-    issue(t + DIST);
-    const int slot = t % R;
-    const bf16* Ks = Kp[slot];
-    const bf16* Qs = Qp[slot];
-    const int qrow = wave * 32 + li;
+    for (int pan = 0; pan < NP; ++pan) {
+      // Panel (J, pan) was issued DIST steps ago; the loads issued after it
+      // are the copies of the next DIST - 1 panels.  Loads complete in issue
+      // order, but a store may complete before an older load, so the count
+      // covers loads only: with at most that many operations outstanding,
+      // no load older than the last DIST - 1 panels' can be.
+      wait_vm<(DIST - 1) * 2 * LI>();
+      slot_barrier();  // every lane's part of the panel; the slot read last step is free
+      {
+        // the panel DIST steps ahead; past the end, the last panel again
+        // (every step issues the same number of copies)
+        int Jn = J + (pan + DIST) / NP, pn = (pan + DIST) % NP;
+        if (Jn >= J1) {
+          Jn = J1 - 1;
+          pn = NP - 1;
+        }
+        issue(Jn, pn, (pan + DIST) % R);
+      }
+      const bf16* Ks = Kp[pan % R];
+      const bf16* Qs = Qp[pan % R];
+      const int qrow = wave * 32 + li;
 #pragma unroll
-    for (int kk = 0; kk < KP / 16; ++kk) {
-      const bf16x8 bq = *reinterpret_cast<const bf16x8*>(
-          Qs + qrow * KP + (((2 * kk + h) ^ chunk_swizzle<KP * 2>(qrow)) * 8));
+      for (int kk = 0; kk < KS / 16; ++kk) {
+        const bf16x8 bq = *reinterpret_cast<const bf16x8*>(
+            Qs + row_chunk_elem<KS, chunk_swizzle<KS * 2>>(qrow, 2 * kk + h));
 #pragma unroll
-      for (int kb = 0; kb < B / 32; ++kb) {
-        const int row = kb * 32 + li;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            Ks + row * KP + (((2 * kk + h) ^ chunk_swizzle<KP * 2>(row)) * 8));
-        acc[kb] = mfma_bf16_32x32x16(a, bq, acc[kb]);
+        for (int kb = 0; kb < B / 32; ++kb) {
+          const int row = kb * 32 + li;
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+              Ks + row_chunk_elem<KS, chunk_swizzle<KS * 2>>(row, 2 * kk + h));
+          acc[kb] = mfma_bf16_32x32x16(a, bq, (pan == 0 && kk == 0) ? f32x16{} : acc[kb]);
+        }
       }
     }
-    if (t % NP == NP - 1) {
-      // Epilogue of tile J: tile maximum, exponentials, tile sum.
-      const int J = J0 + t / NP;
-      if (J == nt - 1 && (n % B) != 0) {
-#pragma unroll
-        for (int kb = 0; kb < B / 32; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (J * B + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3) >= n) acc[kb][r] = -INFINITY;
-      }
-      float mx = -INFINITY;
+    // Epilogue of tile J: tile maximum, exponentials, tile sum.
+    if (J == nt - 1 && (n % B) != 0) {
 #pragma unroll
       for (int kb = 0; kb < B / 32; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m = mx * c;
-      float lsum = 0.f;
-      u32x4* Eu = E + e_unit<B>(head, I, J, nt, wave, 0) * 64 + lane;
+        for (int r = 0; r < 16; ++r)
+          if (J * B + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3) >= n) acc[kb][r] = -INFINITY;
+    }
+    float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < B / 32; ++kb) {
+    for (int kb = 0; kb < B / 32; ++kb)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          uint32_t pk[4];
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m = mx * c;
+    float lsum = 0.f;
+    u32x4* Eu = E + e_unit<B>(head, I, J, nt, wave, 0) * 64 + lane;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 8 * half + 2 * i;
-            pk[i] = pack_bf16x2(fast_exp2(__builtin_fmaf(acc[kb][r], c, -m)),
-                                fast_exp2(__builtin_fmaf(acc[kb][r + 1], c, -m)));
-            lsum = add_bf16x2(pk[i], lsum);
-          }
-          Eu[(kb * 2 + half) * 64] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+    for (int kb = 0; kb < B / 32; ++kb) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 8 * half + 2 * i;
+          pk[i] = pack_bf16x2(fast_exp2(__builtin_fmaf(acc[kb][r], c, -m)),
+                              fast_exp2(__builtin_fmaf(acc[kb][r + 1], c, -m)));
+          lsum = add_bf16x2(pk[i], lsum);
         }
-        acc[kb] = f32x16{};
+        // E is read once, by the value product: stream it past the caches
+        __builtin_nontemporal_store(u32x4{pk[0], pk[1], pk[2], pk[3]},
+                                    &Eu[(kb * 2 + half) * 64]);
       }
-      lsum += __shfl_xor(lsum, 32);
-      if (qok && h == 0) {
-        const size_t sidx = ((size_t)head * nt + J) * n + q;
-        mst[sidx] = m;
-        lst[sidx] = lsum;
-      }
+    }
+    lsum += __shfl_xor(lsum, 32);
+    if (qok && h == 0) {
+      const size_t sidx = ((size_t)head * nt + J) * n + q;
+      mst[sidx] = m;
+      lst[sidx] = lsum;
     }
   }
   wait_vm<0>();  // no copy into LDS may outlive the workgroup
@@ -258,7 +277,6 @@ __global__ __launch_bounds__(B * 2) void sc_value_product(const bf16* __restrict
   const int head = tile / (nt * NCT);
   const int rem = tile - head * nt * NCT;
   const int I = rem / NCT, ct = rem - (rem / NCT) * NCT;
-  const bf16* Vh = V + (size_t)head * n * D + ct * BD;
   const int q = I * B + wave * 32 + li;
   const bool qok = q < n;
 
@@ -275,16 +293,28 @@ __global__ __launch_bounds__(B * 2) void sc_value_product(const bf16* __restrict
   if (ct == 0 && lse != nullptr && qok && h == 0)
     lse[(size_t)head * n + q] = (m + __log2f(l)) * kLn2;
 
-  int vrow[LI], vcol[LI];
+  // Buffer resources: V of this head (keys past n read as zeros, where E
+  // is 0 too), the E units of query tile I ((J, wave, kb, half) order, 1 KiB
+  // each) and the statistics of this head.  Per-lane byte offsets are
+  // constant; the panel's own offset is scalar.
+  const rsrc_t rv = buffer_rsrc(V + (size_t)head * n * D, (uint32_t)n * (D * 2));
+  const rsrc_t re = buffer_rsrc(E + e_unit<B>(head, I, 0, nt, 0, 0) * 64,
+                                (uint32_t)nt * (NW * PPT * 2 * 1024));
+  const rsrc_t rm = buffer_rsrc(mst + (size_t)head * nt * n, (uint32_t)(nt * n) * 4u);
+  uint32_t voff[LI];
 #pragma unroll
   for (int it = 0; it < LI; ++it) {
     const int p = (wave * LI + it) * 64 + lane;
-    const int row = p / CPR, phys = p % CPR;
-    vrow[it] = row;
-    vcol[it] = (phys ^ vtr_swizzle<BD * 2>(row)) * 8;
+    voff[it] = (uint32_t)((p / CPR) * D * 2 + ct * BD * 2 +
+                          tile_copy_chunk<BD, vtr_swizzle<BD * 2>>(p) * 16);
   }
-  // E units of this wave: (J, wave, kb, half) order
-  const u32x4* Ew = E + e_unit<B>(head, I, 0, nt, wave, 0) * 64 + lane;
+  const uint32_t eoff = (uint32_t)((wave * PPT * 2) * 1024 + lane * 16);
+  // LDS destinations: this wave's part of slot 0 of each ring (scalar)
+  const uint32_t wu = (uint32_t)__builtin_amdgcn_readfirstlane(wave);
+  const uint32_t vl = lds_addr(&Vp[0][0]) + wu * (LI * 1024u);
+  const uint32_t el = lds_addr(&Ep[0][0]) + wu * 2048u;
+  const uint32_t ml = lds_addr(&Ms[0][0]) + wu * 256u;
+  const uint32_t moff = (uint32_t)(qok ? q : 0) * 4u;
   const int T = nt * PPT;
   // Copy panel t's V, this wave's two E units and each lane's m_IJ into
   // slot t % R.  Panels past the end copy the last one again (same number
@@ -292,15 +322,15 @@ __global__ __launch_bounds__(B * 2) void sc_value_product(const bf16* __restrict
   auto issue = [&](int t) {
     t = min(t, T - 1);
     const int J = t / PPT, kb = t - (t / PPT) * PPT, slot = t % R;
+    const uint32_t sv = (uint32_t)(J * B + kb * KP) * (D * 2);
 #pragma unroll
-    for (int it = 0; it < LI; ++it) {
-      const int key = min(J * B + kb * KP + vrow[it], n - 1);  // E is 0 for keys past n
-      dma16(Vh + (size_t)key * D + vcol[it], &Vp[slot][(wave * LI + it) * 64 * 8]);
-    }
-    const u32x4* p = Ew + ((size_t)J * NW * PPT * 2 + kb * 2) * 64;
-    dma16(p, &Ep[slot][(wave * 2 + 0) * 64 * 8]);
-    dma16(p + 64, &Ep[slot][(wave * 2 + 1) * 64 * 8]);
-    dma4(mr + (size_t)J * n, &Ms[slot][wave * 64]);
+    for (int it = 0; it < LI; ++it)
+      dma16_buf_at(rv, voff[it], sv, vl + slot * (KP * BD * 2) + it * 1024u);
+    // E is read once: non-temporal, so V stays cached for the other tiles
+    const uint32_t se = (uint32_t)(J * NW * PPT * 2 + kb * 2) * 1024u;
+    dma16_buf_nt_at(re, eoff, se, el + slot * (NW * 2 * 1024));
+    dma16_buf_nt_at(re, eoff + 1024u, se, el + slot * (NW * 2 * 1024) + 1024u);
+    dma4_buf_at(rm, moff, (uint32_t)(J * n) * 4u, ml + slot * (NW * 64 * 4));
   };
 
   f32x16 out[BD / 32];
@@ -402,16 +432,17 @@ namespace {
 
 // On-chip elements per workgroup, each counted once whatever its width, and
 // every pipeline slot counted: the larger of the two products' footprints.
-// Scores: the b x b score tile and R slots each of the K and Q panels (LDS,
-// b x KP each).  Value product: the b x bd output tile and R slots each of
-// the V panel (KP x bd) and the E panel (b x KP), both in LDS; the per-row
-// statistics (b values per slot) are not counted.  R = 3 for b = 128, 2 for
-// b = 64.
+// Scores: the b x b score tile and R_s = 2 slots each of the K and Q panels
+// (LDS, b x KS each, KS = 64 at b = 128, 32 at b = 64).  Value product: the b x bd output tile and R_v slots
+// each of the V panel (KP x bd) and the E panel (b x KP), both in LDS,
+// R_v = 4 for b = 128, 2 for b = 64; the per-row statistics (b values per
+// slot) are not counted.
 int64_t footprint(int64_t b, int64_t d) {
   const int64_t bd = b < d ? b : d;
-  const int64_t r = b >= 128 ? 3 : 2;  // ScDist<b>::R
-  const int64_t s = b * b + 2 * r * b * KP;
-  const int64_t v = b * bd + r * (KP * bd + b * KP);
+  const int64_t ks = b >= 128 ? 64 : 32;  // ScScoreCfg<b>::KS (R_s = 2)
+  const int64_t rv = b >= 128 ? 4 : 2;    // ScDist<b>::R
+  const int64_t s = b * b + 2 * 2 * b * ks;
+  const int64_t v = b * bd + rv * (KP * bd + b * KP);
   return s > v ? s : v;
 }
 
@@ -429,6 +460,11 @@ template <int D, int B>
 hipError_t launch(const void* Q, const void* K, const void* V, float* O, float* lse, int64_t bh,
                   int64_t n, float scale, void* ws, hipStream_t stream) {
   const ScLayout L = sc_layout(bh, n, B);
+  // the kernels address one head's E tiles and statistics with 32-bit
+  // buffer offsets
+  if ((uint64_t)L.nt * B * B * 2 >= (uint64_t(1) << 32) ||
+      (uint64_t)L.nt * n * 4 >= (uint64_t(1) << 32))
+    return hipErrorInvalidValue;
   char* base = static_cast<char*>(ws);
   u32x4* E = reinterpret_cast<u32x4*>(base + L.e_off);
   float* mst = reinterpret_cast<float*>(base + L.m_off);

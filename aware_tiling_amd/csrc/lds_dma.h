@@ -53,6 +53,14 @@ __device__ __forceinline__ void dma4(const void* gsrc, void* lds_wave_base) {
       : "v"(gsrc), "s"(lds)
       : "memory", "m0");
 }
+// LDS byte address of a pointer into a __shared__ array.  Kernels take it
+// once per ring (a constant) and add slot and wave offsets as scalars, which
+// spares every copy the generic-to-LDS pointer conversion and its null test.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(
+      reinterpret_cast<const char*>(p));
+}
+
 // Buffer resource (V#) for `bytes` bytes from `base`: raw addressing, no
 // stride, the range check against `bytes` turning every read past the end
 // into zeros.  Built with scalar instructions from a wave-uniform base.
@@ -82,14 +90,55 @@ __device__ __forceinline__ void dma16_buf(rsrc_t rs, uint32_t voff, uint32_t sof
       : "v"(voff), "s"(rs), "s"(soff), "s"(lds)
       : "memory", "m0");
 }
+// Copies through a buffer resource with the LDS destination given as a
+// wave-uniform LDS byte address (see lds_addr): 16 bytes per lane, the same
+// with the nt (non-temporal) policy for data read once (the lines are marked
+// for early eviction, so such a stream does not push reused operands out of
+// the caches), and 4 bytes per lane (lane l's 4 bytes at lds + 4 l).
+__device__ __forceinline__ void dma16_buf_at(rsrc_t rs, uint32_t voff, uint32_t soff,
+                                             uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, %2 offen lds"
+      :
+      : "v"(voff), "s"(rs), "s"(soff), "s"(lds)
+      : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_buf_nt_at(rsrc_t rs, uint32_t voff, uint32_t soff,
+                                                uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, %2 offen nt lds"
+      :
+      : "v"(voff), "s"(rs), "s"(soff), "s"(lds)
+      : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_buf_at(rsrc_t rs, uint32_t voff, uint32_t soff,
+                                            uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %0, %1, %2 offen lds"
+      :
+      : "v"(voff), "s"(rs), "s"(soff), "s"(lds)
+      : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
-// Workgroup barrier without a memory fence: every lane has already waited
-// for its own copies with an exact vmcnt, and later copies stay in flight
-// across it (a fence would wait for them).  The empty asm statements keep
-// the compiler from moving memory accesses across the barrier.
+// Workgroup barrier that frees a ring slot for the next copies, without a
+// full memory fence: every lane has already waited for its own copies with
+// an exact vmcnt, and later copies stay in flight across it (a fence would
+// wait for them).  It does wait for this wave's own LDS reads
+// (lgkmcnt(0)): the compiler may issue a step's last reads before the
+// barrier and consume them after it, and s_barrier alone does not wait for
+// them, so another wave could start a copy into the slot they still read.
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
 __device__ __forceinline__ void slot_barrier() {
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unchanged
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }

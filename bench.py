@@ -28,8 +28,11 @@ Reported (one JSON line on stdout):
   cpu_baseline the float64 oracle on the host cores, on a bounded sample of
                rows of the same workload (about 15 s of CPU work);
   secondary    the small-cache square-tile path (batch 1 x 8 heads, N 4096,
-               d 256) and the backward (batch 2 x 16 heads, N 4096, d 128)
-               timed the same way, when built (not part of `value`).
+               d 256), the backward (batch 2 x 16 heads, N 4096, d 128) and
+               the other paths, when built (not part of `value`): each leg
+               warmed up for 0.3 s, then K back-to-back calls between one
+               pair of HIP events (per-call event pairs would add about
+               10 us of device time to each sub-millisecond call).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-secondary]
                        [--legs a,b] [--secondary-only]
@@ -59,6 +62,7 @@ HEADLINE = "fwd_bf16_b1h32_n16384_d128_qx4"
 METRIC = "attention fwd TFLOP/s (4N²d/head) and % of bf16 MFMA peak; HBM GB/s at 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_fwd_n16384_d128.json")
 COPY_BYTES = 1 << 30  # counter calibration: bytes read and written per copy
+SECONDARY_WARM_S = 0.3  # warm-up of each secondary leg before it is timed
 KERNEL_SOURCES = ["aware_tiling_amd/csrc/fwd_fused.hip", "aware_tiling_amd/csrc/device_common.h"]
 
 
@@ -70,15 +74,39 @@ def kernel_digest(paths=KERNEL_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
-def time_launches(fn, steps: int, warmup: int):
+def time_launches(fn, steps: int, warmup: int, batch: bool = False, warm_s: float = 0.0):
     """Mean ms per launch from HIP events on the current stream, and the
-    wall-clock ms per step between synchronisations."""
+    wall-clock ms per step between synchronisations.
+
+    Default: every launch bracketed by its own pair of events (the per-launch
+    distribution).  batch=True: one pair of events around the `steps`
+    back-to-back launches, for sub-millisecond paths, where an event pair
+    between launches costs about 10 us of device time.  warm_s: keep warming
+    up for that many seconds after the `warmup` launches (the clocks of an
+    idle GPU ramp up over the first tens of milliseconds of work)."""
     import torch
 
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    if warm_s > 0:
+        t_end = time.perf_counter() + warm_s
+        while time.perf_counter() < t_end:
+            for _ in range(8):
+                fn()
+            torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    if batch:
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        s.record(stream)
+        for _ in range(steps):
+            fn()
+        e.record(stream)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+        ms = s.elapsed_time(e) / steps
+        return ms, wall_ms, [ms]
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t0 = time.perf_counter()
@@ -571,7 +599,8 @@ def smallcache_sweep(args, at, torch, dev):
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
         print(f"[bench] small-cache tile b={b} M={m_elems}", file=sys.stderr, flush=True)
         ms, _, _ = time_launches(lambda: at.attn_fwd_smallcache(
-            q, k, v, m_elems, w.scale, out=o, lse=lse, workspace=ws), args.steps, args.warmup)
+            q, k, v, m_elems, w.scale, out=o, lse=lse, workspace=ws), args.steps, args.warmup,
+            batch=True, warm_s=SECONDARY_WARM_S)
         # per launch, bytes: every (query tile, key tile) reads a b x d panel of Q
         # and of K; every (query tile, b-wide output column block) reads a
         # b x N panel of E and an N x b panel of V -- 4 N^2 d / b bf16 elements
@@ -603,9 +632,9 @@ def secondary(args, at, torch, dev):
         need = int(at.lib().attn_fwd_smallcache_workspace_size(w.bh, w.n, w.d, m_elems))
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
         ms_sc, _, _ = time_launches(lambda: at.attn_fwd_smallcache(
-            q, k, v, m_elems, w.scale, out=o, lse=lse, workspace=ws), args.steps, args.warmup)
+            q, k, v, m_elems, w.scale, out=o, lse=lse, workspace=ws), args.steps, args.warmup, batch=True, warm_s=SECONDARY_WARM_S)
         ms_fu, _, _ = time_launches(lambda: at.attn_fwd(q, k, v, w.scale, out=o, lse=lse),
-                                    args.steps, args.warmup)
+                                    args.steps, args.warmup, batch=True, warm_s=SECONDARY_WARM_S)
         b = at.smallcache_tile(w.d, m_elems)
         res["smallcache"] = {"workload": w.name, "m_elems": m_elems, "tile_b": b,
                              "ms": round(ms_sc, 4),
@@ -620,9 +649,9 @@ def secondary(args, at, torch, dev):
             need = int(at.lib().attn_fwd_smallcache_workspace_size(w.bh, w.n, w.d, m_same))
             ws2 = torch.empty(need, dtype=torch.uint8, device=dev)
             ms_fb, _, _ = time_launches(lambda: at.attn_fwd_budget(
-                q, k, v, m_same, w.scale, out=o, lse=lse), args.steps, args.warmup)
+                q, k, v, m_same, w.scale, out=o, lse=lse), args.steps, args.warmup, batch=True, warm_s=SECONDARY_WARM_S)
             ms_sb, _, _ = time_launches(lambda: at.attn_fwd_smallcache(
-                q, k, v, m_same, w.scale, out=o, lse=lse, workspace=ws2), args.steps, args.warmup)
+                q, k, v, m_same, w.scale, out=o, lse=lse, workspace=ws2), args.steps, args.warmup, batch=True, warm_s=SECONDARY_WARM_S)
             res["smallcache"]["same_budget"] = {
                 "m_elems": m_same,
                 "fused_query_rows": 32, "fused_ms": round(ms_fb, 4),
@@ -650,7 +679,7 @@ def secondary(args, at, torch, dev):
         need = int(at.lib().attn_bwd_workspace_size(w.bh, w.n, w.d))
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         ms, _, _ = time_launches(lambda: at.attn_bwd(q, k, v, o, do, lse, w.scale, workspace=ws,
-                                                     grads=grads), args.steps, args.warmup)
+                                                     grads=grads), args.steps, args.warmup, batch=True, warm_s=SECONDARY_WARM_S)
         fl = 10.0 * w.n * w.n * w.d * w.bh  # 2 products recomputed-free count: 5 GEMMs
         res["backward"] = {"workload": w.name, "ms": round(ms, 4),
                            "tflops_at_10N2d": round(fl / (ms * 1e-3) / 1e12, 2)}
@@ -669,7 +698,7 @@ def secondary(args, at, torch, dev):
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
         ms, _, _ = time_launches(lambda: at.attn_bwd_smallcache(
             q, k, v, o, do, lse, m_sc, w.scale, workspace=ws, grads=grads),
-            args.steps, args.warmup)
+            args.steps, args.warmup, batch=True, warm_s=SECONDARY_WARM_S)
         npad = -(-w.n // b) * b
         fl = 10.0 * w.n * w.n * w.d * w.bh
         # n x n traffic of the schedule: P^T and dS^T written once, P^T read
@@ -697,9 +726,9 @@ def secondary(args, at, torch, dev):
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         ms, _, _ = time_launches(lambda: at.attn_fwd_blocksparse(q, k, v, mask, w.scale, out=o,
                                                                  lse=lse, workspace=ws),
-                                 args.steps, args.warmup)
+                                 args.steps, args.warmup, batch=True, warm_s=SECONDARY_WARM_S)
         ms_dense, _, _ = time_launches(lambda: at.attn_fwd(q, k, v, w.scale, out=o, lse=lse),
-                                       args.steps, args.warmup)
+                                       args.steps, args.warmup, batch=True, warm_s=SECONDARY_WARM_S)
         # kept query-key pairs: per kept block, its valid queries x valid keys
         sizes = torch.full((nb,), at.SPARSE_BLOCK, dtype=torch.float64)
         sizes[-1] = w.n - (nb - 1) * at.SPARSE_BLOCK
@@ -725,7 +754,7 @@ def secondary(args, at, torch, dev):
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         ms, _, _ = time_launches(lambda: at.attn_fwd_splitk(q, k, v, 0, w.scale, out=o, lse=lse,
                                                             workspace=ws),
-                                 args.steps, args.warmup)
+                                 args.steps, args.warmup, batch=True, warm_s=SECONDARY_WARM_S)
         # compulsory bytes: Q, K, V in bf16; O and lse in fp32
         byts = w.bh * (nq * w.d * 2 + 2 * w.n * w.d * 2 + nq * w.d * 4 + nq * 4)
         res[w.kind + "_" + name.split("_")[0]] = {

@@ -228,14 +228,15 @@ def test_library_links_no_oracle(lib):
 
 
 def test_smallcache_tile_selection(lib):
-    # footprint(b) = max(b^2 + 2*R*b*32, b*bd + R*(32*bd + b*32)), bd = min(b, d),
-    # R = 3 slots for b = 128 and 2 for b = 64: the score tile plus R slots of
-    # the Q and K panels, or the output tile plus R slots of the V and E panels
-    assert lib.attn_smallcache_onchip_elems(128) == 40960
+    # footprint(b) = max(b^2 + 2*2*b*ks, b*bd + R*(32*bd + b*32)), bd = min(b, d):
+    # the score tile plus two slots of the Q and K panels (ks = 64 columns for
+    # b = 128, 32 for b = 64), or the output tile plus R slots of the V and E
+    # panels (R = 4 for b = 128, 2 for b = 64)
+    assert lib.attn_smallcache_onchip_elems(128) == 128 * 128 + 4 * 128 * 64 == 49152
     assert lib.attn_smallcache_onchip_elems(64) == 12288
     assert lib.attn_smallcache_tile(256, 49152) == 128
-    assert lib.attn_smallcache_tile(256, 40960) == 128
-    assert lib.attn_smallcache_tile(256, 40959) == 64
+    assert lib.attn_smallcache_tile(256, 49151) == 64
+    assert lib.attn_smallcache_tile(256, 40960) == 64
     assert lib.attn_smallcache_tile(256, 12288) == 64
     assert lib.attn_smallcache_tile(256, 12287) == 0
     assert lib.attn_smallcache_tile(128, 16000) == 64  # b=128 would not be below d^2
