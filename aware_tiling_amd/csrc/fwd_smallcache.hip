@@ -82,8 +82,9 @@ __device__ __forceinline__ size_t e_unit(int head, int I, int J, int nt, int wav
 
 }  // namespace
 
-// Panel pipelines: every operand panel is copied global -> LDS DIST panels
-// ahead of the one being multiplied, into a ring of R = DIST + 1 slots.  The
+// Panel pipelines: operand panels are copied global -> LDS ahead of the ones
+// being multiplied, into a ring of R slots (DIST = R - 1 panels ahead for the
+// scores; two at a time, two ahead, for the value product at R = 4).  The
 // on-chip footprint is then b^2 + 2 R_s b KS for the scores (K and Q panels,
 // b x KS each) and b bd + R_v (KP bd + b KP) for the value product (V panels
 // KP x bd, E panels b x KP).
@@ -98,8 +99,7 @@ struct ScScoreCfg {
 };
 template <int B>
 struct ScDist {
-  static constexpr int R = B >= 128 ? 4 : 2;
-  static constexpr int DIST = R - 1;
+  static constexpr int R = B >= 128 ? 4 : 2;  // value-product ring slots
 };
 
 // ---------------------------------------------------------------------------
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(B * 2) void sc_value_product(const bf16* __restrict
   constexpr int PCH = KP * CPR;      // chunks per V panel (KP keys)
   constexpr int LI = PCH / NT;
   constexpr int PPT = B / KP;        // panels per key tile
-  constexpr int DIST = ScDist<B>::DIST, R = ScDist<B>::R;
+  constexpr int R = ScDist<B>::R;
   constexpr int OPS = LI + 2 + 1;    // copies per lane per panel: V, E (2 units), m_IJ
   static_assert(PCH % NT == 0, "panel chunks must split evenly over the lanes");
   static_assert(KP == 32 && B / 32 == PPT, "one panel is one 32-key block of the score tile");
@@ -354,6 +354,12 @@ __global__ __launch_bounds__(B * 2) void sc_value_product(const bf16* __restrict
   }
   const uint32_t e_off = (uint32_t)(((wave * 2) * 64 + lane) * 8) * 2u;
 
+  // PPS panels per barrier: two with a four-slot ring (half the barriers;
+  // the next two panels' copies in flight while two are multiplied).
+  constexpr int PPS = R >= 4 ? 2 : 1;
+  constexpr int AHEAD = R - PPS;  // panels issued ahead of the ones in use
+  static_assert(PPT % PPS == 0, "barrier groups must not straddle key tiles");
+
   // Key tile J: A_J = V_J^T E_IJ^T over its PPT panels, then out += f_IJ A_J.
   // E enters the MFMA as stored (bf16); the row factor is applied in fp32
   // once per tile.  P = (J PPT) % R is the ring slot of the tile's first
@@ -366,12 +372,15 @@ __global__ __launch_bounds__(B * 2) void sc_value_product(const bf16* __restrict
     for (int kb = 0; kb < PPT; ++kb) {
       const int t = J * PPT + kb;
       const int slot_rt = (P + kb) % R;  // constant after unrolling
-      // panel t's copies are complete once at most the later DIST - 1
-      // panels' copies are outstanding (vector-memory operations complete
-      // in issue order)
-      wait_vm<(DIST - 1) * OPS>();
-      slot_barrier();  // every lane's part of panel t; slot (t - 1) % R is free
-      issue(t + DIST);
+      if (kb % PPS == 0) {
+        // panels t .. t + PPS - 1 are complete once at most the later
+        // AHEAD - PPS panels' copies are outstanding (loads complete in
+        // issue order; the only store before this point is older)
+        wait_vm<(AHEAD - PPS) * OPS>();
+        slot_barrier();  // every lane's part of them; the previous PPS slots are free
+#pragma unroll
+        for (int p = 0; p < PPS; ++p) issue(t + AHEAD + p);
+      }
       if (kb == 0) f = qok ? fast_exp2(Ms[slot_rt][wave * 64 + lane] - m) * inv : 0.f;  // f_IJ
       const char* Vs = reinterpret_cast<const char*>(Vp[slot_rt]);
       const char* Es = reinterpret_cast<const char*>(Ep[slot_rt]);
@@ -398,7 +407,7 @@ __global__ __launch_bounds__(B * 2) void sc_value_product(const bf16* __restrict
   };
 
 #pragma unroll
-  for (int s = 0; s < DIST; ++s) issue(s);
+  for (int s = 0; s < AHEAD; ++s) issue(s);
   for (int J = 0; J < nt; ++J) {
     const int P = (J * PPT) % R;
     if (P == 0) {

@@ -370,17 +370,21 @@ def summarize_smallcache_sweep(pmc_dir: str, timing_path: str, out_path: str):
     square-tile schedule's exact panel count and the page's N^2 d / sqrt(M)
     model.  Expects <dir>/scread_, scfetch_, scwrite_, scmfma_, copyread_,
     copyfetch_ and copywrite_ counter_collection.csv."""
+    def per_kernel(fname, counter):
+        # mean per dispatch of each kernel: {(b, is_value_product): mean}
+        return counter_means(os.path.join(pmc_dir, fname), counter,
+                             lambda n: (smallcache_sweep_key(n), "value" in n)
+                             if smallcache_sweep_key(n) else None)
+
     def sums(fname, counter):
-        # mean per dispatch of each kernel, summed over the two kernels of a b
-        per = counter_means(os.path.join(pmc_dir, fname), counter,
-                            lambda n: (smallcache_sweep_key(n), "value" in n)
-                            if smallcache_sweep_key(n) else None)
+        # summed over the two kernels of a b
         out = {}
-        for (b, _), v in per.items():
+        for (b, _), v in per_kernel(fname, counter).items():
             out[b] = out.get(b, 0.0) + v
         return out
 
     cu = sums("scread_counter_collection.csv", "TCC_READ_SECTORS_sum")
+    cu_k = per_kernel("scread_counter_collection.csv", "TCC_READ_SECTORS_sum")
     fe = sums("scfetch_counter_collection.csv", "FETCH_SIZE")
     wr = sums("scwrite_counter_collection.csv", "WRITE_SIZE")
     busy = mfma_busy(pmc_dir, "scmfma_counter_collection.csv", smallcache_sweep_key)
@@ -404,6 +408,19 @@ def summarize_smallcache_sweep(pmc_dir: str, timing_path: str, out_path: str):
             f"{fe.get(b, float('nan')) * fe_unit / 1e9:.3f} GB | "
             f"{wr.get(b, float('nan')) * wr_unit / 1e9:.3f} GB | {r['exp_matrix_bytes'] / 1e9:.3f} GB | "
             f"{fmt_busy(busy.get(b))} |")
+    lines += ["", "Per kernel, CU->L2 read bytes against its half of the schedule "
+              "(2 N^2 d / b bf16 elements per head each: the scores read a b x d panel of Q "
+              "and of K per tile, the value product a b x N panel of E and an N x b panel "
+              "of V per output tile):", "",
+              "| b | sc_scores_exp | its schedule | ratio | sc_value_product | its schedule | "
+              "ratio |", "|" + "---|" * 7]
+    for r in rows:
+        b = r["tile_b"]
+        half = r["sched_read_bytes"] / 2
+        sc = cu_k.get((b, False), float("nan")) * rd_unit
+        vp = cu_k.get((b, True), float("nan")) * rd_unit
+        lines.append(f"| {b} | {sc / 1e9:.3f} GB | {half / 1e9:.3f} GB | {sc / half:.3f} | "
+                     f"{vp / 1e9:.3f} GB | {half / 1e9:.3f} GB | {vp / half:.3f} |")
     text = "\n".join(lines) + "\n"
     text += (f"\nCounter scaling: one TCC_READ_SECTORS unit = {rd_unit:.2f} bytes, one FETCH_SIZE "
              f"unit = {fe_unit:.1f} bytes, one WRITE_SIZE unit = {wr_unit:.1f} bytes (a plain "
