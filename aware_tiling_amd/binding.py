@@ -51,6 +51,7 @@ SIGNATURES = {
     "attn_smallcache_tile": (_i64, [_i64, _i64]),
     "attn_smallcache_onchip_elems": (_i64, [_i64]),
     "attn_bwd_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "attn_bwd_onchip_elems": (_i64, [_i64]),
     "attn_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _int,
                         _vp, _sz, _vp]),
     "attn_bwd_smallcache_tile": (_i64, [_i64, _i64]),
@@ -467,6 +468,12 @@ def attn_bwd_smallcache(q, k, v, o, do, lse, m_elems: int, scale: float | None =
 
 def bwd_smallcache_tile(d: int, m_elems: int) -> int:
     return int(lib().attn_bwd_smallcache_tile(d, m_elems))
+
+
+def bwd_onchip_elems(d: int) -> int:
+    """On-chip elements of one attn_bwd workgroup (the larger kernel; 0 =
+    unsupported d)."""
+    return int(lib().attn_bwd_onchip_elems(d))
 
 
 def fwd_onchip_elems(d: int, dtype: torch.dtype = torch.bfloat16) -> int:

@@ -281,6 +281,8 @@ size_t attn_bwd_workspace_size(int64_t bh, int64_t n, int64_t d) {
   return at::bwd_workspace_bytes(bh, n, d);
 }
 
+int64_t attn_bwd_onchip_elems(int64_t d) { return at::bwd_onchip_elems(d); }
+
 attn_status attn_bwd(const void* Q, const void* K, const void* V, const float* O,
                      const void* dO, const float* lse, float* dQ, float* dK, float* dV,
                      int64_t bh, int64_t n, int64_t d, float scale, attn_dtype dtype,

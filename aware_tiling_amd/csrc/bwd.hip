@@ -30,6 +30,7 @@
 //     dQ^T += K^T dS^T with K^T read transposed.  Recomputing S and dP here
 //     costs 4 N^2 d more flops than accumulating dQ with atomics, and keeps
 //     the result deterministic.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -145,6 +146,12 @@ struct DkdvCfg {
   static constexpr int WAVE_CHUNKS = CHUNKS / NW;
   static constexpr int INSTS = WAVE_CHUNKS / 64;
   static constexpr int TILE = BQ * D;
+  // on-chip elements of one workgroup, each counted once whatever its width
+  // and one stage of each streamed tile (as for the forward): the K and V
+  // rows, the dK^T and dV^T accumulators, a Q and a dO tile, their lse and D
+  // values, and the S/P and dP/dS tiles of all waves
+  static constexpr int64_t ONCHIP =
+      4 * (int64_t)BKV * D + 2 * (int64_t)BQ * D + 2 * BQ + 2 * (int64_t)BKV * BQ;
   static_assert(CHUNKS % (NW * 64) == 0, "tile must split into whole wave loads");
 };
 
@@ -407,6 +414,10 @@ struct DqCfg {
   static constexpr int WAVE_CHUNKS = CHUNKS / NW;
   static constexpr int INSTS = WAVE_CHUNKS / 64;
   static constexpr int TILE = BC * D;
+  // on-chip elements (as DkdvCfg): the Q and dO rows, the dQ^T accumulators,
+  // the lse and D values, a K and a V tile, and the S^T and dP^T tiles
+  static constexpr int64_t ONCHIP =
+      3 * (int64_t)BQB * D + 2 * BQB + 2 * (int64_t)BC * D + 2 * (int64_t)BQB * BC;
   static_assert(CHUNKS % (NW * 64) == 0, "tile must split into whole wave loads");
 };
 
@@ -647,6 +658,14 @@ hipError_t launch_bwd_preprocess(const float* O, const void* dO, float* Dout, in
 }
 
 bool bwd_supported(int64_t d) { return d == 64 || d == 128; }
+
+int64_t bwd_onchip_elems(int64_t d) {
+  switch (d) {
+    case 64: return std::max(DkdvCfg<64, 8>::ONCHIP, DqCfg<64, 8, 64>::ONCHIP);
+    case 128: return std::max(DkdvCfg<128, 8>::ONCHIP, DqCfg<128, 8, 64>::ONCHIP);
+    default: return 0;
+  }
+}
 
 size_t bwd_workspace_bytes(int64_t bh, int64_t n, int64_t) {
   return 2 * (((size_t)bh * n * 4 + 255) & ~size_t(255));  // D, then lse log2(e)

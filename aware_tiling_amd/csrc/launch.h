@@ -87,6 +87,7 @@ hipError_t launch_fwd_smallcache_bf16(const void* Q, const void* K, const void* 
 
 // Backward.
 bool bwd_supported(int64_t d);
+int64_t bwd_onchip_elems(int64_t d);  // larger of the dK/dV and dQ kernels' footprints
 size_t bwd_workspace_bytes(int64_t bh, int64_t n, int64_t d);
 hipError_t launch_bwd_bf16(const void* Q, const void* K, const void* V, const float* O,
                            const void* dO, const float* lse, float* dQ, float* dK, float* dV,

@@ -37,7 +37,8 @@ Reported (one JSON line on stdout):
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-secondary]
                        [--legs a,b] [--secondary-only]
        python bench.py --calibrate-copy          (copy kernel for counter scaling)
-       python bench.py --summarize-counters DIR  (write the traffic summary)
+       python bench.py --profile-leg LEG [--calls C]  (one leg, for a counter run)
+       python bench.py --summarize-leg-counters DIR  (write the per-leg traffic summary)
        python bench.py --tile-sweep [--steps K]   (fused forward at B_r x B_c shapes)
        python bench.py --summarize-sweep DIR TIMING.jsonl OUT.md  (sweep table)
        python bench.py --smallcache-sweep [--steps K]   (square tiles at each b, d = 256)
@@ -60,15 +61,33 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
 HEADLINE = "fwd_bf16_b1h32_n16384_d128_qx4"
 METRIC = "attention fwd TFLOP/s (4N²d/head) and % of bf16 MFMA peak; HBM GB/s at 1 GPU"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_fwd_n16384_d128.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 COPY_BYTES = 1 << 30  # counter calibration: bytes read and written per copy
 SECONDARY_WARM_S = 0.3  # warm-up of each secondary leg before it is timed
-KERNEL_SOURCES = ["aware_tiling_amd/csrc/fwd_fused.hip", "aware_tiling_amd/csrc/device_common.h"]
+COMMON_SOURCES = ["aware_tiling_amd/csrc/device_common.h", "aware_tiling_amd/csrc/index_maps.h",
+                  "aware_tiling_amd/csrc/lds_dma.h"]
+# Per leg: the kernel sources its counter bytes are keyed by, and the kernel
+# name substrings that make up one call (the forward calls that produce a
+# backward leg's O and lse are not among them).
+LEGS = {
+    "headline": (["aware_tiling_amd/csrc/fwd_fused.hip"], ("fwd_fused_bf16",)),
+    "smallcache": (["aware_tiling_amd/csrc/fwd_smallcache.hip"],
+                   ("sc_scores_exp", "sc_value_product")),
+    "backward": (["aware_tiling_amd/csrc/bwd.hip"], ("bwd_preprocess", "bwd_dkdv3", "bwd_dq3")),
+    "smallcache_backward_d256": (["aware_tiling_amd/csrc/bwd_smallcache.hip",
+                                  "aware_tiling_amd/csrc/bwd.hip"], ("bwd_preprocess", "sb_")),
+    "smallcache_backward_d128": (["aware_tiling_amd/csrc/bwd_smallcache.hip",
+                                  "aware_tiling_amd/csrc/bwd.hip"], ("bwd_preprocess", "sb_")),
+}
+SMALLCACHE_M = 49152  # 3/4 of d^2 at d = 256: the small-cache regime M < d^2
+SMALLCACHE_BWD = {"smallcache_backward_d256": ("bwd_smallcache_bf16_b1h8_n4096_d256", 49152),
+                  "smallcache_backward_d128": ("bwd_bf16_b2h16_n4096_d128", 12288)}
 
 
-def kernel_digest(paths=KERNEL_SOURCES) -> str:
+def kernel_digest(leg: str = "headline") -> str:
+    """Digest of the sources a leg's kernels are built from."""
     h = hashlib.sha256()
-    for p in paths:
+    for p in COMMON_SOURCES + LEGS[leg][0]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -174,17 +193,123 @@ def measured_peaks(torch, dev, at=None) -> dict:
             "copy_gbps": round(2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9, 1), **loops}
 
 
-def traffic_for_launch():
-    """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current kernel source (else None)."""
+def leg_traffic(leg: str):
+    """The committed counter summary of one leg (HBM bytes per call, read and
+    written), if it was taken on the leg's current kernel sources, else None."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
+            t = json.load(f).get("legs", {}).get(leg)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_digest") != kernel_digest():
+    if not t or t.get("kernel_digest") != kernel_digest(leg):
         return None
-    return t.get("bytes_per_launch")
+    return t
+
+
+def traffic_for_launch():
+    """HBM bytes per launch of the headline kernel (None when stale)."""
+    t = leg_traffic("headline")
+    return t["bytes_per_call"] if t else None
+
+
+def leg_call(leg: str, at, torch, dev):
+    """Inputs in HBM and a no-argument call of one leg: (fn, workload, info)."""
+    from aware_tiling_amd.inputs import WORKLOADS, workload_inputs
+
+    if leg == "headline":
+        w = WORKLOADS[HEADLINE]
+        q, k, v = (t.to(dev) for t in workload_inputs(w))
+        o = torch.empty((w.bh, w.n, w.d), dtype=torch.float32, device=dev)
+        lse = torch.empty((w.bh, w.n), dtype=torch.float32, device=dev)
+        return (lambda: at.attn_fwd(q, k, v, w.scale, out=o, lse=lse)), w, {}
+    if leg == "smallcache":
+        w = WORKLOADS["smallcache_bf16_b1h8_n4096_d256"]
+        q, k, v = (t.to(dev) for t in workload_inputs(w))
+        o = torch.empty((w.bh, w.n, w.d), dtype=torch.float32, device=dev)
+        lse = torch.empty((w.bh, w.n), dtype=torch.float32, device=dev)
+        need = int(at.lib().attn_fwd_smallcache_workspace_size(w.bh, w.n, w.d, SMALLCACHE_M))
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        return (lambda: at.attn_fwd_smallcache(q, k, v, SMALLCACHE_M, w.scale, out=o, lse=lse,
+                                               workspace=ws)), w, {"m_elems": SMALLCACHE_M,
+                                                                   "q": q, "k": k, "v": v,
+                                                                   "o": o, "lse": lse}
+    if leg == "backward":
+        w = WORKLOADS["bwd_bf16_b2h16_n4096_d128"]
+        q, k, v, do = (t.to(dev) for t in workload_inputs(w))
+        o, lse = at.attn_fwd(q, k, v, w.scale)
+        grads = tuple(torch.empty((w.bh, w.n, w.d), dtype=torch.float32, device=dev)
+                      for _ in range(3))
+        need = int(at.lib().attn_bwd_workspace_size(w.bh, w.n, w.d))
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        return (lambda: at.attn_bwd(q, k, v, o, do, lse, w.scale, workspace=ws, grads=grads)), w, \
+            {"m_elems": at.bwd_onchip_elems(w.d)}
+    if leg in SMALLCACHE_BWD:
+        name, m_sc = SMALLCACHE_BWD[leg]
+        w = WORKLOADS[name]
+        q, k, v, do = (t.to(dev) for t in workload_inputs(w))
+        o, lse = at.attn_fwd(q, k, v, w.scale)
+        grads = tuple(torch.empty((w.bh, w.n, w.d), dtype=torch.float32, device=dev)
+                      for _ in range(3))
+        need = int(at.lib().attn_bwd_smallcache_workspace_size(w.bh, w.n, w.d, m_sc))
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        return (lambda: at.attn_bwd_smallcache(q, k, v, o, do, lse, m_sc, w.scale, workspace=ws,
+                                               grads=grads)), w, {"m_elems": m_sc}
+    raise SystemExit(f"unknown leg {leg}")
+
+
+def profile_leg(leg: str, calls: int, at, torch, dev):
+    """One warm call and `calls` more of one leg, for a counter run: the
+    counters of the leg's kernels summed over all dispatches, divided by
+    calls + 1, give its bytes per call."""
+    fn, w, _ = leg_call(leg, at, torch, dev)
+    torch.cuda.synchronize()
+    for _ in range(calls + 1):
+        fn()
+    torch.cuda.synchronize()
+    print(json.dumps({"leg": leg, "workload": w.name, "calls": calls + 1}), flush=True)
+
+
+def summarize_leg_counters(pmc_dir: str, out_path: str = TRAFFIC_FILE):
+    """HBM bytes per call of each profiled leg from rocprofv3 --pmc CSVs:
+    <dir>/<leg>_fetch_counter_collection.csv and <leg>_write_..., taken on
+    `--profile-leg <leg> --calls C`, and copyfetch_ / copywrite_ taken on
+    `--calibrate-copy`.  Each counter (KiB per dispatch) is scaled by what it
+    reads for a plain copy of COPY_BYTES."""
+    import csv
+
+    def total(fname, counter, subs):
+        tot, disp = 0.0, 0
+        with open(os.path.join(pmc_dir, fname)) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter and any(x in r["Kernel_Name"] for x in subs):
+                    tot += float(r["Counter_Value"])
+                    disp += 1
+        return tot, disp
+
+    cf = copy_counter(os.path.join(pmc_dir, "copyfetch_counter_collection.csv"), "FETCH_SIZE")
+    cw = copy_counter(os.path.join(pmc_dir, "copywrite_counter_collection.csv"), "WRITE_SIZE")
+    rf, rw = COPY_BYTES / cf, COPY_BYTES / cw  # bytes per counter unit
+    legs = {}
+    for leg, (_, subs) in LEGS.items():
+        fpath = os.path.join(pmc_dir, f"{leg}_fetch_counter_collection.csv")
+        if not os.path.exists(fpath):
+            continue
+        with open(os.path.join(pmc_dir, f"{leg}_calls.json")) as f:
+            calls = [json.loads(x) for x in f if x.startswith("{")][-1]["calls"]
+        fe, nf = total(f"{leg}_fetch_counter_collection.csv", "FETCH_SIZE", subs)
+        wr, nw = total(f"{leg}_write_counter_collection.csv", "WRITE_SIZE", subs)
+        legs[leg] = {"kernel_digest": kernel_digest(leg), "calls": calls,
+                     "dispatches": [nf, nw],
+                     "read_bytes_per_call": round(fe * rf / calls),
+                     "write_bytes_per_call": round(wr * rw / calls),
+                     "bytes_per_call": round((fe * rf + wr * rw) / calls)}
+    summary = {"copy_calibration": {"copy_bytes": COPY_BYTES, "fetch_size_kib": cf,
+                                    "write_size_kib": cw, "bytes_per_fetch_unit": rf,
+                                    "bytes_per_write_unit": rw},
+               "legs": legs}
+    with open(out_path, "w") as f:
+        json.dump(summary, f, indent=1)
+    print(json.dumps(summary))
 
 
 def cpu_baseline(w, cpu_inputs, target_s: float = 15.0):
@@ -218,46 +343,6 @@ def cpu_baseline(w, cpu_inputs, target_s: float = 15.0):
                       f"{dt:.1f} s; TFLOP/s at 4*N*d flops per query row",
             "seconds": round(dt, 2),
             "full_workload_seconds_est": round(dt * w.n * w.bh / (heads * nrows), 1)}
-
-
-def summarize_counters(pmc_dir: str, out_path: str = TRAFFIC_FILE):
-    """Turn rocprofv3 --pmc CSVs into the traffic summary bench.py reports.
-
-    Expects <dir>/fetch_counter_collection.csv and write_..., taken on a
-    bench run, and copyfetch_/copywrite_ taken on `--calibrate-copy`.  Each
-    counter (KiB per dispatch) is scaled by what it reads for a plain copy of
-    COPY_BYTES, so bytes = counter * COPY_BYTES / counter_on_copy."""
-    import csv
-    import statistics
-
-    def per_dispatch(fname, counter, kernel_substr):
-        vals = []
-        with open(os.path.join(pmc_dir, fname)) as f:
-            for r in csv.DictReader(f):
-                if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]:
-                    vals.append(float(r["Counter_Value"]))
-        if not vals:
-            raise SystemExit(f"no {counter} rows for {kernel_substr} in {fname}")
-        return statistics.mean(vals), len(vals)
-
-    fetch, nf = per_dispatch("fetch_counter_collection.csv", "FETCH_SIZE", "fwd_fused_bf16")
-    write, nw = per_dispatch("write_counter_collection.csv", "WRITE_SIZE", "fwd_fused_bf16")
-    cf, _ = per_dispatch("copyfetch_counter_collection.csv", "FETCH_SIZE", "copyBuffer")
-    cw, _ = per_dispatch("copywrite_counter_collection.csv", "WRITE_SIZE", "copyBuffer")
-    rf, rw = COPY_BYTES / cf, COPY_BYTES / cw  # bytes per counter unit
-    summary = {
-        "kernel_digest": kernel_digest(),
-        "bytes_per_launch": round(fetch * rf + write * rw),
-        "read_bytes_per_launch": round(fetch * rf),
-        "write_bytes_per_launch": round(write * rw),
-        "fetch_size_kib_per_dispatch": fetch, "write_size_kib_per_dispatch": write,
-        "dispatches": [nf, nw],
-        "copy_calibration": {"copy_bytes": COPY_BYTES, "fetch_size_kib": cf, "write_size_kib": cw,
-                             "bytes_per_fetch_unit": rf, "bytes_per_write_unit": rw},
-    }
-    with open(out_path, "w") as f:
-        json.dump(summary, f, indent=1)
-    print(json.dumps(summary))
 
 
 def counter_means(path: str, counter: str, key_of) -> dict:
@@ -434,8 +519,8 @@ def main():
     if len(sys.argv) >= 5 and sys.argv[1] == "--summarize-smallcache-sweep":
         summarize_smallcache_sweep(sys.argv[2], sys.argv[3], sys.argv[4])
         return
-    if len(sys.argv) >= 3 and sys.argv[1] == "--summarize-counters":
-        summarize_counters(sys.argv[2])
+    if len(sys.argv) >= 3 and sys.argv[1] == "--summarize-leg-counters":
+        summarize_leg_counters(sys.argv[2])
         return
     if len(sys.argv) >= 5 and sys.argv[1] == "--summarize-sweep":
         summarize_sweep(sys.argv[2], sys.argv[3], sys.argv[4])
@@ -457,6 +542,9 @@ def main():
     ap.add_argument("--smallcache-sweep", action="store_true",
                     help="time the square-tile forward at every tile b on the d = 256 "
                          "small-cache workload (one JSON line per tile) and exit")
+    ap.add_argument("--profile-leg", default=None, choices=sorted(LEGS),
+                    help="run one leg --calls + 1 times (for a counter run) and exit")
+    ap.add_argument("--calls", type=int, default=3)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB three times (to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -481,6 +569,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 3}))
+        return
+    if args.profile_leg:
+        profile_leg(args.profile_leg, args.calls, at, torch, dev)
         return
     if args.tile_sweep:
         tile_sweep(args, at, torch, dev)
@@ -630,6 +721,48 @@ def smallcache_sweep(args, at, torch, dev):
         del ws
 
 
+def theorem_1_1(w, m: int) -> dict:
+    """Theorem 1.1 of the page "On Fine-Grained I/O Complexity of Attention
+    Backward Passes": Theta(min((n^2 d^2 + n d^3) / M, (n^2 d + n d^2) /
+    sqrt(M))) transfers per head, evaluated without its constant (elements,
+    reported as bf16 bytes) -- a model, not a pinned parity."""
+    n, d = w.n, w.d
+    large = (n * n * d * d + n * d ** 3) / m
+    small = (n * n * d + n * d * d) / math.sqrt(m)
+    return {"name": "theorem_1_1", "regime": "large-cache (M >= d^2)" if m >= d * d
+            else "small-cache (M < d^2)", "m_elems": m,
+            "elements": round(w.bh * min(large, small)), "bytes": round(2 * w.bh * min(large, small))}
+
+
+def page_fwd_smallcache(w, m: int) -> dict:
+    """The exposition's N^2 d / sqrt(M) + N d movement for the square-tile
+    forward (table under "Putting the regimes together"), per head, as bf16
+    bytes -- a model without its constant."""
+    el = w.n * w.n * w.d / math.sqrt(m) + w.n * w.d
+    return {"name": "N^2 d / sqrt(M) + N d", "m_elems": m, "elements": round(w.bh * el),
+            "bytes": round(2 * w.bh * el)}
+
+
+def leg_bytes(leg: str, ms: float, floor_bytes: float, model: dict,
+              with_roofline: bool = True) -> dict:
+    """HBM bytes of one call of a leg from the committed counter summary
+    (None when it was taken on other kernel sources), their ratio to the
+    page's model, and (with_roofline) the leg's roofline against its HBM
+    floor: floor_bytes / 8 TB/s over the measured time."""
+    t = leg_traffic(leg)
+    out = {"hbm_floor_bytes": round(floor_bytes), "model": model,
+           "counter_bytes": t["bytes_per_call"] if t else None,
+           "counter_read_bytes": t["read_bytes_per_call"] if t else None,
+           "counter_write_bytes": t["write_bytes_per_call"] if t else None,
+           "counter_to_model": round(t["bytes_per_call"] / model["bytes"], 3) if t else None}
+    if with_roofline:
+        gbps = floor_bytes / (ms * 1e-3) / 1e9
+        out["roofline"] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
+                           "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                           "what": "HBM floor bytes / measured time"}
+    return out
+
+
 def secondary(args, at, torch, dev):
     from aware_tiling_amd.inputs import WORKLOADS, workload_inputs
 
@@ -639,26 +772,28 @@ def secondary(args, at, torch, dev):
     def want(name):
         return legs is None or name in legs
 
-    w = WORKLOADS["smallcache_bf16_b1h8_n4096_d256"]
-    m_elems = 49152  # 3/4 of d^2: the small-cache regime M < d^2
-    if want("smallcache") and at.smallcache_tile(w.d, m_elems) > 0:
+    if want("smallcache") and at.smallcache_tile(256, SMALLCACHE_M) > 0:
+        fn, w, info = leg_call("smallcache", at, torch, dev)
         print(f"[bench] timing {w.name}", file=sys.stderr, flush=True)
-        q, k, v = (t.to(dev) for t in workload_inputs(w))
-        o = torch.empty((w.bh, w.n, w.d), dtype=torch.float32, device=dev)
-        lse = torch.empty((w.bh, w.n), dtype=torch.float32, device=dev)
-        need = int(at.lib().attn_fwd_smallcache_workspace_size(w.bh, w.n, w.d, m_elems))
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
-        ms_sc, _, _ = time_launches(lambda: at.attn_fwd_smallcache(
-            q, k, v, m_elems, w.scale, out=o, lse=lse, workspace=ws), args.steps, args.warmup, batch=True, warm_s=SECONDARY_WARM_S)
+        q, k, v, o, lse = (info[x] for x in ("q", "k", "v", "o", "lse"))
+        m_elems = info["m_elems"]
+        ms_sc, _, _ = time_launches(fn, args.steps, args.warmup, batch=True,
+                                    warm_s=SECONDARY_WARM_S)
         ms_fu, _, _ = time_launches(lambda: at.attn_fwd(q, k, v, w.scale, out=o, lse=lse),
                                     args.steps, args.warmup, batch=True, warm_s=SECONDARY_WARM_S)
         b = at.smallcache_tile(w.d, m_elems)
+        # HBM floor: Q, K, V read and O, lse written once, and the exponentiated
+        # matrix E written once and read once (bf16)
+        e_bytes = w.bh * w.n * w.n * 2
+        floor = w.bh * (3 * w.n * w.d * 2 + w.n * w.d * 4 + w.n * 4) + 2 * e_bytes
         res["smallcache"] = {"workload": w.name, "m_elems": m_elems, "tile_b": b,
+                             "onchip_elems": int(at.lib().attn_smallcache_onchip_elems(b)),
                              "ms": round(ms_sc, 4),
                              "tflops": round(w.fwd_flops / (ms_sc * 1e-3) / 1e12, 2),
                              "fused_ms_same_inputs": round(ms_fu, 4),
                              "fused_tflops": round(w.fwd_flops / (ms_fu * 1e-3) / 1e12, 2),
-                             "exp_matrix_bytes": w.bh * w.n * w.n * 2}
+                             "exp_matrix_bytes": e_bytes,
+                             **leg_bytes("smallcache", ms_sc, floor, page_fwd_smallcache(w, m_elems))}
         # both schedules held to the same budget below d^2: the fused one with
         # 32-row query blocks (K, V read once per block) and the square tiles
         m_same = at.fwd_budget_onchip_elems(w.d)
@@ -666,9 +801,11 @@ def secondary(args, at, torch, dev):
             need = int(at.lib().attn_fwd_smallcache_workspace_size(w.bh, w.n, w.d, m_same))
             ws2 = torch.empty(need, dtype=torch.uint8, device=dev)
             ms_fb, _, _ = time_launches(lambda: at.attn_fwd_budget(
-                q, k, v, m_same, w.scale, out=o, lse=lse), args.steps, args.warmup, batch=True, warm_s=SECONDARY_WARM_S)
+                q, k, v, m_same, w.scale, out=o, lse=lse), args.steps, args.warmup, batch=True,
+                warm_s=SECONDARY_WARM_S)
             ms_sb, _, _ = time_launches(lambda: at.attn_fwd_smallcache(
-                q, k, v, m_same, w.scale, out=o, lse=lse, workspace=ws2), args.steps, args.warmup, batch=True, warm_s=SECONDARY_WARM_S)
+                q, k, v, m_same, w.scale, out=o, lse=lse, workspace=ws2), args.steps,
+                args.warmup, batch=True, warm_s=SECONDARY_WARM_S)
             res["smallcache"]["same_budget"] = {
                 "m_elems": m_same,
                 "fused_query_rows": 32, "fused_ms": round(ms_fb, 4),
@@ -678,56 +815,48 @@ def secondary(args, at, torch, dev):
                 "smallcache_ms": round(ms_sb, 4),
                 "smallcache_tflops": round(w.fwd_flops / (ms_sb * 1e-3) / 1e12, 2)}
             del ws2
-        del q, k, v, o, lse, ws
-    w = WORKLOADS["bwd_bf16_b2h16_n4096_d128"]
-    q0 = torch.zeros((1, 64, w.d), dtype=torch.bfloat16, device=dev)
-    try:
-        at.attn_bwd(q0, q0, q0, torch.zeros((1, 64, w.d), device=dev), q0,
-                    torch.zeros((1, 64), device=dev))
-        has_bwd = True
-    except at.AttnError:
-        has_bwd = False
-    if want("backward") and has_bwd:
+        del fn, info, q, k, v, o, lse
+        torch.cuda.empty_cache()
+    if want("backward"):
+        fn, w, info = leg_call("backward", at, torch, dev)
         print(f"[bench] timing {w.name}", file=sys.stderr, flush=True)
-        q, k, v, do = (t.to(dev) for t in workload_inputs(w))
-        o, lse = at.attn_fwd(q, k, v, w.scale)
-        grads = tuple(torch.empty((w.bh, w.n, w.d), dtype=torch.float32, device=dev)
-                      for _ in range(3))
-        need = int(at.lib().attn_bwd_workspace_size(w.bh, w.n, w.d))
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-        ms, _, _ = time_launches(lambda: at.attn_bwd(q, k, v, o, do, lse, w.scale, workspace=ws,
-                                                     grads=grads), args.steps, args.warmup, batch=True, warm_s=SECONDARY_WARM_S)
-        fl = 10.0 * w.n * w.n * w.d * w.bh  # 2 products recomputed-free count: 5 GEMMs
-        res["backward"] = {"workload": w.name, "ms": round(ms, 4),
-                           "tflops_at_10N2d": round(fl / (ms * 1e-3) / 1e12, 2)}
-    for name, m_sc in ((("bwd_smallcache_bf16_b1h8_n4096_d256", 49152),
-                        ("bwd_bf16_b2h16_n4096_d128", 12288))
-                       if want("smallcache_backward") else ()):
-        w = WORKLOADS[name]
+        ms, _, _ = time_launches(fn, args.steps, args.warmup, batch=True, warm_s=SECONDARY_WARM_S)
+        fl = 10.0 * w.n * w.n * w.d * w.bh  # five n x n x d products, 2 n^2 d flops each
+        m = info["m_elems"]
+        # HBM floor: Q, K, V, dO (bf16), O, lse read, dQ, dK, dV (fp32) written
+        floor = w.bh * (4 * w.n * w.d * 2 + w.n * w.d * 4 + w.n * 4 + 3 * w.n * w.d * 4)
+        res["backward"] = {
+            "workload": w.name, "ms": round(ms, 4), "onchip_elems": m,
+            "tflops_at_10N2d": round(fl / (ms * 1e-3) / 1e12, 2),
+            "roofline": {"bound": "mfma", "achieved": round(fl / (ms * 1e-3) / 1e12, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+            **leg_bytes("backward", ms, floor, theorem_1_1(w, m), with_roofline=False)}
+        del fn, info
+        torch.cuda.empty_cache()
+    for leg in (SMALLCACHE_BWD if want("smallcache_backward") else ()):
+        fn, w, info = leg_call(leg, at, torch, dev)
+        m_sc = info["m_elems"]
         b = at.bwd_smallcache_tile(w.d, m_sc)
         print(f"[bench] timing small-cache backward {w.name} M={m_sc}", file=sys.stderr,
               flush=True)
-        q, k, v, do = (t.to(dev) for t in workload_inputs(w))
-        o, lse = at.attn_fwd(q, k, v, w.scale)
-        grads = tuple(torch.empty((w.bh, w.n, w.d), dtype=torch.float32, device=dev)
-                      for _ in range(3))
-        need = int(at.lib().attn_bwd_smallcache_workspace_size(w.bh, w.n, w.d, m_sc))
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
-        ms, _, _ = time_launches(lambda: at.attn_bwd_smallcache(
-            q, k, v, o, do, lse, m_sc, w.scale, workspace=ws, grads=grads),
-            args.steps, args.warmup, batch=True, warm_s=SECONDARY_WARM_S)
+        ms, _, _ = time_launches(fn, args.steps, args.warmup, batch=True, warm_s=SECONDARY_WARM_S)
         npad = -(-w.n // b) * b
         fl = 10.0 * w.n * w.n * w.d * w.bh
         # n x n traffic of the schedule: P^T and dS^T written once, P^T read
         # once (dV), dS^T read twice (dK, dQ); bf16
         nn_bytes = 5 * w.bh * npad * npad * 2
-        res["smallcache_backward_d%d" % w.d] = {
+        # HBM floor: that n x n traffic and the backward's own inputs and outputs
+        floor = nn_bytes + w.bh * (4 * w.n * w.d * 2 + w.n * w.d * 4 + w.n * 4 +
+                                   3 * w.n * w.d * 4)
+        res[leg] = {
             "workload": w.name, "m_elems": m_sc, "tile_b": b,
             "onchip_elems": int(at.lib().attn_bwd_smallcache_onchip_elems(w.d, m_sc)),
             "ms": round(ms, 4), "tflops_at_10N2d": round(fl / (ms * 1e-3) / 1e12, 2),
             "nxn_bytes": nn_bytes,
-            "nxn_gbps": round(nn_bytes / (ms * 1e-3) / 1e9, 1)}
-        del q, k, v, do, o, lse, grads, ws
+            "nxn_gbps": round(nn_bytes / (ms * 1e-3) / 1e9, 1),
+            **leg_bytes(leg, ms, floor, theorem_1_1(w, m_sc))}
+        del fn, info
         torch.cuda.empty_cache()
     from aware_tiling_amd.inputs import make_block_mask
 

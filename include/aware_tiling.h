@@ -332,6 +332,17 @@ int64_t attn_smallcache_onchip_elems(int64_t b);
  *   bf16 only, d in {64, 128}.
  */
 size_t attn_bwd_workspace_size(int64_t bh, int64_t n, int64_t d);
+
+/*
+ * On-chip elements M held by one workgroup of attn_bwd for head dimension d:
+ * the larger of its two kernels' resident sets (the dK/dV kernel's key rows,
+ * accumulators, one query tile and score tiles; the dQ kernel's query rows,
+ * accumulator, one key tile and score tiles), each element counted once
+ * whatever its width and one stage of each streamed tile, as for
+ * attn_fwd_onchip_elems: the M of Theorem 1.1 on the page "On Fine-Grained
+ * I/O Complexity of Attention Backward Passes".  0 for an unsupported d.
+ */
+int64_t attn_bwd_onchip_elems(int64_t d);
 attn_status attn_bwd(const void* Q, const void* K, const void* V,
                      const float* O, const void* dO, const float* lse,
                      float* dQ, float* dK, float* dV, int64_t bh, int64_t n,

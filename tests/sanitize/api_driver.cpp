@@ -98,6 +98,7 @@ int main() {
                 run([&] { return attn_bwd(p, base, base, fp, base, fp, fp, fp, fp, bh, n, d, sc, ATTN_BF16, base, w, nullptr); }, pok);
             }
             (void)attn_bwd_workspace_size(bh, n, d);
+            (void)attn_bwd_onchip_elems(d);
             (void)attn_fwd_onchip_elems(d, ATTN_BF16);
             (void)attn_fwd_query_block(d, ATTN_F32);
             (void)attn_fwd_budget_onchip_elems(d);

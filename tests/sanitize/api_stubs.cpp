@@ -99,6 +99,7 @@ hipError_t launch_fwd_smallcache_bf16(const void*, const void*, const void*, flo
   return launched();
 }
 bool bwd_supported(int64_t d) { return d == 64 || d == 128; }
+int64_t bwd_onchip_elems(int64_t d) { return bwd_supported(d) ? 1 : 0; }
 size_t bwd_workspace_bytes(int64_t bh, int64_t n, int64_t) { return 2 * align256_bytes((size_t)bh * n * 4); }
 hipError_t launch_bwd_bf16(const void*, const void*, const void*, const float*, const void*,
                            const float*, float*, float*, float*, int64_t, int64_t, int64_t, float,

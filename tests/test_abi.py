@@ -277,6 +277,19 @@ def test_splitk_validation_and_sizes(lib):
         assert s == 1 or (k_ + s - 1) // s >= 192
 
 
+def test_bwd_onchip_elems(lib):
+    # the larger of the two kernels' resident sets (one stage of each streamed
+    # tile): dK/dV 4 Bkv d + 2 Bq d + 2 Bq + 2 Bkv Bq with Bkv = 256 keys and
+    # Bq = 32 queries (64 at d = 64); dQ 3 Bqb d + 2 Bqb + 2 Bc d + 2 Bqb Bc with
+    # Bqb = 256 queries and Bc = 64 keys; both >= d^2 (the large-cache regime)
+    dkdv = lambda d, bq: 4 * 256 * d + 2 * bq * d + 2 * bq + 2 * 256 * bq
+    dq = lambda d: 3 * 256 * d + 2 * 256 + 2 * 64 * d + 2 * 256 * 64
+    assert lib.attn_bwd_onchip_elems(128) == max(dkdv(128, 32), dq(128)) == 155712
+    assert lib.attn_bwd_onchip_elems(64) == max(dkdv(64, 64), dq(64))
+    assert lib.attn_bwd_onchip_elems(128) >= 128 * 128
+    assert lib.attn_bwd_onchip_elems(256) == 0 and lib.attn_bwd_onchip_elems(-1) == 0
+
+
 def test_bwd_smallcache_tile_selection_and_validation(lib):
     # footprint(b, stages) = max(2 b^2 + 4 b 16 stages, b^2 + 2 b 16 stages)
     tile, onchip = lib.attn_bwd_smallcache_tile, lib.attn_bwd_smallcache_onchip_elems

@@ -27,14 +27,69 @@ def test_percentile_nearest_rank():
 
 def test_traffic_summary_applies_only_to_its_kernel_source(tmp_path, monkeypatch):
     f = tmp_path / "traffic.json"
-    f.write_text(json.dumps({"kernel_digest": bench.kernel_digest(), "bytes_per_launch": 123}))
+    leg = {"kernel_digest": bench.kernel_digest("headline"), "bytes_per_call": 123,
+           "read_bytes_per_call": 100, "write_bytes_per_call": 23}
+    f.write_text(json.dumps({"legs": {"headline": leg}}))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
     assert bench.traffic_for_launch() == 123
-    f.write_text(json.dumps({"kernel_digest": "0" * 16, "bytes_per_launch": 123}))
+    assert bench.leg_traffic("backward") is None  # not profiled
+    f.write_text(json.dumps({"legs": {"headline": dict(leg, kernel_digest="0" * 16)}}))
     assert bench.traffic_for_launch() is None
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.json"))
     assert bench.traffic_for_launch() is None
 
+
+def test_leg_digests_follow_their_sources():
+    # each leg is keyed by its own kernel file; the shared headers key all
+    assert bench.kernel_digest("backward") != bench.kernel_digest("headline")
+    assert (bench.kernel_digest("smallcache_backward_d256") ==
+            bench.kernel_digest("smallcache_backward_d128"))
+
+
+def test_leg_counter_summary_scales_by_the_copy_and_divides_by_calls(tmp_path):
+    # the calibration copy of COPY_BYTES reads 1000 FETCH_SIZE units and 500
+    # WRITE_SIZE units: one unit = COPY_BYTES / 1000 and COPY_BYTES / 500 bytes
+    _counter_csv(tmp_path / "copyfetch_counter_collection.csv",
+                 [("__amd_rocclr_copyBuffer", "FETCH_SIZE", 1000.0)])
+    _counter_csv(tmp_path / "copywrite_counter_collection.csv",
+                 [("__amd_rocclr_copyBuffer", "WRITE_SIZE", 500.0)])
+    # two calls of the backward: three kernels each, plus a forward call that
+    # is not part of the leg
+    rows_f = [("bwd_preprocess<128>", "FETCH_SIZE", 1.0), ("bwd_dkdv3<128, 8>", "FETCH_SIZE", 10.0),
+              ("bwd_dq3<128, 8, 64>", "FETCH_SIZE", 20.0)] * 2
+    rows_f.append(("fwd_fused_bf16_direct_kernel<128, 8, 64, 2>", "FETCH_SIZE", 999.0))
+    rows_w = [("bwd_preprocess<128>", "WRITE_SIZE", 2.0), ("bwd_dkdv3<128, 8>", "WRITE_SIZE", 4.0),
+              ("bwd_dq3<128, 8, 64>", "WRITE_SIZE", 6.0)] * 2
+    _counter_csv(tmp_path / "backward_fetch_counter_collection.csv", rows_f)
+    _counter_csv(tmp_path / "backward_write_counter_collection.csv", rows_w)
+    (tmp_path / "backward_calls.json").write_text('noise\n{"leg": "backward", "calls": 2}\n')
+    out = tmp_path / "t.json"
+    bench.summarize_leg_counters(str(tmp_path), str(out))
+    t = json.loads(out.read_text())
+    leg = t["legs"]["backward"]
+    rf, rw = bench.COPY_BYTES / 1000.0, bench.COPY_BYTES / 500.0
+    assert leg["read_bytes_per_call"] == round(31.0 * rf)
+    assert leg["write_bytes_per_call"] == round(12.0 * rw)
+    assert leg["bytes_per_call"] == round(31.0 * rf + 12.0 * rw)
+    assert leg["dispatches"] == [6, 6] and leg["kernel_digest"] == bench.kernel_digest("backward")
+    assert set(t["legs"]) == {"backward"}
+
+
+def test_theorem_1_1_takes_the_term_of_its_regime():
+    class W:
+        bh, n, d = 2, 4096, 128
+    w = W()
+    n, d = w.n, w.d
+    big = bench.theorem_1_1(w, 4 * d * d)  # M >= d^2: (n^2 d^2 + n d^3) / M
+    assert big["regime"].startswith("large")
+    assert big["elements"] == round(2 * (n * n * d * d + n * d ** 3) / (4 * d * d))
+    small = bench.theorem_1_1(w, d * d // 4)  # M < d^2: (n^2 d + n d^2) / sqrt(M)
+    assert small["regime"].startswith("small")
+    assert small["elements"] == round(2 * (n * n * d + n * d * d) / (d / 2))
+    assert small["bytes"] == round(2 * 2 * (n * n * d + n * d * d) / (d / 2))
+    # at M = d^2 the two terms coincide
+    eq = bench.theorem_1_1(w, d * d)
+    assert eq["elements"] == round(2 * (n * n * d + n * d * d) / d)
 
 
 def _counter_csv(path, rows):
