@@ -320,7 +320,7 @@ def cpu_baseline(w, cpu_inputs, target_s: float = 15.0):
 
     q, k, v = cpu_inputs
     flops_row = 4.0 * w.n * w.d
-    calib = 32
+    calib = 256  # enough rows to occupy every host thread
     qd0 = q[:1, :calib].double().numpy()
     kd0, vd0 = k[:1].double().numpy(), v[:1].double().numpy()
     oracle.attn_fwd(qd0[:, :8], kd0, vd0, w.scale)  # load + warm
@@ -368,11 +368,16 @@ def copy_counter(path: str, counter: str) -> float:
 
 
 def fused_sweep_key(name: str):
-    """(B_r, B_c) of a d = 128 direct fused-forward kernel name, else None."""
+    """(B_r, B_c) of a d = 128 direct fused-forward kernel name (demangled or
+    mangled), else None."""
     import re
 
-    m = re.search(r"fwd_fused_bf16_direct_kernel<128, (\d+), (\d+),", name)
-    return (32 * int(m.group(1)), int(m.group(2))) if m else None
+    m = re.search(r"fwd_fused_bf16_direct_kernel(?:<128, (\d+), (\d+),|ILi128ELi(\d+)ELi(\d+)E)",
+                  name)
+    if not m:
+        return None
+    nw, bc = (m.group(1), m.group(2)) if m.group(1) else (m.group(3), m.group(4))
+    return (32 * int(nw), int(bc))
 
 
 def mfma_busy(pmc_dir: str, fname: str, key_of) -> dict:

@@ -103,6 +103,9 @@ def test_sweep_kernel_keys():
     assert bench.fused_sweep_key(
         "at::fwd_fused_bf16_direct_kernel<128, 8, 64, true, 2, false, 2, 0, true>(x)") == (256, 64)
     assert bench.fused_sweep_key("at::fwd_fused_bf16_direct_kernel<256, 4, 32>(x)") is None
+    assert bench.fused_sweep_key(
+        "_ZN2at28fwd_fused_bf16_direct_kernelILi128ELi4ELi32ELi2EEEvPKDF16b") == (128, 32)
+    assert bench.fused_sweep_key("_ZN2at28fwd_fused_bf16_direct_kernelILi256ELi4ELi32E") is None
     assert bench.smallcache_sweep_key("void at::sc_scores_exp<256, 128>(a)") == 128
     assert bench.smallcache_sweep_key("_ZN2at16sc_value_productILi256ELi64EEEvPKDF16b") == 64
     assert bench.smallcache_sweep_key("_ZN2at16sc_value_productILi128ELi64EEEvPKDF16b") is None
