@@ -52,6 +52,10 @@ SIGNATURES = {
     "attn_smallcache_onchip_elems": (_i64, [_i64]),
     "attn_bwd_workspace_size": (_sz, [_i64, _i64, _i64]),
     "attn_bwd_onchip_elems": (_i64, [_i64]),
+    "attn_bwd_tiles": (ctypes.c_char_p, [_i64]),
+    "attn_bwd_tile_info": (_int, [ctypes.c_char_p, _i64, _vp, _vp, _vp, _vp]),
+    "attn_bwd_tile": (_int, [ctypes.c_char_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
+                             _i64, _i64, _f32, _int, _vp, _sz, _vp]),
     "attn_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _int,
                         _vp, _sz, _vp]),
     "attn_bwd_smallcache_tile": (_i64, [_i64, _i64]),
@@ -423,6 +427,42 @@ def attn_fwd_smallcache(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, m_ele
                                    _stream(q, stream))
     _check("attn_fwd_smallcache", rc)
     return out, lse
+
+
+def bwd_tiles(d: int) -> list[str]:
+    """Names of the blockwise backward's compiled tile shapes for head
+    dimension d, the default (the one attn_bwd uses) first."""
+    return lib().attn_bwd_tiles(d).decode().split()
+
+
+def bwd_tile_info(tile: str, d: int) -> dict:
+    """Keys per dK/dV workgroup, queries per dQ workgroup, keys per dQ tile
+    and on-chip elements of a named backward tile shape at head dimension d."""
+    vals = [ctypes.c_int64(0) for _ in range(4)]
+    rc = lib().attn_bwd_tile_info(tile.encode(), d, *(ctypes.byref(x) for x in vals))
+    _check("attn_bwd_tile_info", rc)
+    return {"keys_per_block": vals[0].value, "queries_per_block": vals[1].value,
+            "key_tile": vals[2].value, "onchip_elems": vals[3].value}
+
+
+def attn_bwd_tile(tile: str, q, k, v, o, do, lse, scale: float | None = None, workspace=None,
+                  grads=None, stream=None):
+    """attn_bwd with the named tile shape (tile sweeps and tests)."""
+    bh, n, d = _bwd_operands(q, k, v, o, do, lse)
+    scale = default_scale(d) if scale is None else float(scale)
+    dq, dk, dv = _grads(grads, bh, n, d, q.device)
+    if workspace is None:
+        need = int(lib().attn_bwd_workspace_size(bh, n, d))
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    else:
+        _check_workspace(workspace, q.device)
+    rc = lib().attn_bwd_tile(tile.encode(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                             o.data_ptr(), do.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+                             dk.data_ptr(), dv.data_ptr(), bh, n, d, scale, _dtype_code(q),
+                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                             _stream(q, stream))
+    _check("attn_bwd_tile", rc)
+    return dq, dk, dv
 
 
 def attn_bwd(q, k, v, o, do, lse, scale: float | None = None, workspace=None, grads=None,

@@ -283,13 +283,17 @@ size_t attn_bwd_workspace_size(int64_t bh, int64_t n, int64_t d) {
 
 int64_t attn_bwd_onchip_elems(int64_t d) { return at::bwd_onchip_elems(d); }
 
-attn_status attn_bwd(const void* Q, const void* K, const void* V, const float* O,
-                     const void* dO, const float* lse, float* dQ, float* dK, float* dV,
-                     int64_t bh, int64_t n, int64_t d, float scale, attn_dtype dtype,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+attn_status bwd_checked(const char* tile, const void* Q, const void* K, const void* V,
+                        const float* O, const void* dO, const float* lse, float* dQ, float* dK,
+                        float* dV, int64_t bh, int64_t n, int64_t d, float scale,
+                        attn_dtype dtype, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (!shape_ok(bh, n, d) || !scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
-  if (!at::bwd_supported(d)) return ATTN_ERR_UNSUPPORTED;
+  if (!at::bwd_supported(d) || at::bwd_tile_info(d, tile).keys_per_block == 0)
+    return ATTN_ERR_UNSUPPORTED;
   if (bh * n == 0) return ATTN_OK;
   const void* ptrs[] = {Q, K, V, O, dO, lse, dQ, dK, dV};
   for (const void* p : ptrs)
@@ -298,7 +302,42 @@ attn_status attn_bwd(const void* Q, const void* K, const void* V, const float* O
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned256(workspace)))
     return ATTN_ERR_WORKSPACE;
   return launch_status(at::launch_bwd_bf16(Q, K, V, O, dO, lse, dQ, dK, dV, bh, n, d, scale,
-                                           workspace, static_cast<hipStream_t>(stream)));
+                                           workspace, tile, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+attn_status attn_bwd(const void* Q, const void* K, const void* V, const float* O,
+                     const void* dO, const float* lse, float* dQ, float* dK, float* dV,
+                     int64_t bh, int64_t n, int64_t d, float scale, attn_dtype dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_checked(nullptr, Q, K, V, O, dO, lse, dQ, dK, dV, bh, n, d, scale, dtype, workspace,
+                     workspace_bytes, stream);
+}
+
+const char* attn_bwd_tiles(int64_t d) { return at::bwd_tile_names(d); }
+
+attn_status attn_bwd_tile_info(const char* tile, int64_t d, int64_t* keys_per_block,
+                               int64_t* queries_per_block, int64_t* key_tile,
+                               int64_t* onchip_elems) {
+  if (!tile) return ATTN_ERR_INVALID_ARG;
+  const at::BwdTileInfo t = at::bwd_tile_info(d, tile);
+  if (t.keys_per_block == 0) return ATTN_ERR_UNSUPPORTED;
+  if (keys_per_block) *keys_per_block = t.keys_per_block;
+  if (queries_per_block) *queries_per_block = t.queries_per_block;
+  if (key_tile) *key_tile = t.key_tile;
+  if (onchip_elems) *onchip_elems = t.onchip;
+  return ATTN_OK;
+}
+
+attn_status attn_bwd_tile(const char* tile, const void* Q, const void* K, const void* V,
+                          const float* O, const void* dO, const float* lse, float* dQ, float* dK,
+                          float* dV, int64_t bh, int64_t n, int64_t d, float scale,
+                          attn_dtype dtype, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (!tile) return ATTN_ERR_INVALID_ARG;
+  return bwd_checked(tile, Q, K, V, O, dO, lse, dQ, dK, dV, bh, n, d, scale, dtype, workspace,
+                     workspace_bytes, stream);
 }
 
 int64_t attn_bwd_smallcache_tile(int64_t d, int64_t m_elems) {

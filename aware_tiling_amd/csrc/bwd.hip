@@ -31,6 +31,7 @@
 //     costs 4 N^2 d more flops than accumulating dQ with atomics, and keeps
 //     the result deterministic.
 #include <algorithm>
+#include <cstring>
 #include <type_traits>
 
 #include "device_common.h"
@@ -147,11 +148,11 @@ struct DkdvCfg {
   static constexpr int INSTS = WAVE_CHUNKS / 64;
   static constexpr int TILE = BQ * D;
   // on-chip elements of one workgroup, each counted once whatever its width
-  // and one stage of each streamed tile (as for the forward): the K and V
-  // rows, the dK^T and dV^T accumulators, a Q and a dO tile, their lse and D
-  // values, and the S/P and dP/dS tiles of all waves
+  // and every pipeline slot counted (as for the forward): the K and V rows,
+  // the dK^T and dV^T accumulators, both stages of the Q and dO tiles and of
+  // their lse and D values, and the S/P and dP/dS tiles of all waves
   static constexpr int64_t ONCHIP =
-      4 * (int64_t)BKV * D + 2 * (int64_t)BQ * D + 2 * BQ + 2 * (int64_t)BKV * BQ;
+      4 * (int64_t)BKV * D + 4 * (int64_t)BQ * D + 4 * BQ + 2 * (int64_t)BKV * BQ;
   static_assert(CHUNKS % (NW * 64) == 0, "tile must split into whole wave loads");
 };
 
@@ -415,9 +416,10 @@ struct DqCfg {
   static constexpr int INSTS = WAVE_CHUNKS / 64;
   static constexpr int TILE = BC * D;
   // on-chip elements (as DkdvCfg): the Q and dO rows, the dQ^T accumulators,
-  // the lse and D values, a K and a V tile, and the S^T and dP^T tiles
+  // the lse and D values, both stages of the K and V tiles, and the S^T and
+  // dP^T tiles
   static constexpr int64_t ONCHIP =
-      3 * (int64_t)BQB * D + 2 * BQB + 2 * (int64_t)BC * D + 2 * (int64_t)BQB * BC;
+      3 * (int64_t)BQB * D + 2 * BQB + 4 * (int64_t)BC * D + 2 * (int64_t)BQB * BC;
   static_assert(CHUNKS % (NW * 64) == 0, "tile must split into whole wave loads");
 };
 
@@ -598,9 +600,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq3(
 
 namespace {
 
-// Eight waves per workgroup in both kernels: bwd_dkdv3 (one wave per 32
-// keys; per 32 queries S, then dP, then dV and dK) and bwd_dq3.
-template <int D>
+// bwd_dkdv3 with NWKV waves (one wave per 32 keys; per 32 queries S, then
+// dP, then dV and dK) and bwd_dq3 with NWQ waves (one per 32 queries) and
+// BC-key tiles.  The default is eight waves in both and 64-key tiles.
+template <int D, int NWKV = 8, int NWQ = 8, int BC = 64>
 hipError_t launch(const void* Q, const void* K, const void* V, const float* O, const void* dO,
                   const float* lse, float* dQ, float* dK, float* dV, int64_t bh, int64_t n,
                   float scale, void* ws, hipStream_t stream) {
@@ -618,20 +621,52 @@ hipError_t launch(const void* Q, const void* K, const void* V, const float* O, c
                      stream, O, g, Dbuf, rows, lse, lse2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  constexpr int NW = 8;
-  using Ckv = DkdvCfg<D, NW>;
+  using Ckv = DkdvCfg<D, NWKV>;
   const int nkb = (int)((n + Ckv::BKV - 1) / Ckv::BKV);
   const int total_kv = (int)(bh * nkb);
-  hipLaunchKernelGGL((bwd_dkdv3<D, NW>), dim3(total_kv), dim3(NW * 64), 0, stream, q, k, v, g,
-                     lse2, Dbuf, dK, dV, (int)n, nkb, total_kv, c, scale);
+  hipLaunchKernelGGL((bwd_dkdv3<D, NWKV>), dim3(total_kv), dim3(NWKV * 64), 0, stream, q, k, v,
+                     g, lse2, Dbuf, dK, dV, (int)n, nkb, total_kv, c, scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  using Cq = DqCfg<D, NW, 64>;
+  using Cq = DqCfg<D, NWQ, BC>;
   const int nqb = (int)((n + Cq::BQB - 1) / Cq::BQB);
   const int total_q = (int)(bh * nqb);
-  hipLaunchKernelGGL((bwd_dq3<D, NW, 64>), dim3(total_q), dim3(NW * 64), 0, stream, q, k, v, g,
-                     lse, Dbuf, dQ, (int)n, nqb, total_q, c, scale);
+  hipLaunchKernelGGL((bwd_dq3<D, NWQ, BC>), dim3(total_q), dim3(NWQ * 64), 0, stream, q, k, v,
+                     g, lse, Dbuf, dQ, (int)n, nqb, total_q, c, scale);
   return hipGetLastError();
+}
+
+// Compiled tile shapes, per head dimension the default first: keys per
+// dK/dV workgroup (k), queries per dQ workgroup (q), keys per dQ tile (c).
+// Every shape processes each wave's 32 rows in the same order, so all give
+// the same bits.
+typedef hipError_t (*BwdLaunch)(const void*, const void*, const void*, const float*,
+                                const void*, const float*, float*, float*, float*, int64_t,
+                                int64_t, float, void*, hipStream_t);
+struct BwdEntry {
+  const char* name;
+  int d;
+  BwdTileInfo info;
+  BwdLaunch fn;
+};
+
+template <int D, int NWKV, int NWQ, int BC>
+BwdEntry bwd_entry(const char* name) {
+  return BwdEntry{name, D,
+                  BwdTileInfo{32 * NWKV, 32 * NWQ, BC,
+                              std::max(DkdvCfg<D, NWKV>::ONCHIP, DqCfg<D, NWQ, BC>::ONCHIP)},
+                  &launch<D, NWKV, NWQ, BC>};
+}
+
+const BwdEntry* bwd_pick(int64_t d, const char* name) {
+  static const BwdEntry table[] = {
+      bwd_entry<128, 8, 8, 64>("k256q256c64"), bwd_entry<128, 4, 8, 64>("k128q256c64"),
+      bwd_entry<128, 8, 4, 64>("k256q128c64"), bwd_entry<128, 8, 8, 32>("k256q256c32"),
+      bwd_entry<64, 8, 8, 64>("k256q256c64"),
+  };
+  for (const BwdEntry& e : table)
+    if (e.d == d && (name == nullptr || std::strcmp(name, e.name) == 0)) return &e;
+  return nullptr;
 }
 
 }  // namespace
@@ -659,11 +694,18 @@ hipError_t launch_bwd_preprocess(const float* O, const void* dO, float* Dout, in
 
 bool bwd_supported(int64_t d) { return d == 64 || d == 128; }
 
-int64_t bwd_onchip_elems(int64_t d) {
+int64_t bwd_onchip_elems(int64_t d) { return bwd_tile_info(d).onchip; }
+
+BwdTileInfo bwd_tile_info(int64_t d, const char* tile) {
+  const BwdEntry* e = bwd_pick(d, tile);
+  return e ? e->info : BwdTileInfo{0, 0, 0, 0};
+}
+
+const char* bwd_tile_names(int64_t d) {
   switch (d) {
-    case 64: return std::max(DkdvCfg<64, 8>::ONCHIP, DqCfg<64, 8, 64>::ONCHIP);
-    case 128: return std::max(DkdvCfg<128, 8>::ONCHIP, DqCfg<128, 8, 64>::ONCHIP);
-    default: return 0;
+    case 128: return "k256q256c64 k128q256c64 k256q128c64 k256q256c32";
+    case 64: return "k256q256c64";
+    default: return "";
   }
 }
 
@@ -674,12 +716,10 @@ size_t bwd_workspace_bytes(int64_t bh, int64_t n, int64_t) {
 hipError_t launch_bwd_bf16(const void* Q, const void* K, const void* V, const float* O,
                            const void* dO, const float* lse, float* dQ, float* dK, float* dV,
                            int64_t bh, int64_t n, int64_t d, float scale, void* workspace,
-                           hipStream_t stream) {
-  switch (d) {
-    case 64: return launch<64>(Q, K, V, O, dO, lse, dQ, dK, dV, bh, n, scale, workspace, stream);
-    case 128: return launch<128>(Q, K, V, O, dO, lse, dQ, dK, dV, bh, n, scale, workspace, stream);
-    default: return hipErrorInvalidValue;
-  }
+                           const char* tile, hipStream_t stream) {
+  const BwdEntry* e = bwd_pick(d, tile);
+  if (!e) return hipErrorInvalidValue;
+  return e->fn(Q, K, V, O, dO, lse, dQ, dK, dV, bh, n, scale, workspace, stream);
 }
 
 }  // namespace at

@@ -119,7 +119,11 @@ struct DirectCfg {
   static constexpr int INSTS = WAVE_CHUNKS / 64;   // load instructions per wave per tensor
   static constexpr int TILE = BC * D;              // bf16 elements per tile
   static constexpr int LDS_ELEMS = 4 * TILE;       // K[2], V[2]
-  static constexpr int64_t ONCHIP = (int64_t)BR * D * 2 + 2 * BR + 2 * BC * D + (int64_t)BR * BC;
+  // on-chip elements of one workgroup, each counted once whatever its width
+  // and every pipeline slot counted: Q and U blocks, (m, l), both slots of
+  // the K and V rings, the score tiles of the current and the next key tile
+  static constexpr int64_t ONCHIP =
+      (int64_t)BR * D * 2 + 2 * BR + 4 * BC * D + 2 * (int64_t)BR * BC;
   static_assert(CHUNKS % (NW * 64) == 0, "tile must split into whole wave loads");
 };
 
@@ -492,7 +496,9 @@ struct PingCfg {
   static constexpr int INSTS = WAVE_CHUNKS / 64;
   static constexpr int TILE = BC * D;
   static constexpr int LDS_ELEMS = 4 * TILE;
-  static constexpr int64_t ONCHIP = (int64_t)BR * D * 2 + 2 * BR + 2 * BC * D + (int64_t)BR * BC;
+  // as DirectCfg, with one score tile per wave (no next tile in flight)
+  static constexpr int64_t ONCHIP =
+      (int64_t)BR * D * 2 + 2 * BR + 4 * BC * D + (int64_t)BR * BC;
   static_assert(CHUNKS % (NW * 64) == 0, "tile must split into whole wave loads");
 };
 
@@ -751,6 +757,8 @@ template <int D>
 struct F32Cfg {
   static constexpr int NW = 4, BC = 32, NT = 256, BR = NW * 32;
   static constexpr int KLD = D + 2;  // padded K row (floats)
+  // single-buffered: Q and U blocks, (m, l), one K and one V tile, the
+  // score tile
   static constexpr int64_t ONCHIP = (int64_t)BR * D * 2 + 2 * BR + 2 * BC * D + (int64_t)BR * BC;
 };
 

@@ -87,12 +87,22 @@ hipError_t launch_fwd_smallcache_bf16(const void* Q, const void* K, const void* 
 
 // Backward.
 bool bwd_supported(int64_t d);
-int64_t bwd_onchip_elems(int64_t d);  // larger of the dK/dV and dQ kernels' footprints
+// Blockwise backward tile shapes: keys per dK/dV workgroup, queries per dQ
+// workgroup, keys per dQ tile, and on-chip elements (the larger kernel's).
+struct BwdTileInfo {
+  int keys_per_block, queries_per_block, key_tile;
+  int64_t onchip;
+};
+// `tile` names a compiled shape for d (nullptr: the default); all zeros if
+// unknown.  bwd_tile_names(d): the names, default first, space separated.
+BwdTileInfo bwd_tile_info(int64_t d, const char* tile = nullptr);
+const char* bwd_tile_names(int64_t d);
+int64_t bwd_onchip_elems(int64_t d);  // the default shape's footprint
 size_t bwd_workspace_bytes(int64_t bh, int64_t n, int64_t d);
 hipError_t launch_bwd_bf16(const void* Q, const void* K, const void* V, const float* O,
                            const void* dO, const float* lse, float* dQ, float* dK, float* dV,
                            int64_t bh, int64_t n, int64_t d, float scale, void* workspace,
-                           hipStream_t stream);
+                           const char* tile, hipStream_t stream);
 
 // D_i = <dO_i, O_i> for rows = bh * n rows of width d in {64, 128, 256}.
 hipError_t launch_bwd_preprocess(const float* O, const void* dO, float* Dout, int64_t rows,

@@ -43,6 +43,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-seco
        python bench.py --summarize-sweep DIR TIMING.jsonl OUT.md  (sweep table)
        python bench.py --smallcache-sweep [--steps K]   (square tiles at each b, d = 256)
        python bench.py --summarize-smallcache-sweep DIR TIMING.jsonl OUT.md
+       python bench.py --bwd-tile-sweep [--steps K]   (blockwise backward at each tile shape)
+       python bench.py --summarize-bwd-sweep DIR TIMING.jsonl OUT.md
 """
 from __future__ import annotations
 
@@ -520,12 +522,103 @@ def summarize_smallcache_sweep(pmc_dir: str, timing_path: str, out_path: str):
     print(text)
 
 
+
+def bwd_sweep_key(name: str):
+    """("dkdv", waves) or ("dq", waves, key tile) of a d = 128 blockwise
+    backward kernel name (demangled or mangled), else None."""
+    import re
+
+    m = re.search(r"bwd_dkdv3(?:<128, (\d+)>|ILi128ELi(\d+)E)", name)
+    if m:
+        return ("dkdv", int(m.group(1) or m.group(2)))
+    m = re.search(r"bwd_dq3(?:<128, (\d+), (\d+)>|ILi128ELi(\d+)ELi(\d+)E)", name)
+    if m:
+        nw, bc = (m.group(1), m.group(2)) if m.group(1) else (m.group(3), m.group(4))
+        return ("dq", int(nw), int(bc))
+    return None
+
+
+def summarize_bwd_sweep(pmc_dir: str, timing_path: str, out_path: str):
+    """Markdown table of the blockwise backward's tile sweep: per shape, the
+    dK/dV and dQ kernels' CU->L2 read bytes (TCC_READ_SECTORS) and L2-miss
+    read bytes (FETCH_SIZE), scaled by a plain copy, against the schedule's
+    count, and the two kernels' matrix-core busy fraction.  Expects
+    <dir>/bwdread_, bwdfetch_, bwdmfma_, copyread_ and copyfetch_
+    counter_collection.csv."""
+    def means(fname, counter):
+        return counter_means(os.path.join(pmc_dir, fname), counter, bwd_sweep_key)
+
+    cu = means("bwdread_counter_collection.csv", "TCC_READ_SECTORS_sum")
+    fe = means("bwdfetch_counter_collection.csv", "FETCH_SIZE")
+    busy_c = means("bwdmfma_counter_collection.csv", "SQ_VALU_MFMA_BUSY_CYCLES")
+    grbm = means("bwdmfma_counter_collection.csv", "GRBM_GUI_ACTIVE")
+    rd_unit = COPY_BYTES / copy_counter(os.path.join(pmc_dir, "copyread_counter_collection.csv"),
+                                        "TCC_READ_SECTORS_sum")
+    fe_unit = COPY_BYTES / copy_counter(os.path.join(pmc_dir, "copyfetch_counter_collection.csv"),
+                                        "FETCH_SIZE")
+    rows = [json.loads(line) for line in open(timing_path) if line.startswith("{")]
+    lines = ["| tile | keys per dK/dV block | queries per dQ block | keys per dQ tile | "
+             "M (elements) | ms | TFLOP/s at 10N^2d | CU->L2 read bytes | schedule | ratio | "
+             "L2-miss read bytes | matrix core busy |", "|" + "---|" * 12]
+    for r in rows:
+        ks = (("dkdv", r["keys_per_block"] // 32),
+              ("dq", r["queries_per_block"] // 32, r["key_tile"]))
+        c = sum(cu.get(x, float("nan")) for x in ks) * rd_unit
+        f = sum(fe.get(x, float("nan")) for x in ks) * fe_unit
+        cyc = sum(grbm.get(x, float("nan")) for x in ks) / 8.0
+        busy = sum(busy_c.get(x, float("nan")) for x in ks) / (1024.0 * cyc)
+        lines.append(
+            f"| {r['tile']} | {r['keys_per_block']} | {r['queries_per_block']} | {r['key_tile']} | "
+            f"{r['onchip_elems']:,} | {r['ms']} | {r['tflops_at_10N2d']} | {c / 1e9:.2f} GB | "
+            f"{r['sched_read_bytes'] / 1e9:.2f} GB | {c / r['sched_read_bytes']:.3f} | "
+            f"{f / 1e9:.3f} GB | {fmt_busy(busy)} |")
+    text = "\n".join(lines) + "\n"
+    text += (f"\nCounter scaling: one TCC_READ_SECTORS unit = {rd_unit:.2f} bytes and one "
+             f"FETCH_SIZE unit = {fe_unit:.1f} bytes (a plain copy of {COPY_BYTES} bytes).\n")
+    with open(out_path, "w") as f:
+        f.write(text)
+    print(text)
+
+
+def bwd_tile_sweep(args, at, torch, dev):
+    """Time the blockwise backward at every compiled tile shape (d = 128) on
+    the backward workload; one JSON line per shape."""
+    fn, w, info = leg_call("backward", at, torch, dev)
+    del fn
+    from aware_tiling_amd.inputs import workload_inputs
+
+    q, k, v, do = (t.to(dev) for t in workload_inputs(w))
+    o, lse = at.attn_fwd(q, k, v, w.scale)
+    grads = tuple(torch.empty((w.bh, w.n, w.d), dtype=torch.float32, device=dev)
+                  for _ in range(3))
+    need = int(at.lib().attn_bwd_workspace_size(w.bh, w.n, w.d))
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    fl = 10.0 * w.n * w.n * w.d * w.bh
+    for name in at.bwd_tiles(w.d):
+        t = at.bwd_tile_info(name, w.d)
+        print(f"[bench] backward tile {name}", file=sys.stderr, flush=True)
+        ms, _, _ = time_launches(lambda: at.attn_bwd_tile(name, q, k, v, o, do, lse, w.scale,
+                                                          workspace=ws, grads=grads),
+                                 args.steps, args.warmup, batch=True, warm_s=SECONDARY_WARM_S)
+        # CU->L2 reads of the schedule, bf16: every dK/dV block reads all of Q
+        # and dO (and its own K, V rows once); every dQ block all of K and V
+        # (and its own Q, dO rows once)
+        nd2 = w.n * w.d * 2
+        sched = w.bh * (2 * nd2 * (-(-w.n // t["keys_per_block"])) + 2 * nd2 +
+                        2 * nd2 * (-(-w.n // t["queries_per_block"])) + 2 * nd2)
+        print(json.dumps({"tile": name, **t, "ms": round(ms, 4),
+                          "tflops_at_10N2d": round(fl / (ms * 1e-3) / 1e12, 2),
+                          "sched_read_bytes": sched}), flush=True)
+
 def main():
     if len(sys.argv) >= 5 and sys.argv[1] == "--summarize-smallcache-sweep":
         summarize_smallcache_sweep(sys.argv[2], sys.argv[3], sys.argv[4])
         return
     if len(sys.argv) >= 3 and sys.argv[1] == "--summarize-leg-counters":
         summarize_leg_counters(sys.argv[2])
+        return
+    if len(sys.argv) >= 5 and sys.argv[1] == "--summarize-bwd-sweep":
+        summarize_bwd_sweep(sys.argv[2], sys.argv[3], sys.argv[4])
         return
     if len(sys.argv) >= 5 and sys.argv[1] == "--summarize-sweep":
         summarize_sweep(sys.argv[2], sys.argv[3], sys.argv[4])
@@ -544,6 +637,9 @@ def main():
     ap.add_argument("--tile-sweep", action="store_true",
                     help="time every query-block x key-tile shape of the fused forward on the "
                          "headline workload (one JSON line per shape) and exit")
+    ap.add_argument("--bwd-tile-sweep", action="store_true",
+                    help="time the blockwise backward at every compiled tile shape (d = 128) "
+                         "on the backward workload (one JSON line per shape) and exit")
     ap.add_argument("--smallcache-sweep", action="store_true",
                     help="time the square-tile forward at every tile b on the d = 256 "
                          "small-cache workload (one JSON line per tile) and exit")
@@ -583,6 +679,9 @@ def main():
         return
     if args.smallcache_sweep:
         smallcache_sweep(args, at, torch, dev)
+        return
+    if args.bwd_tile_sweep:
+        bwd_tile_sweep(args, at, torch, dev)
         return
     if args.secondary_only:
         print(json.dumps({"secondary": secondary(args, at, torch, dev)}), flush=True)

@@ -105,9 +105,10 @@ attn_status attn_fwd(const void* Q, const void* K, const void* V, float* O,
 
 /*
  * On-chip elements M held by one workgroup of attn_fwd for head dimension d
- * (query block, its accumulators and statistics, the key/value tiles and the
- * score tile, each element counted once whatever its width), the quantity
- * the exposition calls the fast-memory size M; and the query-block rows B.
+ * (query block, its accumulators and statistics, the key/value tiles of
+ * every pipeline slot and the score tiles in flight, each element counted
+ * once whatever its width), the quantity the exposition calls the
+ * fast-memory size M; and the query-block rows B.
  * Returns 0 for unsupported (d, dtype).
  */
 int64_t attn_fwd_onchip_elems(int64_t d, attn_dtype dtype);
@@ -334,11 +335,40 @@ int64_t attn_smallcache_onchip_elems(int64_t b);
 size_t attn_bwd_workspace_size(int64_t bh, int64_t n, int64_t d);
 
 /*
+ * attn_bwd_tile -- attn_bwd with the tile shape named explicitly, for tile
+ * sweeps and tests of every compiled shape (attn_bwd always takes the
+ * default).  A shape is keys per dK/dV workgroup (k), queries per dQ
+ * workgroup (q) and keys per dQ tile (c); every shape gives the same bits.
+ *
+ *   attn_bwd_tiles(d) : space-separated names of the shapes compiled for
+ *             head dimension d, the default first; "" if none (static
+ *             storage).
+ *   attn_bwd_tile_info : keys per dK/dV workgroup, queries per dQ
+ *             workgroup, keys per dQ tile and on-chip elements (as
+ *             attn_bwd_onchip_elems) of shape `tile` at d; any output
+ *             pointer may be NULL.  ATTN_ERR_UNSUPPORTED for an unknown
+ *             (tile, d), ATTN_ERR_INVALID_ARG for a NULL name.
+ *   attn_bwd_tile : arguments, results and errors as attn_bwd, plus
+ *             ATTN_ERR_INVALID_ARG for a NULL name and ATTN_ERR_UNSUPPORTED
+ *             for an unknown one.
+ */
+const char* attn_bwd_tiles(int64_t d);
+attn_status attn_bwd_tile_info(const char* tile, int64_t d, int64_t* keys_per_block,
+                               int64_t* queries_per_block, int64_t* key_tile,
+                               int64_t* onchip_elems);
+attn_status attn_bwd_tile(const char* tile, const void* Q, const void* K,
+                          const void* V, const float* O, const void* dO,
+                          const float* lse, float* dQ, float* dK, float* dV,
+                          int64_t bh, int64_t n, int64_t d, float scale,
+                          attn_dtype dtype, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
  * On-chip elements M held by one workgroup of attn_bwd for head dimension d:
  * the larger of its two kernels' resident sets (the dK/dV kernel's key rows,
  * accumulators, one query tile and score tiles; the dQ kernel's query rows,
  * accumulator, one key tile and score tiles), each element counted once
- * whatever its width and one stage of each streamed tile, as for
+ * whatever its width and every pipeline slot counted, as for
  * attn_fwd_onchip_elems: the M of Theorem 1.1 on the page "On Fine-Grained
  * I/O Complexity of Attention Backward Passes".  0 for an unsupported d.
  */

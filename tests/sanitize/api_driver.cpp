@@ -94,8 +94,12 @@ int main() {
                 (void)attn_bwd_smallcache_onchip_elems(d, x);
                 (void)attn_smallcache_onchip_elems(x);
               }
-              for (size_t w : wss)
+              for (size_t w : wss) {
                 run([&] { return attn_bwd(p, base, base, fp, base, fp, fp, fp, fp, bh, n, d, sc, ATTN_BF16, base, w, nullptr); }, pok);
+                run([&] { return attn_bwd_tile("k256q256c64", p, base, base, fp, base, fp, fp, fp, fp, bh, n, d, sc, ATTN_BF16, base, w, nullptr); }, pok);
+                run([&] { return attn_bwd_tile("nope", p, base, base, fp, base, fp, fp, fp, fp, bh, n, d, sc, ATTN_BF16, base, w, nullptr); }, false);
+                run([&] { return attn_bwd_tile(nullptr, p, base, base, fp, base, fp, fp, fp, fp, bh, n, d, sc, ATTN_BF16, base, w, nullptr); }, false);
+              }
             }
             (void)attn_bwd_workspace_size(bh, n, d);
             (void)attn_bwd_onchip_elems(d);
@@ -106,6 +110,9 @@ int main() {
             (void)attn_fwd_tile_info("default", d, &a, &b, &c);
             (void)attn_fwd_tile_info("nope", d, nullptr, nullptr, nullptr);
             (void)attn_fwd_tiles(d);
+            (void)attn_bwd_tiles(d);
+            (void)attn_bwd_tile_info("k256q256c64", d, &a, &b, &c, &a);
+            (void)attn_bwd_tile_info("nope", d, nullptr, nullptr, nullptr, nullptr);
           }
     for (int64_t wg : {(int64_t)-1, (int64_t)0, (int64_t)1, (int64_t)INT32_MAX, (int64_t)INT32_MAX + 1, BIG})
       for (int32_t it : {-1, 0, 1, INT32_MAX})

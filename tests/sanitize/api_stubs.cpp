@@ -100,10 +100,16 @@ hipError_t launch_fwd_smallcache_bf16(const void*, const void*, const void*, flo
 }
 bool bwd_supported(int64_t d) { return d == 64 || d == 128; }
 int64_t bwd_onchip_elems(int64_t d) { return bwd_supported(d) ? 1 : 0; }
+BwdTileInfo bwd_tile_info(int64_t d, const char* tile) {
+  if (!bwd_supported(d)) return BwdTileInfo{0, 0, 0, 0};
+  if (tile == nullptr || std::strcmp(tile, "k256q256c64") == 0) return BwdTileInfo{256, 256, 64, 1};
+  return BwdTileInfo{0, 0, 0, 0};
+}
+const char* bwd_tile_names(int64_t d) { return bwd_supported(d) ? "k256q256c64" : ""; }
 size_t bwd_workspace_bytes(int64_t bh, int64_t n, int64_t) { return 2 * align256_bytes((size_t)bh * n * 4); }
 hipError_t launch_bwd_bf16(const void*, const void*, const void*, const float*, const void*,
                            const float*, float*, float*, float*, int64_t, int64_t, int64_t, float,
-                           void*, hipStream_t) {
+                           void*, const char*, hipStream_t) {
   return launched();
 }
 bool bwd_smallcache_supported(int64_t d) { return d == 128 || d == 256; }

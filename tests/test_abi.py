@@ -107,6 +107,43 @@ def test_fwd_tile_validation(lib):
     assert call(q=None, o=None, n=0) == OK
 
 
+def test_bwd_tile_listing_and_validation(lib):
+    """attn_bwd_tiles lists the backward's compiled shapes, the default first
+    (the one attn_bwd runs, whose on-chip count attn_bwd_onchip_elems
+    reports); the names decode to keys per dK/dV workgroup, queries per dQ
+    workgroup and keys per dQ tile; unknown names are refused before any
+    launch."""
+    expect = {128: ["k256q256c64", "k128q256c64", "k256q128c64", "k256q256c32"],
+              64: ["k256q256c64"]}
+    for d, names in expect.items():
+        assert binding.bwd_tiles(d) == names
+        assert binding.bwd_tile_info(names[0], d)["onchip_elems"] == lib.attn_bwd_onchip_elems(d)
+        for name in names:
+            info = binding.bwd_tile_info(name, d)
+            k, rest = name[1:].split("q")
+            qb, c = rest.split("c")
+            assert (info["keys_per_block"], info["queries_per_block"], info["key_tile"]) == (
+                int(k), int(qb), int(c))
+            assert info["onchip_elems"] >= d * d  # large-cache regime
+    assert binding.bwd_tiles(256) == []
+    assert lib.attn_bwd_tile_info(b"nope", 128, None, None, None, None) == UNSUPPORTED
+    assert lib.attn_bwd_tile_info(b"k128q256c64", 64, None, None, None, None) == UNSUPPORTED
+    assert lib.attn_bwd_tile_info(None, 128, None, None, None, None) == INVALID
+    ws = lib.attn_bwd_workspace_size(2, 512, 128)
+
+    def call(tile=b"k128q256c64", q=FAKE, dv=FAKE, d=128, dtype=BF16, w=FAKE * 256, n=512):
+        return lib.attn_bwd_tile(tile, q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dv, 2, n, d,
+                                 0.08, dtype, w, ws, None)
+    assert call(tile=None) == INVALID
+    assert call(tile=b"nope") == UNSUPPORTED
+    assert call(d=64) == UNSUPPORTED  # k128q256c64 exists only at d = 128
+    assert call(dtype=F32) == UNSUPPORTED
+    assert call(q=None) == INVALID
+    assert call(dv=FAKE + 8) == INVALID
+    assert call(w=None) == WORKSPACE
+    assert call(q=None, dv=None, n=0) == OK
+
+
 def fwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, bh=1, n=128, d=64, scale=0.125,
         dtype=BF16):
     return lib.attn_fwd(q, k, v, o, lse, bh, n, d, scale, dtype, None)
@@ -141,6 +178,10 @@ def test_fwd_tile_queries(lib):
         # the fused kernel is the large-cache schedule: M >= d^2
         assert m >= d * d
     assert lib.attn_fwd_onchip_elems(96, BF16) == 0
+    # the d = 128 default (256 query rows, 64-key tiles): Q and U blocks, (m, l),
+    # both slots of the K and V rings, the current and the next score tile
+    assert lib.attn_fwd_onchip_elems(128, BF16) == (2 * 256 * 128 + 2 * 256 + 4 * 64 * 128
+                                                    + 2 * 256 * 64) == 131584
     assert lib.attn_fwd_query_block(64, F32) > 0
 
 
@@ -278,13 +319,13 @@ def test_splitk_validation_and_sizes(lib):
 
 
 def test_bwd_onchip_elems(lib):
-    # the larger of the two kernels' resident sets (one stage of each streamed
-    # tile): dK/dV 4 Bkv d + 2 Bq d + 2 Bq + 2 Bkv Bq with Bkv = 256 keys and
-    # Bq = 32 queries (64 at d = 64); dQ 3 Bqb d + 2 Bqb + 2 Bc d + 2 Bqb Bc with
+    # the larger of the two kernels' resident sets (every pipeline slot):
+    # dK/dV 4 Bkv d + 4 Bq d + 4 Bq + 2 Bkv Bq with Bkv = 256 keys and Bq = 32
+    # queries (64 at d = 64); dQ 3 Bqb d + 2 Bqb + 4 Bc d + 2 Bqb Bc with
     # Bqb = 256 queries and Bc = 64 keys; both >= d^2 (the large-cache regime)
-    dkdv = lambda d, bq: 4 * 256 * d + 2 * bq * d + 2 * bq + 2 * 256 * bq
-    dq = lambda d: 3 * 256 * d + 2 * 256 + 2 * 64 * d + 2 * 256 * 64
-    assert lib.attn_bwd_onchip_elems(128) == max(dkdv(128, 32), dq(128)) == 155712
+    dkdv = lambda d, bq: 4 * 256 * d + 4 * bq * d + 4 * bq + 2 * 256 * bq
+    dq = lambda d: 3 * 256 * d + 2 * 256 + 4 * 64 * d + 2 * 256 * 64
+    assert lib.attn_bwd_onchip_elems(128) == max(dkdv(128, 32), dq(128)) == 164352
     assert lib.attn_bwd_onchip_elems(64) == max(dkdv(64, 64), dq(64))
     assert lib.attn_bwd_onchip_elems(128) >= 128 * 128
     assert lib.attn_bwd_onchip_elems(256) == 0 and lib.attn_bwd_onchip_elems(-1) == 0

@@ -126,3 +126,40 @@ def test_mfma_busy_sums_the_kernels_of_one_key(tmp_path):
     assert set(busy) == {128}
     assert abs(busy[128] - (1280.0 + 2560.0) / (128.0 * (20.0 + 30.0))) < 1e-12
     assert bench.mfma_busy(str(tmp_path), "absent.csv", bench.smallcache_sweep_key) == {}
+
+
+def test_bwd_sweep_keys_and_summary(tmp_path):
+    assert bench.bwd_sweep_key("void at::bwd_dkdv3<128, 8>(a)") == ("dkdv", 8)
+    assert bench.bwd_sweep_key("_ZN2at9bwd_dkdv3ILi128ELi4EEEvPKDF16b") == ("dkdv", 4)
+    assert bench.bwd_sweep_key("void at::bwd_dq3<128, 8, 32>(a)") == ("dq", 8, 32)
+    assert bench.bwd_sweep_key("_ZN2at7bwd_dq3ILi128ELi4ELi64EEEvPK") == ("dq", 4, 64)
+    assert bench.bwd_sweep_key("void at::bwd_dq3<64, 8, 64>(a)") is None
+    assert bench.bwd_sweep_key("bwd_preprocess<128>") is None
+    # one shape: its dK/dV and dQ kernels' counters add; copy calibration
+    # makes one TCC_READ_SECTORS unit 2 bytes and one FETCH_SIZE unit 4
+    c = bench.COPY_BYTES
+    _counter_csv(tmp_path / "copyread_counter_collection.csv",
+                 [("__amd_rocclr_copyBuffer", "TCC_READ_SECTORS_sum", c / 2)])
+    _counter_csv(tmp_path / "copyfetch_counter_collection.csv",
+                 [("__amd_rocclr_copyBuffer", "FETCH_SIZE", c / 4)])
+    dk, dq = "void at::bwd_dkdv3<128, 8>(a)", "void at::bwd_dq3<128, 8, 64>(a)"
+    _counter_csv(tmp_path / "bwdread_counter_collection.csv",
+                 [(dk, "TCC_READ_SECTORS_sum", 300.0), (dq, "TCC_READ_SECTORS_sum", 200.0)])
+    _counter_csv(tmp_path / "bwdfetch_counter_collection.csv",
+                 [(dk, "FETCH_SIZE", 10.0), (dq, "FETCH_SIZE", 5.0)])
+    _counter_csv(tmp_path / "bwdmfma_counter_collection.csv",
+                 [(dk, "SQ_VALU_MFMA_BUSY_CYCLES", 1024.0 * 30), (dk, "GRBM_GUI_ACTIVE", 8 * 60.0),
+                  (dq, "SQ_VALU_MFMA_BUSY_CYCLES", 1024.0 * 10), (dq, "GRBM_GUI_ACTIVE", 8 * 40.0)])
+    timing = tmp_path / "t.jsonl"
+    timing.write_text(json.dumps({"tile": "k256q256c64", "keys_per_block": 256,
+                                  "queries_per_block": 256, "key_tile": 64, "onchip_elems": 9,
+                                  "ms": 1.0, "tflops_at_10N2d": 2.0,
+                                  "sched_read_bytes": 1000.0}) + "\n")
+    out = tmp_path / "t.md"
+    bench.summarize_bwd_sweep(str(tmp_path), str(timing), str(out))
+    row = [line for line in out.read_text().splitlines() if line.startswith("| k256")][0]
+    cells = [x.strip() for x in row.strip("|").split("|")]
+    assert cells[7] == f"{1000 / 1e9:.2f} GB"       # (300 + 200) sectors x 2 bytes
+    assert cells[9] == "1.000"                          # against the 1000-byte schedule
+    assert cells[10] == f"{60 / 1e9:.3f} GB"           # (10 + 5) x 4 bytes
+    assert cells[11] == bench.fmt_busy(40.0 / 100.0)   # (30 + 10) / (60 + 40)

@@ -87,3 +87,30 @@ def test_bwd_rejects_unsupported_head_dim():
     o, lse = at.attn_fwd(q, k, v)
     with pytest.raises(at.AttnError):
         at.attn_bwd(q, k, v, o, do, lse)
+
+
+BWD_TILE_CASES = [(2, 300, 128, 89, 1.0), (1, 1000, 128, 90, 4.0), (1, 33, 128, 91, 1.0)]
+
+
+@pytest.mark.parametrize("bh,n,d,seed,q_mult", BWD_TILE_CASES,
+                         ids=[f"{c[0]}x{c[1]}x{c[2]}-q{c[4]:g}" for c in BWD_TILE_CASES])
+def test_bwd_every_tile_shape_gives_the_default_bits(bh, n, d, seed, q_mult):
+    """Every compiled backward tile shape (attn_bwd_tile) processes each
+    wave's 32 rows in the same order as the default, so its gradients equal
+    attn_bwd's bit for bit; the default is held to the oracle above."""
+    (qc, kc, vc, doc), (q, k, v, do) = inputs(bh, n, d, "bf16", seed, q_mult, with_do=True)
+    scale = at.default_scale(d)
+    o, lse = at.attn_fwd(q, k, v, scale)
+    ref = at.attn_bwd(q, k, v, o, do, lse, scale)
+    tiles = at.bwd_tiles(d)
+    assert len(tiles) > 1
+    rq, rk, rv, _, _ = oracle.attn_bwd(f64(qc), f64(kc), f64(vc), f64(doc), scale)
+    for tile in tiles:
+        say(f"attn_bwd_tile {tile} bh={bh} n={n} d={d} qx{q_mult}")
+        got = at.attn_bwd_tile(tile, q, k, v, o, do, lse, scale)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dQ", "dK", "dV"), got, ref):
+            assert torch.equal(a, b), f"{tile}: {name} differs from the default"
+    check(f64(ref[0]), rq, TOL["bf16"], f"dQ {bh}x{n}x{d}", grad_scaled=q_mult > 1.0)
+    check(f64(ref[1]), rk, TOL["bf16"], f"dK {bh}x{n}x{d}", grad_scaled=q_mult > 1.0)
+    check(f64(ref[2]), rv, TOL["bf16"], f"dV {bh}x{n}x{d}", grad_scaled=q_mult > 1.0)
