@@ -73,9 +73,10 @@ struct IntC {
 // need only one barrier per step: the K buffer written in step j held K_j,
 // last read in step j-1, and the V buffer written held V_{j-1}, also last
 // read in step j-1.  Steps are unrolled in pairs so every LDS offset is a
-// compile-time constant; only the last tile takes the key mask.  Rows past
-// n are clamped to row n-1 when loading (finite data; those keys are masked
-// in the last tile), so no load leaves the tensor.
+// compile-time constant; only the last tile takes the key mask.  Copies go
+// through a buffer resource whose range ends at the head's last key, so rows
+// past n land as zeros (those keys are masked in the last tile) and no load
+// leaves the tensor.
 
 // Arguments of the direct-load forward body.  Queries [bh, nq, d], keys and
 // values [bh, nk, d]; outputs [splits, bh, nq, d] and [splits, bh, nq].
@@ -749,7 +750,8 @@ __global__ __launch_bounds__(512, 1) void fwd_fused_bf16_pingpong_kernel(
 // ---------------------------------------------------------------------------
 // fp32 path: same schedule with v_mfma_f32_32x32x2_f32 and exact per-tile
 // rescaling.  One wave per 32 query rows, 4 waves, 32-key tiles, single
-// LDS buffer.  Each lane holds one element of each MFMA operand, so the
+// LDS buffer (one wave per SIMD: at d = 256 the Q rows and U take 256 of a
+// lane's 512 registers).  Each lane holds one element of each MFMA operand, so the
 // value tile stays row-major: for the PV step t the lane pair feeds key
 // 8(t/4) + 4h + t%4, exactly the key its score register t holds.
 
@@ -1113,7 +1115,7 @@ hipError_t launch_fwd_sparse_bf16(const void* Q, const void* K, const void* V, f
 }
 
 bool fused_bf16_supported(int64_t d) { return pick(d) != nullptr; }
-bool fused_f32_supported(int64_t d) { return d == 64 || d == 128; }
+bool fused_f32_supported(int64_t d) { return d == 64 || d == 128 || d == 256; }
 
 FusedTileInfo fused_bf16_tile_info(int64_t d, const char* tile) {
   const FusedEntry* e = pick(d, tile);
@@ -1150,6 +1152,7 @@ FusedTileInfo fused_f32_tile_info(int64_t d) {
   switch (d) {
     case 64: return FusedTileInfo{F32Cfg<64>::BR, F32Cfg<64>::BC, F32Cfg<64>::ONCHIP};
     case 128: return FusedTileInfo{F32Cfg<128>::BR, F32Cfg<128>::BC, F32Cfg<128>::ONCHIP};
+    case 256: return FusedTileInfo{F32Cfg<256>::BR, F32Cfg<256>::BC, F32Cfg<256>::ONCHIP};
     default: return FusedTileInfo{0, 0, 0};
   }
 }
@@ -1174,6 +1177,7 @@ hipError_t launch_fwd_fused_f32(const float* Q, const float* K, const float* V, 
   switch (d) {
     case 64: return launch_f32<64>(Q, K, V, O, lse, bh, n, c, stream);
     case 128: return launch_f32<128>(Q, K, V, O, lse, bh, n, c, stream);
+    case 256: return launch_f32<256>(Q, K, V, O, lse, bh, n, c, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -96,8 +96,8 @@ const char* attn_version(void);
  *   O       : [bh, n, d] float (device, written)
  *   lse     : [bh, n] float, natural-log log-sum-exp of each row of scaled
  *             scores, log(sum_j exp(scale <q_i,k_j>)); may be NULL.
- *   bh >= 0, n >= 0 (bh*n == 0 is a no-op), d in {64, 128, 256} for bf16,
- *   d in {64, 128} for f32.
+ *   bh >= 0, n >= 0 (bh*n == 0 is a no-op), d in {64, 128, 256} for bf16
+ *   and for f32.
  */
 attn_status attn_fwd(const void* Q, const void* K, const void* V, float* O,
                      float* lse, int64_t bh, int64_t n, int64_t d, float scale,

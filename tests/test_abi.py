@@ -155,7 +155,7 @@ def test_fwd_validation(lib):
     assert fwd(lib, q=FAKE + 2) == INVALID  # misaligned
     assert fwd(lib, lse=FAKE + 4) == INVALID
     assert fwd(lib, d=96) == UNSUPPORTED
-    assert fwd(lib, d=256, dtype=F32) == UNSUPPORTED
+    assert fwd(lib, d=96, dtype=F32) == UNSUPPORTED
     assert fwd(lib, dtype=7) == UNSUPPORTED
     assert fwd(lib, scale=0.0) == INVALID
     assert fwd(lib, scale=-1.0) == INVALID
@@ -182,7 +182,12 @@ def test_fwd_tile_queries(lib):
     # both slots of the K and V rings, the current and the next score tile
     assert lib.attn_fwd_onchip_elems(128, BF16) == (2 * 256 * 128 + 2 * 256 + 4 * 64 * 128
                                                     + 2 * 256 * 64) == 131584
-    assert lib.attn_fwd_query_block(64, F32) > 0
+    for d in (64, 128, 256):
+        assert lib.attn_fwd_query_block(d, F32) == 128
+        # single-buffered fp32 tiles: Q and U blocks, (m, l), one K and one V
+        # tile of 32 keys, one score tile
+        assert lib.attn_fwd_onchip_elems(d, F32) == 2 * 128 * d + 2 * 128 + 2 * 32 * d + 128 * 32
+    assert lib.attn_fwd_query_block(96, F32) == 0
 
 
 def test_smallcache_validation(lib):

@@ -27,6 +27,8 @@ SMALL = [
     (2, 300, 64, "f32", 11, 1.0),
     (1, 129, 128, "f32", 12, 1.0),
     (1, 1, 64, "f32", 13, 1.0),
+    (1, 200, 256, "f32", 14, 1.0),
+    (2, 65, 256, "f32", 15, 4.0),
     (2, 300, 64, "bf16", 21, 1.0),
     (3, 1000, 128, "bf16", 22, 1.0),
     (1, 257, 256, "bf16", 23, 1.0),
