@@ -171,7 +171,7 @@ struct DkdvCfg {
 // issued S, dP, dV, dK, so that the exponentials overlap the dP MFMAs and
 // dS the dV MFMAs.
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dkdv3(
+__global__ __launch_bounds__(NW * 64, (D >= 256 ? 1 : 8 / NW)) void bwd_dkdv3(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ Dg,
     float* __restrict__ dK, float* __restrict__ dV, int n, int nkb, int total, float c,
@@ -434,7 +434,7 @@ struct DqCfg {
 // unrolled by two so that the stage is a constant.  Operands are read two
 // MFMAs ahead.
 template <int D, int NW, int BC>
-__global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq3(
+__global__ __launch_bounds__(NW * 64, (D >= 256 ? 1 : 8 / NW)) void bwd_dq3(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dg,
     float* __restrict__ dQ, int n, int nqb, int total, float c, float scale) {
@@ -663,6 +663,9 @@ const BwdEntry* bwd_pick(int64_t d, const char* name) {
       bwd_entry<128, 8, 8, 64>("k256q256c64"), bwd_entry<128, 4, 8, 64>("k128q256c64"),
       bwd_entry<128, 8, 4, 64>("k256q128c64"), bwd_entry<128, 8, 8, 32>("k256q256c32"),
       bwd_entry<64, 8, 8, 64>("k256q256c64"),
+      // d = 256: four waves, one per SIMD (a wave's dK^T and dV^T alone
+      // take 256 of its 512 registers)
+      bwd_entry<256, 4, 4, 64>("k128q128c64"),
   };
   for (const BwdEntry& e : table)
     if (e.d == d && (name == nullptr || std::strcmp(name, e.name) == 0)) return &e;
@@ -692,7 +695,7 @@ hipError_t launch_bwd_preprocess(const float* O, const void* dO, float* Dout, in
   return hipGetLastError();
 }
 
-bool bwd_supported(int64_t d) { return d == 64 || d == 128; }
+bool bwd_supported(int64_t d) { return d == 64 || d == 128 || d == 256; }
 
 int64_t bwd_onchip_elems(int64_t d) { return bwd_tile_info(d).onchip; }
 
@@ -705,6 +708,7 @@ const char* bwd_tile_names(int64_t d) {
   switch (d) {
     case 128: return "k256q256c64 k128q256c64 k256q128c64 k256q256c32";
     case 64: return "k256q256c64";
+    case 256: return "k128q128c64";
     default: return "";
   }
 }

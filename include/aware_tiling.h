@@ -330,7 +330,8 @@ int64_t attn_smallcache_onchip_elems(int64_t b);
  *   dQ, dK, dV  : [bh, n, d] float (device, written)
  *   workspace   : at least attn_bwd_workspace_size(bh, n, d) bytes,
  *                 256-byte aligned; contents on return unspecified.
- *   bf16 only, d in {64, 128}.
+ *   bf16 only, d in {64, 128, 256} (at d = 256 four waves, one per SIMD, of
+ *   128 keys or queries per workgroup).
  */
 size_t attn_bwd_workspace_size(int64_t bh, int64_t n, int64_t d);
 

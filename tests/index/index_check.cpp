@@ -282,6 +282,7 @@ int main() {
   check_fused_forward<128, 4, 64>("fwd d128 4x64 (split, sparse)");
   check_backward<128, 8>();
   check_backward<64, 8>();
+  check_backward<256, 4>();
 
   std::printf("index maps: %ld checks passed\n", g_checks);
   return 0;

@@ -114,7 +114,7 @@ def test_bwd_tile_listing_and_validation(lib):
     workgroup and keys per dQ tile; unknown names are refused before any
     launch."""
     expect = {128: ["k256q256c64", "k128q256c64", "k256q128c64", "k256q256c32"],
-              64: ["k256q256c64"]}
+              64: ["k256q256c64"], 256: ["k128q128c64"]}
     for d, names in expect.items():
         assert binding.bwd_tiles(d) == names
         assert binding.bwd_tile_info(names[0], d)["onchip_elems"] == lib.attn_bwd_onchip_elems(d)
@@ -125,7 +125,7 @@ def test_bwd_tile_listing_and_validation(lib):
             assert (info["keys_per_block"], info["queries_per_block"], info["key_tile"]) == (
                 int(k), int(qb), int(c))
             assert info["onchip_elems"] >= d * d  # large-cache regime
-    assert binding.bwd_tiles(256) == []
+    assert binding.bwd_tiles(96) == []
     assert lib.attn_bwd_tile_info(b"nope", 128, None, None, None, None) == UNSUPPORTED
     assert lib.attn_bwd_tile_info(b"k128q256c64", 64, None, None, None, None) == UNSUPPORTED
     assert lib.attn_bwd_tile_info(None, 128, None, None, None, None) == INVALID
@@ -325,15 +325,18 @@ def test_splitk_validation_and_sizes(lib):
 
 def test_bwd_onchip_elems(lib):
     # the larger of the two kernels' resident sets (every pipeline slot):
-    # dK/dV 4 Bkv d + 4 Bq d + 4 Bq + 2 Bkv Bq with Bkv = 256 keys and Bq = 32
-    # queries (64 at d = 64); dQ 3 Bqb d + 2 Bqb + 4 Bc d + 2 Bqb Bc with
-    # Bqb = 256 queries and Bc = 64 keys; both >= d^2 (the large-cache regime)
-    dkdv = lambda d, bq: 4 * 256 * d + 4 * bq * d + 4 * bq + 2 * 256 * bq
-    dq = lambda d: 3 * 256 * d + 2 * 256 + 4 * 64 * d + 2 * 256 * 64
-    assert lib.attn_bwd_onchip_elems(128) == max(dkdv(128, 32), dq(128)) == 164352
-    assert lib.attn_bwd_onchip_elems(64) == max(dkdv(64, 64), dq(64))
-    assert lib.attn_bwd_onchip_elems(128) >= 128 * 128
-    assert lib.attn_bwd_onchip_elems(256) == 0 and lib.attn_bwd_onchip_elems(-1) == 0
+    # dK/dV 4 Bkv d + 4 Bq d + 4 Bq + 2 Bkv Bq with Bkv keys per workgroup
+    # (256; 128 at d = 256) and Bq = 32 queries (64 at d = 64); dQ 3 Bqb d +
+    # 2 Bqb + 4 Bc d + 2 Bqb Bc with Bqb queries per workgroup (256; 128 at
+    # d = 256) and Bc = 64 keys; all >= d^2 (the large-cache regime)
+    dkdv = lambda d, bkv, bq: 4 * bkv * d + 4 * bq * d + 4 * bq + 2 * bkv * bq
+    dq = lambda d, bqb: 3 * bqb * d + 2 * bqb + 4 * 64 * d + 2 * bqb * 64
+    assert lib.attn_bwd_onchip_elems(128) == max(dkdv(128, 256, 32), dq(128, 256)) == 164352
+    assert lib.attn_bwd_onchip_elems(64) == max(dkdv(64, 256, 64), dq(64, 256))
+    assert lib.attn_bwd_onchip_elems(256) == max(dkdv(256, 128, 32), dq(256, 128)) == 180480
+    for d in (64, 128, 256):
+        assert lib.attn_bwd_onchip_elems(d) >= d * d
+    assert lib.attn_bwd_onchip_elems(96) == 0 and lib.attn_bwd_onchip_elems(-1) == 0
 
 
 def test_bwd_smallcache_tile_selection_and_validation(lib):

@@ -29,6 +29,9 @@ CASES = [
     (1, 513, 128, 86, 4.0),
     (1, 300, 128, 87, 20.0),  # peaked weights
     (3, 160, 64, 88, 1.0),
+    (1, 200, 256, 92, 1.0),
+    (2, 129, 256, 93, 4.0),
+    (1, 1, 256, 94, 1.0),
 ]
 
 
@@ -83,10 +86,25 @@ def test_bwd_deterministic():
 
 
 def test_bwd_rejects_unsupported_head_dim():
-    (_, (q, k, v, do)) = inputs(1, 64, 256, "bf16", 90, with_do=True)
-    o, lse = at.attn_fwd(q, k, v)
+    (_, (q, k, v, do)) = inputs(1, 64, 96, "bf16", 90, with_do=True)
+    o = torch.zeros(q.shape, dtype=torch.float32, device=q.device)
+    lse = torch.zeros(q.shape[:2], dtype=torch.float32, device=q.device)
     with pytest.raises(at.AttnError):
         at.attn_bwd(q, k, v, o, do, lse)
+
+
+def test_bwd_d256_workload_every_head():
+    """The blockwise backward at d = 256 (four waves, 128 keys or queries
+    per workgroup) on the batch 1 x 8 heads, N 4096 workload of the
+    small-cache backward, every head against the oracle, and against the
+    small-cache backward's gradients on the same inputs."""
+    w = WORKLOADS["bwd_smallcache_bf16_b1h8_n4096_d256"]
+    say(f"attn_bwd d=256 on {w.name}")
+    (qc, kc, vc, doc), (q, k, v, do), (dq, dk, dv), scale = _grads(w.bh, w.n, w.d, w.seed, 1.0)
+    rq, rk, rv, _, _ = oracle.attn_bwd(f64(qc), f64(kc), f64(vc), f64(doc), scale)
+    check(f64(dq), rq, TOL["bf16"], "dQ d256 all heads")
+    check(f64(dk), rk, TOL["bf16"], "dK d256 all heads")
+    check(f64(dv), rv, TOL["bf16"], "dV d256 all heads")
 
 
 BWD_TILE_CASES = [(2, 300, 128, 89, 1.0), (1, 1000, 128, 90, 4.0), (1, 33, 128, 91, 1.0)]
