@@ -76,6 +76,8 @@ LEGS = {
     "smallcache": (["aware_tiling_amd/csrc/fwd_smallcache.hip"],
                    ("sc_scores_exp", "sc_value_product")),
     "backward": (["aware_tiling_amd/csrc/bwd.hip"], ("bwd_preprocess", "bwd_dkdv3", "bwd_dq3")),
+    "backward_d256": (["aware_tiling_amd/csrc/bwd.hip"],
+                      ("bwd_preprocess", "bwd_dkdv3", "bwd_dq3")),
     "smallcache_backward_d256": (["aware_tiling_amd/csrc/bwd_smallcache.hip",
                                   "aware_tiling_amd/csrc/bwd.hip"], ("bwd_preprocess", "sb_")),
     "smallcache_backward_d128": (["aware_tiling_amd/csrc/bwd_smallcache.hip",
@@ -84,6 +86,10 @@ LEGS = {
 SMALLCACHE_M = 49152  # 3/4 of d^2 at d = 256: the small-cache regime M < d^2
 SMALLCACHE_BWD = {"smallcache_backward_d256": ("bwd_smallcache_bf16_b1h8_n4096_d256", 49152),
                   "smallcache_backward_d128": ("bwd_bf16_b2h16_n4096_d128", 12288)}
+# the blockwise (large-cache) backward on its own workload and on the d = 256
+# workload of the small-cache backward
+BLOCKWISE_BWD = {"backward": "bwd_bf16_b2h16_n4096_d128",
+                 "backward_d256": "bwd_smallcache_bf16_b1h8_n4096_d256"}
 
 
 def kernel_digest(leg: str = "headline") -> str:
@@ -235,8 +241,8 @@ def leg_call(leg: str, at, torch, dev):
                                                workspace=ws)), w, {"m_elems": SMALLCACHE_M,
                                                                    "q": q, "k": k, "v": v,
                                                                    "o": o, "lse": lse}
-    if leg == "backward":
-        w = WORKLOADS["bwd_bf16_b2h16_n4096_d128"]
+    if leg in BLOCKWISE_BWD:
+        w = WORKLOADS[BLOCKWISE_BWD[leg]]
         q, k, v, do = (t.to(dev) for t in workload_inputs(w))
         o, lse = at.attn_fwd(q, k, v, w.scale)
         grads = tuple(torch.empty((w.bh, w.n, w.d), dtype=torch.float32, device=dev)
@@ -921,21 +927,21 @@ def secondary(args, at, torch, dev):
             del ws2
         del fn, info, q, k, v, o, lse
         torch.cuda.empty_cache()
-    if want("backward"):
-        fn, w, info = leg_call("backward", at, torch, dev)
-        print(f"[bench] timing {w.name}", file=sys.stderr, flush=True)
+    for leg in (BLOCKWISE_BWD if want("backward") else ()):
+        fn, w, info = leg_call(leg, at, torch, dev)
+        print(f"[bench] timing blockwise backward {w.name}", file=sys.stderr, flush=True)
         ms, _, _ = time_launches(fn, args.steps, args.warmup, batch=True, warm_s=SECONDARY_WARM_S)
         fl = 10.0 * w.n * w.n * w.d * w.bh  # five n x n x d products, 2 n^2 d flops each
         m = info["m_elems"]
         # HBM floor: Q, K, V, dO (bf16), O, lse read, dQ, dK, dV (fp32) written
         floor = w.bh * (4 * w.n * w.d * 2 + w.n * w.d * 4 + w.n * 4 + 3 * w.n * w.d * 4)
-        res["backward"] = {
+        res[leg] = {
             "workload": w.name, "ms": round(ms, 4), "onchip_elems": m,
             "tflops_at_10N2d": round(fl / (ms * 1e-3) / 1e12, 2),
             "roofline": {"bound": "mfma", "achieved": round(fl / (ms * 1e-3) / 1e12, 2),
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
-            **leg_bytes("backward", ms, floor, theorem_1_1(w, m), with_roofline=False)}
+            **leg_bytes(leg, ms, floor, theorem_1_1(w, m), with_roofline=False)}
         del fn, info
         torch.cuda.empty_cache()
     for leg in (SMALLCACHE_BWD if want("smallcache_backward") else ()):
