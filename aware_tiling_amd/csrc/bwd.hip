@@ -83,38 +83,21 @@ __global__ __launch_bounds__(256) void bwd_preprocess(const float* __restrict__ 
 
 // ---------------------------------------------------------------------------
 // dK/dV and dQ kernels.  Tiles of Q and dO (dK/dV kernel) and of K and V
-// (dQ kernel) go global -> LDS with global_load_lds_dwordx4 and stay
-// row-major.  These copies are issued from inline assembly (dma16), so that
-// the next tile's copies stay in flight while the current tile is read (with
+// (dQ kernel) go global -> LDS with buffer_load_dwordx4 ... lds and stay
+// row-major.  These copies are issued from inline assembly, so that the
+// next tile's copies stay in flight while the current tile is read (with
 // compiler-visible copies in flight every wait for an LDS read becomes
-// lgkmcnt(0)) and are waited for only at the end of the step.  The
-// transposed operands (Q^T, dO^T, K^T) come from
-// ds_read_b64_tr_b16 on the same tiles, whose swizzle (dual_swizzle) keeps
-// both the row-wise and the transposed reads free of bank conflicts.  No
-// staging registers and no vector-ALU transposition, so two waves fit per
-// SIMD.  Rows past n are clamped to n-1 on load; the kernels give those rows
-// zero weight (lse = +inf for queries, explicit mask for keys).
+// lgkmcnt(0)) and are waited for only at the end of the step.  They go
+// through a buffer resource whose range ends at the head's last row, with
+// the tile start as a scalar offset: one code path for every tile, and rows
+// past n land as zeros, which the kernels give zero weight (lse = +inf for
+// queries, an explicit mask for keys).  The transposed operands (Q^T,
+// dO^T, K^T) come from ds_read_b64_tr_b16 on the same tiles, whose swizzle
+// (dual_swizzle) keeps both the row-wise and the transposed reads free of
+// bank conflicts.  No staging registers and no vector-ALU transposition, so
+// two waves fit per SIMD at d <= 128.
 
 namespace {
-
-template <int D, bool ASM = false>
-__device__ __forceinline__ void tile_load_lds(const bf16* src, bf16* dst, int t, int rows_per_tile,
-                                              int n, int wave, int lane, int wave_chunks,
-                                              int insts, bool dual) {
-  constexpr int CPR = D / 8;
-  const int rbase = t * rows_per_tile;
-  for (int it = 0; it < insts; ++it) {
-    const int p0 = wave * wave_chunks + it * 64;
-    const int p = p0 + lane;
-    const int logical = dual ? tile_copy_chunk<D, dual_swizzle<D * 2>>(p)
-                             : tile_copy_chunk<D, chunk_swizzle<D * 2>>(p);
-    const int grow = min(rbase + p / CPR, n - 1);
-    if constexpr (ASM)
-      dma16(src + (size_t)grow * D + logical * 8, dst + p0 * 8);
-    else
-      load_lds_16(src + (size_t)grow * D + logical * 8, dst + p0 * 8);
-  }
-}
 
 // Transposed A operand (32 rows of the d dimension x 16 rows of the tile)
 // from a row-major dual-swizzled tile: k-slots follow the score
@@ -242,26 +225,23 @@ __global__ __launch_bounds__(NW * 64, (D >= 256 ? 1 : 8 / NW)) void bwd_dkdv3(
       troff[db][piece] = (uint32_t)tile_elem<D, dual_swizzle<D * 2>>(
                              tr_read_row(lane, piece), db * 32 + tr_read_col(lane)) * 2u;
 
+  // Q and dO tiles through buffer resources over the head's n rows: rows
+  // past n land as zeros (and get lse = +inf below, so weight 0).
+  const rsrc_t rsQ = buffer_rsrc(Qh, (uint32_t)n * (D * 2));
+  const rsrc_t rsG = buffer_rsrc(dOh, (uint32_t)n * (D * 2));
+  const uint32_t tiles_lds = lds_addr(tiles);
   auto load = [&](int i, int stage) {
-    char* qdst = tiles + stage * 2 * TILE_B;
-    if ((i + 1) * BQ <= n) {
-      const char* qb = reinterpret_cast<const char*>(Qh) + (size_t)i * BQ * D * 2;
-      const char* gb = reinterpret_cast<const char*>(dOh) + (size_t)i * BQ * D * 2;
+    const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane(i * BQ) * (D * 2);
+    const uint32_t ql = tiles_lds + stage * 2 * TILE_B;
 #pragma unroll
-      for (int it = 0; it < C::INSTS; ++it) {
-        const int p0 = wave * C::WAVE_CHUNKS + it * 64;
-        dma16(qb + toff[it], qdst + p0 * 16);
-        dma16(gb + toff[it], qdst + TILE_B + p0 * 16);
-      }
-    } else {
-      tile_load_lds<D, true>(Qh, reinterpret_cast<bf16*>(qdst), i, BQ, n, wave, lane,
-                             C::WAVE_CHUNKS, C::INSTS, true);
-      tile_load_lds<D, true>(dOh, reinterpret_cast<bf16*>(qdst + TILE_B), i, BQ, n, wave, lane,
-                             C::WAVE_CHUNKS, C::INSTS, true);
+    for (int it = 0; it < C::INSTS; ++it) {
+      const uint32_t p0 = (uint32_t)(wave * C::WAVE_CHUNKS + it * 64) * 16;
+      dma16_buf_at(rsQ, toff[it], so, ql + p0);
+      dma16_buf_at(rsG, toff[it], so, ql + TILE_B + p0);
     }
     if (wave * 64 < 2 * BQ) {  // whole waves: 2 BQ is a multiple of 64
-      // A query row past n (a clamped copy of row n-1) gets lse2 = +inf, so
-      // its weights are exactly 0; its D stays finite.
+      // A query row past n (zeros in the Q and dO tiles) gets lse2 = +inf,
+      // so its weights are exactly 0; its D stays finite.
       float* st = stats + stage * 2 * BQ;
       const int which = tid / BQ, r = tid - which * BQ;
       const int qrow = min(i * BQ + r, n - 1);
@@ -485,22 +465,19 @@ __global__ __launch_bounds__(NW * 64, (D >= 256 ? 1 : 8 / NW)) void bwd_dq3(
     for (int piece = 0; piece < 2; ++piece)
       tk[db][piece] = (uint32_t)tile_elem<D, dual_swizzle<D * 2>>(
                           tr_read_row(lane, piece), db * 32 + tr_read_col(lane)) * 2u;
+  // K and V tiles through buffer resources over the head's n rows: rows
+  // past n land as zeros (those keys are masked below).
+  const rsrc_t rsK = buffer_rsrc(Kh, (uint32_t)n * (D * 2));
+  const rsrc_t rsV = buffer_rsrc(Vh, (uint32_t)n * (D * 2));
+  const uint32_t tiles_lds = lds_addr(tiles);
   auto load = [&](int j, int stage) {
-    char* kdst = tiles + stage * 2 * TILE_B;
-    if ((j + 1) * BC <= n) {
-      const char* kb = reinterpret_cast<const char*>(Kh) + (size_t)j * BC * D * 2;
-      const char* vb = reinterpret_cast<const char*>(Vh) + (size_t)j * BC * D * 2;
+    const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane(j * BC) * (D * 2);
+    const uint32_t kl = tiles_lds + stage * 2 * TILE_B;
 #pragma unroll
-      for (int it = 0; it < C::INSTS; ++it) {
-        const int p0 = wave * C::WAVE_CHUNKS + it * 64;
-        dma16(kb + koff[it], kdst + p0 * 16);
-        dma16(vb + voff[it], kdst + TILE_B + p0 * 16);
-      }
-    } else {
-      tile_load_lds<D, true>(Kh, reinterpret_cast<bf16*>(kdst), j, BC, n, wave, lane,
-                             C::WAVE_CHUNKS, C::INSTS, true);
-      tile_load_lds<D, true>(Vh, reinterpret_cast<bf16*>(kdst + TILE_B), j, BC, n, wave, lane,
-                             C::WAVE_CHUNKS, C::INSTS, false);
+    for (int it = 0; it < C::INSTS; ++it) {
+      const uint32_t p0 = (uint32_t)(wave * C::WAVE_CHUNKS + it * 64) * 16;
+      dma16_buf_at(rsK, koff[it], so, kl + p0);
+      dma16_buf_at(rsV, voff[it], so, kl + TILE_B + p0);
     }
   };
 
