@@ -560,27 +560,20 @@ __global__ __launch_bounds__(512, 1) void fwd_fused_bf16_pingpong_kernel(
     koff[it] = tile_copy_src<D, chunk_swizzle<D * 2>>(p);
     voff[it] = tile_copy_src<D, vtr_swizzle<D * 2>>(p);
   }
-  // Full tiles: wave-uniform tile base + per-lane offsets; a partial last
-  // tile clamps its rows to n-1.
-  auto load_tile = [&](const bf16* src, bf16* dst, int t, auto swz) {
-    const int kbase = t * BC;
-    const uint32_t* offs = decltype(swz)::is_v ? voff : koff;
-    if (kbase + BC <= n) {
-      const char* tb = reinterpret_cast<const char*>(src) + (size_t)kbase * (D * 2);
+  // Tile copies through one buffer resource per head (K, V) whose range
+  // ends at row n: the tile start is a scalar offset, and rows of a partial
+  // last tile past n land as zeros (their scores are masked, their values
+  // weigh 0).  Issued from inline assembly; each slot's copies are waited
+  // for before the barrier that ends it.
+  const rsrc_t rsK = buffer_rsrc(Kh, (uint32_t)n * (D * 2));
+  const rsrc_t rsV = buffer_rsrc(Vh, (uint32_t)n * (D * 2));
+  auto load_tile = [&](bf16* dst, int t, auto swz) {
+    const bool is_v = decltype(swz)::is_v;
+    const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane(t * BC) * (D * 2);
 #pragma unroll
-      for (int it = 0; it < C::INSTS; ++it)
-        load_lds_16(tb + offs[it], dst + (wave * C::WAVE_CHUNKS + it * 64) * 8);
-    } else {
-#pragma unroll
-      for (int it = 0; it < C::INSTS; ++it) {
-        const int p0 = wave * C::WAVE_CHUNKS + it * 64;
-        const int p = p0 + lane;
-        const int row = p / C::CPR, phys = p % C::CPR;
-        const int logical = phys ^ swz(row);
-        const int grow = min(kbase + row, n - 1);
-        load_lds_16(src + (size_t)grow * D + logical * 8, dst + p0 * 8);
-      }
-    }
+    for (int it = 0; it < C::INSTS; ++it)
+      dma16_buf(is_v ? rsV : rsK, is_v ? voff[it] : koff[it], so,
+                dst + (wave * C::WAVE_CHUNKS + it * 64) * 8);
   };
 
   f32x16 s[BC / 32][QB];
@@ -693,9 +686,9 @@ __global__ __launch_bounds__(512, 1) void fwd_fused_bf16_pingpong_kernel(
   };
 
   // Prologue: K_0, V_0, K_1; S_0 and P_0 in every wave.
-  load_tile(Kh, Kb, 0, kswz);
-  load_tile(Vh, Vb, 0, vswz);
-  if (nt > 1) load_tile(Kh, Kb + C::TILE, 1, kswz);
+  load_tile(Kb, 0, kswz);
+  load_tile(Vb, 0, vswz);
+  if (nt > 1) load_tile(Kb + C::TILE, 1, kswz);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   compute_s(Kb);
@@ -708,8 +701,8 @@ __global__ __launch_bounds__(512, 1) void fwd_fused_bf16_pingpong_kernel(
   // belong to slot 2j and their wait to the end of slot 2j+1; the group
   // branches below only place those.
   auto loads = [&](int j) {
-    if (j + 2 < nt) load_tile(Kh, Kb + (j & 1) * C::TILE, j + 2, kswz);
-    if (j + 1 < nt) load_tile(Vh, Vb + ((j + 1) & 1) * C::TILE, j + 1, vswz);
+    if (j + 2 < nt) load_tile(Kb + (j & 1) * C::TILE, j + 2, kswz);
+    if (j + 1 < nt) load_tile(Vb + ((j + 1) & 1) * C::TILE, j + 1, vswz);
   };
   if (grp == 1) {
     loads(0);
