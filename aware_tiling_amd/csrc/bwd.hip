@@ -522,17 +522,19 @@ __global__ __launch_bounds__(NW * 64, (D >= 256 ? 1 : 8 / NW)) void bwd_dq3(
         dp = mfma_bf16_32x32x16(use(2 * kk + 1), dogreg[kk], dp);
       }
       const int kbase = j * BC + kb * 32;
-      const bool tail = kbase + 32 > n;
+      // keys past n (zero rows of the tile) get s = -inf, so p = 0; one
+      // uniform branch for the block keeps the exponentials in one basic
+      // block with the MFMAs around them
+      if (kbase + 32 > n) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kbase + 8 * (r >> 2) + 4 * h + (r & 3) >= n) s[r] = -INFINITY;
+      }
       uint32_t dsk[8];
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        float p0 = fast_exp2(__builtin_fmaf(s[r], c, -l2));
-        float p1 = fast_exp2(__builtin_fmaf(s[r + 1], c, -l2));
-        if (tail) {
-          const int k0 = kbase + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (k0 >= n) p0 = 0.f;
-          if (k0 + 1 >= n) p1 = 0.f;
-        }
+        const float p0 = fast_exp2(__builtin_fmaf(s[r], c, -l2));
+        const float p1 = fast_exp2(__builtin_fmaf(s[r + 1], c, -l2));
         dsk[r >> 1] = pack_bf16x2(p0 * (dp[r] - dq_d), p1 * (dp[r + 1] - dq_d));
       }
       // dQ^T += K^T dS^T over these 32 keys.
