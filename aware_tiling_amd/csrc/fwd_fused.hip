@@ -375,7 +375,35 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
 
   const float lt = l + __shfl_xor(l, 32);
   const float inv = 1.0f / lt;
-  if (q < nq) {
+  if constexpr (D >= 256 && !SKIP && !LIST) {
+    // 1 KB output rows: each wave turns its 32 rows around in its quarter of
+    // the (now free) K/V ring, half a row (512 bytes) at a time, so that
+    // every store instruction writes two whole half-rows; 16-byte chunks are
+    // XOR-swizzled by row (row r's chunk c at c ^ r)
+    __syncthreads();  // every wave is done with the K/V ring
+    f32x4* const st = reinterpret_cast<f32x4*>(smem) + wave * 32 * 32;
+    const int qw = qblk * C::BR + wave * 32;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int db4 = 0; db4 < 4; ++db4)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int db = half * 4 + db4;
+          const int cidx = db4 * 8 + 2 * g + h;
+          st[li * 32 + (cidx ^ li)] = f32x4{uacc[db][4 * g + 0] * inv, uacc[db][4 * g + 1] * inv,
+                                            uacc[db][4 * g + 2] * inv, uacc[db][4 * g + 3] * inv};
+        }
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        const int idx = it * 64 + lane, r = idx >> 5, cidx = idx & 31;
+        const f32x4 v = st[r * 32 + (cidx ^ r)];
+        if (qw + r < nq)
+          *reinterpret_cast<f32x4*>(Oh + (size_t)(qw + r) * D + half * 128 + cidx * 4) = v;
+      }
+    }
+    if (q < nq && h == 0 && lseh != nullptr) lseh[q] = (m + __log2f(lt)) * kLn2;
+  } else if (q < nq) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
