@@ -113,6 +113,32 @@ __device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int ks, int db, i
   return __builtin_bit_cast(bf16x8, (u32x4{part[0][0], part[0][1], part[1][0], part[1][1]}));
 }
 
+// Stores 32 rows of D fp32 accumulators, times `mul`, whose lane (li, h)
+// holds row li, columns 32 db + 8 g + 4 h .. +3 in acc[db][4 g ..], through
+// the wave's LDS region `st` (32 rows of D / 4 16-byte chunks, chunk c of row
+// r at c ^ r), so that every store instruction writes whole rows; rows at or
+// past `rows` are not stored.  The caller has finished with that LDS.
+template <int D>
+__device__ __forceinline__ void store_rows_lds(const f32x16 (&acc)[D / 32], float mul, f32x4* st,
+                                               float* dst, int rows, int lane) {
+  constexpr int CPR = D / 4;
+  const int li = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = db * 8 + 2 * g + h;
+      st[li * CPR + (c ^ li)] = f32x4{acc[db][4 * g] * mul, acc[db][4 * g + 1] * mul,
+                                      acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul};
+    }
+#pragma unroll
+  for (int it = 0; it < 32 * CPR / 64; ++it) {
+    const int idx = it * 64 + lane, r = idx / CPR, c = idx % CPR;
+    const f32x4 v = st[r * CPR + (c ^ r)];
+    if (r < rows) *reinterpret_cast<f32x4*>(dst + (size_t)r * D + c * 4) = v;
+  }
+}
+
 template <int D>
 __device__ __forceinline__ bf16x8 row_operand(const bf16* tile, int row, int chunk, bool dual) {
   return *reinterpret_cast<const bf16x8*>(
@@ -371,7 +397,14 @@ __global__ __launch_bounds__(NW * 64, (D >= 256 ? 1 : 8 / NW)) void bwd_dkdv3(
   }
   if (i < nqt) step(std::integral_constant<int, 0>{}, i);
 
-  if (key < n) {
+  if constexpr (D >= 256) {
+    // 1 KB rows leave through LDS (whole rows per store instruction)
+    __syncthreads();  // every wave is done with the tiles, V rows and stats
+    f32x4* const st = reinterpret_cast<f32x4*>(smem) + wave * 32 * (D / 4);
+    const int k0 = kblk * C::BKV + wave * 32;
+    store_rows_lds<D>(dkt, scale, st, dK + hoff + (size_t)k0 * D, n - k0, lane);
+    store_rows_lds<D>(dvt, 1.f, st, dV + hoff + (size_t)k0 * D, n - k0, lane);
+  } else if (key < n) {
     float* dKr = dK + hoff + (size_t)key * D;
     float* dVr = dV + hoff + (size_t)key * D;
 #pragma unroll
@@ -561,7 +594,12 @@ __global__ __launch_bounds__(NW * 64, (D >= 256 ? 1 : 8 / NW)) void bwd_dq3(
   }
   if (j < nkt) step(std::integral_constant<int, 0>{}, j);
 
-  if (q < n) {
+  if constexpr (D >= 256) {
+    __syncthreads();  // every wave is done with the K and V tiles
+    f32x4* const st = reinterpret_cast<f32x4*>(tiles) + wave * 32 * (D / 4);
+    const int q0 = qblk * C::BQB + wave * 32;
+    store_rows_lds<D>(dqt, scale, st, dQ + hoff + (size_t)q0 * D, n - q0, lane);
+  } else if (q < n) {
     float* dQr = dQ + hoff + (size_t)q * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
