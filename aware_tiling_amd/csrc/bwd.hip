@@ -15,21 +15,23 @@
 // Three kernels, stream ordered:
 //  1. bwd_preprocess: D_i = <dO_i, O_i> and lse_i log2(e) into the
 //     workspace.
-//  2. bwd_dkdv3: one workgroup per (head, block of 256 keys), one wave per
-//     32 keys.  Each wave keeps its K rows as MFMA B operands and the
+//  2. bwd_dkdv3: one workgroup per (head, block of 256 keys; 128 at
+//     d = 256), one wave per 32 keys.  Each wave keeps its K rows as MFMA B operands and the
 //     transposed accumulators dK^T, dV^T (d x 32 keys) in registers, its V
 //     rows in LDS, and streams query tiles of Q, dO, lse, D through
 //     double-buffered LDS.  Scores are computed as S = Q K^T so that a lane
 //     owns one key: the bf16 P and dS tiles then feed dV^T += dO^T P and
 //     dK^T += Q^T dS straight from registers, with Q^T and dO^T read from
 //     the same row-major LDS tiles by transposing reads.
-//  3. bwd_dq3: one workgroup per (head, block of 256 queries), one wave per
-//     32 queries.  Each wave keeps Q and dO as B operands, lse and D as
+//  3. bwd_dq3: one workgroup per (head, block of 256 queries; 128 at
+//     d = 256), one wave per 32 queries.  Each wave keeps Q and dO as B operands, lse and D as
 //     per-lane scalars, and dQ^T in registers, and streams 64-key tiles of
 //     K and V through LDS: S^T = K Q^T, dP^T = V dO^T, dS^T, and
 //     dQ^T += K^T dS^T with K^T read transposed.  Recomputing S and dP here
 //     costs 4 N^2 d more flops than accumulating dQ with atomics, and keeps
 //     the result deterministic.
+// At d = 256 the gradients' 1 KB rows leave through LDS (store_rows_lds),
+// so that every store instruction writes whole rows.
 #include <algorithm>
 #include <cstring>
 #include <type_traits>
