@@ -227,7 +227,7 @@ attn_status attn_fwd_blocksparse(const void* Q, const void* K, const void* V, fl
                                  void* stream) {
   if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (!shape_ok(bh, n, d) || !scale_ok(scale)) return ATTN_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
   if (bh * n == 0) return ATTN_OK;
   if (!(mask_heads == 1 || mask_heads == bh) || !block_mask) return ATTN_ERR_INVALID_ARG;
   if (!Q || !K || !V || !O) return ATTN_ERR_INVALID_ARG;

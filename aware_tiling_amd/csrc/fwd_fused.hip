@@ -182,7 +182,7 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
   if constexpr (LIST) {
     const int row = (A.mask_heads == 1 ? 0 : head) * A.nqb + qblk;
     tlist = A.tiles + (size_t)row * A.tile_cap;
-    nt = A.counts[row];
+    nt = A.counts[row] * (64 / BC);  // listed tiles are 64 keys: 64 / BC tiles of BC each
     if (nt == 0) {
       if (q < nq) {
 #pragma unroll
@@ -198,11 +198,18 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
   }
   // first key of the t-th tile visited
   auto kbase_of = [&](int t) -> int {
-    if constexpr (LIST)
-      return __builtin_amdgcn_readfirstlane(tlist[t]) * BC;  // uniform: keeps the base scalar
-    else
+    if constexpr (LIST) {
+      constexpr int SUB = 64 / BC;  // BC-key tiles per listed 64-key tile
+      // uniform: keeps the base scalar
+      return __builtin_amdgcn_readfirstlane(tlist[t / SUB]) * 64 + (t % SUB) * BC;
+    } else {
       return t * BC;
+    }
   };
+  // The second half of the last listed tile can lie wholly past n: dropping
+  // it leaves the last tile visited as the only partial one.
+  if constexpr (LIST && BC < 64)
+    if (kbase_of(nt - 1) >= n) --nt;
 
   // Issue the copies of tile t of K or V into the LDS tile `dst`.  Lane
   // chunk p of this wave is LDS chunk (row, phys); it fetches logical chunk
@@ -375,7 +382,7 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
 
   const float lt = l + __shfl_xor(l, 32);
   const float inv = 1.0f / lt;
-  if constexpr (D >= 256 && !SKIP && !LIST) {
+  if constexpr (D >= 256) {
     // 1 KB output rows: each wave turns its 32 rows around in its quarter of
     // the (now free) K/V ring, half a row (512 bytes) at a time, so that
     // every store instruction writes two whole half-rows; 16-byte chunks are
@@ -430,7 +437,7 @@ fwd_fused_bf16_direct_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
 // [s kchunk, (s+1) kchunk) and writes its own normalised output and lse
 // (the partials that the merge kernel combines).
 template <int D, int NW, int BC>
-__global__ __launch_bounds__(NW * 64, (8 / NW > 0 ? 8 / NW : 1)) void fwd_split_bf16_kernel(
+__global__ __launch_bounds__(NW * 64, (D >= 256 ? 1 : (8 / NW > 0 ? 8 / NW : 1))) void fwd_split_bf16_kernel(
     const DirectArgs A) {
   direct_body<D, NW, BC, true, false>(A);
 }
@@ -438,7 +445,7 @@ __global__ __launch_bounds__(NW * 64, (8 / NW > 0 ? 8 / NW : 1)) void fwd_split_
 // Block-sparse entry: one workgroup per (head, 128-query block), visiting
 // the key tiles its tile list names.
 template <int D, int NW, int BC>
-__global__ __launch_bounds__(NW * 64, (8 / NW > 0 ? 8 / NW : 1)) void fwd_sparse_bf16_kernel(
+__global__ __launch_bounds__(NW * 64, (D >= 256 ? 1 : (8 / NW > 0 ? 8 / NW : 1))) void fwd_sparse_bf16_kernel(
     const DirectArgs A) {
   direct_body<D, NW, BC, false, true>(A);
 }
@@ -959,16 +966,21 @@ hipError_t launch_f32(const float* Q, const float* K, const float* V, float* O, 
 
 // Key-split (rectangular / decoding) forward: the direct kernel in its
 // SKIP form with four waves (128-row query blocks) when a head has at most
-// 128 queries, else eight.
+// 128 queries, else eight; at d = 256 always four waves (one per SIMD) and
+// 32-key tiles, the shape of the d = 256 fused forward.
 typedef void (*SplitKernel)(DirectArgs);
 
 template <int D>
 hipError_t launch_split(const void* Q, const void* K, const void* V, float* O, float* lse,
                         int64_t bh, int64_t nq, int64_t nk, float c, int64_t splits,
                         void* workspace, hipStream_t stream) {
-  const bool narrow = nq <= 128;
+  const bool narrow = D >= 256 || nq <= 128;
   const int nw = narrow ? 4 : 8;
-  const SplitKernel kern = narrow ? &fwd_split_bf16_kernel<D, 4, 64> : &fwd_split_bf16_kernel<D, 8, 64>;
+  SplitKernel kern;
+  if constexpr (D >= 256)
+    kern = &fwd_split_bf16_kernel<D, 4, 32>;
+  else
+    kern = narrow ? &fwd_split_bf16_kernel<D, 4, 64> : &fwd_split_bf16_kernel<D, 8, 64>;
   const int br = nw * 32;
   const int64_t kchunk = splitk_key_chunk(nk, splits);
   const int64_t eff = (nk + kchunk - 1) / kchunk;
@@ -1000,7 +1012,7 @@ hipError_t launch_split(const void* Q, const void* K, const void* V, float* O, f
 
 size_t align256_bytes(size_t b) { return (b + 255) / 256 * 256; }
 
-bool splitk_supported(int64_t d) { return d == 64 || d == 128; }
+bool splitk_supported(int64_t d) { return d == 64 || d == 128 || d == 256; }
 
 // Automatic chunk count.  The eight-wave form (more than 128 queries per
 // head) is bound by the matrix core and one workgroup fills a CU, so one
@@ -1043,6 +1055,7 @@ hipError_t launch_fwd_splitk_bf16(const void* Q, const void* K, const void* V, f
   switch (d) {
     case 64: return launch_split<64>(Q, K, V, O, lse, bh, nq, nk, c, splits, workspace, stream);
     case 128: return launch_split<128>(Q, K, V, O, lse, bh, nq, nk, c, splits, workspace, stream);
+    case 256: return launch_split<256>(Q, K, V, O, lse, bh, nq, nk, c, splits, workspace, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1128,6 +1141,10 @@ hipError_t launch_fwd_sparse_bf16(const void* Q, const void* K, const void* V, f
       break;
     case 128:
       hipLaunchKernelGGL((fwd_sparse_bf16_kernel<128, 4, 64>), dim3(total), dim3(256), 0, stream,
+                         args);
+      break;
+    case 256:  // four waves (one per SIMD), two 32-key tiles per listed tile
+      hipLaunchKernelGGL((fwd_sparse_bf16_kernel<256, 4, 32>), dim3(total), dim3(256), 0, stream,
                          args);
       break;
     default: return hipErrorInvalidValue;

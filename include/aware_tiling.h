@@ -198,7 +198,7 @@ int64_t attn_fwd_budget_onchip_elems(int64_t d);
  *             is used).  It holds the per-chunk o_s and lse_s; contents on
  *             return are unspecified.
  *   bh*nq == 0 is a no-op; nk must be >= 1 otherwise (ATTN_ERR_INVALID_ARG).
- *   bf16 only, d in {64, 128}.
+ *   bf16 only, d in {64, 128, 256}.
  */
 int64_t attn_fwd_splitk_splits(int64_t bh, int64_t nq, int64_t nk, int64_t d,
                                int64_t splits);
@@ -261,7 +261,7 @@ attn_status attn_fwd_splitk_noalloc(const void* Q, const void* K, const void* V,
  *                attn_fwd_blocksparse_workspace_size(bh, n, mask_heads)
  *                bytes, 256-byte aligned (per-row tile lists built from the
  *                mask on the device).  Contents on return unspecified.
- *   Other arguments as attn_fwd; bf16 only, d in {64, 128}.
+ *   Other arguments as attn_fwd; bf16 only, d in {64, 128, 256}.
  */
 #define ATTN_SPARSE_BLOCK 128
 size_t attn_fwd_blocksparse_workspace_size(int64_t bh, int64_t n,

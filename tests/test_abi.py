@@ -87,7 +87,7 @@ def test_splitk_noalloc_validation(lib):
     assert lib.attn_fwd_splitk_workspace_size(64, 200, 4096, 128, 16) > \
         binding.SPLITK_NOALLOC_SCRATCH_BYTES
     assert call(q=None) == INVALID
-    assert call(d=256) == UNSUPPORTED
+    assert call(d=96) == UNSUPPORTED
     assert call(dtype=F32) == UNSUPPORTED
     assert call(splits=300) == INVALID
     assert call(nk=0) == INVALID
@@ -300,7 +300,7 @@ def test_splitk_validation_and_sizes(lib):
     assert call(nk_=0) == INVALID  # softmax over no keys
     assert call(s=-1) == INVALID
     assert call(s=257) == INVALID
-    assert call(d_=256) == UNSUPPORTED
+    assert call(d_=96) == UNSUPPORTED
     assert call(dt=F32) == UNSUPPORTED
     assert call(scale=0.0) == INVALID
     assert call(q=None, o=None, nq_=0) == OK  # empty query set is a no-op
@@ -385,7 +385,7 @@ def test_blocksparse_validation_and_sizes(lib):
     assert call(q=None) == INVALID
     assert call(mask=None) == INVALID
     assert call(mh=2) == INVALID
-    assert call(d_=256) == UNSUPPORTED
+    assert call(d_=96) == UNSUPPORTED
     assert call(dt=F32) == UNSUPPORTED
     assert call(w=None) == WORKSPACE
     assert call(wsb=ws - 1) == WORKSPACE

@@ -49,6 +49,8 @@ CASES = [
     (2, 640, 64, 404, 1.0, 2, 0.35, False),
     (1, 257, 128, 405, 1.0, 1, 1.0, True),     # every block kept
     (1, 700, 128, 406, 20.0, 1, 0.5, True),    # peaked weights
+    (2, 333, 256, 407, 1.0, 1, 0.5, False),    # d = 256, last 64-key tile < 32 keys
+    (1, 300, 256, 408, 4.0, 1, 1.0, True),     # last 32 keys partial
 ]
 
 
@@ -117,7 +119,7 @@ def test_blocksparse_rejects_bad_arguments():
     (_, (q, k, v)) = inputs(1, 200, 128, "bf16", 410)
     with pytest.raises(ValueError):
         at.attn_fwd_blocksparse(q, k, v, torch.ones((1, 3, 3), dtype=torch.uint8, device="cuda"))
-    (_, (q2, k2, v2)) = inputs(1, 200, 256, "bf16", 411)
+    (_, (q2, k2, v2)) = inputs(1, 200, 96, "bf16", 411)
     with pytest.raises(at.AttnError):
         at.attn_fwd_blocksparse(q2, k2, v2, torch.ones((1, 2, 2), dtype=torch.uint8,
                                                        device="cuda"))

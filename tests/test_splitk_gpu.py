@@ -33,6 +33,8 @@ CASES = [
     (1, 5, 65, 64, 2, 208, 1.0),      # chunks of 64 and 1 keys
     (2, 5, 3000, 128, 9, 209, 20.0),  # peaked weights: chunk lse far apart
     (4, 129, 2048, 128, 16, 210, 1.0),
+    (2, 3, 1500, 256, 0, 214, 1.0),   # d = 256: four-wave kernel, 32-key steps
+    (1, 140, 333, 256, 3, 215, 4.0),  # d = 256, nq > 128, ragged chunks
 ]
 
 
@@ -107,7 +109,7 @@ def test_splitk_rejects_bad_arguments():
     (_, (q, k, v)) = _inputs(1, 4, 100, 128, 212, 1.0)
     with pytest.raises(at.AttnError):
         at.attn_fwd_splitk(q, k, v, 300)
-    (_, (q2, k2, v2)) = _inputs(1, 4, 100, 256, 213, 1.0)
+    (_, (q2, k2, v2)) = _inputs(1, 4, 100, 96, 213, 1.0)
     with pytest.raises(at.AttnError):
         at.attn_fwd_splitk(q2, k2, v2, 2)
     # no keys: undefined softmax, refused
