@@ -44,6 +44,7 @@
 namespace at {
 
 constexpr float kTau = 24.0f;
+constexpr float kSumLimit = 16777216.0f;  // 2^kTau
 
 template <int V>
 struct IntC {
@@ -137,6 +138,11 @@ struct DirectCfg {
 template <int D, int NW, int BC, bool SKIP = false, bool LIST = false>
 __device__ __forceinline__ void direct_body(const DirectArgs& A) {
   using C = DirectCfg<D, NW, BC>;
+  // Row maximum only when a tile's sum shows it moved (one wave per SIMD at
+  // d = 256, where the maximum's vector instructions are not hidden by a
+  // second wave's matrix work; with two waves per SIMD the test before the
+  // value product delays it more than the maximum costs).
+  constexpr bool LAZY = D >= 256;
   const float c = A.c;
   __shared__ __attribute__((aligned(1024))) bf16 smem[C::LDS_ELEMS];
   bf16* const Kb = smem;                // [2][TILE]
@@ -253,7 +259,8 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
         s[kb] = mfma_bf16_32x32x16(a, qreg[kk], s[kb]);
       }
   };
-  auto softmax_max = [&](f32x16 (&s)[BC / 32], bool mask, int kbase) {
+  // scores of keys past n (a partial last tile) to -inf
+  auto mask_keys = [&](f32x16 (&s)[BC / 32], bool mask, int kbase) {
     if (mask) {
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb)
@@ -261,6 +268,9 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
         for (int r = 0; r < 16; ++r)
           if (kbase + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3) >= n) s[kb][r] = -INFINITY;
     }
+  };
+  auto softmax_max = [&](f32x16 (&s)[BC / 32], bool mask, int kbase) {
+    mask_keys(s, mask, kbase);
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb)
@@ -279,7 +289,8 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
       for (int db = 0; db < D / 32; ++db) uacc[db] *= alpha;
     }
   };
-  auto softmax_exp = [&](const f32x16 (&s)[BC / 32], uint32_t (&pk)[BC / 32][8]) {
+  // P = exp2(c S - m) as packed bf16 and l plus the tile's sum of P
+  auto exps = [&](const f32x16 (&s)[BC / 32], uint32_t (&pk)[BC / 32][8]) -> float {
     float lsum = l;
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb)
@@ -291,6 +302,22 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
         pk[kb][r >> 1] = pp;
         lsum = add_bf16x2(pp, lsum);
       }
+    return lsum;
+  };
+  // The tile's exponentials, the maximum taken first (softmax_max) or, with
+  // LAZY, only when they show that it moved: every weight stays <= 2^kTau
+  // while m holds, so a tile sum above 2^kTau (or inf or NaN, as on the
+  // first tile, where m = -inf) is the only case that needs the maximum; the
+  // tile is then exponentiated again with the updated m.  Both orders give
+  // the same P, l and m.
+  auto softmax_exp = [&](f32x16 (&s)[BC / 32], uint32_t (&pk)[BC / 32][8]) {
+    float lsum = exps(s, pk);
+    if constexpr (LAZY) {
+      if (__builtin_amdgcn_ballot_w64(!(lsum - l <= kSumLimit)) != 0) {
+        softmax_max(s, false, 0);
+        lsum = exps(s, pk);
+      }
+    }
     l = lsum;
   };
   // U^T += V^T P^T with the V^T operand from transposed LDS reads
@@ -336,7 +363,7 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
     constexpr int P = decltype(par)::value;
     f32x16 s_next[BC / 32];
     if (active) {
-      softmax_max(s_cur, false, 0);
+      if constexpr (!LAZY) softmax_max(s_cur, false, 0);
       compute_s(Kb + (P ^ 1) * C::TILE, s_next);
       // issue each score MFMA's K read four MFMAs ahead of it
       constexpr int NS = (D / 16) * (BC / 32);
@@ -372,10 +399,12 @@ __device__ __forceinline__ void direct_body(const DirectArgs& A) {
   }
   if (active) {
     uint32_t pk[BC / 32][8];
-    if constexpr (LIST)
-      softmax_max(s_cur, kbase_of(j) + BC > n, kbase_of(j));
+    const int kbase = kbase_of(j);  // the last tile, partial if it runs past n
+    const bool mask = kbase + BC > n;
+    if constexpr (LAZY)
+      mask_keys(s_cur, mask, kbase);
     else
-      softmax_max(s_cur, (n % BC) != 0, j * BC);
+      softmax_max(s_cur, mask, kbase);
     softmax_exp(s_cur, pk);
     pv(Vb + (j & 1) * C::TILE, pk);
   }
