@@ -696,47 +696,62 @@ __global__ __launch_bounds__(512, 1) void fwd_fused_bf16_pingpong_kernel(
             for (int qb = 0; qb < QB; ++qb) s[kb][qb][r] = -INFINITY;
           }
     }
-    bool need_any = false;
-    float mn[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-      mx = pair_max_xor32(mx);
-      const float mc = mx * c;
-      const bool need = mc > m[qb] + kTau;
-      mn[qb] = need ? mc : m[qb];
-      need_any |= need;
-    }
-    // rare: some lane's maximum moved; lanes that keep m get alpha = 1
-    if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
+    // P against the current m; the row maximum is taken only when a tile
+    // sum above 2^kTau (or inf or NaN: the first tile, where m = -inf)
+    // shows that it may have moved, and the tile is then exponentiated
+    // again: the same P, l and m as with the maximum taken first
+    float lsum[QB];
+    auto exps = [&]() {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const float alpha = fast_exp2(m[qb] - mn[qb]);
-        m[qb] = mn[qb];
-        l[qb] *= alpha;
+        lsum[qb] = l[qb];
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) uacc[db][qb] *= alpha;
+        for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const float p0 = fast_exp2(__builtin_fmaf(s[kb][qb][r], c, -m[qb]));
+            const float p1 = fast_exp2(__builtin_fmaf(s[kb][qb][r + 1], c, -m[qb]));
+            const uint32_t pp = pack_bf16x2(p0, p1);
+            pk[kb][qb][r >> 1] = pp;
+            lsum[qb] = add_bf16x2(pp, lsum[qb]);
+          }
       }
-    }
+    };
+    exps();
+    bool over = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float lsum = l[qb];
+    for (int qb = 0; qb < QB; ++qb) over |= !(lsum[qb] - l[qb] <= kSumLimit);
+    if (__builtin_amdgcn_ballot_w64(over) != 0) {
+      bool need_any = false;
+      float mn[QB];
 #pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(__builtin_fmaf(s[kb][qb][r], c, -m[qb]));
-          const float p1 = fast_exp2(__builtin_fmaf(s[kb][qb][r + 1], c, -m[qb]));
-          const uint32_t pp = pack_bf16x2(p0, p1);
-          pk[kb][qb][r >> 1] = pp;
-          lsum = add_bf16x2(pp, lsum);
+        for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
+        mx = pair_max_xor32(mx);
+        const float mc = mx * c;
+        const bool need = mc > m[qb] + kTau;
+        mn[qb] = need ? mc : m[qb];
+        need_any |= need;
+      }
+      // lanes that keep m get alpha = 1
+      if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float alpha = fast_exp2(m[qb] - mn[qb]);
+          m[qb] = mn[qb];
+          l[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) uacc[db][qb] *= alpha;
         }
-      l[qb] = lsum;
+      }
+      exps();
     }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l[qb] = lsum[qb];
   };
   // Matrix phase X_j and vector phase Y_j.
   auto phase_x = [&](int j) {
