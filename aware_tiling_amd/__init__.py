@@ -5,7 +5,7 @@ from .binding import (SPARSE_BLOCK, AttnError, attn_bwd, attn_bwd_smallcache, at
                       attn_fwd_blocksparse, attn_fwd_budget, attn_fwd_smallcache,
                       attn_fwd_splitk, attn_fwd_splitk_noalloc, attn_fwd_tile, attn_bwd_tile,
                       bwd_onchip_elems, bwd_smallcache_tile, bwd_tile_info, bwd_tiles,
-                      calib_mfma_loop,
+                      calib_mfma_loop, calib_stream_read,
                       default_scale, fwd_budget_onchip_elems, fwd_onchip_elems,
                       fwd_query_block, fwd_tile_info, fwd_tiles, lib, smallcache_tile,
                       splitk_splits)
@@ -13,7 +13,7 @@ from .binding import (SPARSE_BLOCK, AttnError, attn_bwd, attn_bwd_smallcache, at
 __all__ = ["AttnError", "SPARSE_BLOCK", "attn_fwd", "attn_fwd_blocksparse", "attn_fwd_budget",
            "attn_fwd_splitk", "attn_fwd_splitk_noalloc", "attn_fwd_smallcache", "attn_fwd_tile", "attn_bwd",
            "attn_bwd_smallcache", "attn_bwd_tile", "bwd_onchip_elems", "bwd_smallcache_tile",
-           "bwd_tile_info", "bwd_tiles", "calib_mfma_loop",
+           "bwd_tile_info", "bwd_tiles", "calib_mfma_loop", "calib_stream_read",
            "default_scale",
            "fwd_budget_onchip_elems", "fwd_onchip_elems", "fwd_query_block", "fwd_tile_info",
            "fwd_tiles", "lib", "smallcache_tile", "splitk_splits"]

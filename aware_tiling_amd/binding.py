@@ -36,6 +36,7 @@ SIGNATURES = {
     "attn_fwd_budget": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _f32, _int, _i64, _vp]),
     "attn_fwd_budget_onchip_elems": (_i64, [_i64]),
     "attn_calib_mfma_loop": (_int, [_vp, _i64, ctypes.c_int32, _f32, _vp]),
+    "attn_calib_stream_read": (_int, [_vp, _i64, _vp, _i64, _vp]),
     "attn_fwd_splitk_splits": (_i64, [_i64, _i64, _i64, _i64, _i64]),
     "attn_fwd_splitk_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "attn_fwd_splitk": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _int, _i64,
@@ -295,6 +296,21 @@ def calib_mfma_loop(out: torch.Tensor, iters: int, amp: float = 1.0, stream=None
                                     _stream(out, stream))
     _check("attn_calib_mfma_loop", rc)
     return wgs * int(iters) * 4 * 4 * 2 * 32 * 32 * 16
+
+
+def calib_stream_read(src: torch.Tensor, out: torch.Tensor, stream=None) -> int:
+    """Calibration streaming read of all of src over out.numel() // 256
+    workgroups; returns the bytes it reads. src: contiguous CUDA tensor of a
+    multiple of 16 bytes; out: int32 CUDA tensor, one word per thread."""
+    if not _on_gpu(src) or not src.is_contiguous():
+        raise ValueError("src must be a contiguous CUDA tensor")
+    if out.dtype != torch.int32 or not _on_gpu(out) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int32 CUDA tensor")
+    nbytes = src.numel() * src.element_size()
+    rc = lib().attn_calib_stream_read(src.data_ptr(), nbytes, out.data_ptr(), out.numel() // 256,
+                                      _stream(out, stream))
+    _check("attn_calib_stream_read", rc)
+    return nbytes
 
 
 def splitk_splits(bh: int, nq: int, nk: int, d: int, splits: int = 0) -> int:

@@ -391,4 +391,13 @@ attn_status attn_calib_mfma_loop(float* out, int64_t workgroups, int32_t iters, 
       at::launch_calib_mfma_loop(out, workgroups, iters, amp, static_cast<hipStream_t>(stream)));
 }
 
+attn_status attn_calib_stream_read(const void* src, int64_t bytes, uint32_t* out,
+                                   int64_t workgroups, void* stream) {
+  if (!src || !aligned16(src) || bytes < 16 || bytes % 16 != 0 || !out || !aligned16(out) ||
+      workgroups < 1 || workgroups > INT32_MAX / 256)
+    return ATTN_ERR_INVALID_ARG;
+  return launch_status(at::launch_calib_stream_read(src, bytes, out, workgroups,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

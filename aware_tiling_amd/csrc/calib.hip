@@ -1,5 +1,6 @@
-// Calibration kernel: a matrix-core loop with no memory traffic, for the
-// reachable bf16 MFMA rate of the device (beside the published peak).
+// Calibration kernels, for rates this device reaches beside its published
+// peaks: a matrix-core loop with no memory traffic (bf16 MFMA rate) and a
+// streaming read (HBM read bandwidth).
 //
 // Every wave runs `iters` rounds of four independent accumulation chains of
 // v_mfma_f32_32x32x16_bf16 (the instruction the attention kernels use) on
@@ -48,6 +49,30 @@ hipError_t launch_calib_mfma_loop(float* out, int64_t workgroups, int iters, flo
                                   hipStream_t stream) {
   hipLaunchKernelGGL(calib_mfma_loop, dim3((unsigned)workgroups), dim3(256), 0, stream, out, iters,
                      amp);
+  return hipGetLastError();
+}
+
+// Streaming read: thread t of the grid reads the 16-byte chunks t, t + T,
+// t + 2T, ... (T threads in the grid) with non-temporal loads, so each
+// wave-load covers 1 KB of consecutive memory, and writes the XOR of what
+// it read (one word per thread, so the loads are not removed).
+__global__ __launch_bounds__(256) void calib_stream_read(const u32x4* __restrict__ src,
+                                                        int64_t chunks,
+                                                        uint32_t* __restrict__ out) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  uint32_t x = 0;
+  for (int64_t i = t; i < chunks; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(&src[i]);
+    x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  out[t] = x;
+}
+
+hipError_t launch_calib_stream_read(const void* src, int64_t bytes, uint32_t* out,
+                                    int64_t workgroups, hipStream_t stream) {
+  hipLaunchKernelGGL(calib_stream_read, dim3((unsigned)workgroups), dim3(256), 0, stream,
+                     static_cast<const u32x4*>(src), bytes / 16, out);
   return hipGetLastError();
 }
 

@@ -127,5 +127,8 @@ hipError_t launch_bwd_smallcache_bf16(const void* Q, const void* K, const void* 
 // Matrix-core loop for the reachable bf16 MFMA rate (calib.hip).
 hipError_t launch_calib_mfma_loop(float* out, int64_t workgroups, int iters, float amp,
                                   hipStream_t stream);
+// Streaming read for the reachable HBM read bandwidth (calib.hip).
+hipError_t launch_calib_stream_read(const void* src, int64_t bytes, uint32_t* out,
+                                    int64_t workgroups, hipStream_t stream);
 
 }  // namespace at

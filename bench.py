@@ -22,9 +22,11 @@ Reported (one JSON line on stdout):
                measured L2-miss bytes (traffic) / launch time;
   launch_ms_*  min, median, p90, max over the timed launches, and
                cold_launch_ms with L2 and MALL flushed by a 512 MB write;
-  measured_peaks  a library bf16 GEMM, a device copy and the library's
-               matrix-core loop (random and zero operands) on the same GPU,
-               the reachable rates beside the published peaks;
+  measured_peaks  a library bf16 GEMM, a device copy, the library's
+               matrix-core loop (random and zero operands) and its
+               streaming read (2 GiB) on the same GPU, the reachable rates
+               beside the published peaks (the decoding leg also reports
+               its bandwidth as a fraction of the streaming read);
   cpu_baseline the float64 oracle on the host cores, on a bounded sample of
                rows of the same workload (about 15 s of CPU work);
   secondary    the small-cache square-tile path (batch 1 x 8 heads, N 4096,
@@ -177,7 +179,8 @@ def measured_peaks(torch, dev, at=None) -> dict:
     (8192^3, torch.matmul), a 1 GiB device-to-device copy and, when the
     library is built, its matrix-core loop (the attention kernels' MFMA
     instruction on register operands, no memory traffic) with random bf16
-    operands and with zero operands, at two waves per SIMD."""
+    operands and with zero operands, at two waves per SIMD, and its
+    streaming read of 2 GiB (best of three grid sizes)."""
     loops = {}
     if at is not None:
         out = torch.empty(512 * 256, dtype=torch.float32, device=dev)
@@ -196,6 +199,17 @@ def measured_peaks(torch, dev, at=None) -> dict:
     dst = torch.empty_like(src)
     copy_ms, _, _ = time_launches(lambda: dst.copy_(src), 10, 3)
     del src, dst
+    if at is not None:
+        # streaming read of 2 GiB, the best of three grid sizes
+        src = torch.ones(2 * COPY_BYTES, dtype=torch.uint8, device=dev)
+        best = 0.0
+        for wgs in (1024, 2048, 4096):
+            out = torch.empty(wgs * 256, dtype=torch.int32, device=dev)
+            ms, _, _ = time_launches(lambda: at.calib_stream_read(src, out), 10, 3)
+            best = max(best, 2 * COPY_BYTES / (ms * 1e-3) / 1e9)
+            del out
+        loops["stream_read_gbps"] = round(best, 1)
+        del src
     torch.cuda.empty_cache()
     return {"gemm_bf16_tflops": round(2 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
             "copy_gbps": round(2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9, 1), **loops}
@@ -757,6 +771,10 @@ def main():
 
     if not args.no_secondary:
         out["secondary"] = secondary(args, at, torch, dev)
+        dec = out["secondary"].get("splitk_decode")
+        if dec is not None and "stream_read_gbps" in out["measured_peaks"]:
+            dec["frac_of_measured_stream_read"] = round(
+                dec["hbm_gbps"] / out["measured_peaks"]["stream_read_gbps"], 4)
 
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -436,6 +436,23 @@ attn_status attn_bwd_smallcache(const void* Q, const void* K, const void* V,
 attn_status attn_calib_mfma_loop(float* out, int64_t workgroups, int32_t iters, float amp,
                                  void* stream);
 
+/*
+ * attn_calib_stream_read -- calibration, not part of the attention method: a
+ * streaming read of `bytes` bytes of device memory, timed by the caller for
+ * the HBM read bandwidth this device reaches (the ceiling of the decoding
+ * path, which reads K and V once).  `workgroups` workgroups of 256 threads;
+ * thread t reads the 16-byte chunks t, t + T, t + 2T, ... (T = 256
+ * workgroups) with non-temporal loads and writes the XOR of their words.
+ *
+ *   src : bytes bytes (device, read; 16-byte aligned).
+ *   out : workgroups * 256 uint32 (device, written; 16-byte aligned).
+ *   ATTN_ERR_INVALID_ARG for a null or unaligned pointer, bytes not a
+ *   positive multiple of 16, or workgroups outside [1, 2^31 / 256).
+ *   Asynchronous on `stream`.
+ */
+attn_status attn_calib_stream_read(const void* src, int64_t bytes, uint32_t* out,
+                                   int64_t workgroups, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

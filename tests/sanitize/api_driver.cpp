@@ -119,6 +119,12 @@ int main() {
         for (float amp : {1.0f, 0.0f, NAN, INFINITY})
           for (size_t pi = 0; pi < ptrs.size(); ++pi)
             run([&] { return attn_calib_mfma_loop(static_cast<float*>(ptrs[pi]), wg, it, amp, nullptr); }, pi == 0);
+    for (int64_t wg : {(int64_t)-1, (int64_t)0, (int64_t)1, (int64_t)INT32_MAX / 256, (int64_t)INT32_MAX, BIG})
+      for (int64_t nb : {(int64_t)-16, (int64_t)0, (int64_t)8, (int64_t)16, (int64_t)1 << 20, ((int64_t)1 << 20) + 4, BIG})
+        for (size_t pi = 0; pi < ptrs.size(); ++pi)
+          for (size_t po = 0; po < ptrs.size(); ++po)
+            run([&] { return attn_calib_stream_read(ptrs[pi], nb, static_cast<uint32_t*>(ptrs[po]), wg, nullptr); },
+                pi == 0 && po == 0);
   }
   // empty problems: success without a launch, even with null pointers
   g_launch_result = hipSuccess;

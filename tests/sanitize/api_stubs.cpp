@@ -130,5 +130,6 @@ hipError_t launch_bwd_smallcache_bf16(const void*, const void*, const void*, con
   return launched();
 }
 hipError_t launch_calib_mfma_loop(float*, int64_t, int, float, hipStream_t) { return launched(); }
+hipError_t launch_calib_stream_read(const void*, int64_t, uint32_t*, int64_t, hipStream_t) { return launched(); }
 
 }  // namespace at

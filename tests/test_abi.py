@@ -404,3 +404,17 @@ def test_calib_mfma_loop_validation(lib):
     assert call(iters=0) == INVALID
     assert call(amp=float("nan")) == INVALID
     assert call(amp=float("inf")) == INVALID
+
+
+def test_calib_stream_read_validation(lib):
+    call = lambda src=FAKE, nb=1 << 20, out=FAKE, wgs=64: lib.attn_calib_stream_read(
+        src, nb, out, wgs, None)
+    assert call(src=None) == INVALID
+    assert call(src=FAKE + 8) == INVALID
+    assert call(nb=0) == INVALID
+    assert call(nb=-16) == INVALID
+    assert call(nb=(1 << 20) + 4) == INVALID
+    assert call(out=None) == INVALID
+    assert call(out=FAKE + 4) == INVALID
+    assert call(wgs=0) == INVALID
+    assert call(wgs=1 << 23) == INVALID
