@@ -148,9 +148,9 @@ attn_status attn_fwd_budget(const void* Q, const void* K, const void* V, float* 
 namespace {
 
 // Effective split count of attn_fwd_splitk, or 0 if the request is invalid.
-int64_t splitk_count(int64_t bh, int64_t nq, int64_t nk, int64_t splits) {
+int64_t splitk_count(int64_t bh, int64_t nq, int64_t nk, int64_t d, int64_t splits) {
   if (splits < 0 || splits > 256 || nk <= 0) return 0;
-  const int64_t req = splits == 0 ? at::splitk_auto_splits(bh, nq, nk) : splits;
+  const int64_t req = splits == 0 ? at::splitk_auto_splits(bh, nq, nk, d) : splits;
   return req;
 }
 
@@ -158,14 +158,14 @@ int64_t splitk_count(int64_t bh, int64_t nq, int64_t nk, int64_t splits) {
 
 int64_t attn_fwd_splitk_splits(int64_t bh, int64_t nq, int64_t nk, int64_t d, int64_t splits) {
   if (!shape_ok(bh, nq, d) || !shape_ok(bh, nk, d) || !at::splitk_supported(d)) return 0;
-  const int64_t req = splitk_count(bh, nq, nk, splits);
+  const int64_t req = splitk_count(bh, nq, nk, d, splits);
   return req ? at::splitk_effective_splits(nk, req) : 0;
 }
 
 size_t attn_fwd_splitk_workspace_size(int64_t bh, int64_t nq, int64_t nk, int64_t d,
                                       int64_t splits) {
   if (!shape_ok(bh, nq, d) || !shape_ok(bh, nk, d) || !at::splitk_supported(d)) return 0;
-  const int64_t req = splitk_count(bh, nq, nk, splits);
+  const int64_t req = splitk_count(bh, nq, nk, d, splits);
   return req ? at::splitk_workspace_bytes(bh, nq, nk, d, req) : 0;
 }
 
@@ -180,7 +180,7 @@ attn_status attn_fwd_splitk(const void* Q, const void* K, const void* V, float* 
   if (splits < 0 || splits > 256) return ATTN_ERR_INVALID_ARG;
   if (bh * nq == 0) return ATTN_OK;
   if (nk == 0) return ATTN_ERR_INVALID_ARG;  // softmax over no keys is undefined
-  const int64_t req = splitk_count(bh, nq, nk, splits);
+  const int64_t req = splitk_count(bh, nq, nk, d, splits);
   const int64_t eff = at::splitk_effective_splits(nk, req);
   if (eff * bh * ((nq + 127) / 128) >= (int64_t(1) << 31)) return ATTN_ERR_INVALID_ARG;
   if (!Q || !K || !V || !O) return ATTN_ERR_INVALID_ARG;
@@ -203,7 +203,7 @@ attn_status attn_fwd_splitk_noalloc(const void* Q, const void* K, const void* V,
   if (splits < 0 || splits > 256) return ATTN_ERR_INVALID_ARG;
   if (bh * nq == 0) return ATTN_OK;
   if (nk == 0) return ATTN_ERR_INVALID_ARG;
-  const int64_t req = splitk_count(bh, nq, nk, splits);
+  const int64_t req = splitk_count(bh, nq, nk, d, splits);
   const int64_t eff = at::splitk_effective_splits(nk, req);
   if (eff * bh * ((nq + 127) / 128) >= (int64_t(1) << 31)) return ATTN_ERR_INVALID_ARG;
   if (!Q || !K || !V || !O) return ATTN_ERR_INVALID_ARG;

@@ -466,7 +466,7 @@ fwd_fused_bf16_direct_kernel(const bf16* __restrict__ Q, const bf16* __restrict_
 // [s kchunk, (s+1) kchunk) and writes its own normalised output and lse
 // (the partials that the merge kernel combines).
 template <int D, int NW, int BC>
-__global__ __launch_bounds__(NW * 64, (D >= 256 ? 1 : (8 / NW > 0 ? 8 / NW : 1))) void fwd_split_bf16_kernel(
+__global__ __launch_bounds__(NW * 64, (D >= 256 ? 1 : (NW == 1 ? 2 : 8 / NW))) void fwd_split_bf16_kernel(
     const DirectArgs A) {
   direct_body<D, NW, BC, true, false>(A);
 }
@@ -1009,9 +1009,11 @@ hipError_t launch_f32(const float* Q, const float* K, const float* V, float* O, 
 }
 
 // Key-split (rectangular / decoding) forward: the direct kernel in its
-// SKIP form with four waves (128-row query blocks) when a head has at most
-// 128 queries, else eight; at d = 256 always four waves (one per SIMD) and
-// 32-key tiles, the shape of the d = 256 fused forward.
+// SKIP form with one wave and 32-key tiles when a head has at most 32
+// queries (decoding: a 32 KB K/V ring, so five workgroups share a CU and
+// no wave sits idle), four waves (128-row query blocks) up to 128 queries,
+// else eight; at d = 256 always four waves (one per SIMD) and 32-key tiles,
+// the shape of the d = 256 fused forward.
 typedef void (*SplitKernel)(DirectArgs);
 
 template <int D>
@@ -1019,12 +1021,15 @@ hipError_t launch_split(const void* Q, const void* K, const void* V, float* O, f
                         int64_t bh, int64_t nq, int64_t nk, float c, int64_t splits,
                         void* workspace, hipStream_t stream) {
   const bool narrow = D >= 256 || nq <= 128;
-  const int nw = narrow ? 4 : 8;
+  const bool single = D <= 128 && nq <= 32;
+  const int nw = single ? 1 : narrow ? 4 : 8;
   SplitKernel kern;
   if constexpr (D >= 256)
     kern = &fwd_split_bf16_kernel<D, 4, 32>;
   else
-    kern = narrow ? &fwd_split_bf16_kernel<D, 4, 64> : &fwd_split_bf16_kernel<D, 8, 64>;
+    kern = single   ? &fwd_split_bf16_kernel<D, 1, 32>
+           : narrow ? &fwd_split_bf16_kernel<D, 4, 64>
+                    : &fwd_split_bf16_kernel<D, 8, 64>;
   const int br = nw * 32;
   const int64_t kchunk = splitk_key_chunk(nk, splits);
   const int64_t eff = (nk + kchunk - 1) / kchunk;
@@ -1061,14 +1066,17 @@ bool splitk_supported(int64_t d) { return d == 64 || d == 128 || d == 256; }
 // Automatic chunk count.  The eight-wave form (more than 128 queries per
 // head) is bound by the matrix core and one workgroup fills a CU, so one
 // round of 256 workgroups is the target (more chunks only add merge
-// traffic); the four-wave form serves short query blocks (decoding), which
-// are bound by the K/V stream, and two rounds of its two-per-CU workgroups
-// (1024) keep the most loads in flight.  Measured on the decode and chunk
-// workloads: 4 and 2 chunks, the fastest of 1..64.
-int64_t splitk_auto_splits(int64_t bh, int64_t nq, int64_t nk) {
+// traffic); the four-wave form serves short query blocks, bound by the K/V
+// stream, where two rounds of its two-per-CU workgroups (1024) keep the most
+// loads in flight; the one-wave decoding form (at most 32 queries, d <= 128)
+// runs five workgroups per CU, and 512 of them (two per CU, the chunks
+// twice as long) were the fastest.  Measured on the decode and chunk
+// workloads: 2 and 2 chunks.
+int64_t splitk_auto_splits(int64_t bh, int64_t nq, int64_t nk, int64_t d) {
+  const bool single = d <= 128 && nq <= 32;
   const bool narrow = nq <= 128;
-  const int64_t br = narrow ? 128 : 256;
-  const int64_t target = narrow ? 1024 : 256;
+  const int64_t br = single ? 32 : narrow ? 128 : 256;
+  const int64_t target = single ? 512 : narrow ? 1024 : 256;
   const int64_t wgs = bh * ((nq + br - 1) / br);
   int64_t s = (target + wgs - 1) / wgs;
   s = std::min<int64_t>(s, (nk + 255) / 256);  // at least 256 keys per chunk

@@ -47,7 +47,7 @@ hipError_t launch_fwd_fused_f32(const float* Q, const float* K, const float* V, 
 // directly and needs no workspace.
 size_t align256_bytes(size_t b);
 bool splitk_supported(int64_t d);
-int64_t splitk_auto_splits(int64_t bh, int64_t nq, int64_t nk);
+int64_t splitk_auto_splits(int64_t bh, int64_t nq, int64_t nk, int64_t d);
 int64_t splitk_key_chunk(int64_t nk, int64_t splits);
 int64_t splitk_effective_splits(int64_t nk, int64_t splits);
 size_t splitk_workspace_bytes(int64_t bh, int64_t nq, int64_t nk, int64_t d, int64_t splits);

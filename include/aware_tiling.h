@@ -183,13 +183,17 @@ int64_t attn_fwd_budget_onchip_elems(int64_t d);
  * a chunk ("Softmax without storing the score matrix"): with lse_s and o_s
  * the log-sum-exp and normalised output of chunk s,
  *     lse = log sum_s exp(lse_s),   o = sum_s exp(lse_s - lse) o_s.
- * The result is the same function as attn_fwd (identical when nq == nk).
+ * The result is the same function as attn_fwd (bit for bit the same when
+ * nq == nk > 32 and one chunk is used: at most 32 queries with d <= 128 run
+ * a one-wave form with 32-key tiles, whose rounding order differs).
  *
  *   Q       : [bh, nq, d] bf16;  K, V : [bh, nk, d] bf16 (device, read only)
  *   O       : [bh, nq, d] float; lse : [bh, nq] float or NULL (as attn_fwd)
  *   splits  : requested chunk count, 1..256, or 0 for an automatic choice
  *             (one round of workgroups over the device for more than 128
- *             queries a head, two rounds for fewer; >= 256 keys a chunk).
+ *             queries a head, two rounds for fewer, 512 one-wave
+ *             workgroups for at most 32 queries with d <= 128; >= 256 keys
+ *             a chunk).
  *             Chunks are whole 64-key tiles, so fewer may be used; see
  *             attn_fwd_splitk_splits().
  *   workspace, workspace_bytes : device scratch of at least

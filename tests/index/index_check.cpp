@@ -280,6 +280,8 @@ int main() {
   check_fused_forward<64, 8, 64>("fwd d64 8x64");
   check_fused_forward<64, 4, 64>("fwd d64 4x64 (split, sparse)");
   check_fused_forward<128, 4, 64>("fwd d128 4x64 (split, sparse)");
+  check_fused_forward<64, 1, 32>("fwd d64 1x32 (decoding split)");
+  check_fused_forward<128, 1, 32>("fwd d128 1x32 (decoding split)");
   check_backward<128, 8>();
   check_backward<64, 8>();
   check_backward<256, 4>();

@@ -52,7 +52,7 @@ hipError_t launch_fwd_fused_f32(const float*, const float*, const float*, float*
 }
 size_t align256_bytes(size_t b) { return (b + 255) / 256 * 256; }
 bool splitk_supported(int64_t d) { return d == 64 || d == 128; }
-int64_t splitk_auto_splits(int64_t, int64_t, int64_t nk) { return nk > 1024 ? 4 : 1; }
+int64_t splitk_auto_splits(int64_t, int64_t, int64_t nk, int64_t) { return nk > 1024 ? 4 : 1; }
 int64_t splitk_key_chunk(int64_t nk, int64_t splits) {
   const int64_t per = (nk + splits - 1) / splits;
   return (per + 63) / 64 * 64;
