@@ -51,6 +51,7 @@ CASES = [
     (1, 700, 128, 406, 20.0, 1, 0.5, True),    # peaked weights
     (2, 333, 256, 407, 1.0, 1, 0.5, False),    # d = 256, last 64-key tile < 32 keys
     (1, 300, 256, 408, 4.0, 1, 1.0, True),     # last 32 keys partial
+    (1, 500, 256, 409, 20.0, 1, 0.5, True),    # d = 256, peaked weights
 ]
 
 

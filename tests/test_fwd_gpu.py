@@ -39,6 +39,7 @@ SMALL = [
     (2, 513, 128, "bf16", 28, 4.0),
     (1, 700, 64, "bf16", 29, 40.0),  # scores in the hundreds: max-rescaling path
     (1, 640, 128, "bf16", 30, 40.0),
+    (1, 500, 256, "bf16", 31, 40.0),  # d = 256: maximum taken only when a tile sum shows it moved
 ]
 
 

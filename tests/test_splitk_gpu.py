@@ -35,6 +35,8 @@ CASES = [
     (4, 129, 2048, 128, 16, 210, 1.0),
     (2, 3, 1500, 256, 0, 214, 1.0),   # d = 256: four-wave kernel, 32-key steps
     (1, 140, 333, 256, 3, 215, 4.0),  # d = 256, nq > 128, ragged chunks
+    (1, 40, 2000, 256, 5, 216, 20.0),  # d = 256, peaked weights
+    (3, 20, 1500, 64, 3, 217, 20.0),   # one-wave decoding form, peaked weights
 ]
 
 
